@@ -1,0 +1,41 @@
+"""Reference oracle for one block of the joint audio-video DiT.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+this package: only the test suite, the smoke check in ``__graft_entry__`` and
+the CPU-baseline leg of ``bench.py`` use it.  It shares no code with the HIP
+library and reads no value the library produced.
+
+The oracle is plain and slow on purpose: integer layout work in pure Python
+ints, floating-point stages in NumPy float64 with no intermediate rounding,
+each stage written as its textbook definition.  ``oracle.brute`` repeats every
+floating-point stage with explicit Python loops for tiny inputs.
+
+Sources (cited by title and section throughout):
+
+* [H3-NFT]     "DiffusionNFT on MiniMax H3: Open-Source RL Training for Joint
+               Audio-Video Generation" (gpts24.com news page).
+* [VeRL-Omni]  "多模态强化学习工程解析：VeRL-Omni 架构与 MiniMax-H3 训练实录"
+               (princepride.github.io, VeRL-Omni RL blog).
+* [vLLM-Omni]  "Joint Audio-Video Generation in Production: Architecture Deep
+               Dive into MiniMax-H3 and vLLM-Omni" (princepride.github.io,
+               vLLM-Omni blog, English).
+
+Readings where those pages leave a step open are listed in each function's
+docstring.  Pins for every function live in ``tests/test_oracle_*.py``.
+Parity of the pack order and of the RoPE pair convention is pinned by the
+stated readings only (the pages fix neither), see ``oracle.layout`` and
+``oracle.block.rope3d``.
+"""
+from .layout import (MOD_AUDIO, MOD_TEXT, MOD_VIDEO, SAMPLES_PER_AUDIO_TOKEN,
+                     SPATIAL_DOWNSAMPLE, TEMPORAL_DOWNSAMPLE, grid_from_media,
+                     pack_layout, request_length)
+from .block import (adaln_modulate, attention, attention_probs, block_forward,
+                    out_proj_gated, qkv_project, rope3d, rope_frequencies)
+
+__all__ = [
+    "MOD_VIDEO", "MOD_AUDIO", "MOD_TEXT", "SAMPLES_PER_AUDIO_TOKEN",
+    "SPATIAL_DOWNSAMPLE", "TEMPORAL_DOWNSAMPLE", "grid_from_media",
+    "pack_layout", "request_length", "adaln_modulate", "qkv_project",
+    "rope3d", "rope_frequencies", "attention", "attention_probs",
+    "out_proj_gated", "block_forward",
+]

@@ -1,0 +1,100 @@
+"""Pure-Python loop versions of every floating-point stage, for tiny inputs.
+
+Test infrastructure only.  Lists of Python floats, the math module and
+explicit loops: no NumPy.  Used to check oracle.block on N <= 16, D <= 16.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence
+
+
+def adaln(x: List[List[float]], modality, table, eps: float = 1e-6):
+    out = []
+    for i, row in enumerate(x):
+        d = len(row)
+        mu = sum(row) / d
+        var = sum((v - mu) ** 2 for v in row) / d
+        inv = 1.0 / math.sqrt(var + eps)
+        m = modality[i]
+        out.append([(row[c] - mu) * inv * (1.0 + table[m][1][c]) + table[m][0][c]
+                    for c in range(d)])
+    return out
+
+
+def linear(x, w, b=None):
+    out = []
+    for row in x:
+        r = []
+        for j, wr in enumerate(w):
+            acc = 0.0
+            for c in range(len(row)):
+                acc += row[c] * wr[c]
+            if b is not None:
+                acc += b[j]
+            r.append(acc)
+        out.append(r)
+    return out
+
+
+def rope(x, pos, n_heads, head_dim, sections, theta=10000.0):
+    out = [list(r) for r in x]
+    for i in range(len(x)):
+        for h in range(n_heads):
+            base = h * head_dim
+            off = 0
+            for a, s in enumerate(sections):
+                for j in range(s // 2):
+                    omega = theta ** (-2.0 * j / s)
+                    phi = pos[i][a] * omega
+                    u = x[i][base + off + 2 * j]
+                    w = x[i][base + off + 2 * j + 1]
+                    out[i][base + off + 2 * j] = u * math.cos(phi) - w * math.sin(phi)
+                    out[i][base + off + 2 * j + 1] = u * math.sin(phi) + w * math.cos(phi)
+                off += s
+    return out
+
+
+def attention(q, k, v, cu_seqlens, n_heads, head_dim, causal=False, scale=None):
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    n = len(q)
+    out = [[0.0] * (n_heads * head_dim) for _ in range(n)]
+    for s in range(len(cu_seqlens) - 1):
+        a, b = cu_seqlens[s], cu_seqlens[s + 1]
+        for i in range(a, b):
+            for h in range(n_heads):
+                base = h * head_dim
+                keys = [j for j in range(a, b) if (not causal or j <= i)]
+                sc = []
+                for j in keys:
+                    dot = 0.0
+                    for c in range(head_dim):
+                        dot += q[i][base + c] * k[j][base + c]
+                    sc.append(dot * scale)
+                mx = max(sc)
+                e = [math.exp(t - mx) for t in sc]
+                tot = sum(e)
+                for c in range(head_dim):
+                    acc = 0.0
+                    for jj, j in enumerate(keys):
+                        acc += e[jj] / tot * v[j][base + c]
+                    out[i][base + c] = acc
+    return out
+
+
+def block(x, modality, pos, cu_seqlens, table, w_qkv, w_o, n_heads, head_dim,
+          sections: Sequence[int], theta=10000.0, eps=1e-6, causal=False,
+          b_qkv=None, b_o=None):
+    d = len(x[0])
+    y = adaln(x, modality, table, eps)
+    qkv = linear(y, w_qkv, b_qkv)
+    q = [r[:d] for r in qkv]
+    k = [r[d:2 * d] for r in qkv]
+    v = [r[2 * d:] for r in qkv]
+    q = rope(q, pos, n_heads, head_dim, sections, theta)
+    k = rope(k, pos, n_heads, head_dim, sections, theta)
+    o = attention(q, k, v, cu_seqlens, n_heads, head_dim, causal)
+    z = linear(o, w_o, b_o)
+    return [[x[i][c] + table[modality[i]][2][c] * z[i][c] for c in range(d)]
+            for i in range(len(x))]
