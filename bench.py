@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark: one DiT block forward (attention half) at the full 58,758-token pack.
+
+A step is one dit_block_forward over the full-shape workload: AdaLN ->
+fused QKV -> 3D RoPE -> packed attention -> to_out.0 + gated residual, bf16
+with float32 accumulation, inputs resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is the block's algorithmic TFLOP/s; the
+attention kernel (85% of the block's FLOPs) is the dominant kernel for the
+roofline entry, timed with HIP events recorded by the library around each
+stage on the stream the kernels run on.  ``cpu_baseline`` times the float64
+oracle on a bounded row sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DiT-block ms + attention TFLOP/s at 58,758 tokens; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6       # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def block_flops(n_tokens, d, cu, causal=False):
+    """Algorithmic FLOPs: attention 4*D*(visible q,k pairs); QKV 6*N*D^2; out 2*N*D^2."""
+    pairs = 0
+    for a, b in zip(cu, cu[1:]):
+        L = b - a
+        pairs += L * (L + 1) // 2 if causal else L * L
+    attn = 4.0 * d * pairs
+    qkv = 6.0 * n_tokens * d * d
+    out = 2.0 * n_tokens * d * d
+    return attn, qkv, out
+
+
+def elementwise_bytes(n_tokens, d, elt=2):
+    """adaln: read x + write y (+ modality); rope: read+write q and k (+ positions)."""
+    adaln = n_tokens * (2 * d * elt + 1)
+    rope = n_tokens * (4 * d * elt + 12)
+    return adaln, rope
+
+
+def cpu_baseline(wl, inp, lay, rows_n: int):
+    """Oracle (float64 NumPy) on a bounded sample: every stage for `rows_n` query rows,
+    attention of those rows against all keys of their segment (synthetic k, v)."""
+    import oracle
+    import synth
+    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
+    rng_rows = np.random.Generator(np.random.PCG64(7)).choice(n, size=rows_n, replace=False)
+    rows = np.sort(rng_rows)
+    k_h = synth.normal_array((n, d), seed=901, dtype="bf16")
+    v_h = synth.normal_array((n, d), seed=902, dtype="bf16")
+    t0 = time.perf_counter()
+    y = oracle.adaln_modulate(inp.x, lay["modality"], inp.table, wl.eps, rows=rows)
+    qkv = oracle.qkv_project(y, inp.w_qkv)
+    q = np.zeros((n, d))
+    q[rows] = oracle.rope3d(qkv[:, :d], np.asarray(lay["pos"])[rows], H, Dh, wl.sections, wl.theta)
+    _ = oracle.rope3d(qkv[:, d:2 * d], np.asarray(lay["pos"])[rows], H, Dh, wl.sections, wl.theta)
+    o = oracle.attention(q, k_h, v_h, lay["cu_seqlens"], H, Dh, rows=rows)
+    _ = oracle.out_proj_gated(o, inp.w_o, inp.x, lay["modality"], inp.table, rows=rows)
+    dt = time.perf_counter() - t0
+    seg_len = {}
+    cu = lay["cu_seqlens"]
+    for a, b in zip(cu, cu[1:]):
+        for r in rows[(rows >= a) & (rows < b)]:
+            seg_len[int(r)] = b - a
+    flops = sum(4.0 * d * L + 8.0 * d * d for L in seg_len.values())
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s",
+                cores=len(os.sched_getaffinity(0)), kind="oracle",
+                sample=(f"{rows_n} random query rows of the full 58,758-token block through "
+                        f"every stage (attention against all keys of their segment), "
+                        f"float64 NumPy; {dt:.1f} s"),
+                seconds=dt)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="full", choices=["small", "medium", "full", "varlen"])
+    ap.add_argument("--causal", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-block", action="store_true",
+                    help="skip the per-stage standalone timings (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the block is measured on one MI355X).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import joint_audio_video_amd as jav
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
+    print(f"# bench: workload={wl.name} N={n} D={d} H={H} steps={args.steps} "
+          f"warmup={args.warmup}", file=sys.stderr, flush=True)
+    inp = synth.block_inputs(wl)
+    lay = jav.pack_layout([r.grid for r in wl.requests])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev)
+
+    x, w_qkv, w_o = bf(inp.x), bf(inp.w_qkv), bf(inp.w_o)
+    table = torch.from_numpy(inp.table).to(dev)
+    mod = torch.from_numpy(lay["modality"]).to(dev)
+    pos = torch.from_numpy(lay["pos"]).to(dev)
+    cu = torch.from_numpy(lay["cu_seqlens"]).to(dev)
+    ms_len = lay["max_seqlen"]
+    desc = jav.block_desc(jav.DIT_BF16, d, H, Dh, wl.sections, wl.theta, wl.eps,
+                          causal=args.causal)
+    out = torch.empty_like(x)
+    ws = torch.empty(jav.block_workspace_bytes(desc, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        jav.block_forward(desc, x, mod, pos, cu, ms_len, table, w_qkv, w_o, out=out,
+                          workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    jav.profile_enable(args.steps)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    stage_sum, ncalls = jav.profile_read()
+    jav.profile_enable(0)
+    ms_step = total_ms / args.steps
+    stage_ms = {s: v / max(ncalls, 1) for s, v in zip(jav.STAGES, stage_sum)}
+    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}",
+          file=sys.stderr, flush=True)
+
+    cu_list = lay["cu_seqlens"].tolist()
+    attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
+    blk_f = attn_f + qkv_f + out_f
+    adaln_b, rope_b = elementwise_bytes(n, d)
+    attn_tflops = attn_f / (stage_ms["attn"] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(blk_f / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, N(0,0.1) AdaLN table)",
+        "config": {
+            "workload": (f"{wl.name}: one DiT block, {n:,} packed tokens "
+                         + " + ".join(f"[video {r.t}x{r.h}x{r.w} + audio 2x{r.audio_per_ch} "
+                                      f"+ text {r.text_len}]" for r in wl.requests)
+                         + f", d_model {d}, {H} heads x {Dh}, "
+                         + ("causal" if args.causal else "bidirectional") + " attention"),
+            "n_tokens": n, "d_model": d, "n_heads": H, "head_dim": Dh,
+            "segments": len(cu_list) - 1, "causal": bool(args.causal),
+        },
+        "block_ms": round(ms_step, 4),
+        "block_frac_of_bf16_peak": round(blk_f / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "attention_ms": round(stage_ms["attn"], 4),
+        "attention_tflops": round(attn_tflops, 2),
+        "attention_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "qkv_tflops": round(qkv_f / (stage_ms["qkv"] * 1e-3) / 1e12, 2),
+        "out_proj_tflops": round(out_f / (stage_ms["out"] * 1e-3) / 1e12, 2),
+        "adaln_gbs": round(adaln_b / (stage_ms["adaln"] * 1e-3) / 1e9, 1),
+        "rope_gbs": round(rope_b / (stage_ms["rope"] * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "attn_bf16_kernel",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        import oracle
+        olay = oracle.pack_layout([r.grid for r in wl.requests])
+        cb = cpu_baseline(wl, inp, olay, args.cpu_rows)
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 6)
+        rec["cpu_baseline"] = cb
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

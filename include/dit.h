@@ -1,0 +1,261 @@
+/*
+ * dit.h -- C ABI of libdit: one block of the joint audio-video DiT (MiniMax-H3)
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by title and section:
+ *   [H3-NFT]    "DiffusionNFT on MiniMax H3: Open-Source RL Training for Joint
+ *               Audio-Video Generation" (gpts24.com news page).
+ *   [VeRL-Omni] "多模态强化学习工程解析：VeRL-Omni 架构与 MiniMax-H3 训练实录"
+ *               (princepride.github.io VeRL-Omni RL blog).
+ *   [vLLM-Omni] "Joint Audio-Video Generation in Production: Architecture Deep
+ *               Dive into MiniMax-H3 and vLLM-Omni" (princepride.github.io
+ *               vLLM-Omni blog, English).
+ *
+ * The block: per-modality AdaLN -> fused QKV projection -> 3D (t, h, w) RoPE on
+ * q and k -> softmax attention inside cu_seqlens segments -> output projection
+ * -> gated residual.  The FFN half of the layer is not part of this library.
+ *
+ * Conventions shared by every device entry point
+ * ----------------------------------------------
+ * Ownership.  The caller owns every buffer.  The library allocates no device
+ *   memory and keeps no per-call state (apart from the optional profiling
+ *   events, which the caller creates and frees through dit_profile_*).
+ * Execution.  Device entry points only enqueue work on `stream` (a
+ *   hipStream_t; NULL means the null stream) and never synchronise.  DIT_OK
+ *   means "validated and enqueued"; a fault inside a kernel surfaces at the
+ *   caller's next synchronisation.
+ * Layout.  Row-major, one token per row.  `ld_*` is the distance in elements
+ *   between consecutive rows.  In a q/k/v/o row, head h occupies columns
+ *   [h*head_dim, (h+1)*head_dim).  Weights are [out][in] (torch Linear): a
+ *   projection computes x W^T.
+ * Element types.  DIT_BF16: activations and weights are bfloat16 bit patterns
+ *   (uint16); arithmetic is float32; every bf16 store rounds to nearest even.
+ *   DIT_F32: everything float32.  The AdaLN table is float32 for both.
+ * Effective length.  `n_tokens` is the effective token count.  Rows at or past
+ *   n_tokens are never read or written, whatever the buffers' padded size, so
+ *   a caller trims alignment padding by passing the effective length and a
+ *   pointer offset, with no copy ([vLLM-Omni] section 6, "Boundary Trimming
+ *   for Packed Attention").  n_tokens == 0 is a no-op returning DIT_OK.
+ * Alignment.  Device pointers must be 16-byte aligned and every ld a multiple
+ *   of 16 bytes (8 bf16 or 4 f32 elements); otherwise DIT_EUNSUPPORTED.
+ * Errors.  Host-side argument checks return DIT_EINVAL / DIT_EUNSUPPORTED /
+ *   DIT_EWORKSPACE before anything is enqueued; a failed launch returns
+ *   DIT_EHIP.  dit_last_error() gives the calling thread's message for its
+ *   last non-OK status.  There is never a silent fallback to another path: a
+ *   combination a kernel does not implement is DIT_EUNSUPPORTED ([H3-NFT]
+ *   section "The Six Silent Failures" and [VeRL-Omni] section 5.2 ask for an
+ *   explicit error instead of a silent mis-registration).
+ * Device-array contents are a contract and are not checked on the hot path:
+ *   cu_seqlens[0] == 0, non-decreasing, cu_seqlens[n_seqs] == n_tokens, every
+ *   segment no longer than max_seqlen, every modality id < 3, positions >= 0.
+ *   dit_pack_layout() produces such arrays.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ABI_VERSION 1
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_EINVAL = 1,        /* bad argument (null pointer, inconsistent sizes, ...) */
+  DIT_EUNSUPPORTED = 2,  /* valid but not implemented (head_dim, alignment, ...) */
+  DIT_EWORKSPACE = 3,    /* workspace missing or too small */
+  DIT_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} dit_status;
+
+typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype;
+
+/* Modality ids of the packed sequence ([vLLM-Omni] section 3: each token
+ * carries a text / video / audio tag). */
+enum { DIT_MOD_VIDEO = 0, DIT_MOD_AUDIO = 1, DIT_MOD_TEXT = 2, DIT_NUM_MOD = 3 };
+
+/* Rows of the per-modality AdaLN table, float32 [DIT_NUM_MOD][3][d_model]. */
+enum { DIT_ADA_SHIFT = 0, DIT_ADA_SCALE = 1, DIT_ADA_GATE = 2 };
+
+int dit_abi_version(void);
+
+/* Message of the calling thread's last non-OK status ("" if none).  The
+ * string stays valid until the thread's next library call. */
+const char* dit_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Host-only integer layout (bit-exact)                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Media of one request: pixel frames and size, audio samples per stereo
+ * channel at 32 kHz, and text tokens. */
+typedef struct {
+  int32_t frames, height_px, width_px;
+  int64_t audio_samples_per_ch;
+  int32_t text_len;
+} dit_media;
+
+/* Token grid of one request: video latent grid t x h x w, audio latent tokens
+ * per channel, text tokens. */
+typedef struct {
+  int32_t t, h, w, audio_per_ch, text_len;
+} dit_grid;
+
+/* [H3-NFT] section "MiniMax H3 and Why Joint Audio-Video Generation
+ * Complicates RL Training": the video VAE compresses 16x in space and 4x in
+ * time (temporally causal) and a 1x2x2 patchify follows (32x in space); the
+ * audio VAE gives 40 latent tokens per second per channel of 32 kHz stereo
+ * audio (800 samples per token).  t = 1 + (frames - 1) / 4, h = height_px / 32,
+ * w = width_px / 32, audio_per_ch = audio_samples_per_ch / 800.  frames == 0,
+ * or a zero height or width, gives a request without video (t = h = w = 0).
+ * DIT_EINVAL for a null pointer, a negative count, (frames - 1) % 4 != 0,
+ * a size not a multiple of 32, or samples not a multiple of 800 (nothing is
+ * cropped or padded). */
+dit_status dit_grid_from_media(const dit_media* m, dit_grid* g);
+
+/* Pack n_reqs requests into one sequence ([vLLM-Omni] section 3, "Packed
+ * Sequences and Modality Identity Preservation"; order video, audio, text as
+ * in its section 1 pipeline table).  Per request: video rows in row-major
+ * (t, h, w) order (w fastest) with id DIT_MOD_VIDEO and position (t, h, w);
+ * then audio channel 0 frames k = 0..n-1, then channel 1 frames k = 0..n-1,
+ * id DIT_MOD_AUDIO, position (k, 0, 0); then text token j, id DIT_MOD_TEXT,
+ * position (j, 0, 0).  Positions restart at 0 in every request and modality.
+ * Outputs (host buffers, caller-owned): modality[capacity_tokens] (uint8),
+ * pos_thw[capacity_tokens][3] (int32), cu_seqlens[n_reqs + 1] (int32),
+ * *n_tokens, *max_seqlen.  DIT_EINVAL for null pointers, n_reqs < 1, a
+ * negative grid entry, or a total above capacity_tokens or INT32_MAX. */
+dit_status dit_pack_layout(const dit_grid* reqs, int32_t n_reqs,
+                           uint8_t* modality, int32_t* pos_thw, int32_t* cu_seqlens,
+                           int64_t capacity_tokens, int64_t* n_tokens,
+                           int32_t* max_seqlen);
+
+/* ------------------------------------------------------------------------ */
+/* Device stages (asynchronous on `stream`; all pointers device memory)      */
+/* ------------------------------------------------------------------------ */
+
+/* Per-modality adaptive LayerNorm ([H3-NFT] section on H3's architecture:
+ * AdaLN branches per modality whose outputs can be precomputed and cached;
+ * [VeRL-Omni] section 3: all modalities share AdaLN modulation).  For token i
+ * with m = modality[i]: LayerNorm over d_model (biased variance, no affine of
+ * its own), then y = xhat * (1 + table[m][SCALE]) + table[m][SHIFT].
+ * x: [n_tokens][ld_x]; modality: uint8 [n_tokens]; table: f32 [3][3][d_model];
+ * y: [n_tokens][ld_y], must not overlap x.  eps > 0 (1e-6 in the block).
+ * DIT_EINVAL: null pointer, d_model < 1, ld < d_model, eps <= 0, bad dtype.
+ * DIT_EUNSUPPORTED: d_model above 16384 or not a multiple of 8 (bf16) / 4 (f32). */
+dit_status adaln_modulate(dit_dtype dt, const void* x, int64_t ld_x,
+                          const uint8_t* modality, const float* table,
+                          void* y, int64_t ld_y, int64_t n_tokens, int32_t d_model,
+                          float eps, void* stream);
+
+/* 3D rotary position embedding of q and k, in place ([H3-NFT] section on
+ * H3's architecture: RoPE over time, height and width; [vLLM-Omni] section 3:
+ * positions per row, modality-independent position spaces).  head_dim splits
+ * into sections[0..2] (t, h, w) at offsets 0, s_t, s_t + s_h; inside section a
+ * the adjacent pair (x[o+2j], x[o+2j+1]) is rotated by phi = pos[a] *
+ * theta^(-2j / s_a): (u, w) -> (u cos phi - w sin phi, u sin phi + w cos phi).
+ * Every head is rotated alike; a pair with phi == 0 is left bit-identical.
+ * q: [n_tokens][ld_q], k: [n_tokens][ld_k] (may be strided views into one
+ * fused qkv buffer); pos_thw: int32 [n_tokens][3].  k may be NULL (q only).
+ * DIT_EINVAL: null q/pos, n_heads < 1, sections odd or not summing to
+ * head_dim, theta <= 0, ld < n_heads * head_dim.
+ * DIT_EUNSUPPORTED: head_dim not 64 or 128. */
+dit_status rope3d_apply(dit_dtype dt, void* q, int64_t ld_q, void* k, int64_t ld_k,
+                        const int32_t* pos_thw, int64_t n_tokens, int32_t n_heads,
+                        int32_t head_dim, const int32_t sections[3], float theta,
+                        void* stream);
+
+/* Softmax attention over a packed sequence ([vLLM-Omni] section 3: the
+ * kernel derives its mask from cu_seqlens, so a token attends only to keys of
+ * its own segment; section 1: audio and video share one attention context;
+ * [H3-NFT] "Limitations": the released weights use full attention).  Per
+ * segment [cu[s], cu[s+1]) and head h: o_i = sum_j softmax_j(scale q_i . k_j)
+ * v_j over keys j of the segment (j <= i too when causal != 0).
+ * q, k, v, o: [n_tokens][ld] with n_heads * head_dim columns used; o must not
+ * overlap q, k or v.  cu_seqlens: device int32 [n_seqs + 1].  softmax_scale
+ * 0 means 1/sqrt(head_dim).  Zero-length segments are allowed.
+ * DIT_EINVAL: null pointer, n_seqs < 1, max_seqlen < 1 with n_tokens > 0,
+ * n_heads < 1, ld too small, softmax_scale < 0.
+ * DIT_EUNSUPPORTED: head_dim not 64 or 128 (bf16 needs 128). */
+dit_status attn_packed(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                       int64_t ld_k, const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                       const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                       int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                       float softmax_scale, int32_t causal, void* stream);
+
+/* Fused QKV projection ([VeRL-Omni] section 5.2: the rollout side packs the Q,
+ * K and V projections into one matrix; [H3-NFT] names them to_q, to_k, to_v):
+ * qkv = y W_qkv^T (+ b_qkv).  w_qkv rows are to_q, then to_k, then to_v:
+ * [3 d_model][d_model]; b_qkv [3 d_model] or NULL; qkv: [n_tokens][ld_qkv]
+ * with columns [0, D) q, [D, 2D) k, [2D, 3D) v; must not overlap y.
+ * DIT_EINVAL: null pointer, ld too small.  DIT_EUNSUPPORTED: d_model not a
+ * multiple of 64. */
+dit_status qkv_project(dit_dtype dt, const void* y, int64_t ld_y, const void* w_qkv,
+                       const void* b_qkv, void* qkv, int64_t ld_qkv, int64_t n_tokens,
+                       int32_t d_model, void* stream);
+
+/* Output projection to_out.0 ([H3-NFT]) and gated residual with the gate row of
+ * the per-modality AdaLN table: out = x + table[m][GATE] * (o W_o^T + b_o).
+ * o: [n_tokens][ld_o] (heads side by side); w_o [d_model][d_model]; b_o
+ * [d_model] or NULL; x, out: [n_tokens][ld]; out may be x itself (in place),
+ * but must not otherwise overlap x or o.  Errors as qkv_project. */
+dit_status out_proj_gated(dit_dtype dt, const void* o, int64_t ld_o, const void* w_o,
+                          const void* b_o, const void* x, int64_t ld_x,
+                          const uint8_t* modality, const float* table, void* out,
+                          int64_t ld_out, int64_t n_tokens, int32_t d_model, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The whole attention half of the block                                      */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  dit_dtype dtype;
+  int32_t d_model, n_heads, head_dim;
+  int32_t rope_sections[3];   /* t, h, w; even, summing to head_dim */
+  float rope_theta;           /* 10000 */
+  float ln_eps;               /* 1e-6 */
+  float softmax_scale;        /* 0 => 1/sqrt(head_dim) */
+  int32_t causal;             /* 0: bidirectional inside each segment */
+} dit_block_desc;
+
+/* Bytes of scratch dit_block_forward needs: y [N][D] + qkv [N][3D] + o [N][D]
+ * elements, each region rounded up to 256 bytes.  0 for a bad descriptor. */
+size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
+
+/* x, out: [n_tokens][d_model] contiguous (out may equal x); modality, pos_thw,
+ * cu_seqlens as above (device); ada_table f32 [3][3][d_model]; w_qkv
+ * [3D][D]; w_o [D][D]; biases nullable; workspace: device, at least
+ * dit_block_workspace_bytes() bytes, 256-byte aligned.  Enqueues adaln_modulate
+ * -> qkv_project -> rope3d_apply -> attn_packed -> out_proj_gated on stream.
+ * Errors: those of the stages, plus DIT_EWORKSPACE. */
+dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
+                             const uint8_t* modality, const int32_t* pos_thw,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                             int64_t n_tokens, const float* ada_table,
+                             const void* w_qkv, const void* b_qkv,
+                             const void* w_o, const void* b_o,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Optional stage timing of dit_block_forward (measurement plumbing)         */
+/* ------------------------------------------------------------------------ */
+
+enum { DIT_STAGE_ADALN = 0, DIT_STAGE_QKV = 1, DIT_STAGE_ROPE = 2,
+       DIT_STAGE_ATTN = 3, DIT_STAGE_OUT = 4, DIT_NUM_STAGES = 5 };
+
+/* max_calls > 0: create HIP events for that many subsequent dit_block_forward
+ * calls (process-wide; each call records DIT_NUM_STAGES + 1 events on its
+ * stream).  max_calls == 0: stop recording and destroy the events. */
+dit_status dit_profile_enable(int32_t max_calls);
+
+/* Wait for the recorded events and write, per stage, the summed milliseconds
+ * over the *n_calls recorded calls into stage_ms[DIT_NUM_STAGES]; then reset
+ * the record (events are kept for reuse). */
+dit_status dit_profile_read(float* stage_ms, int32_t* n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

@@ -1,0 +1,291 @@
+"""joint_audio_video_amd: one block of the joint audio-video DiT on MI355X.
+
+Thin ctypes binding over ``libdit.so`` (the C ABI declared in
+``include/dit.h``).  This module only marshals arguments: every step of the
+block runs in the library's HIP kernels.  PyTorch supplies device memory and
+the current HIP stream.  If the library is missing this module raises at
+import; there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+# torch first: libdit binds to the HIP runtime torch has already loaded (one
+# HIP/HSA runtime per process), see build.py.
+import torch  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdit.so")
+
+DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EWORKSPACE, DIT_EHIP = range(5)
+DIT_F32, DIT_BF16 = 0, 1
+MOD_VIDEO, MOD_AUDIO, MOD_TEXT = 0, 1, 2
+STAGES = ("adaln", "qkv", "rope", "attn", "out")
+
+_STATUS_NAMES = {1: "DIT_EINVAL", 2: "DIT_EUNSUPPORTED", 3: "DIT_EWORKSPACE", 4: "DIT_EHIP"}
+
+EXPORTED = (
+    "dit_abi_version", "dit_last_error", "dit_grid_from_media", "dit_pack_layout",
+    "adaln_modulate", "rope3d_apply", "attn_packed", "qkv_project", "out_proj_gated",
+    "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
+)
+
+
+class DitError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Media(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("height_px", ctypes.c_int32),
+                ("width_px", ctypes.c_int32), ("audio_samples_per_ch", ctypes.c_int64),
+                ("text_len", ctypes.c_int32)]
+
+
+class _Grid(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("audio_per_ch", ctypes.c_int32), ("text_len", ctypes.c_int32)]
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("d_model", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_sections", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
+                ("ln_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("causal", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m joint_audio_video_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    sig = {
+        "dit_abi_version": (ctypes.c_int, []),
+        "dit_last_error": (ctypes.c_char_p, []),
+        "dit_grid_from_media": (ctypes.c_int, [ctypes.POINTER(_Media), ctypes.POINTER(_Grid)]),
+        "dit_pack_layout": (ctypes.c_int, [ctypes.POINTER(_Grid), I32, P, P, P, I64,
+                                           ctypes.POINTER(I64), ctypes.POINTER(I32)]),
+        "adaln_modulate": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, F32, P]),
+        "rope3d_apply": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, I32, I32,
+                                        ctypes.POINTER(I32), F32, P]),
+        "attn_packed": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P, I32, I32,
+                                       I64, I32, I32, F32, I32, P]),
+        "qkv_project": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, P]),
+        "out_proj_gated": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, P, P, P, I64, I64,
+                                          I32, P]),
+        "dit_block_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
+        "dit_block_forward": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32, I32,
+                                             I64, P, P, P, P, P, P, SZ, P]),
+        "dit_profile_enable": (ctypes.c_int, [I32]),
+        "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return _lib.dit_abi_version()
+
+
+def last_error() -> str:
+    return _lib.dit_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != DIT_OK:
+        raise DitError(status, last_error())
+
+
+# ---------------------------------------------------------------------------
+# host layout
+# ---------------------------------------------------------------------------
+
+def grid_from_media(frames: int, height_px: int, width_px: int, audio_samples_per_ch: int,
+                    text_len: int) -> Tuple[int, int, int, int, int]:
+    m = _Media(frames, height_px, width_px, audio_samples_per_ch, text_len)
+    g = _Grid()
+    _check(_lib.dit_grid_from_media(ctypes.byref(m), ctypes.byref(g)))
+    return (g.t, g.h, g.w, g.audio_per_ch, g.text_len)
+
+
+def pack_layout(grids: Sequence[Sequence[int]], capacity: Optional[int] = None) -> dict:
+    """Returns dict(modality uint8[N], pos int32[N][3], cu_seqlens int32[R+1], max_seqlen, n_tokens)."""
+    n = len(grids)
+    arr = (_Grid * max(n, 1))(*[_Grid(*map(int, g)) for g in grids])
+    if capacity is None:
+        capacity = sum(max(0, g[0] * g[1] * g[2]) + 2 * max(0, g[3]) + max(0, g[4])
+                       for g in grids)
+    cap = max(int(capacity), 1)
+    mod = np.zeros(cap, dtype=np.uint8)
+    pos = np.zeros((cap, 3), dtype=np.int32)
+    cu = np.zeros(n + 1, dtype=np.int32)
+    nt = ctypes.c_int64(0)
+    ms = ctypes.c_int32(0)
+    _check(_lib.dit_pack_layout(arr, n, mod.ctypes.data, pos.ctypes.data, cu.ctypes.data,
+                                int(capacity), ctypes.byref(nt), ctypes.byref(ms)))
+    k = nt.value
+    return dict(modality=mod[:k], pos=pos[:k], cu_seqlens=cu, max_seqlen=ms.value, n_tokens=k)
+
+
+# ---------------------------------------------------------------------------
+# device stages (torch tensors in, results written in place / into `out`)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DIT_BF16
+    if t.dtype == torch.float32:
+        return DIT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _rows(t) -> Tuple[int, int]:
+    """(pointer, ld) of a 2-D row-major view with unit column stride."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.data_ptr(), t.stride(0)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def adaln_modulate(x, modality, table, eps: float = 1e-6, out=None, n_tokens=None,
+                   stream=None):
+    """y = LN(x) * (1 + table[m][1]) + table[m][0] per token (libdit adaln_modulate)."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    d = x.shape[1]
+    if out is None:
+        out = torch.empty((x.shape[0], d), dtype=x.dtype, device=x.device)
+    px, ldx = _rows(x)
+    py, ldy = _rows(out)
+    _check(_lib.adaln_modulate(_dtype_code(x), px, ldx, modality.data_ptr(), table.data_ptr(),
+                               py, ldy, n, d, float(eps), _stream(stream)))
+    return out
+
+
+def rope3d_apply(q, k, pos, n_heads: int, head_dim: int, sections: Sequence[int],
+                 theta: float = 10000.0, n_tokens=None, stream=None):
+    """Rotate q (and k, unless None) in place (libdit rope3d_apply)."""
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    pq, ldq = _rows(q)
+    pk, ldk = (0, 0) if k is None else _rows(k)
+    sec = (ctypes.c_int32 * 3)(*[int(s) for s in sections])
+    _check(_lib.rope3d_apply(_dtype_code(q), pq, ldq, pk, ldk, pos.data_ptr(), n, n_heads,
+                             head_dim, sec, float(theta), _stream(stream)))
+
+
+def attn_packed(q, k, v, cu_seqlens, max_seqlen: int, n_heads: int, head_dim: int,
+                softmax_scale: float = 0.0, causal: bool = False, out=None, n_tokens=None,
+                stream=None):
+    """Packed-sequence softmax attention (libdit attn_packed)."""
+    torch = _torch()
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    if out is None:
+        out = torch.empty((q.shape[0], n_heads * head_dim), dtype=q.dtype, device=q.device)
+    pq, ldq = _rows(q)
+    pk, ldk = _rows(k)
+    pv, ldv = _rows(v)
+    po, ldo = _rows(out)
+    n_seqs = cu_seqlens.numel() - 1
+    _check(_lib.attn_packed(_dtype_code(q), pq, ldq, pk, ldk, pv, ldv, po, ldo,
+                            cu_seqlens.data_ptr(), n_seqs, int(max_seqlen), n, n_heads,
+                            head_dim, float(softmax_scale), int(bool(causal)), _stream(stream)))
+    return out
+
+
+def qkv_project(y, w_qkv, b_qkv=None, out=None, n_tokens=None, stream=None):
+    """qkv = y W_qkv^T (+ b) (libdit qkv_project)."""
+    torch = _torch()
+    n = y.shape[0] if n_tokens is None else int(n_tokens)
+    d = y.shape[1]
+    if out is None:
+        out = torch.empty((y.shape[0], 3 * d), dtype=y.dtype, device=y.device)
+    py, ldy = _rows(y)
+    po, ldo = _rows(out)
+    _check(_lib.qkv_project(_dtype_code(y), py, ldy, w_qkv.data_ptr(), _ptr(b_qkv), po, ldo, n,
+                            d, _stream(stream)))
+    return out
+
+
+def out_proj_gated(o, w_o, x, modality, table, b_o=None, out=None, n_tokens=None, stream=None):
+    """out = x + table[m][2] * (o W_o^T + b) (libdit out_proj_gated)."""
+    torch = _torch()
+    n = o.shape[0] if n_tokens is None else int(n_tokens)
+    d = w_o.shape[0]
+    if out is None:
+        out = torch.empty((x.shape[0], d), dtype=x.dtype, device=x.device)
+    po, ldo = _rows(o)
+    px, ldx = _rows(x)
+    pout, ldout = _rows(out)
+    _check(_lib.out_proj_gated(_dtype_code(o), po, ldo, w_o.data_ptr(), _ptr(b_o), px, ldx,
+                               modality.data_ptr(), table.data_ptr(), pout, ldout, n, d,
+                               _stream(stream)))
+    return out
+
+
+def block_desc(dtype_code: int, d_model: int, n_heads: int, head_dim: int,
+               sections: Sequence[int], theta: float = 10000.0, eps: float = 1e-6,
+               softmax_scale: float = 0.0, causal: bool = False) -> BlockDesc:
+    return BlockDesc(dtype_code, d_model, n_heads, head_dim, (ctypes.c_int32 * 3)(*sections),
+                     theta, eps, softmax_scale, int(bool(causal)))
+
+
+def block_workspace_bytes(desc: BlockDesc, n_tokens: int) -> int:
+    return int(_lib.dit_block_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def block_forward(desc: BlockDesc, x, modality, pos, cu_seqlens, max_seqlen: int, table, w_qkv,
+                  w_o, b_qkv=None, b_o=None, out=None, workspace=None, n_tokens=None,
+                  stream=None):
+    """The attention half of one DiT block (libdit dit_block_forward)."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    if out is None:
+        out = torch.empty_like(x)
+    need = block_workspace_bytes(desc, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(_lib.dit_block_forward(ctypes.byref(desc), x.data_ptr(), out.data_ptr(),
+                                  modality.data_ptr(), pos.data_ptr(), cu_seqlens.data_ptr(),
+                                  cu_seqlens.numel() - 1, int(max_seqlen), n, table.data_ptr(),
+                                  w_qkv.data_ptr(), _ptr(b_qkv), w_o.data_ptr(), _ptr(b_o),
+                                  workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+def profile_enable(max_calls: int) -> None:
+    _check(_lib.dit_profile_enable(int(max_calls)))
+
+
+def profile_read() -> Tuple[List[float], int]:
+    """Summed per-stage milliseconds of the recorded dit_block_forward calls, and their count."""
+    ms = (ctypes.c_float * len(STAGES))()
+    n = ctypes.c_int32(0)
+    _check(_lib.dit_profile_read(ms, ctypes.byref(n)))
+    return list(ms), n.value

@@ -1,0 +1,396 @@
+// C ABI shell of libdit: argument validation, error text, workspace carving,
+// stage dispatch and optional stage timing.  All compute runs in the HIP
+// kernels of this directory; nothing here touches tensor data.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+#include "dit.h"
+#include "errors.h"
+
+namespace dit {
+
+char* error_buffer() {
+  static thread_local char buf[512] = {0};
+  return buf;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elt_size(dit_dtype dt) { return dt == DIT_BF16 ? 2 : 4; }
+
+bool dtype_ok(dit_dtype dt) { return dt == DIT_BF16 || dt == DIT_F32; }
+
+// ld counts elements; rows must start on 16-byte boundaries.
+bool ld_aligned(dit_dtype dt, int64_t ld) { return (ld * (int64_t)elt_size(dt)) % 16 == 0; }
+
+dit_status hip_fail(hipError_t e, const char* what) {
+  return fail(DIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- optional stage timing ----
+struct Profiler {
+  std::mutex mu;
+  int max_calls = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;   // max_calls * (DIT_NUM_STAGES + 1)
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+// Returns the event array for one call, or nullptr when not recording.
+hipEvent_t* prof_slot() {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  if (p.max_calls == 0 || p.used >= p.max_calls) return nullptr;
+  return &p.ev[(size_t)(p.used++) * (DIT_NUM_STAGES + 1)];
+}
+
+dit_status check_stream_rows(int64_t n_tokens) {
+  if (n_tokens < 0) return fail(DIT_EINVAL, "n_tokens < 0");
+  if (n_tokens > INT32_MAX) return fail(DIT_EUNSUPPORTED, "n_tokens above 2^31-1");
+  return DIT_OK;
+}
+
+// Rope frequencies theta^(-2j/s_a) for every pair of a head, in double.
+void rope_freqs(const int32_t* sec, double theta, int head_dim, double* out) {
+  int p = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < sec[a] / 2; ++j) out[p++] = std::pow(theta, -2.0 * j / (double)sec[a]);
+  (void)head_dim;
+}
+
+}  // namespace
+}  // namespace dit
+
+using namespace dit;
+
+extern "C" int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+extern "C" const char* dit_last_error(void) { return error_buffer(); }
+
+// ---------------------------------------------------------------------------
+
+static dit_status adaln_check(dit_dtype dt, const void* x, int64_t ld_x, const uint8_t* modality,
+                              const float* table, void* y, int64_t ld_y, int64_t n_tokens,
+                              int32_t d_model, float eps) {
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "adaln_modulate: unknown dtype %d", (int)dt);
+  if (!x || !modality || !table || !y) return fail(DIT_EINVAL, "adaln_modulate: null pointer");
+  if (d_model < 1) return fail(DIT_EINVAL, "adaln_modulate: d_model < 1");
+  if (ld_x < d_model || ld_y < d_model) return fail(DIT_EINVAL, "adaln_modulate: ld < d_model");
+  if (!(eps > 0.0f)) return fail(DIT_EINVAL, "adaln_modulate: eps must be > 0");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  const int per_vec = dt == DIT_BF16 ? 8 : 4;
+  const int max_d = dt == DIT_BF16 ? 16384 : 8192;
+  if (d_model % per_vec != 0 || d_model > max_d)
+    return fail(DIT_EUNSUPPORTED, "adaln_modulate: d_model %d unsupported", d_model);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(table) || !ld_aligned(dt, ld_x) ||
+      !ld_aligned(dt, ld_y))
+    return fail(DIT_EUNSUPPORTED, "adaln_modulate: pointers/ld must be 16-byte aligned");
+  return DIT_OK;
+}
+
+extern "C" dit_status adaln_modulate(dit_dtype dt, const void* x, int64_t ld_x,
+                                     const uint8_t* modality, const float* table, void* y,
+                                     int64_t ld_y, int64_t n_tokens, int32_t d_model, float eps,
+                                     void* stream) {
+  clear_error();
+  if (dit_status st = adaln_check(dt, x, ld_x, modality, table, y, ld_y, n_tokens, d_model, eps))
+    return st;
+  if (n_tokens == 0) return DIT_OK;
+  hipError_t e = launch_adaln(dt == DIT_BF16, x, ld_x, modality, table, y, ld_y, n_tokens,
+                              d_model, eps, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "adaln_modulate launch");
+}
+
+// ---------------------------------------------------------------------------
+
+static dit_status rope_check(dit_dtype dt, void* q, int64_t ld_q, void* k, int64_t ld_k,
+                             const int32_t* pos, int64_t n_tokens, int32_t n_heads,
+                             int32_t head_dim, const int32_t* sec, float theta) {
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "rope3d_apply: unknown dtype %d", (int)dt);
+  if (!q || !pos || !sec) return fail(DIT_EINVAL, "rope3d_apply: null pointer");
+  if (n_heads < 1 || head_dim < 1) return fail(DIT_EINVAL, "rope3d_apply: n_heads/head_dim < 1");
+  for (int a = 0; a < 3; ++a)
+    if (sec[a] < 0 || sec[a] % 2 != 0)
+      return fail(DIT_EINVAL, "rope3d_apply: section %d = %d must be even and >= 0", a, sec[a]);
+  if (sec[0] + sec[1] + sec[2] != head_dim)
+    return fail(DIT_EINVAL, "rope3d_apply: sections sum to %d, head_dim is %d",
+                sec[0] + sec[1] + sec[2], head_dim);
+  if (!(theta > 0.0f)) return fail(DIT_EINVAL, "rope3d_apply: theta must be > 0");
+  const int64_t width = (int64_t)n_heads * head_dim;
+  if (ld_q < width || (k && ld_k < width)) return fail(DIT_EINVAL, "rope3d_apply: ld too small");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(DIT_EUNSUPPORTED, "rope3d_apply: head_dim %d (64 or 128 only)", head_dim);
+  if (!aligned16(q) || !ld_aligned(dt, ld_q) || (k && (!aligned16(k) || !ld_aligned(dt, ld_k))))
+    return fail(DIT_EUNSUPPORTED, "rope3d_apply: pointers/ld must be 16-byte aligned");
+  return DIT_OK;
+}
+
+extern "C" dit_status rope3d_apply(dit_dtype dt, void* q, int64_t ld_q, void* k, int64_t ld_k,
+                                   const int32_t* pos_thw, int64_t n_tokens, int32_t n_heads,
+                                   int32_t head_dim, const int32_t sections[3], float theta,
+                                   void* stream) {
+  clear_error();
+  if (dit_status st = rope_check(dt, q, ld_q, k, ld_k, pos_thw, n_tokens, n_heads, head_dim,
+                                 sections, theta))
+    return st;
+  if (n_tokens == 0) return DIT_OK;
+  double freq[64];
+  rope_freqs(sections, (double)theta, head_dim, freq);
+  hipError_t e = launch_rope(dt == DIT_BF16, q, ld_q, k, ld_k, pos_thw, n_tokens, n_heads,
+                             head_dim, sections[0], sections[1], freq, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "rope3d_apply launch");
+}
+
+// ---------------------------------------------------------------------------
+
+static dit_status attn_check(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                             int64_t ld_k, const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                             const int32_t* cu, int32_t n_seqs, int32_t max_seqlen,
+                             int64_t n_tokens, int32_t n_heads, int32_t head_dim, float scale) {
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "attn_packed: unknown dtype %d", (int)dt);
+  if (!q || !k || !v || !o || !cu) return fail(DIT_EINVAL, "attn_packed: null pointer");
+  if (n_seqs < 1) return fail(DIT_EINVAL, "attn_packed: n_seqs < 1");
+  if (n_tokens > 0 && max_seqlen < 1) return fail(DIT_EINVAL, "attn_packed: max_seqlen < 1");
+  if (n_heads < 1 || head_dim < 1) return fail(DIT_EINVAL, "attn_packed: n_heads/head_dim < 1");
+  if (!(scale >= 0.0f)) return fail(DIT_EINVAL, "attn_packed: softmax_scale < 0");
+  const int64_t width = (int64_t)n_heads * head_dim;
+  if (ld_q < width || ld_k < width || ld_v < width || ld_o < width)
+    return fail(DIT_EINVAL, "attn_packed: ld too small");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (max_seqlen > n_tokens && n_tokens > 0)
+    return fail(DIT_EINVAL, "attn_packed: max_seqlen %d > n_tokens", max_seqlen);
+  if (n_seqs > 65535 || n_heads > 65535)
+    return fail(DIT_EUNSUPPORTED, "attn_packed: more than 65535 segments or heads");
+  if (dt == DIT_BF16 ? head_dim != 128 : (head_dim != 64 && head_dim != 128))
+    return fail(DIT_EUNSUPPORTED, "attn_packed: head_dim %d unsupported for this dtype", head_dim);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !ld_aligned(dt, ld_q) ||
+      !ld_aligned(dt, ld_k) || !ld_aligned(dt, ld_v) || !ld_aligned(dt, ld_o))
+    return fail(DIT_EUNSUPPORTED, "attn_packed: pointers/ld must be 16-byte aligned");
+  return DIT_OK;
+}
+
+extern "C" dit_status attn_packed(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                                  int64_t ld_k, const void* v, int64_t ld_v, void* o,
+                                  int64_t ld_o, const int32_t* cu_seqlens, int32_t n_seqs,
+                                  int32_t max_seqlen, int64_t n_tokens, int32_t n_heads,
+                                  int32_t head_dim, float softmax_scale, int32_t causal,
+                                  void* stream) {
+  clear_error();
+  if (dit_status st = attn_check(dt, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens, n_seqs,
+                                 max_seqlen, n_tokens, n_heads, head_dim, softmax_scale))
+    return st;
+  if (n_tokens == 0) return DIT_OK;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  hipError_t e = launch_attn(dt == DIT_BF16, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens,
+                             n_seqs, max_seqlen, n_tokens, n_heads, head_dim, scale,
+                             causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_packed launch");
+}
+
+// ---------------------------------------------------------------------------
+
+static dit_status proj_check(const char* who, dit_dtype dt, const void* a, int64_t lda,
+                             const void* w, void* c, int64_t ldc, int64_t n_tokens,
+                             int32_t d_model, int64_t width_out) {
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "%s: unknown dtype %d", who, (int)dt);
+  if (!a || !w || !c) return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (d_model < 1) return fail(DIT_EINVAL, "%s: d_model < 1", who);
+  if (lda < d_model || ldc < width_out) return fail(DIT_EINVAL, "%s: ld too small", who);
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (d_model % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: d_model %d is not a multiple of 64", who, d_model);
+  if (!aligned16(a) || !aligned16(w) || !aligned16(c) || !ld_aligned(dt, lda) ||
+      !ld_aligned(dt, ldc))
+    return fail(DIT_EUNSUPPORTED, "%s: pointers/ld must be 16-byte aligned", who);
+  return DIT_OK;
+}
+
+extern "C" dit_status qkv_project(dit_dtype dt, const void* y, int64_t ld_y, const void* w_qkv,
+                                  const void* b_qkv, void* qkv, int64_t ld_qkv, int64_t n_tokens,
+                                  int32_t d_model, void* stream) {
+  clear_error();
+  if (dit_status st = proj_check("qkv_project", dt, y, ld_y, w_qkv, qkv, ld_qkv, n_tokens,
+                                 d_model, 3 * (int64_t)d_model))
+    return st;
+  if (n_tokens == 0) return DIT_OK;
+  GemmEpilogue ep{0, b_qkv, nullptr, 0, nullptr, nullptr};
+  hipError_t e = launch_gemm(dt == DIT_BF16, y, ld_y, w_qkv, qkv, ld_qkv, n_tokens, 3 * d_model,
+                             d_model, ep, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "qkv_project launch");
+}
+
+extern "C" dit_status out_proj_gated(dit_dtype dt, const void* o, int64_t ld_o, const void* w_o,
+                                     const void* b_o, const void* x, int64_t ld_x,
+                                     const uint8_t* modality, const float* table, void* out,
+                                     int64_t ld_out, int64_t n_tokens, int32_t d_model,
+                                     void* stream) {
+  clear_error();
+  if (dit_status st = proj_check("out_proj_gated", dt, o, ld_o, w_o, out, ld_out, n_tokens,
+                                 d_model, d_model))
+    return st;
+  if (!x || !modality || !table) return fail(DIT_EINVAL, "out_proj_gated: null pointer");
+  if (ld_x < d_model) return fail(DIT_EINVAL, "out_proj_gated: ld_x too small");
+  if (!aligned16(x) || !ld_aligned(dt, ld_x))
+    return fail(DIT_EUNSUPPORTED, "out_proj_gated: pointers/ld must be 16-byte aligned");
+  if (x == out && ld_x != ld_out)
+    return fail(DIT_EINVAL, "out_proj_gated: in-place needs ld_x == ld_out");
+  if (n_tokens == 0) return DIT_OK;
+  GemmEpilogue ep{1, b_o, x, ld_x, modality, table + 2 * (size_t)d_model};
+  hipError_t e = launch_gemm(dt == DIT_BF16, o, ld_o, w_o, out, ld_out, n_tokens, d_model,
+                             d_model, ep, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "out_proj_gated launch");
+}
+
+// ---------------------------------------------------------------------------
+
+static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+extern "C" size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens) {
+  if (!d || !dtype_ok(d->dtype) || d->d_model < 1 || n_tokens < 0) return 0;
+  const size_t es = elt_size(d->dtype), n = (size_t)n_tokens, D = (size_t)d->d_model;
+  return round256(n * D * es) + round256(n * 3 * D * es) + round256(n * D * es);
+}
+
+extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
+                                        const uint8_t* modality, const int32_t* pos_thw,
+                                        const int32_t* cu_seqlens, int32_t n_seqs,
+                                        int32_t max_seqlen, int64_t n_tokens,
+                                        const float* ada_table, const void* w_qkv,
+                                        const void* b_qkv, const void* w_o, const void* b_o,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!d) return fail(DIT_EINVAL, "dit_block_forward: null descriptor");
+  const dit_dtype dt = d->dtype;
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "dit_block_forward: unknown dtype %d", (int)dt);
+  const int32_t D = d->d_model, H = d->n_heads, Dh = d->head_dim;
+  if (D < 1 || H < 1 || Dh < 1 || (int64_t)H * Dh != D)
+    return fail(DIT_EINVAL, "dit_block_forward: d_model %d != n_heads %d * head_dim %d", D, H, Dh);
+  if (!x || !out || !modality || !pos_thw || !cu_seqlens || !ada_table || !w_qkv || !w_o)
+    return fail(DIT_EINVAL, "dit_block_forward: null pointer");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  const size_t need = dit_block_workspace_bytes(d, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "dit_block_forward: workspace %zu bytes, need %zu",
+                workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "dit_block_forward: workspace must be 256-byte aligned");
+
+  const size_t es = elt_size(dt), n = (size_t)n_tokens;
+  char* ws = static_cast<char*>(workspace);
+  void* y = ws;
+  char* qkv = ws + round256(n * D * es);
+  void* o = qkv + round256(n * 3 * (size_t)D * es);
+  void* q = qkv;
+  void* k = qkv + (size_t)D * es;
+  void* v = qkv + 2 * (size_t)D * es;
+
+  // Validate every stage before enqueuing any of them.
+  if (dit_status st = adaln_check(dt, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps))
+    return st;
+  if (dit_status st = proj_check("qkv_project", dt, y, D, w_qkv, qkv, 3 * (int64_t)D, n_tokens,
+                                 D, 3 * (int64_t)D))
+    return st;
+  if (dit_status st = rope_check(dt, q, 3 * (int64_t)D, k, 3 * (int64_t)D, pos_thw, n_tokens, H,
+                                 Dh, d->rope_sections, d->rope_theta))
+    return st;
+  if (dit_status st = attn_check(dt, q, 3 * (int64_t)D, k, 3 * (int64_t)D, v, 3 * (int64_t)D, o,
+                                 D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
+                                 d->softmax_scale))
+    return st;
+  if (dit_status st = proj_check("out_proj_gated", dt, o, D, w_o, out, D, n_tokens, D, D))
+    return st;
+  if (!aligned16(x) || !aligned16(out))
+    return fail(DIT_EUNSUPPORTED, "dit_block_forward: x/out must be 16-byte aligned");
+  if (n_tokens == 0) return DIT_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+  };
+  hipError_t e;
+  mark(0);
+  e = launch_adaln(dt == DIT_BF16, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: adaln launch");
+  mark(1);
+  GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr};
+  e = launch_gemm(dt == DIT_BF16, y, D, w_qkv, qkv, 3 * (int64_t)D, n_tokens, 3 * D, D, ep_qkv, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: qkv launch");
+  mark(2);
+  double freq[64];
+  rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
+  e = launch_rope(dt == DIT_BF16, q, 3 * (int64_t)D, k, 3 * (int64_t)D, pos_thw, n_tokens, H, Dh,
+                  d->rope_sections[0], d->rope_sections[1], freq, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope launch");
+  mark(3);
+  const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
+  e = launch_attn(dt == DIT_BF16, q, 3 * (int64_t)D, k, 3 * (int64_t)D, v, 3 * (int64_t)D, o, D,
+                  cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh, scale, d->causal != 0, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: attention launch");
+  mark(4);
+  GemmEpilogue ep_out{1, b_o, x, D, modality, ada_table + 2 * (size_t)D};
+  e = launch_gemm(dt == DIT_BF16, o, D, w_o, out, D, n_tokens, D, D, ep_out, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: out-proj launch");
+  mark(5);
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------------------
+
+extern "C" dit_status dit_profile_enable(int32_t max_calls) {
+  clear_error();
+  if (max_calls < 0) return fail(DIT_EINVAL, "dit_profile_enable: max_calls < 0");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.clear();
+  p.max_calls = 0;
+  p.used = 0;
+  if (max_calls == 0) return DIT_OK;
+  p.ev.resize((size_t)max_calls * (DIT_NUM_STAGES + 1));
+  for (auto& e : p.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (auto& e2 : p.ev)
+        if (e2) (void)hipEventDestroy(e2);
+      p.ev.clear();
+      return hip_fail(r, "dit_profile_enable: hipEventCreate");
+    }
+  }
+  p.max_calls = max_calls;
+  return DIT_OK;
+}
+
+extern "C" dit_status dit_profile_read(float* stage_ms, int32_t* n_calls) {
+  clear_error();
+  if (!stage_ms || !n_calls) return fail(DIT_EINVAL, "dit_profile_read: null pointer");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (int s = 0; s < DIT_NUM_STAGES; ++s) stage_ms[s] = 0.0f;
+  for (int c = 0; c < p.used; ++c) {
+    hipEvent_t* ev = &p.ev[(size_t)c * (DIT_NUM_STAGES + 1)];
+    hipError_t r = hipEventSynchronize(ev[DIT_NUM_STAGES]);
+    if (r != hipSuccess) return hip_fail(r, "dit_profile_read: hipEventSynchronize");
+    for (int s = 0; s < DIT_NUM_STAGES; ++s) {
+      float ms = 0.0f;
+      r = hipEventElapsedTime(&ms, ev[s], ev[s + 1]);
+      if (r != hipSuccess) return hip_fail(r, "dit_profile_read: hipEventElapsedTime");
+      stage_ms[s] += ms;
+    }
+  }
+  *n_calls = p.used;
+  p.used = 0;
+  return DIT_OK;
+}

@@ -1,0 +1,142 @@
+// Per-modality adaptive LayerNorm: y = LN(x) * (1 + scale[m]) + shift[m].
+//
+// [H3-NFT] section "MiniMax H3 and Why Joint Audio-Video Generation Complicates
+// RL Training": AdaLN branches are per modality and their modulation outputs
+// can be cached, so the kernel reads a precomputed float32 table
+// [3 modalities][shift, scale, gate][d_model]; the modality id of each token
+// picks its rows.
+//
+// HBM-bound (about 2*d_model*elt bytes per token).  One wave per token row:
+// the row is read once with 16-byte loads into registers, mean and variance
+// are two exact passes over the registers (wave reductions), and the
+// modulated row is written with 16-byte stores.  Table rows come from L2.
+#include "common.h"
+
+namespace dit {
+namespace {
+
+constexpr int kWaves = 4;   // rows per workgroup
+
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> { static constexpr int N = 8; };   // bf16 bits
+template <> struct Vec<float> { static constexpr int N = 4; };
+
+__device__ __forceinline__ void unpack(const uint4& r, float* f, uint16_t) {
+  f[0] = bf16lo(r.x); f[1] = bf16hi(r.x); f[2] = bf16lo(r.y); f[3] = bf16hi(r.y);
+  f[4] = bf16lo(r.z); f[5] = bf16hi(r.z); f[6] = bf16lo(r.w); f[7] = bf16hi(r.w);
+}
+__device__ __forceinline__ void unpack(const uint4& r, float* f, float) {
+  f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+  f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+}
+__device__ __forceinline__ uint4 pack(const float* f, uint16_t) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                    pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+__device__ __forceinline__ uint4 pack(const float* f, float) {
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                    __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+
+// NV = 16-byte vectors per lane (row of nvec <= 64*NV vectors).
+template <typename T, int NV>
+__global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
+    const T* __restrict__ x, int64_t ld_x, const uint8_t* __restrict__ mod,
+    const float* __restrict__ table, T* __restrict__ y, int64_t ld_y, int64_t n, int d,
+    float eps) {
+  constexpr int E = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int nvec = d / E;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld_x);
+
+  uint4 raw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    raw[i] = c < nvec ? xr[c] : make_uint4(0, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float f[E];
+    unpack(raw[i], f, T());
+#pragma unroll
+    for (int e = 0; e < E; ++e) s += f[e];
+  }
+  const float inv_d = 1.0f / (float)d;
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i < nvec) {
+      float f[E];
+      unpack(raw[i], f, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float t = f[e] - mean;
+        q = fmaf(t, t, q);
+      }
+    }
+  }
+  const float var = wave_sum(q) * inv_d;
+  const float rstd = 1.0f / sqrtf(var + eps);
+
+  const int m = mod[row];
+  const float4* shift = reinterpret_cast<const float4*>(table + (size_t)(3 * m + 0) * d);
+  const float4* scale = reinterpret_cast<const float4*>(table + (size_t)(3 * m + 1) * d);
+  uint4* yr = reinterpret_cast<uint4*>(y + row * ld_y);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nvec) {
+      float f[E], o[E];
+      unpack(raw[i], f, T());
+#pragma unroll
+      for (int e4 = 0; e4 < E / 4; ++e4) {
+        const float4 sh = shift[c * (E / 4) + e4];
+        const float4 sc = scale[c * (E / 4) + e4];
+        const float shv[4] = {sh.x, sh.y, sh.z, sh.w};
+        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xh = (f[4 * e4 + e] - mean) * rstd;
+          o[4 * e4 + e] = fmaf(xh, 1.0f + scv[e], shv[e]);
+        }
+      }
+      yr[c] = pack(o, T());
+    }
+  }
+}
+
+template <typename T>
+hipError_t dispatch(const void* x, int64_t ld_x, const uint8_t* mod, const float* table, void* y,
+                    int64_t ld_y, int64_t n, int d, float eps, hipStream_t s) {
+  const int nvec = d / Vec<T>::N;
+  const int need = (nvec + 63) / 64;
+  const dim3 grid((unsigned)((n + kWaves - 1) / kWaves)), block(64 * kWaves);
+  const T* xp = static_cast<const T*>(x);
+  T* yp = static_cast<T*>(y);
+#define DIT_ADALN_CASE(NVV)                                                                \
+  if (need <= NVV) {                                                                       \
+    adaln_kernel<T, NVV><<<grid, block, 0, s>>>(xp, ld_x, mod, table, yp, ld_y, n, d, eps); \
+    return hipGetLastError();                                                              \
+  }
+  DIT_ADALN_CASE(1) DIT_ADALN_CASE(2) DIT_ADALN_CASE(3) DIT_ADALN_CASE(4) DIT_ADALN_CASE(5)
+  DIT_ADALN_CASE(6) DIT_ADALN_CASE(8) DIT_ADALN_CASE(10) DIT_ADALN_CASE(12) DIT_ADALN_CASE(16)
+  DIT_ADALN_CASE(20) DIT_ADALN_CASE(24) DIT_ADALN_CASE(32)
+#undef DIT_ADALN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_adaln(int bf16, const void* x, int64_t ld_x, const uint8_t* mod,
+                        const float* table, void* y, int64_t ld_y, int64_t n, int d, float eps,
+                        hipStream_t s) {
+  return bf16 ? dispatch<uint16_t>(x, ld_x, mod, table, y, ld_y, n, d, eps, s)
+              : dispatch<float>(x, ld_x, mod, table, y, ld_y, n, d, eps, s);
+}
+
+}  // namespace dit

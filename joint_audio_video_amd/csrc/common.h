@@ -1,0 +1,87 @@
+// Internal helpers shared by the libdit kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 storage is raw 16-bit patterns; widening is exact.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// Sum / max over all 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Value pair {v[l], v[l ^ 32]} via v_permlane32_swap; combining the two
+// results with a commutative op gives the same value in lanes l and l ^ 32.
+__device__ __forceinline__ float half_swap_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace dit
+
+// Launchers implemented in the .hip files; all return hipGetLastError() of the launch.
+namespace dit {
+
+hipError_t launch_adaln(int bf16, const void* x, int64_t ld_x, const uint8_t* mod,
+                        const float* table, void* y, int64_t ld_y, int64_t n, int d,
+                        float eps, hipStream_t s);
+
+// freq_d: host array of head_dim/2 pair frequencies theta^(-2j/s_axis), in double.
+hipError_t launch_rope(int bf16, void* q, int64_t ld_q, void* k, int64_t ld_k,
+                       const int32_t* pos, int64_t n, int n_heads, int head_dim,
+                       int s_t, int s_h, const double* freq_d, hipStream_t s);
+
+hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                       const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                       const int32_t* cu, int n_seqs, int max_seqlen, int64_t n_tokens,
+                       int n_heads, int head_dim, float scale, int causal, hipStream_t s);
+
+// C = A B^T (+ bias), A [M][K], B [N][K]; epilogue 0: store C; 1: gated residual
+// out = x + table[mod][GATE] * C.
+struct GemmEpilogue {
+  int kind;                 // 0 plain, 1 gated residual
+  const void* bias;         // [N] or null
+  const void* x;            // residual input (kind 1)
+  int64_t ld_x;
+  const uint8_t* mod;       // modality ids (kind 1)
+  const float* gate;        // table + GATE row offset; row stride 3*N floats (kind 1)
+};
+hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c,
+                       int64_t ldc, int64_t m, int n, int k, const GemmEpilogue& ep,
+                       hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,230 @@
+// Projections of the block: C = A B^T (+ bias), with two epilogues.
+//   plain:          qkv = y W_qkv^T + b          (fused to_q | to_k | to_v)
+//   gated residual: out = x + gate[m] * (o W_o^T + b)   (to_out.0)
+// [VeRL-Omni] section 5.2 (Q, K, V packed into one matrix on the rollout
+// side); [H3-NFT] (projection names to_q, to_k, to_v, to_out.0).
+//
+// bf16 path: CDNA4 bf16 MFMA (v_mfma_f32_32x32x16_bf16), float32 accumulate.
+// Workgroup tile 256x256x64, four waves in a 2x2 arrangement, each owning a
+// 128x128 sub-tile as 4x4 MFMA blocks (256 accumulators per lane, held in the
+// AGPR half of the register file).  A and B tiles are staged through LDS
+// (double-buffered, 128 KB) with an XOR swizzle of the 16-byte chunk index so
+// the 32 rows an MFMA fragment read touches fall in distinct banks.  Both
+// operands are K-contiguous ([rows][K]), so every fragment is one 16-byte LDS
+// read.  Tiles are handed out XCD-aware: the hardware deals workgroups to the
+// 8 XCDs round-robin, so the launch index is remapped so that each XCD works
+// through a contiguous range of an M-grouped tile order and its L2 sees
+// neighbouring A and B panels.
+//
+// float32 path: a plain LDS-tiled VALU kernel (the tiny float32 workload only
+// needs to be exact, not fast).
+#include "common.h"
+
+namespace dit {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;
+
+struct EpiArgs {
+  int kind;
+  const uint16_t* bias;
+  const uint16_t* x;
+  int64_t ld_x;
+  const uint8_t* mod;
+  const float* gate;
+  int64_t gate_stride;      // floats between the gate rows of two modalities
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// Logical tile id for this workgroup: XCD-contiguous ranges, then M-grouping.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int pid = blockIdx.x;
+  const int xcd = pid & 7, idx = pid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const int group_span = kGroupM * tiles_n;
+  const int group = logical / group_span;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = logical - group * group_span;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+    uint16_t* C, int64_t ldc, int M, int N, int K, EpiArgs ep) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // Global -> LDS staging: 8 chunks of A and 8 of B per thread per k-step.
+  uint4 ra[8], rb[8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = idx >> 3, ch = idx & 7;
+      const int gm = m0 + row, gn = n0 + row;
+      ra[i] = gm < M ? *reinterpret_cast<const uint4*>(A + (int64_t)gm * lda + k0 + ch * 8)
+                     : make_uint4(0, 0, 0, 0);
+      rb[i] = gn < N ? *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + k0 + ch * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<uint4*>(&As[buf][row * BK + swz(row, ch) * 8]) = ra[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][row * BK + swz(row, ch) * 8]) = rb[i];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const uint16_t* as = As[buf];
+    const uint16_t* bs = Bs[buf];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = wm * 128 + mb * 32 + l32;
+        af[mb] = *reinterpret_cast<const bf16x8*>(&as[row * BK + swz(row, 2 * ks + g) * 8]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int row = wn * 128 + nb * 32 + l32;
+        bfr[nb] = *reinterpret_cast<const bf16x8*>(&bs[row * BK + swz(row, 2 * ks + g) * 8]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[mb][nb][i] sits at row (i/4)*8 + g*4 + i%4, column l32 of its block.
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int col = n0 + wn * 128 + nb * 32 + l32;
+    if (col >= N) continue;
+    const float bias = ep.bias ? bf16_to_f32(ep.bias[col]) : 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = m0 + wm * 128 + mb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        if (row < M) {
+          float v = acc[mb][nb][i] + bias;
+          if (ep.kind == 1) {
+            const float gt = ep.gate[ep.mod[row] * ep.gate_stride + col];
+            v = fmaf(gt, v, bf16_to_f32(ep.x[(int64_t)row * ep.ld_x + col]));
+          }
+          C[(int64_t)row * ldc + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+// ---- float32 path ----
+constexpr int FT = 64, FK = 16;
+
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
+                                                        const float* __restrict__ B,
+                                                        float* C, int64_t ldc, int M,
+                                                        int N, int K, const float* bias,
+                                                        int kind, const float* x, int64_t ld_x,
+                                                        const uint8_t* mod, const float* gate,
+                                                        int64_t gate_stride) {
+  __shared__ float As[FK][FT + 1];
+  __shared__ float Bs[FK][FT + 1];
+  const int m0 = blockIdx.y * FT, n0 = blockIdx.x * FT;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += FK) {
+    for (int i = threadIdx.x; i < FT * FK; i += 256) {
+      const int r = i / FK, c = i % FK;
+      As[c][r] = (m0 + r < M) ? A[(int64_t)(m0 + r) * lda + k0 + c] : 0.0f;
+      Bs[c][r] = (n0 + r < N) ? B[(int64_t)(n0 + r) * K + k0 + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < FK; ++kk) {
+      float a[4], b[4];
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= N) continue;
+      float v = acc[i][j] + (bias ? bias[col] : 0.0f);
+      if (kind == 1) v = fmaf(gate[mod[row] * gate_stride + col], v, x[(int64_t)row * ld_x + col]);
+      C[(int64_t)row * ldc + col] = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c, int64_t ldc,
+                       int64_t m, int n, int k, const GemmEpilogue& ep, hipStream_t s) {
+  if (k % BK != 0 || m > INT32_MAX) return hipErrorInvalidValue;
+  // gate rows of the table are 3*N floats apart (table [3][3][N], N = d_model)
+  const int64_t gate_stride = 3 * (int64_t)n;
+  if (bf16) {
+    const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
+              ep.ld_x, ep.mod, ep.gate, gate_stride};
+    gemm_bf16_kernel<<<dim3(tiles), dim3(kThreads), 0, s>>>(
+        static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
+        static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
+  } else {
+    const dim3 grid((n + FT - 1) / FT, (unsigned)((m + FT - 1) / FT));
+    gemm_f32_kernel<<<grid, dim3(256), 0, s>>>(
+        static_cast<const float*>(a), lda, static_cast<const float*>(b), static_cast<float*>(c),
+        ldc, (int)m, n, k, static_cast<const float*>(ep.bias), ep.kind,
+        static_cast<const float*>(ep.x), ep.ld_x, ep.mod, ep.gate, gate_stride);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dit

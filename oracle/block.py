@@ -237,16 +237,29 @@ def block_forward(x, modality, pos, cu_seqlens, table, w_qkv, w_o, *,
     by cu_seqlens) and [H3-NFT] (AdaLN per modality, projection names).
 
     Returns every stage (float64): y, q, k, v (before RoPE), q_rot, k_rot, o
-    and out.  With ``rows``, o and out hold only those rows (k and v are still
-    computed for every token, since attention needs them).
+    and out.  With ``rows``, o and out hold only those rows, and q / q_rot are
+    filled only at those rows (k and v are still computed for every token,
+    since attention needs them).
     """
     x = np.asarray(x)
-    d = x.shape[1]
+    n, d = x.shape
+    w = np.asarray(w_qkv)
+    bias = [None] * 3 if b_qkv is None else [np.asarray(b_qkv)[i * d:(i + 1) * d] for i in range(3)]
     y = adaln_modulate(x, modality, table, eps)
-    qkv = qkv_project(y, w_qkv, b_qkv)
-    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
-    q_rot = rope3d(q, pos, n_heads, head_dim, sections, theta)
+    k = qkv_project(y, w[d:2 * d], bias[1])
+    v = qkv_project(y, w[2 * d:], bias[2])
     k_rot = rope3d(k, pos, n_heads, head_dim, sections, theta)
+    if rows is None:
+        q = qkv_project(y, w[:d], bias[0])
+        q_rot = rope3d(q, pos, n_heads, head_dim, sections, theta)
+    else:
+        # queries are only needed for the requested rows; scatter them into a
+        # full-size array so that attention() can index them by token
+        idx = _rows(rows, n)
+        q = np.zeros((n, d))
+        q[idx] = qkv_project(y[idx], w[:d], bias[0])
+        q_rot = np.zeros((n, d))
+        q_rot[idx] = rope3d(q[idx], np.asarray(pos)[idx], n_heads, head_dim, sections, theta)
     o = attention(q_rot, k_rot, v, cu_seqlens, n_heads, head_dim, causal, scale, rows)
     out = out_proj_gated(o, w_o, x, modality, table, b_o, rows)
     return dict(y=y, q=q, k=k, v=v, q_rot=q_rot, k_rot=k_rot, o=o, out=out)

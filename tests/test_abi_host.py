@@ -1,0 +1,144 @@
+"""The C ABI on the CPU: symbols, host layout bit-exact against the oracle, and
+argument validation that returns before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import joint_audio_video_amd as jav
+import oracle
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dit.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_exported_set():
+    assert _declared_functions() == sorted(jav.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(jav.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert jav.abi_version() == 1
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_grid_from_media_matches_oracle(name):
+    for r in synth.WORKLOADS[name].requests:
+        assert jav.grid_from_media(*r.media) == oracle.grid_from_media(*r.media)
+
+
+@pytest.mark.parametrize("media", [
+    (121, 288, 448, 32000, 7), (1, 32, 32, 0, 0), (0, 0, 0, 1600, 3), (5, 0, 64, 0, 1),
+    (0, 256, 256, 800, 0)])
+def test_grid_from_media_edge_cases(media):
+    assert jav.grid_from_media(*media) == oracle.grid_from_media(*media)
+
+
+@pytest.mark.parametrize("bad", [(120, 256, 256, 0, 0), (5, 400, 640, 0, 0), (5, 256, 256, 801, 0),
+                                 (-1, 256, 256, 0, 0), (5, 256, 256, 0, -1)])
+def test_grid_from_media_rejects(bad):
+    with pytest.raises(ValueError):
+        oracle.grid_from_media(*bad)
+    with pytest.raises(jav.DitError) as e:
+        jav.grid_from_media(*bad)
+    assert e.value.status == jav.DIT_EINVAL
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_pack_layout_bit_exact(name):
+    grids = [r.grid for r in synth.WORKLOADS[name].requests]
+    ref = oracle.pack_layout(grids)
+    got = jav.pack_layout(grids)
+    assert got["n_tokens"] == ref["n_tokens"]
+    assert got["max_seqlen"] == ref["max_seqlen"]
+    np.testing.assert_array_equal(got["cu_seqlens"], np.array(ref["cu_seqlens"], np.int32))
+    np.testing.assert_array_equal(got["modality"], np.array(ref["modality"], np.uint8))
+    np.testing.assert_array_equal(got["pos"], np.array(ref["pos"], np.int32).reshape(-1, 3))
+
+
+def test_pack_layout_golden_and_page_example():
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pack_tiny.json")))
+    got = jav.pack_layout(g["grids"])
+    assert got["modality"].tolist() == g["modality"]
+    assert got["pos"].tolist() == g["pos"]
+    assert got["cu_seqlens"].tolist() == g["cu_seqlens"]
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "cu_seqlens_example.json")))
+    got = jav.pack_layout([(0, 0, 0, 0, n) for n in ex["lengths_three"]])
+    assert got["cu_seqlens"].tolist() == ex["cu_three"]
+
+
+def test_pack_layout_errors():
+    with pytest.raises(jav.DitError) as e:
+        jav.pack_layout([(2, 2, 2, 1, 1)], capacity=5)
+    assert e.value.status == jav.DIT_EINVAL
+    with pytest.raises(jav.DitError):
+        jav.pack_layout([(1, 1, -1, 0, 0)])
+    with pytest.raises(jav.DitError):
+        jav.pack_layout([])
+
+
+def _call(fn, *args):
+    return getattr(jav._lib, fn)(*args)
+
+
+def test_device_entry_points_validate_before_enqueue():
+    """Bad host scalars are rejected with exact codes; nothing touches a device."""
+    fake = 1 << 20            # never dereferenced: validation fails first
+    sec = (ctypes.c_int32 * 3)(32, 48, 48)
+    bad_sec = (ctypes.c_int32 * 3)(31, 49, 48)
+    # adaln
+    assert _call("adaln_modulate", 7, fake, 64, fake, fake, fake, 64, 10, 64, 1e-6, None) == jav.DIT_EINVAL
+    assert _call("adaln_modulate", jav.DIT_BF16, None, 64, fake, fake, fake, 64, 10, 64, 1e-6, None) == jav.DIT_EINVAL
+    assert _call("adaln_modulate", jav.DIT_BF16, fake, 32, fake, fake, fake, 64, 10, 64, 1e-6, None) == jav.DIT_EINVAL
+    assert _call("adaln_modulate", jav.DIT_BF16, fake, 64, fake, fake, fake, 64, 10, 64, 0.0, None) == jav.DIT_EINVAL
+    assert _call("adaln_modulate", jav.DIT_BF16, fake + 2, 64, fake, fake, fake, 64, 10, 64, 1e-6, None) == jav.DIT_EUNSUPPORTED
+    assert _call("adaln_modulate", jav.DIT_BF16, fake, 68, fake, fake, fake, 68, 10, 68, 1e-6, None) == jav.DIT_EUNSUPPORTED
+    assert "adaln_modulate" in jav.last_error()
+    # rope
+    assert _call("rope3d_apply", jav.DIT_BF16, fake, 384, fake, 384, fake, 10, 3, 128, bad_sec, 1e4, None) == jav.DIT_EINVAL
+    assert _call("rope3d_apply", jav.DIT_BF16, fake, 100, fake, 384, fake, 10, 3, 128, sec, 1e4, None) == jav.DIT_EINVAL
+    assert _call("rope3d_apply", jav.DIT_BF16, fake, 384, fake, 384, fake, 10, 3, 128, sec, 0.0, None) == jav.DIT_EINVAL
+    sec96 = (ctypes.c_int32 * 3)(32, 32, 32)
+    assert _call("rope3d_apply", jav.DIT_BF16, fake, 384, fake, 384, fake, 10, 4, 96, sec96, 1e4, None) == jav.DIT_EUNSUPPORTED
+    # attention
+    A = [jav.DIT_BF16, fake, 5120, fake, 5120, fake, 5120, fake, 5120]
+    assert _call("attn_packed", *A, fake, 0, 10, 10, 40, 128, 0.0, 0, None) == jav.DIT_EINVAL     # n_seqs
+    assert _call("attn_packed", *A, fake, 1, 0, 10, 40, 128, 0.0, 0, None) == jav.DIT_EINVAL      # max_seqlen
+    assert _call("attn_packed", *A, fake, 1, 10, 10, 40, 128, -1.0, 0, None) == jav.DIT_EINVAL    # scale
+    assert _call("attn_packed", *A, fake, 1, 10, 10, 80, 64, 0.0, 0, None) == jav.DIT_EUNSUPPORTED  # bf16 dh 64
+    assert _call("attn_packed", *A, None, 1, 10, 10, 40, 128, 0.0, 0, None) == jav.DIT_EINVAL
+    # n_tokens == 0 is a no-op even with a null stream
+    assert _call("attn_packed", *A, fake, 1, 0, 0, 40, 128, 0.0, 0, None) == jav.DIT_OK
+    # projections
+    assert _call("qkv_project", jav.DIT_BF16, fake, 4096, fake, None, fake, 15360, 10, 5120, None) == jav.DIT_EINVAL
+    assert _call("qkv_project", jav.DIT_BF16, fake, 5120, fake, None, fake, 15360, 10, 5064, None) == jav.DIT_EUNSUPPORTED
+    assert _call("out_proj_gated", jav.DIT_BF16, fake, 5120, fake, None, None, 5120, fake, fake, fake, 5120, 10, 5120, None) == jav.DIT_EINVAL
+
+
+def test_block_workspace_and_descriptor_checks():
+    desc = jav.block_desc(jav.DIT_BF16, 5120, 40, 128, (32, 48, 48))
+    n = 58758
+    want = sum(((n * w * 2 + 255) // 256) * 256 for w in (5120, 15360, 5120))
+    assert jav.block_workspace_bytes(desc, n) == want
+    fake = 1 << 20
+    args = [fake, fake, fake, fake, fake, 1, 100, 100, fake, fake, None, fake, None]
+    # workspace too small
+    st = jav._lib.dit_block_forward(ctypes.byref(desc), *args, fake, 10, None)
+    assert st == jav.DIT_EWORKSPACE
+    bad = jav.block_desc(jav.DIT_BF16, 5120, 40, 64, (16, 24, 24))   # D != H * Dh
+    st = jav._lib.dit_block_forward(ctypes.byref(bad), *args, fake, 1 << 40, None)
+    assert st == jav.DIT_EINVAL
+    assert jav.block_workspace_bytes(jav.block_desc(9, 64, 1, 64, (16, 24, 24)), 10) == 0

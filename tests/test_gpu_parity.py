@@ -1,0 +1,332 @@
+"""Parity of every libdit entry point against the float64 oracle (MI355X only).
+
+Each stage is checked on its own seeded inputs (so errors do not compound),
+and the whole block end to end from the original inputs.  Inputs come from
+``synth``; the library's own host layout feeds the device, the oracle's own
+layout feeds the oracle (the two are bit-identical, see test_abi_host.py).
+Large workloads are compared on sampled rows that include the first and last
+rows of every segment and the ragged tail.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check, dev, dev_f32, dev_int, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def jav():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import joint_audio_video_amd as m
+    return m
+
+
+@functools.lru_cache(maxsize=2)
+def _inputs(name):
+    return synth.block_inputs(synth.WORKLOADS[name])
+
+
+@functools.lru_cache(maxsize=4)
+def _layout(name):
+    wl = synth.WORKLOADS[name]
+    return oracle.pack_layout([r.grid for r in wl.requests])
+
+
+def _dev_layout(jav, name):
+    import torch
+    wl = synth.WORKLOADS[name]
+    lay = jav.pack_layout([r.grid for r in wl.requests])
+    return (dev_int(lay["modality"], torch.uint8), dev_int(lay["pos"], torch.int32),
+            dev_int(lay["cu_seqlens"], torch.int32), lay["max_seqlen"])
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# adaln_modulate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "small", "medium", "full"])
+def test_adaln_parity(jav, name):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = _inputs(name)
+    lay = _layout(name)
+    mod_d, _, _, _ = _dev_layout(jav, name)
+    print(f"adaln {name} N={wl.n_tokens} D={wl.d_model}", flush=True)
+    x = dev(inp.x, wl.dtype)
+    y = jav.adaln_modulate(x, mod_d, dev_f32(inp.table), eps=wl.eps)
+    _sync()
+    rows = None if name != "full" else sample_rows(lay["cu_seqlens"], wl.n_tokens, limit=4000)
+    ref = oracle.adaln_modulate(inp.x, lay["modality"], inp.table, wl.eps, rows=rows)
+    got = host(y) if rows is None else host(y[torch.from_numpy(rows).cuda()])
+    check(got, ref, wl.dtype, f"adaln[{name}]")
+
+
+def test_adaln_strided_rows_and_trim(jav):
+    """Rows inside wider buffers; only n_tokens rows are touched."""
+    import torch
+    d, n, rows_alloc = 1536, 1000, 1040
+    x_full = synth.normal_array((rows_alloc, d + 64), seed=70, dtype="bf16")
+    table = synth.normal_array((3, 3, d), seed=71, std=0.1)
+    mod = synth.uniform_ints((rows_alloc,), 0, 3, seed=72).astype(np.uint8)
+    x = dev(x_full, "bf16")
+    y = torch.full((rows_alloc, d + 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    jav.adaln_modulate(x[:, :d], dev_int(mod, torch.uint8), dev_f32(table), out=y[:, :d],
+                       n_tokens=n)
+    _sync()
+    ref = oracle.adaln_modulate(x_full[:n, :d], mod[:n], table)
+    check(host(y[:n, :d]), ref, "bf16", "adaln strided")
+    assert torch.isnan(y[n:]).all() and torch.isnan(y[:, d:]).all()
+
+
+# ---------------------------------------------------------------------------
+# rope3d_apply
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "small", "full"])
+def test_rope_parity_on_fused_qkv(jav, name):
+    import torch
+    wl = synth.WORKLOADS[name]
+    d, H, Dh = wl.d_model, wl.n_heads, wl.head_dim
+    lay = _layout(name)
+    _, pos_d, _, _ = _dev_layout(jav, name)
+    n = wl.n_tokens
+    print(f"rope {name} N={n}", flush=True)
+    qkv_h = synth.normal_array((n, 3 * d), seed=100 + wl.seed, dtype=wl.dtype)
+    qkv = dev(qkv_h, wl.dtype)
+    before = qkv.clone()
+    jav.rope3d_apply(qkv[:, :d], qkv[:, d:2 * d], pos_d, H, Dh, wl.sections, wl.theta)
+    _sync()
+    rows = None if n < 20000 else sample_rows(lay["cu_seqlens"], n, limit=3000)
+    for which, sl in (("q", slice(0, d)), ("k", slice(d, 2 * d))):
+        ref = oracle.rope3d(qkv_h[:, sl], lay["pos"], H, Dh, wl.sections, wl.theta, rows=rows)
+        got = host(qkv[:, sl]) if rows is None else host(qkv[:, sl][torch.from_numpy(rows).cuda()])
+        check(got, ref, wl.dtype, f"rope[{name}].{which}")
+    # v untouched; audio/text rows keep their h and w sections bit for bit
+    assert torch.equal(qkv[:, 2 * d:], before[:, 2 * d:])
+    mod = np.asarray(lay["modality"])
+    at = torch.from_numpy(np.nonzero(mod != 0)[0]).cuda()
+    s_t = wl.sections[0]
+    for sl in (slice(0, d), slice(d, 2 * d)):
+        a = qkv[:, sl].view(n, H, Dh)[at][:, :, s_t:]
+        b = before[:, sl].view(n, H, Dh)[at][:, :, s_t:]
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_rope_q_only_and_zero_positions(jav):
+    import torch
+    n, H, Dh = 300, 4, 128
+    x_h = synth.normal_array((n, H * Dh), seed=110, dtype="bf16")
+    x = dev(x_h, "bf16")
+    jav.rope3d_apply(x, None, dev_int(np.zeros((n, 3), np.int32), torch.int32), H, Dh, (32, 48, 48))
+    _sync()
+    assert torch.equal(x.view(torch.int16), dev(x_h, "bf16").view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# attn_packed
+# ---------------------------------------------------------------------------
+
+def _attn_case(jav, n, H, Dh, cu, dtype, causal, seed, std=1.0, rows=None, max_seqlen=None,
+               label=""):
+    import torch
+    print(f"attn {label} N={n} H={H} cu_len={len(cu) - 1} causal={causal}", flush=True)
+    q_h = synth.normal_array((n, H * Dh), seed=seed, std=std, dtype=dtype)
+    k_h = synth.normal_array((n, H * Dh), seed=seed + 1, std=std, dtype=dtype)
+    v_h = synth.normal_array((n, H * Dh), seed=seed + 2, dtype=dtype)
+    cu_d = dev_int(np.array(cu, np.int32), torch.int32)
+    ms = max_seqlen or max(b - a for a, b in zip(cu, cu[1:]))
+    o = jav.attn_packed(dev(q_h, dtype), dev(k_h, dtype), dev(v_h, dtype), cu_d, ms, H, Dh,
+                        causal=causal)
+    _sync()
+    ref = oracle.attention(q_h, k_h, v_h, cu, H, Dh, causal, rows=rows)
+    got = host(o) if rows is None else host(o[torch.from_numpy(rows).cuda()])
+    check(got, ref, dtype, f"attn[{label}]")
+    return o
+
+
+def test_attention_tiny_f32(jav):
+    wl = synth.WORKLOADS["tiny"]
+    _attn_case(jav, wl.n_tokens, wl.n_heads, wl.head_dim, [0, wl.n_tokens], "f32", False, 200,
+               label="tiny f32")
+    _attn_case(jav, wl.n_tokens, wl.n_heads, wl.head_dim, [0, 100, 101, 328], "f32", True, 201,
+               label="tiny f32 causal varlen")
+
+
+def test_attention_f32_head_dim_128(jav):
+    _attn_case(jav, 200, 2, 128, [0, 77, 200], "f32", False, 205, label="f32 dh128")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_ragged_segments(jav, causal):
+    """Segments of 1, 63, 64, 65, 127, 128, 129 and 300 tokens plus an empty one."""
+    lens = [1, 63, 64, 65, 0, 127, 128, 129, 300]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    _attn_case(jav, cu[-1], 3, 128, cu, "bf16", causal, 210 + causal, label=f"ragged c={causal}")
+
+
+def test_attention_peaky_scores(jav):
+    _attn_case(jav, 700, 2, 128, [0, 700], "bf16", False, 220, std=2.0, label="peaky std2")
+    _attn_case(jav, 700, 2, 128, [0, 333, 700], "bf16", True, 223, std=2.0, label="peaky causal")
+
+
+def test_attention_small(jav):
+    wl = synth.WORKLOADS["small"]
+    rows = sample_rows([0, wl.n_tokens], wl.n_tokens, limit=512)
+    _attn_case(jav, wl.n_tokens, wl.n_heads, 128, [0, wl.n_tokens], "bf16", False, 230, rows=rows,
+               label="small")
+
+
+@pytest.mark.parametrize("variant", ["full", "modality_isolated", "varlen", "varlen_causal"])
+def test_attention_full_shape(jav, variant):
+    wl = synth.WORKLOADS["varlen" if variant.startswith("varlen") else "full"]
+    n, H = wl.n_tokens, wl.n_heads
+    if variant == "modality_isolated":
+        cu = [0, 57040, 58640, 58758]
+    else:
+        cu = list(wl.expected_cu_seqlens)
+    rows = sample_rows(cu, n, extra_every=1499, edge=3, limit=96)
+    _attn_case(jav, n, H, 128, cu, "bf16", variant == "varlen_causal", 240, rows=rows,
+               label=variant)
+
+
+# ---------------------------------------------------------------------------
+# qkv_project / out_proj_gated
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,bias", [("tiny", False), ("tiny", True), ("small", True),
+                                       ("medium", False), ("full", False)])
+def test_qkv_project_parity(jav, name, bias):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, with_bias=True) if bias else _inputs(name)
+    n, d = wl.n_tokens, wl.d_model
+    print(f"qkv {name} bias={bias}", flush=True)
+    y_h = synth.normal_array((n, d), seed=300 + wl.seed, dtype=wl.dtype)
+    out = jav.qkv_project(dev(y_h, wl.dtype), dev(inp.w_qkv, wl.dtype),
+                          dev(inp.b_qkv, wl.dtype) if bias else None)
+    _sync()
+    rows = None if n <= 4096 else sample_rows([0, n], n, limit=700)
+    ref = oracle.qkv_project(y_h if rows is None else y_h[rows], inp.w_qkv,
+                             inp.b_qkv if bias else None)
+    got = host(out) if rows is None else host(out[torch.from_numpy(rows).cuda()])
+    check(got, ref, wl.dtype, f"qkv[{name}]")
+
+
+@pytest.mark.parametrize("name,bias,inplace", [("tiny", True, False), ("small", False, False),
+                                               ("small", True, True), ("full", False, True)])
+def test_out_proj_gated_parity(jav, name, bias, inplace):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, with_bias=True) if bias else _inputs(name)
+    lay = _layout(name)
+    mod_d, _, _, _ = _dev_layout(jav, name)
+    n, d = wl.n_tokens, wl.d_model
+    print(f"out_proj {name} bias={bias} inplace={inplace}", flush=True)
+    o_h = synth.normal_array((n, d), seed=400 + wl.seed, dtype=wl.dtype)
+    x_h = inp.x
+    x = dev(x_h, wl.dtype)
+    out = jav.out_proj_gated(dev(o_h, wl.dtype), dev(inp.w_o, wl.dtype), x, mod_d,
+                             dev_f32(inp.table), dev(inp.b_o, wl.dtype) if bias else None,
+                             out=x if inplace else None)
+    _sync()
+    rows = None if n <= 4096 else sample_rows([0, n], n, limit=700)
+    ref = oracle.out_proj_gated(o_h if rows is None else o_h[rows], inp.w_o, x_h,
+                                lay["modality"], inp.table, inp.b_o if bias else None, rows=rows)
+    got = host(out) if rows is None else host(out[torch.from_numpy(rows).cuda()])
+    check(got, ref, wl.dtype, f"out_proj[{name}]")
+    # the branch alone (out - x), where the residual does not hide errors
+    if rows is None and wl.dtype == "f32":
+        check(got - np.asarray(x_h, np.float64)[: n], ref - x_h, wl.dtype, "branch")
+
+
+# ---------------------------------------------------------------------------
+# dit_block_forward
+# ---------------------------------------------------------------------------
+
+def _block(jav, name, causal=False, with_bias=False, rows=None):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, with_bias=True) if with_bias else _inputs(name)
+    lay = _layout(name)
+    mod_d, pos_d, cu_d, ms = _dev_layout(jav, name)
+    code = jav.DIT_BF16 if wl.dtype == "bf16" else jav.DIT_F32
+    desc = jav.block_desc(code, wl.d_model, wl.n_heads, wl.head_dim, wl.sections, wl.theta,
+                          wl.eps, causal=causal)
+    print(f"block {name} causal={causal} bias={with_bias}", flush=True)
+    out = jav.block_forward(desc, dev(inp.x, wl.dtype), mod_d, pos_d, cu_d, ms,
+                            dev_f32(inp.table), dev(inp.w_qkv, wl.dtype), dev(inp.w_o, wl.dtype),
+                            b_qkv=dev(inp.b_qkv, wl.dtype) if with_bias else None,
+                            b_o=dev(inp.b_o, wl.dtype) if with_bias else None)
+    _sync()
+    ref = oracle.block_forward(inp.x, lay["modality"], lay["pos"], lay["cu_seqlens"], inp.table,
+                               inp.w_qkv, inp.w_o, n_heads=wl.n_heads, head_dim=wl.head_dim,
+                               sections=wl.sections, theta=wl.theta, eps=wl.eps, causal=causal,
+                               b_qkv=inp.b_qkv if with_bias else None,
+                               b_o=inp.b_o if with_bias else None, rows=rows)
+    got = host(out) if rows is None else host(out[torch.from_numpy(rows).cuda()])
+    check(got, ref["out"], wl.dtype, f"block[{name}]")
+    return out
+
+
+def test_block_tiny_f32(jav):
+    _block(jav, "tiny")
+    _block(jav, "tiny", causal=True, with_bias=True)
+
+
+def test_block_small_bf16(jav):
+    wl = synth.WORKLOADS["small"]
+    _block(jav, "small", rows=sample_rows([0, wl.n_tokens], wl.n_tokens, limit=256))
+
+
+def test_block_full_shape_sampled(jav):
+    wl = synth.WORKLOADS["full"]
+    rows = sample_rows([0, wl.n_tokens], wl.n_tokens, extra_every=4999, edge=2, limit=40)
+    _block(jav, "full", rows=rows)
+
+
+def test_block_poison_tail_and_determinism(jav):
+    """Buffers of 58,816 rows whose last 58 rows are NaN give finite outputs that are
+    bit-identical to the unpadded run, leave the tail untouched, and repeat exactly."""
+    import torch
+    wl = synth.WORKLOADS["full"]
+    n, d = wl.n_tokens, wl.d_model
+    inp = _inputs("full")
+    mod_d, pos_d, cu_d, ms = _dev_layout(jav, "full")
+    desc = jav.block_desc(jav.DIT_BF16, d, wl.n_heads, wl.head_dim, wl.sections)
+    x = dev(inp.x, "bf16")
+    tab, wq, wo = dev_f32(inp.table), dev(inp.w_qkv, "bf16"), dev(inp.w_o, "bf16")
+    print("block poison", flush=True)
+    out_ref = jav.block_forward(desc, x, mod_d, pos_d, cu_d, ms, tab, wq, wo)
+    out_rep = jav.block_forward(desc, x, mod_d, pos_d, cu_d, ms, tab, wq, wo)
+    pad = synth.FULL_ALIGNED_TOKENS
+    xp = torch.full((pad, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xp[:n] = x
+    modp = torch.zeros(pad, dtype=torch.uint8, device="cuda")
+    modp[:n] = mod_d
+    modp[n:] = 7                      # invalid ids in the padding must never be read
+    posp = torch.full((pad, 3), -1, dtype=torch.int32, device="cuda")
+    posp[:n] = pos_d
+    outp = torch.full((pad, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(jav.block_workspace_bytes(desc, pad), dtype=torch.uint8, device="cuda")
+    ws.view(torch.bfloat16)[:].fill_(float("nan"))
+    jav.block_forward(desc, xp, modp, posp, cu_d, ms, tab, wq, wo, out=outp, workspace=ws,
+                      n_tokens=n)
+    _sync()
+    assert torch.isfinite(outp[:n].float()).all()
+    assert torch.equal(outp[:n].view(torch.int16), out_ref.view(torch.int16))
+    assert torch.isnan(outp[n:].float()).all()
+    assert torch.equal(out_rep.view(torch.int16), out_ref.view(torch.int16))
