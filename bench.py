@@ -88,7 +88,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="full", choices=["small", "medium", "full", "varlen"])
     ap.add_argument("--causal", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-block", action="store_true",
                     help="skip the per-stage standalone timings (for profiler runs)")

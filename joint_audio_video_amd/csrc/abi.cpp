@@ -3,6 +3,7 @@
 // kernels of this directory; nothing here touches tensor data.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -173,6 +174,8 @@ static dit_status attn_check(dit_dtype dt, const void* q, int64_t ld_q, const vo
     return fail(DIT_EINVAL, "attn_packed: max_seqlen %d > n_tokens", max_seqlen);
   if (n_seqs > 65535 || n_heads > 65535)
     return fail(DIT_EUNSUPPORTED, "attn_packed: more than 65535 segments or heads");
+  if (dt == DIT_BF16 && (double)max_seqlen * (double)std::max(ld_k, ld_v) * 2.0 >= 4294967296.0)
+    return fail(DIT_EUNSUPPORTED, "attn_packed: a segment's K or V rows span 4 GiB or more");
   if (dt == DIT_BF16 ? head_dim != 128 : (head_dim != 64 && head_dim != 128))
     return fail(DIT_EUNSUPPORTED, "attn_packed: head_dim %d unsupported for this dtype", head_dim);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !ld_aligned(dt, ld_q) ||

@@ -38,121 +38,150 @@ namespace dit {
 namespace {
 
 constexpr int DH = 128;
-constexpr int QB = 128;   // queries per workgroup
 constexpr int KB = 64;    // keys per tile
 constexpr int kThreads = 256;
 
-// 32-bit word w (0..3) of a 16-byte vector.
-__device__ __forceinline__ uint32_t word_of(const uint4& r, int w) {
-  return w < 2 ? (w == 0 ? r.x : r.y) : (w == 2 ? r.z : r.w);
+// Buffer resource over [base, base + bytes): raw (unstrided) addressing with
+// the hardware range check, so a load at or past `bytes` reads zero (also
+// when it writes straight into LDS).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, if lane 4k'+q supplies the address of V[K0 + k'][D0 + 4q .. +3], lane j
+// receives V[K0 + k][D0 + j] for k = 0..3: four consecutive keys of one column.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(reinterpret_cast<__attribute__((address_space(3))) char*>(
+          reinterpret_cast<uintptr_t>(p))));
+}
+
+// Reference max moves only when a row's running max grows by more than this
+// (log2 units), so the O rescale is rare; p <= 2^kLazyLog2 meanwhile.
+constexpr float kLazyLog2 = 8.0f;
+
+// Wave = 64 queries (two 32-query blocks); workgroup = 4 waves = 256 queries.
+constexpr int QW = 64;
+constexpr int QBLK = kThreads / 64 * QW;   // 256 queries per workgroup
+
+// LDS tiles, row-major [key][d] (256 B per key row), 16-byte chunks XOR-swizzled:
+// K: chunk ^ (row & 7), so the 32 rows of an S^T fragment read spread over banks;
+// V: chunk ^ 2*(row & 3), so the four rows of a transposed read do.
+__device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 7); }
+__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (2 * (row & 3)); }
+
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, uint16_t* __restrict__ o, int64_t ld_o,
     const int32_t* __restrict__ cu, float scale_log2, int causal) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * DH];   // [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DH * KB];   // [d][key]
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KB * DH];
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
-  const int nqt = (seg1 - seg0 + QB - 1) / QB;
+  const int nqt = (seg1 - seg0 + QBLK - 1) / QBLK;
   if ((int)blockIdx.x >= nqt) return;
   const int qt = causal ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  const int q0 = seg0 + qt * QB;
+  const int q0 = seg0 + qt * QBLK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int qw0 = q0 + wave * 32;
-  const int qrow = qw0 + l32;
-  const bool qvalid = qrow < seg1;
+  const int qw0 = q0 + wave * QW;
 
-  // Q^T fragments (B operand of S^T = K Q^T): lane (query l32, half g) holds
-  // d = 16*ks + 8*g .. +7.
-  bf16x8 qf[DH / 16];
-  {
+  // Q^T fragments (B operand of S^T = K Q^T) for both query blocks: lane
+  // (query l32 of block qb, half g) holds d = 16*ks + 8*g .. +7.
+  bf16x8 qf[2][DH / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw0 + 32 * qb + l32;
     const uint16_t* qp = q + (int64_t)qrow * ld_q + h * DH + g * 8;
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
-      uint4 r = qvalid ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, r);
+      uint4 r = qrow < seg1 ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, r);
     }
   }
 
-  const int kend = causal ? min(seg1, q0 + QB) : seg1;
+  const int kend = causal ? min(seg1, q0 + QBLK) : seg1;
   const int nkt = (kend - seg0 + KB - 1) / KB;
 
-  // Staging: K tile = 64 rows x 16 chunks of 16 B (4 per thread); V tile =
-  // thread (key quad kq = tid/16, d chunk tid%16) loads 4 keys x 8 d.
-  uint4 rk[4], rv[4];
-  const int vkq = tid >> 4, vd0 = (tid & 15) * 8;
-  auto gload = [&](int kb) {
+  // Global -> LDS, 16 bytes per lane straight into LDS: slot s = 256*i + tid of
+  // a tile is key row s/16, physical chunk s%16; the swizzle is applied on the
+  // global side.  Offsets are bytes from key row seg0 of this head; rows past
+  // the segment end fall outside the buffer range and arrive as zeros.
+  const uint32_t seg_rows = (uint32_t)(seg1 - seg0);
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(k + (int64_t)seg0 * ld_k + h * DH, seg_rows * (uint32_t)ld_k * 2u);
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(v + (int64_t)seg0 * ld_v + h * DH, seg_rows * (uint32_t)ld_v * 2u);
+  const int srow = tid >> 4, pch = tid & 15;
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * i + srow;
+    koff[i] = (uint32_t)row * (uint32_t)ld_k * 2u + (uint32_t)k_chunk(row, pch) * 16u;
+    voff[i] = (uint32_t)row * (uint32_t)ld_v * 2u + (uint32_t)v_chunk(row, pch) * 16u;
+  }
+  const uint32_t k_tstep = (uint32_t)KB * (uint32_t)ld_k * 2u;
+  const uint32_t v_tstep = (uint32_t)KB * (uint32_t)ld_v * 2u;
+  auto issue = [&](int buf, int tile) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 4, ch = idx & 15;
-      const int key = kb + row;
-      rk[i] = key < seg1 ? *reinterpret_cast<const uint4*>(k + (int64_t)key * ld_k + h * DH + ch * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + vkq * 4 + i;
-      rv[i] = key < seg1 ? *reinterpret_cast<const uint4*>(v + (int64_t)key * ld_v + h * DH + vd0)
-                         : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 4, ch = idx & 15;
-      *reinterpret_cast<uint4*>(&Ks[buf][row * DH + ((ch ^ (row & 7)) * 8)]) = rk[i];
-    }
-    // transpose 4 keys x 8 d into 8 rows of V^T, 4 keys (8 bytes) each
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int sh = (dd & 1) * 16;
-      const uint32_t a0 = (word_of(rv[0], dd >> 1) >> sh) & 0xffffu;
-      const uint32_t a1 = (word_of(rv[1], dd >> 1) >> sh) & 0xffffu;
-      const uint32_t a2 = (word_of(rv[2], dd >> 1) >> sh) & 0xffffu;
-      const uint32_t a3 = (word_of(rv[3], dd >> 1) >> sh) & 0xffffu;
-      const int row = vd0 + dd;
-      const int chunk = vkq ^ (row & 15);
-      *reinterpret_cast<uint2*>(&Vt[buf][row * KB + chunk * 4]) =
-          make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, &Ks[buf][(256 * i + 64 * wave) * 8], 16, koff[i],
+                                               (int)(tile * k_tstep), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, &Vs[buf][(256 * i + 64 * wave) * 8], 16, voff[i],
+                                               (int)(tile * v_tstep), 0, 0);
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 oacc[DH / 32];
-#pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+  // Per-lane LDS element offsets of the fragment reads.
+  // K (A operand of S^T): key row 32b + l32, logical chunk 2ks + g.
+  // V^T (A operand of O^T): 16-lane group t = lane/16 covers d = 32db + 16(t&1) + j
+  // and lane half g = t>>1; source lane i = 4k' + q points at key row
+  // base + k' (+8 for the second read), d column 32db + 16(t&1) + 4q, where
+  // base = 32b + 16u + 4g for PV step s = 2b + u.
+  const int tq = lane & 15, kk = tq >> 2, qq = tq & 3, t1 = (lane >> 4) & 1;
 
-  gload(seg0);
-  lstore(0);
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  f32x16 oacc[2][DH / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.0f;
+  const float lazy_raw = kLazyLog2 / scale_log2;   // threshold in raw score units
+  const f32x16 zero16 = {};
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int j = 0; j < nkt; ++j) {
     const int buf = j & 1;
     const int kb = seg0 + j * KB;
-    if (j + 1 < nkt) gload(kb + KB);
+    if (j + 1 < nkt) issue(buf ^ 1, j + 1);
+    const uint16_t* ks_t = Ks[buf];
+    const uint16_t* vs_t = Vs[buf];
 
-    // S^T[key][query] for the tile's 64 keys: two 32-key blocks.
-    f32x16 sacc[2];
+    // S^T[key][query]: key blocks b, query blocks qb; each K fragment feeds both.
+    f32x16 sacc[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[b][e] = 0.0f;
       const int krow = 32 * b + l32;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            &Ks[buf][krow * DH + (((2 * ks + g) ^ (krow & 7)) * 8)]);
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[b], 0, 0, 0);
+            ks_t + krow * DH + k_chunk(krow, 2 * ks + g) * 8);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[b][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              kf, qf[qb][ks], ks == 0 ? zero16 : sacc[b][qb], 0, 0, 0);
       }
     }
 
@@ -160,74 +189,103 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const bool need_mask = (kb + KB > seg1) || (causal && kb + KB - 1 > qw0);
     if (need_mask) {
 #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = qw0 + 32 * qb + l32;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
+            if (key >= seg1 || (causal && key > qrow)) sacc[b][qb][e] = -INFINITY;
+          }
+      }
+    }
+
+    float mx[2];
+    bool grow[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = sacc[0][qb][0];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[b][qb][e]);
+      mx[qb] = half_swap_max(m);
+      grow[qb] = mx[qb] > m_run[qb] + lazy_raw;
+    }
+    // Lazy rescale: move the reference max (and rescale O, l) only when some
+    // row's max grew by more than the threshold; o/l is unchanged either way.
+    if (__builtin_amdgcn_ballot_w64(grow[0] || grow[1]) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = grow[qb] ? mx[qb] : m_run[qb];
+        const float alpha =
+            grow[qb] ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2) : 1.0f;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+        m_run[qb] = m_new;
+      }
+    }
+    bf16x8 pf[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float nms = -(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]) * scale_log2;
+      float rs = 0.0f;
+#pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
-          if (key >= seg1 || (causal && key > qrow)) sacc[b][e] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][qb][e], scale_log2, nms));
+          rs += p;
+          pf[qb][2 * b + (e >> 3)][e & 7] = (__bf16)p;
         }
+      l_run[qb] += rs;
     }
 
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[b][e]);
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
-    const float nms = -m_use * scale_log2;
-    float rs = 0.0f;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
-        rs += p;
-        pf[2 * b + (e >> 3)][e & 7] = (__bf16)p;
-      }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-
-    // O^T += V^T P^T.  Step s covers S^T block b = s/2, elements 8(s%2)..+7,
-    // i.e. keys base..base+3 and base+8..base+11 with base = 32b + 16(s%2) + 4g.
+    // O^T += V^T P^T.  Step s = 2b + u covers S^T block b, elements 8u..8u+7:
+    // keys base..base+3 and base+8..base+11 with base = 32b + 16u + 4g.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int c1 = 8 * (s >> 1) + 4 * (s & 1) + g;   // 8-byte chunk (4 keys)
-      const int c2 = c1 + 2;
+      const int base = 32 * (s >> 1) + 16 * (s & 1) + 4 * g;
+      const int r1 = base + kk, r2 = base + 8 + kk;
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        const int drow = 32 * db + l32;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[buf][drow * KB + ((c1 ^ (drow & 15)) * 4)]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[buf][drow * KB + ((c2 ^ (drow & 15)) * 4)]);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
+        const int c = 4 * db + 2 * t1 + (qq >> 1);          // logical 16-byte chunk
+        const v4i16 lo = lds_read_tr16(vs_t + r1 * DH + v_chunk(r1, c) * 8 + (qq & 1) * 4);
+        const v4i16 hi = lds_read_tr16(vs_t + r2 * DH + v_chunk(r2, c) * 8 + (qq & 1) * 4);
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][s], oacc[qb][db], 0, 0, 0);
       }
     }
 
-    if (j + 1 < nkt) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  const float l_tot = half_swap_sum(l_run);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-    uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw0 + 32 * qb + l32;
+    const float l_tot = half_swap_sum(l_run[qb]);
+    const float inv = 1.0f / l_tot;
+    if (qrow < seg1) {
+      uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d = 32 * db + qd * 8 + g * 4;
-        const uint2 w = make_uint2(pack_bf16x2(oacc[db][4 * qd + 0] * inv, oacc[db][4 * qd + 1] * inv),
-                                   pack_bf16x2(oacc[db][4 * qd + 2] * inv, oacc[db][4 * qd + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = w;
-      }
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int d = 32 * db + qd * 8 + g * 4;
+          const uint2 w =
+              make_uint2(pack_bf16x2(oacc[qb][db][4 * qd + 0] * inv, oacc[qb][db][4 * qd + 1] * inv),
+                         pack_bf16x2(oacc[qb][db][4 * qd + 2] * inv, oacc[qb][db][4 * qd + 3] * inv));
+          *reinterpret_cast<uint2*>(op + d) = w;
+        }
+    }
   }
 }
 
@@ -295,7 +353,7 @@ hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int
   if (n_seqs > 65535 || n_heads > 65535 || n_tokens > INT32_MAX) return hipErrorInvalidValue;
   if (bf16) {
     if (head_dim != DH) return hipErrorInvalidValue;
-    const dim3 grid((max_seqlen + QB - 1) / QB, n_seqs, n_heads);
+    const dim3 grid((max_seqlen + QBLK - 1) / QBLK, n_seqs, n_heads);
     attn_bf16_kernel<<<grid, dim3(kThreads), 0, s>>>(
         static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
         static_cast<const uint16_t*>(v), ld_v, static_cast<uint16_t*>(o), ld_o, cu,

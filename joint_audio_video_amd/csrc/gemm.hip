@@ -55,6 +55,7 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsize;
 }
 
+template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
     uint16_t* C, int64_t ldc, int M, int N, int K, EpiArgs ep) {
@@ -71,27 +72,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // Global -> LDS staging: 8 chunks of A and 8 of B per thread per k-step.
-  uint4 ra[8], rb[8];
-  auto gload = [&](int k0) {
+  // Global -> LDS with buffer_load_dwordx4 ... lds: lane slot s = 256*i + tid
+  // of a tile lands at LDS element 8*s, i.e. row s/8, physical chunk s%8.
+  // The swizzle is applied on the global side: that slot holds logical chunk
+  // (s%8) ^ (row & 7).  For this thread the row is 32*i + tid/8 and the
+  // logical chunk (tid&7) ^ ((tid>>3)&7) for every i.  Rows past M (N) are
+  // clamped to the last valid row: their results are never stored.  Offsets
+  // are bytes from the tile's first row; the k offset is a scalar.
+  const int lrow = tid >> 3;
+  const int lchunk = (tid & 7) ^ ((tid >> 3) & 7);
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + (int64_t)m0 * lda), 0, (int)((uint32_t)rows_a * (uint32_t)lda * 2u),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B + (int64_t)n0 * K), 0, (int)((uint32_t)rows_b * (uint32_t)K * 2u),
+      0x00020000);
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    aoff[i] = ((uint32_t)min(32 * i + lrow, rows_a - 1) * (uint32_t)lda + lchunk * 8) * 2u;
+    boff[i] = ((uint32_t)min(32 * i + lrow, rows_b - 1) * (uint32_t)K + lchunk * 8) * 2u;
+  }
+  auto issue = [&](int buf, int k0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 3, ch = idx & 7;
-      const int gm = m0 + row, gn = n0 + row;
-      ra[i] = gm < M ? *reinterpret_cast<const uint4*>(A + (int64_t)gm * lda + k0 + ch * 8)
-                     : make_uint4(0, 0, 0, 0);
-      rb[i] = gn < N ? *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + k0 + ch * 8)
-                     : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<uint4*>(&As[buf][row * BK + swz(row, ch) * 8]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][row * BK + swz(row, ch) * 8]) = rb[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &As[buf][(256 * i + 64 * wave) * 8], 16, aoff[i],
+                                               k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &Bs[buf][(256 * i + 64 * wave) * 8], 16, boff[i],
+                                               k0 * 2, 0, 0);
     }
   };
 
@@ -104,12 +113,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = K / BK;
-  gload(0);
-  lstore(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    if (kt + 1 < nk) issue(buf ^ 1, (kt + 1) * BK);
     const uint16_t* as = As[buf];
     const uint16_t* bs = Bs[buf];
 #pragma unroll
@@ -131,28 +140,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         for (int nb = 0; nb < 4; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // Epilogue.  acc[mb][nb][i] sits at row (i/4)*8 + g*4 + i%4, column l32 of its block.
+  const int row_base = m0 + wm * 128 + g * 4;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int col = n0 + wn * 128 + nb * 32 + l32;
-    if (col >= N) continue;
-    const float bias = ep.bias ? bf16_to_f32(ep.bias[col]) : 0.0f;
+    if (col < N) {
+      const float bias = ep.bias ? bf16_to_f32(ep.bias[col]) : 0.0f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = m0 + wm * 128 + mb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (row < M) {
-          float v = acc[mb][nb][i] + bias;
-          if (ep.kind == 1) {
-            const float gt = ep.gate[ep.mod[row] * ep.gate_stride + col];
-            v = fmaf(gt, v, bf16_to_f32(ep.x[(int64_t)row * ep.ld_x + col]));
+        for (int i = 0; i < 16; ++i) {
+          const int row = row_base + mb * 32 + (i >> 2) * 8 + (i & 3);
+          if (row < M) {
+            float v = acc[mb][nb][i] + bias;
+            if constexpr (KIND == 1) {
+              const float gt = ep.gate[ep.mod[row] * ep.gate_stride + col];
+              v = fmaf(gt, v, bf16_to_f32(ep.x[(int64_t)row * ep.ld_x + col]));
+            }
+            C[(int64_t)row * ldc + col] = f32_to_bf16(v);
           }
-          C[(int64_t)row * ldc + col] = f32_to_bf16(v);
         }
       }
     }
@@ -214,9 +225,14 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
     const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
               ep.ld_x, ep.mod, ep.gate, gate_stride};
-    gemm_bf16_kernel<<<dim3(tiles), dim3(kThreads), 0, s>>>(
-        static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
-        static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
+    if (ep.kind == 1)
+      gemm_bf16_kernel<1><<<dim3(tiles), dim3(kThreads), 0, s>>>(
+          static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
+          static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
+    else
+      gemm_bf16_kernel<0><<<dim3(tiles), dim3(kThreads), 0, s>>>(
+          static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
+          static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
   } else {
     const dim3 grid((n + FT - 1) / FT, (unsigned)((m + FT - 1) / FT));
     gemm_f32_kernel<<<grid, dim3(256), 0, s>>>(
