@@ -49,6 +49,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
@@ -64,9 +65,11 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
 // (log2 units), so the O rescale is rare; p <= 2^kLazyLog2 meanwhile.
 constexpr float kLazyLog2 = 8.0f;
 
-// Wave = 64 queries (two 32-query blocks); workgroup = 4 waves = 256 queries.
-constexpr int QW = 64;
-constexpr int QBLK = kThreads / 64 * QW;   // 256 queries per workgroup
+// Wave = 32 queries; workgroup = 8 waves = 256 queries, two waves per SIMD so
+// one wave's MFMAs overlap the other's softmax.
+constexpr int kWaves = 8;
+constexpr int kAttnThreads = 64 * kWaves;
+constexpr int QBLK = 32 * kWaves;   // queries per workgroup
 
 // LDS tiles, row-major [key][d] (256 B per key row), 16-byte chunks XOR-swizzled:
 // K: chunk ^ (row & 7), so the 32 rows of an S^T fragment read spread over banks;
@@ -74,7 +77,7 @@ constexpr int QBLK = kThreads / 64 * QW;   // 256 queries per workgroup
 __device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 7); }
 __device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (2 * (row & 3)); }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, uint16_t* __restrict__ o, int64_t ld_o,
     const int32_t* __restrict__ cu, float scale_log2, int causal) {
@@ -91,26 +94,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int qw0 = q0 + wave * QW;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
 
-  // Q^T fragments (B operand of S^T = K Q^T) for both query blocks: lane
-  // (query l32 of block qb, half g) holds d = 16*ks + 8*g .. +7.
-  bf16x8 qf[2][DH / 16];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = qw0 + 32 * qb + l32;
+  // Q^T fragments (B operand of S^T = K Q^T): lane (query l32, half g) holds
+  // d = 16*ks + 8*g .. +7.
+  bf16x8 qf[DH / 16];
+  {
     const uint16_t* qp = q + (int64_t)qrow * ld_q + h * DH + g * 8;
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
       uint4 r = qrow < seg1 ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, r);
+      qf[ks] = __builtin_bit_cast(bf16x8, r);
     }
   }
 
   const int kend = causal ? min(seg1, q0 + QBLK) : seg1;
   const int nkt = (kend - seg0 + KB - 1) / KB;
 
-  // Global -> LDS, 16 bytes per lane straight into LDS: slot s = 256*i + tid of
+  // Global -> LDS, 16 bytes per lane straight into LDS: slot s = 512*i + tid of
   // a tile is key row s/16, physical chunk s%16; the swizzle is applied on the
   // global side.  Offsets are bytes from key row seg0 of this head; rows past
   // the segment end fall outside the buffer range and arrive as zeros.
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc(v + (int64_t)seg0 * ld_v + h * DH, seg_rows * (uint32_t)ld_v * 2u);
   const int srow = tid >> 4, pch = tid & 15;
-  uint32_t koff[4], voff[4];
+  uint32_t koff[2], voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * i + srow;
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * i + srow;
     koff[i] = (uint32_t)row * (uint32_t)ld_k * 2u + (uint32_t)k_chunk(row, pch) * 16u;
     voff[i] = (uint32_t)row * (uint32_t)ld_v * 2u + (uint32_t)v_chunk(row, pch) * 16u;
   }
@@ -131,32 +133,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const uint32_t v_tstep = (uint32_t)KB * (uint32_t)ld_v * 2u;
   auto issue = [&](int buf, int tile) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, &Ks[buf][(256 * i + 64 * wave) * 8], 16, koff[i],
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, &Ks[buf][(512 * i + 64 * wave) * 8], 16, koff[i],
                                                (int)(tile * k_tstep), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, &Vs[buf][(256 * i + 64 * wave) * 8], 16, voff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, &Vs[buf][(512 * i + 64 * wave) * 8], 16, voff[i],
                                                (int)(tile * v_tstep), 0, 0);
     }
   };
 
-  // Per-lane LDS element offsets of the fragment reads.
-  // K (A operand of S^T): key row 32b + l32, logical chunk 2ks + g.
-  // V^T (A operand of O^T): 16-lane group t = lane/16 covers d = 32db + 16(t&1) + j
+  // V^T fragment reads: 16-lane group t = lane/16 covers d = 32db + 16(t&1) + j
   // and lane half g = t>>1; source lane i = 4k' + q points at key row
   // base + k' (+8 for the second read), d column 32db + 16(t&1) + 4q, where
   // base = 32b + 16u + 4g for PV step s = 2b + u.
   const int tq = lane & 15, kk = tq >> 2, qq = tq & 3, t1 = (lane >> 4) & 1;
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  f32x16 oacc[2][DH / 32];
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 oacc[DH / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
   const float lazy_raw = kLazyLog2 / scale_log2;   // threshold in raw score units
   const f32x16 zero16 = {};
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -169,8 +168,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     const uint16_t* ks_t = Ks[buf];
     const uint16_t* vs_t = Vs[buf];
 
-    // S^T[key][query]: key blocks b, query blocks qb; each K fragment feeds both.
-    f32x16 sacc[2][2];
+    // S^T[key][query] for the tile's 64 keys: two 32-key blocks.
+    f32x16 sacc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int krow = 32 * b + l32;
@@ -178,72 +177,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       for (int ks = 0; ks < DH / 16; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
             ks_t + krow * DH + k_chunk(krow, 2 * ks + g) * 8);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[b][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              kf, qf[qb][ks], ks == 0 ? zero16 : sacc[b][qb], 0, 0, 0);
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? zero16 : sacc[b],
+                                                          0, 0, 0);
       }
     }
 
     // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.
-    const bool need_mask = (kb + KB > seg1) || (causal && kb + KB - 1 > qw0);
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qrow = qw0 + 32 * qb + l32;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
-            if (key >= seg1 || (causal && key > qrow)) sacc[b][qb][e] = -INFINITY;
-          }
-      }
-    }
-
-    float mx[2];
-    bool grow[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m = sacc[0][qb][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[b][qb][e]);
-      mx[qb] = half_swap_max(m);
-      grow[qb] = mx[qb] > m_run[qb] + lazy_raw;
-    }
-    // Lazy rescale: move the reference max (and rescale O, l) only when some
-    // row's max grew by more than the threshold; o/l is unchanged either way.
-    if (__builtin_amdgcn_ballot_w64(grow[0] || grow[1]) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float m_new = grow[qb] ? mx[qb] : m_run[qb];
-        const float alpha =
-            grow[qb] ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2) : 1.0f;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
-        m_run[qb] = m_new;
-      }
-    }
-    bf16x8 pf[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float nms = -(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]) * scale_log2;
-      float rs = 0.0f;
+    if ((kb + KB > seg1) || (causal && kb + KB - 1 > qw0)) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][qb][e], scale_log2, nms));
-          rs += p;
-          pf[qb][2 * b + (e >> 3)][e & 7] = (__bf16)p;
+          const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
+          if (key >= seg1 || (causal && key > qrow)) sacc[b][e] = -INFINITY;
         }
-      l_run[qb] += rs;
     }
+
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[b][e]);
+    mx = half_swap_max(mx);
+    // Lazy rescale: move the reference max (and rescale O, l) only when some
+    // row's max grew by more than the threshold; o/l is unchanged either way.
+    const bool grow = mx > m_run + lazy_raw;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_run = m_new;
+    }
+    // P = exp2(S*c - m*c) as bf16 MFMA operands; row sums of the rounded P.
+    const float nms = -(m_run == -INFINITY ? 0.0f : m_run) * scale_log2;
+    bf16x8 pf[4];
+    float rs = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        bf16x2 pp;
+        pp[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
+        pp[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[b][e + 1], scale_log2, nms));
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, rs, false);
+        pf[2 * b + (e >> 3)][e & 7] = pp[0];
+        pf[2 * b + (e >> 3)][(e & 7) + 1] = pp[1];
+      }
+    l_run += rs;
 
     // O^T += V^T P^T.  Step s = 2b + u covers S^T block b, elements 8u..8u+7:
     // keys base..base+3 and base+8..base+11 with base = 32b + 16u + 4g.
@@ -258,9 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
         const v4i16 hi = lds_read_tr16(vs_t + r2 * DH + v_chunk(r2, c) * 8 + (qq & 1) * 4);
         const bf16x8 vf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][s], oacc[qb][db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
       }
     }
 
@@ -268,24 +250,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     __syncthreads();
   }
 
+  const float l_tot = half_swap_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (qrow < seg1) {
+    uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = qw0 + 32 * qb + l32;
-    const float l_tot = half_swap_sum(l_run[qb]);
-    const float inv = 1.0f / l_tot;
-    if (qrow < seg1) {
-      uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
+    for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int d = 32 * db + qd * 8 + g * 4;
-          const uint2 w =
-              make_uint2(pack_bf16x2(oacc[qb][db][4 * qd + 0] * inv, oacc[qb][db][4 * qd + 1] * inv),
-                         pack_bf16x2(oacc[qb][db][4 * qd + 2] * inv, oacc[qb][db][4 * qd + 3] * inv));
-          *reinterpret_cast<uint2*>(op + d) = w;
-        }
-    }
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d = 32 * db + qd * 8 + g * 4;
+        const uint2 w = make_uint2(pack_bf16x2(oacc[db][4 * qd + 0] * inv, oacc[db][4 * qd + 1] * inv),
+                                   pack_bf16x2(oacc[db][4 * qd + 2] * inv, oacc[db][4 * qd + 3] * inv));
+        *reinterpret_cast<uint2*>(op + d) = w;
+      }
   }
 }
 
@@ -354,7 +331,7 @@ hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int
   if (bf16) {
     if (head_dim != DH) return hipErrorInvalidValue;
     const dim3 grid((max_seqlen + QBLK - 1) / QBLK, n_seqs, n_heads);
-    attn_bf16_kernel<<<grid, dim3(kThreads), 0, s>>>(
+    attn_bf16_kernel<<<grid, dim3(kAttnThreads), 0, s>>>(
         static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
         static_cast<const uint16_t*>(v), ld_v, static_cast<uint16_t*>(o), ld_o, cu,
         scale * 1.4426950408889634f, causal);
