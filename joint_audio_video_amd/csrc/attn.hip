@@ -81,8 +81,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, uint16_t* __restrict__ o, int64_t ld_o,
     const int32_t* __restrict__ cu, float scale_log2, int causal) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KB * DH];
+  // Two LDS buffers per tensor as distinct objects: with the key loop unrolled
+  // by two, every access names its buffer at compile time, so the compiler can
+  // tell the prefetch into one buffer from the reads of the other and does not
+  // wait for the prefetch before reading.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[KB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[KB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[KB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[KB * DH];
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
@@ -131,12 +137,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   }
   const uint32_t k_tstep = (uint32_t)KB * (uint32_t)ld_k * 2u;
   const uint32_t v_tstep = (uint32_t)KB * (uint32_t)ld_v * 2u;
-  auto issue = [&](int buf, int tile) {
+  auto issue = [&](uint16_t* kdst, uint16_t* vdst, int tile) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, &Ks[buf][(512 * i + 64 * wave) * 8], 16, koff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kdst + (512 * i + 64 * wave) * 8, 16, koff[i],
                                                (int)(tile * k_tstep), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, &Vs[buf][(512 * i + 64 * wave) * 8], 16, voff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vdst + (512 * i + 64 * wave) * 8, 16, voff[i],
                                                (int)(tile * v_tstep), 0, 0);
     }
   };
@@ -157,16 +163,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   const f32x16 zero16 = {};
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  issue(0, 0);
+  issue(Ks0, Vs0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
+  // One key tile: prefetch tile j+1 into (kn, vn), compute tile j from (ks_t, vs_t).
+  auto tile_step = [&](const uint16_t* ks_t, const uint16_t* vs_t, uint16_t* kn, uint16_t* vn,
+                       int j) {
     const int kb = seg0 + j * KB;
-    if (j + 1 < nkt) issue(buf ^ 1, j + 1);
-    const uint16_t* ks_t = Ks[buf];
-    const uint16_t* vs_t = Vs[buf];
+    if (j + 1 < nkt) issue(kn, vn, j + 1);
 
     // S^T[key][query] for the tile's 64 keys: two 32-key blocks.
     f32x16 sacc[2];
@@ -248,6 +253,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int j = 0; j < nkt; j += 2) {
+    tile_step(Ks0, Vs0, Ks1, Vs1, j);
+    if (j + 1 < nkt) tile_step(Ks1, Vs1, Ks0, Vs0, j + 1);
   }
 
   const float l_tot = half_swap_sum(l_run);
