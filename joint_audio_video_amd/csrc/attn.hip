@@ -173,18 +173,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const int kb = seg0 + j * KB;
     if (j + 1 < nkt) issue(kn, vn, j + 1);
 
-    // S^T[key][query] for the tile's 64 keys: two 32-key blocks.
+    // S^T[key][query] for the tile's 64 keys: two 32-key blocks whose MFMA
+    // chains alternate; the K fragments of step ks+1 are read during step ks.
     f32x16 sacc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    auto kfrag = [&](int b, int ks) {
       const int krow = 32 * b + l32;
+      return *reinterpret_cast<const bf16x8*>(ks_t + krow * DH + k_chunk(krow, 2 * ks + g) * 8);
+    };
+    bf16x8 kf0 = kfrag(0, 0), kf1 = kfrag(1, 0);
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            ks_t + krow * DH + k_chunk(krow, 2 * ks + g) * 8);
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? zero16 : sacc[b],
-                                                          0, 0, 0);
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      bf16x8 nk0 = kf0, nk1 = kf1;
+      if (ks + 1 < DH / 16) {
+        nk0 = kfrag(0, ks + 1);
+        nk1 = kfrag(1, ks + 1);
       }
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[ks], ks == 0 ? zero16 : sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[ks], ks == 0 ? zero16 : sacc[1], 0, 0, 0);
+      kf0 = nk0;
+      kf1 = nk1;
     }
 
     // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.

@@ -59,8 +59,14 @@ template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
     uint16_t* C, int64_t ldc, int M, int N, int K, EpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+  // Two LDS buffers per operand as distinct objects: with the k loop unrolled
+  // by two, every access names its buffer at compile time, so the compiler
+  // can tell the prefetch into one buffer from the fragment reads of the other
+  // and does not wait for the prefetch before reading.
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN * BK];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -94,77 +100,104 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     aoff[i] = ((uint32_t)min(32 * i + lrow, rows_a - 1) * (uint32_t)lda + lchunk * 8) * 2u;
     boff[i] = ((uint32_t)min(32 * i + lrow, rows_b - 1) * (uint32_t)K + lchunk * 8) * 2u;
   }
-  auto issue = [&](int buf, int k0) {
+  auto issue = [&](uint16_t* adst, uint16_t* bdst, int k0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &As[buf][(256 * i + 64 * wave) * 8], 16, aoff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, adst + (256 * i + 64 * wave) * 8, 16, aoff[i],
                                                k0 * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &Bs[buf][(256 * i + 64 * wave) * 8], 16, boff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, bdst + (256 * i + 64 * wave) * 8, 16, boff[i],
                                                k0 * 2, 0, 0);
     }
   };
 
   f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  const f32x16 zero16 = {};
 
+  // One k-step of BK: prefetch step kt+1 into (an, bn), multiply from (as, bs).
+  // Fragments of sub-step ks+1 are read while the MFMAs of ks run.
   const int nk = K / BK;
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue(buf ^ 1, (kt + 1) * BK);
-    const uint16_t* as = As[buf];
-    const uint16_t* bs = Bs[buf];
+  // The first step starts every accumulator from an inline zero operand.
+  auto k_step = [&](const uint16_t* as, const uint16_t* bs, uint16_t* an, uint16_t* bn, int kt,
+                    bool first) {
+    if (kt + 1 < nk) issue(an, bn, (kt + 1) * BK);
+    auto frag = [&](const uint16_t* base, int row, int ks) {
+      return *reinterpret_cast<const bf16x8*>(&base[row * BK + swz(row, 2 * ks + g) * 8]);
+    };
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) af[mb] = frag(as, wm * 128 + mb * 32 + l32, 0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(bs, wn * 128 + nb * 32 + l32, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
+      bf16x8 an_[4], bn_[4];
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = wm * 128 + mb * 32 + l32;
-        af[mb] = *reinterpret_cast<const bf16x8*>(&as[row * BK + swz(row, 2 * ks + g) * 8]);
-      }
+        for (int mb = 0; mb < 4; ++mb) an_[mb] = frag(as, wm * 128 + mb * 32 + l32, ks + 1);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int row = wn * 128 + nb * 32 + l32;
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(&bs[row * BK + swz(row, 2 * ks + g) * 8]);
+        for (int nb = 0; nb < 4; ++nb) bn_[nb] = frag(bs, wn * 128 + nb * 32 + l32, ks + 1);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              bfr[nb], af[mb], (first && ks == 0) ? zero16 : acc[mb][nb], 0, 0, 0);
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[i] = an_[i];
+          bfr[i] = bn_[i];
+        }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  issue(As0, Bs0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  k_step(As0, Bs0, As1, Bs1, 0, true);
+  for (int kt = 1; kt < nk; kt += 2) {
+    k_step(As1, Bs1, As0, Bs0, kt, false);
+    if (kt + 1 < nk) k_step(As0, Bs0, As1, Bs1, kt + 1, false);
   }
 
-  // Epilogue.  acc[mb][nb][i] sits at row (i/4)*8 + g*4 + i%4, column l32 of its block.
-  const int row_base = m0 + wm * 128 + g * 4;
+  // Epilogue.  The MFMAs computed C^T: acc[mb][nb][i] is token row
+  // m0 + wm*128 + mb*32 + l32 and feature column n0 + wn*128 + nb*32 +
+  // (i/4)*8 + g*4 + i%4, so each lane holds runs of 4 consecutive features of
+  // one token and stores them as 8 bytes.
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int col = n0 + wn * 128 + nb * 32 + l32;
-    if (col < N) {
-      const float bias = ep.bias ? bf16_to_f32(ep.bias[col]) : 0.0f;
+  for (int mb = 0; mb < 4; ++mb) {
+    const int row = m0 + wm * 128 + mb * 32 + l32;
+    if (row >= M) continue;
+    uint16_t* crow = C + (int64_t)row * ldc;
+    const uint16_t* xrow = KIND == 1 ? ep.x + (int64_t)row * ep.ld_x : nullptr;
+    const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+    for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = row_base + mb * 32 + (i >> 2) * 8 + (i & 3);
-          if (row < M) {
-            float v = acc[mb][nb][i] + bias;
-            if constexpr (KIND == 1) {
-              const float gt = ep.gate[ep.mod[row] * ep.gate_stride + col];
-              v = fmaf(gt, v, bf16_to_f32(ep.x[(int64_t)row * ep.ld_x + col]));
-            }
-            C[(int64_t)row * ldc + col] = f32_to_bf16(v);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[mb][nb][4 * r + e];
+        if (ep.bias) {
+          const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
+          v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
         }
+        if constexpr (KIND == 1) {
+          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
+          const float4 gt = *reinterpret_cast<const float4*>(grow + col);
+          v[0] = fmaf(gt.x, v[0], bf16lo(xv.x));
+          v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
+          v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
+          v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
+        }
+        *reinterpret_cast<uint2*>(crow + col) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
   }
