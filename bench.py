@@ -14,8 +14,12 @@ oracle on a bounded row sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +31,69 @@ sys.path.insert(0, ROOT)
 METRIC = "DiT-block ms + attention TFLOP/s at 58,758 tokens; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6       # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+ATTN_KERNEL = "attn_bf16_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_full_hbm_traffic.md")
+KERNEL_SOURCES = ("joint_audio_video_amd/csrc/attn.hip", "joint_audio_video_amd/csrc/common.h")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the attention kernel's sources: the traffic figure is only valid for it."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None when
+    that summary was taken on different kernel sources (or does not exist)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def summarize_profile(kind: str, out_dir: str) -> int:
+    """Print a markdown summary of rocprofv3 CSV output (committed under profiles/)."""
+    if kind == "stats":
+        files = glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True)
+        if not files:
+            print(f"no kernel_stats.csv under {out_dir}", file=sys.stderr)
+            return 1
+        rows = list(csv.DictReader(open(files[0])))
+        print("| kernel | calls | avg ms | min ms | max ms | total % |")
+        print("|---|---|---|---|---|---|")
+        for r in rows:
+            name = r["Name"]
+            short = name.replace("(anonymous namespace)::", "").replace("void ", "")
+            short = re.sub(r"\(.*", "", short)
+            print(f"| {short[:60]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                  f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | "
+                  f"{float(r['Percentage']):.2f} |")
+        return 0
+    files = glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        print(f"no counter_collection.csv under {out_dir}", file=sys.stderr)
+        return 1
+    per = {}
+    for r in csv.DictReader(open(files[0])):
+        name = r["Kernel_Name"]
+        key = (ATTN_KERNEL if ATTN_KERNEL in name else
+               "copy" if "copy" in name.lower() else None)
+        if key is None:
+            continue
+        per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    for (k, c), vals in sorted(per.items()):
+        print(f"{k} {c} KiB/dispatch: " + ", ".join(f"{v:.0f}" for v in vals))
+    return 0
 
 
 def block_flops(n_tokens, d, cu, causal=False):
@@ -88,11 +155,15 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="full", choices=["small", "medium", "full", "varlen"])
     ap.add_argument("--causal", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only-block", action="store_true",
-                    help="skip the per-stage standalone timings (for profiler runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
+                    help="print a summary of rocprofv3 CSV output: KIND is stats or pmc")
     args = ap.parse_args()
+    if args.summarize_profile:
+        return summarize_profile(*args.summarize_profile)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the block is measured on one MI355X).", file=sys.stderr)
@@ -130,6 +201,15 @@ def main() -> int:
     def step():
         jav.block_forward(desc, x, mod, pos, cu, ms_len, table, w_qkv, w_o, out=out,
                           workspace=ws, stream=stream)
+
+    if args.copy_mib > 0:
+        # a plain copy of known size, so HBM counters can be scaled to bytes
+        n_el = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n_el, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -197,7 +277,7 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic() if (wl.name == "full" and not args.causal) else None,
         },
     }
     if not args.no_cpu_baseline:
