@@ -55,10 +55,9 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, if lane 4k'+q supplies the address of V[K0 + k'][D0 + 4q .. +3], lane j
 // receives V[K0 + k][D0 + j] for k = 0..3: four consecutive keys of one column.
-__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)(reinterpret_cast<__attribute__((address_space(3))) char*>(
-          reinterpret_cast<uintptr_t>(p))));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ v4i16 lds_read_tr16(const lds_u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
 }
 
 // Reference max moves only when a row's running max grows by more than this
@@ -67,9 +66,13 @@ constexpr float kLazyLog2 = 8.0f;
 
 // Wave = 32 queries; workgroup = 8 waves = 256 queries, two waves per SIMD so
 // one wave's MFMAs overlap the other's softmax.
-constexpr int kWaves = 8;
+#ifndef DIT_ATTN_WAVES
+#define DIT_ATTN_WAVES 8
+#endif
+constexpr int kWaves = DIT_ATTN_WAVES;
 constexpr int kAttnThreads = 64 * kWaves;
-constexpr int QBLK = 32 * kWaves;   // queries per workgroup
+constexpr int QBLK = 32 * kWaves;                  // queries per workgroup
+constexpr int kTileLoads = KB * DH * 2 / 16 / kAttnThreads;   // 16-byte loads per thread per tile
 
 // LDS tiles, row-major [key][d] (256 B per key row), 16-byte chunks XOR-swizzled:
 // K: chunk ^ (row & 7), so the 32 rows of an S^T fragment read spread over banks;
@@ -118,8 +121,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   const int kend = causal ? min(seg1, q0 + QBLK) : seg1;
   const int nkt = (kend - seg0 + KB - 1) / KB;
 
-  // Global -> LDS, 16 bytes per lane straight into LDS: slot s = 512*i + tid of
-  // a tile is key row s/16, physical chunk s%16; the swizzle is applied on the
+  // Global -> LDS, 16 bytes per lane straight into LDS: slot s = threads*i + tid
+  // of a tile is key row s/16, physical chunk s%16; the swizzle is applied on the
   // global side.  Offsets are bytes from key row seg0 of this head; rows past
   // the segment end fall outside the buffer range and arrive as zeros.
   const uint32_t seg_rows = (uint32_t)(seg1 - seg0);
@@ -128,10 +131,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc(v + (int64_t)seg0 * ld_v + h * DH, seg_rows * (uint32_t)ld_v * 2u);
   const int srow = tid >> 4, pch = tid & 15;
-  uint32_t koff[2], voff[2];
+  uint32_t koff[kTileLoads], voff[kTileLoads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 32 * i + srow;
+  for (int i = 0; i < kTileLoads; ++i) {
+    const int row = (kAttnThreads / 16) * i + srow;
     koff[i] = (uint32_t)row * (uint32_t)ld_k * 2u + (uint32_t)k_chunk(row, pch) * 16u;
     voff[i] = (uint32_t)row * (uint32_t)ld_v * 2u + (uint32_t)v_chunk(row, pch) * 16u;
   }
@@ -139,11 +142,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   const uint32_t v_tstep = (uint32_t)KB * (uint32_t)ld_v * 2u;
   auto issue = [&](uint16_t* kdst, uint16_t* vdst, int tile) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kdst + (512 * i + 64 * wave) * 8, 16, koff[i],
-                                               (int)(tile * k_tstep), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vdst + (512 * i + 64 * wave) * 8, 16, voff[i],
-                                               (int)(tile * v_tstep), 0, 0);
+    for (int i = 0; i < kTileLoads; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kdst + (kAttnThreads * i + 64 * wave) * 8, 16,
+                                               koff[i], (int)(tile * k_tstep), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vdst + (kAttnThreads * i + 64 * wave) * 8, 16,
+                                               voff[i], (int)(tile * v_tstep), 0, 0);
     }
   };
 
@@ -152,6 +155,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   // base + k' (+8 for the second read), d column 32db + 16(t&1) + 4q, where
   // base = 32b + 16u + 4g for PV step s = 2b + u.
   const int tq = lane & 15, kk = tq >> 2, qq = tq & 3, t1 = (lane >> 4) & 1;
+  // The XOR swizzles distribute over these lane bits, so every fragment
+  // address is one of a few per-lane bases plus a compile-time offset.
+  // V: logical chunk 4db + x (x = 2t1 + q1) of row 4g + kk + ... lands at
+  // physical chunk 4(db ^ zhi) + zlo with z = x ^ 2kk; db even/odd share a base.
+  int v_lane_off[2];
+  {
+    const int z = (2 * t1 + (qq >> 1)) ^ (2 * kk);
+    const int zlo = z & 3, zhi = z >> 2;
+    const int rowpart = (4 * g + kk) * DH + zlo * 8 + (qq & 1) * 4;
+    v_lane_off[0] = rowpart + 32 * zhi;          // d-blocks 0 and 2 (+64)
+    v_lane_off[1] = rowpart + 32 * (1 - zhi);    // d-blocks 1 and 3 (+64)
+  }
+  // K: chunk (2ks + g) ^ (row & 7) of row l32 = 2((ks & 4) | ((ks & 3) ^ v)) + w1
+  // with w = g ^ (l32 & 7), v = w >> 1.
+  int k_lane_off[4];
+  {
+    const int w = g ^ (l32 & 7);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k_lane_off[j] = l32 * DH + 16 * (j ^ (w >> 1)) + 8 * (w & 1);
+  }
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 oacc[DH / 32];
@@ -175,10 +198,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
     // S^T[key][query] for the tile's 64 keys: two 32-key blocks whose MFMA
     // chains alternate; the K fragments of step ks+1 are read during step ks.
+    // Fragment (b, ks) sits at element kbase[ks & 3] + 64*(ks & 4)/4 + 4096*b
+    // (the swizzle only permutes ks within groups of four).
     f32x16 sacc[2];
     auto kfrag = [&](int b, int ks) {
-      const int krow = 32 * b + l32;
-      return *reinterpret_cast<const bf16x8*>(ks_t + krow * DH + k_chunk(krow, 2 * ks + g) * 8);
+      return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ks & 3] + 16 * (ks & 4) + 4096 * b);
     };
     bf16x8 kf0 = kfrag(0, 0), kf1 = kfrag(1, 0);
 #pragma unroll
@@ -245,13 +269,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     // keys base..base+3 and base+8..base+11 with base = 32b + 16u + 4g.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int base = 32 * (s >> 1) + 16 * (s & 1) + 4 * g;
-      const int r1 = base + kk, r2 = base + 8 + kk;
+      const int rows = 32 * (s >> 1) + 16 * (s & 1);   // + 4g + kk (+8 for the high half)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        const int c = 4 * db + 2 * t1 + (qq >> 1);          // logical 16-byte chunk
-        const v4i16 lo = lds_read_tr16(vs_t + r1 * DH + v_chunk(r1, c) * 8 + (qq & 1) * 4);
-        const v4i16 hi = lds_read_tr16(vs_t + r2 * DH + v_chunk(r2, c) * 8 + (qq & 1) * 4);
+        const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db & 1] + 64 * (db >> 1) + rows * DH;
+        const v4i16 lo = lds_read_tr16(p);
+        const v4i16 hi = lds_read_tr16(p + 8 * DH);
         const bf16x8 vf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
