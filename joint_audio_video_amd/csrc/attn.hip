@@ -38,7 +38,11 @@ namespace dit {
 namespace {
 
 constexpr int DH = 128;
-constexpr int KB = 64;    // keys per tile
+#ifndef DIT_ATTN_KB
+#define DIT_ATTN_KB 64
+#endif
+constexpr int KB = DIT_ATTN_KB;   // keys per tile (a multiple of 32)
+constexpr int NKB = KB / 32;      // 32-key blocks per tile
 constexpr int kThreads = 256;
 
 // Buffer resource over [base, base + bytes): raw (unstrided) addressing with
@@ -200,28 +204,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     // chains alternate; the K fragments of step ks+1 are read during step ks.
     // Fragment (b, ks) sits at element kbase[ks & 3] + 64*(ks & 4)/4 + 4096*b
     // (the swizzle only permutes ks within groups of four).
-    f32x16 sacc[2];
+    f32x16 sacc[NKB];
     auto kfrag = [&](int b, int ks) {
       return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ks & 3] + 16 * (ks & 4) + 4096 * b);
     };
-    bf16x8 kf0 = kfrag(0, 0), kf1 = kfrag(1, 0);
+    bf16x8 kf[NKB];
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) kf[b] = kfrag(b, 0);
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
-      bf16x8 nk0 = kf0, nk1 = kf1;
-      if (ks + 1 < DH / 16) {
-        nk0 = kfrag(0, ks + 1);
-        nk1 = kfrag(1, ks + 1);
-      }
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[ks], ks == 0 ? zero16 : sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[ks], ks == 0 ? zero16 : sacc[1], 0, 0, 0);
-      kf0 = nk0;
-      kf1 = nk1;
+      bf16x8 nk[NKB];
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) nk[b] = ks + 1 < DH / 16 ? kfrag(b, ks + 1) : kf[b];
+#pragma unroll
+      for (int b = 0; b < NKB; ++b)
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[b], qf[ks], ks == 0 ? zero16 : sacc[b],
+                                                          0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) kf[b] = nk[b];
     }
 
     // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.
     if ((kb + KB > seg1) || (causal && kb + KB - 1 > qw0)) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < NKB; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
     float mx = sacc[0][0];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NKB; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[b][e]);
     mx = half_swap_max(mx);
@@ -250,10 +256,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     }
     // P = exp2(S*c - m*c) as bf16 MFMA operands; row sums of the rounded P.
     const float nms = -(m_run == -INFINITY ? 0.0f : m_run) * scale_log2;
-    bf16x8 pf[4];
+    bf16x8 pf[2 * NKB];
     float rs = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NKB; ++b)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         bf16x2 pp;
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     // O^T += V^T P^T.  Step s = 2b + u covers S^T block b, elements 8u..8u+7:
     // keys base..base+3 and base+8..base+11 with base = 32b + 16u + 4g.
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2 * NKB; ++s) {
       const int rows = 32 * (s >> 1) + 16 * (s & 1);   // + 4g + kk (+8 for the high half)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
