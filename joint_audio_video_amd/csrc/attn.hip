@@ -8,20 +8,26 @@
 // is a variant ([VeRL-Omni] section 3 mentions causal attention).
 //
 // bf16 path (head_dim 128): flash-style forward on CDNA4 bf16 MFMA.
-//   * Workgroup = 4 waves = 128 queries of one (segment, head); each wave owns
-//     32 queries and walks the segment's keys in tiles of 64.
+//   * Workgroup = 8 waves = 256 queries of one (segment, head), two waves per
+//     SIMD; each wave owns 32 queries and walks the segment's keys in tiles
+//     of 64.
 //   * The products are computed transposed, S^T = K Q^T and O^T = V^T P^T,
 //     with v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
 //     then holds one query column and 16 key (or head-dim) rows, so the
 //     softmax row max/sum is lane-local over 32 scores plus one exchange
 //     between lanes l and l^32 (v_permlane32_swap), and the online-softmax
 //     rescale of O is a per-lane scalar.
-//   * Q stays in registers for the whole key loop.  K tiles ([key][d]) and
-//     transposed V tiles ([d][key]) are double-buffered in LDS (64 KB per
-//     workgroup, two workgroups per CU) with XOR-swizzled chunk indices; the
-//     next tile's global loads are issued before the current tile's MFMAs.
+//   * Q stays in registers for the whole key loop.  K tiles and V tiles (both
+//     [key][d], 256 B rows) are double-buffered in LDS (64 KB per workgroup)
+//     with XOR-swizzled 16-byte chunks, filled by buffer loads that write
+//     straight into LDS; V^T fragments come from transposing LDS reads.
+//   * Ping-pong: the two waves sharing a SIMD run half a phase apart, so one
+//     wave's softmax (exp, convert: plain VALU) overlaps the other's MFMAs.
+//     Row sums are fp32 adds, not v_dot2 (which shares the matrix pipe and
+//     would serialise with the other wave's MFMAs).
 //   * exp2 with log2(e) folded into the scale; P is rounded to bf16 for the
-//     PV product; accumulation in float32.
+//     PV product, its row sum is taken over the fp32 values; accumulation in
+//     float32.
 //   * Masking (segment tail, causal diagonal) runs only on tiles that need
 //     it; out-of-segment K/V rows are zero-filled, never read, so padding rows
 //     holding NaN cannot leak in.  Causal launches longest q-tiles first.
@@ -53,7 +59,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
@@ -68,8 +73,14 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const lds_u16* p) {
 // (log2 units), so the O rescale is rare; p <= 2^kLazyLog2 meanwhile.
 constexpr float kLazyLog2 = 8.0f;
 
-// Wave = 32 queries; workgroup = 8 waves = 256 queries, two waves per SIMD so
-// one wave's MFMAs overlap the other's softmax.
+// LDS fragment reads are issued this many k-steps (S^T) or MFMAs (PV) ahead of
+// the MFMA that consumes them; scheduling fences keep the compiler from
+// sinking them next to their use, which would expose the LDS latency.
+constexpr int kKAhead = 2;
+constexpr int kVAhead = 2;
+
+// Wave = 32 queries; workgroup = 8 waves = 256 queries, two waves per SIMD
+// (waves w and w + 4 share one).
 #ifndef DIT_ATTN_WAVES
 #define DIT_ATTN_WAVES 8
 #endif
@@ -144,14 +155,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   }
   const uint32_t k_tstep = (uint32_t)KB * (uint32_t)ld_k * 2u;
   const uint32_t v_tstep = (uint32_t)KB * (uint32_t)ld_v * 2u;
-  auto issue = [&](uint16_t* kdst, uint16_t* vdst, int tile) {
+  auto issue_k = [&](uint16_t* kdst, int tile) {
 #pragma unroll
-    for (int i = 0; i < kTileLoads; ++i) {
+    for (int i = 0; i < kTileLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kdst + (kAttnThreads * i + 64 * wave) * 8, 16,
                                                koff[i], (int)(tile * k_tstep), 0, 0);
+  };
+  auto issue_v = [&](uint16_t* vdst, int tile) {
+#pragma unroll
+    for (int i = 0; i < kTileLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vdst + (kAttnThreads * i + 64 * wave) * 8, 16,
                                                voff[i], (int)(tile * v_tstep), 0, 0);
-    }
   };
 
   // V^T fragment reads: 16-lane group t = lane/16 covers d = 32db + 16(t&1) + j
@@ -188,43 +202,49 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
   const float lazy_raw = kLazyLog2 / scale_log2;   // threshold in raw score units
   const f32x16 zero16 = {};
-  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  issue(Ks0, Vs0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Ping-pong: the two waves sharing a SIMD (w and w + kWaves/2) are half a
+  // phase apart.  In phase t every wave runs PV of tile t-1 and S^T of tile t;
+  // the leading half does the softmax of tile t after its MFMAs, the lagging
+  // half the softmax of tile t-1 before them, so one wave's exp/convert work
+  // overlaps the other's MFMAs (raised wave priority during the MFMA run
+  // keeps the matrix pipe fed first).  Phase t reads K(t) and V(t-1) and
+  // loads K(t+1) and V(t); the barrier ending it frees both buffers.
+  const bool lagging = wave >= kWaves / 2;
+  f32x16 sacc[NKB];
+  bf16x8 pf[2 * NKB];
 
-  // One key tile: prefetch tile j+1 into (kn, vn), compute tile j from (ks_t, vs_t).
-  auto tile_step = [&](const uint16_t* ks_t, const uint16_t* vs_t, uint16_t* kn, uint16_t* vn,
-                       int j) {
-    const int kb = seg0 + j * KB;
-    if (j + 1 < nkt) issue(kn, vn, j + 1);
-
-    // S^T[key][query] for the tile's 64 keys: two 32-key blocks whose MFMA
-    // chains alternate; the K fragments of step ks+1 are read during step ks.
-    // Fragment (b, ks) sits at element kbase[ks & 3] + 64*(ks & 4)/4 + 4096*b
-    // (the swizzle only permutes ks within groups of four).
-    f32x16 sacc[NKB];
+  // S^T[key][query] of one tile: two 32-key blocks whose MFMA chains
+  // alternate.  Fragment (b, ks) sits at element k_lane_off[ks & 3] +
+  // 16*(ks & 4) + 4096*b (the swizzle only permutes ks within groups of four).
+  auto compute_s = [&](const uint16_t* ks_t) __attribute__((always_inline)) {
     auto kfrag = [&](int b, int ks) {
       return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ks & 3] + 16 * (ks & 4) + 4096 * b);
     };
-    bf16x8 kf[NKB];
+    bf16x8 kf[DH / 16][NKB];
 #pragma unroll
-    for (int b = 0; b < NKB; ++b) kf[b] = kfrag(b, 0);
+    for (int ks = 0; ks < kKAhead; ++ks)
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) kf[ks][b] = kfrag(b, ks);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
-      bf16x8 nk[NKB];
-#pragma unroll
-      for (int b = 0; b < NKB; ++b) nk[b] = ks + 1 < DH / 16 ? kfrag(b, ks + 1) : kf[b];
 #pragma unroll
       for (int b = 0; b < NKB; ++b)
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[b], qf[ks], ks == 0 ? zero16 : sacc[b],
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][b], qf[ks], ks == 0 ? zero16 : sacc[b],
                                                           0, 0, 0);
+      if (ks + kKAhead < DH / 16) {
 #pragma unroll
-      for (int b = 0; b < NKB; ++b) kf[b] = nk[b];
+        for (int b = 0; b < NKB; ++b) kf[ks + kKAhead][b] = kfrag(b, ks + kKAhead);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.
+  // Online softmax of tile j (scores in sacc) into the bf16 operand pf.
+  // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int kb = seg0 + j * KB;
     if ((kb + KB > seg1) || (causal && kb + KB - 1 > qw0)) {
 #pragma unroll
       for (int b = 0; b < NKB; ++b)
@@ -234,7 +254,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
           if (key >= seg1 || (causal && key > qrow)) sacc[b][e] = -INFINITY;
         }
     }
-
     float mx = sacc[0][0];
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
@@ -254,45 +273,66 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
       m_run = m_new;
     }
-    // P = exp2(S*c - m*c) as bf16 MFMA operands; row sums of the rounded P.
     const float nms = -(m_run == -INFINITY ? 0.0f : m_run) * scale_log2;
-    bf16x8 pf[2 * NKB];
     float rs = 0.0f;
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        bf16x2 pp;
-        pp[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
-        pp[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[b][e + 1], scale_log2, nms));
-        rs = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, rs, false);
-        pf[2 * b + (e >> 3)][e & 7] = pp[0];
-        pf[2 * b + (e >> 3)][(e & 7) + 1] = pp[1];
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e + 1], scale_log2, nms));
+        rs += p0 + p1;
+        pf[2 * b + (e >> 3)][e & 7] = (__bf16)p0;
+        pf[2 * b + (e >> 3)][(e & 7) + 1] = (__bf16)p1;
       }
     l_run += rs;
+  };
 
-    // O^T += V^T P^T.  Step s = 2b + u covers S^T block b, elements 8u..8u+7:
-    // keys base..base+3 and base+8..base+11 with base = 32b + 16u + 4g.
+  // O^T += V^T P^T.  MFMA i = 4s + db covers S^T block b = s/2, elements
+  // 8u..8u+7 (u = s%2): keys base..base+3 and base+8..base+11 with
+  // base = 32b + 16u + 4g, head-dim block db.
+  auto pv = [&](const uint16_t* vs_t) __attribute__((always_inline)) {
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const int s = i >> 2, db = i & 3;
+      const int rows = 32 * (s >> 1) + 16 * (s & 1);
+      const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db & 1] + 64 * (db >> 1) + rows * DH;
+      const v4i16 lo = lds_read_tr16(p);
+      const v4i16 hi = lds_read_tr16(p + 8 * DH);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int kN = 2 * NKB * (DH / 32);
+    bf16x8 vf[kN];
 #pragma unroll
-    for (int s = 0; s < 2 * NKB; ++s) {
-      const int rows = 32 * (s >> 1) + 16 * (s & 1);   // + 4g + kk (+8 for the high half)
+    for (int i = 0; i < kVAhead; ++i) vf[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
-        const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db & 1] + 64 * (db >> 1) + rows * DH;
-        const v4i16 lo = lds_read_tr16(p);
-        const v4i16 hi = lds_read_tr16(p + 8 * DH);
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < kN; ++i) {
+      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i >> 2], oacc[i & 3], 0, 0, 0);
+      if (i + kVAhead < kN) vf[i + kVAhead] = vread(i + kVAhead);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
+  auto phase = [&](const uint16_t* kcur, const uint16_t* vprev, uint16_t* knext, uint16_t* vnext,
+                   int t) __attribute__((always_inline)) {
+    if (t + 1 < nkt) issue_k(knext, t + 1);
+    if (t < nkt) issue_v(vnext, t);
+    if (lagging && t >= 1) softmax(t - 1);
+    __builtin_amdgcn_s_setprio(1);
+    if (t >= 1) pv(vprev);
+    if (t < nkt) compute_s(kcur);
+    __builtin_amdgcn_s_setprio(0);
+    if (!lagging && t < nkt) softmax(t);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int j = 0; j < nkt; j += 2) {
-    tile_step(Ks0, Vs0, Ks1, Vs1, j);
-    if (j + 1 < nkt) tile_step(Ks1, Vs1, Ks0, Vs0, j + 1);
+
+  issue_k(Ks0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t <= nkt; t += 2) {
+    phase(Ks0, Vs1, Ks1, Vs0, t);
+    if (t + 1 <= nkt) phase(Ks1, Vs0, Ks0, Vs1, t + 1);
   }
 
   const float l_tot = half_swap_sum(l_run);
