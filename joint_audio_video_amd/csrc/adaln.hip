@@ -7,9 +7,10 @@
 // picks its rows.
 //
 // HBM-bound (about 2*d_model*elt bytes per token).  One wave per token row:
-// the row is read once with 16-byte loads into registers, mean and variance
-// are two exact passes over the registers (wave reductions), and the
-// modulated row is written with 16-byte stores.  Table rows come from L2.
+// the row is read once with 16-byte streaming loads into registers, mean and
+// variance are two exact passes over the registers (wave reductions), and the
+// modulated row is written with 16-byte streaming stores, so the x and y
+// streams do not evict the table rows, which come from L2.
 #include "common.h"
 
 namespace dit {
@@ -38,74 +39,109 @@ __device__ __forceinline__ uint4 pack(const float* f, float) {
                     __float_as_uint(f[2]), __float_as_uint(f[3]));
 }
 
-// NV = 16-byte vectors per lane (row of nvec <= 64*NV vectors).
-template <typename T, int NV>
+// NV = 16-byte vectors per lane (row of nvec <= 64*NV vectors); each wave
+// normalises R consecutive rows.  All R rows are loaded before any
+// reduction, and when the R rows share one modality (the common case in a
+// pack, whose modalities come in long runs) each table vector is loaded once
+// for all of them, dividing the table's L2 traffic by R.
+template <typename T, int NV, int R>
 __global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
     const T* __restrict__ x, int64_t ld_x, const uint8_t* __restrict__ mod,
     const float* __restrict__ table, T* __restrict__ y, int64_t ld_y, int64_t n, int d,
     float eps) {
   constexpr int E = Vec<T>::N;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= n) return;
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
+  if (row0 >= n) return;
   const int nvec = d / E;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld_x);
 
-  uint4 raw[NV];
+  uint4 raw[R][NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = lane + 64 * i;
-    raw[i] = c < nvec ? xr[c] : make_uint4(0, 0, 0, 0);
-  }
-  float s = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (row0 + r) * ld_x);
+    const bool live = row0 + r < n;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float f[E];
-    unpack(raw[i], f, T());
-#pragma unroll
-    for (int e = 0; e < E; ++e) s += f[e];
-  }
-  const float inv_d = 1.0f / (float)d;
-  const float mean = wave_sum(s) * inv_d;
-  float q = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    if (lane + 64 * i < nvec) {
-      float f[E];
-      unpack(raw[i], f, T());
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float t = f[e] - mean;
-        q = fmaf(t, t, q);
-      }
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+      raw[r][i] = live && c < nvec ? ld_stream(xr + c) : make_uint4(0, 0, 0, 0);
     }
   }
-  const float var = wave_sum(q) * inv_d;
-  const float rstd = 1.0f / sqrtf(var + eps);
+  const float inv_d = 1.0f / (float)d;
+  float mean[R], rstd[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float f[E];
+      unpack(raw[r][i], f, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += f[e];
+    }
+    mean[r] = wave_sum(s) * inv_d;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (lane + 64 * i < nvec) {
+        float f[E];
+        unpack(raw[r][i], f, T());
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float t = f[e] - mean[r];
+          q = fmaf(t, t, q);
+        }
+      }
+    }
+    rstd[r] = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+  }
 
-  const int m = mod[row];
-  const float4* shift = reinterpret_cast<const float4*>(table + (size_t)(3 * m + 0) * d);
-  const float4* scale = reinterpret_cast<const float4*>(table + (size_t)(3 * m + 1) * d);
-  uint4* yr = reinterpret_cast<uint4*>(y + row * ld_y);
+  int m[R];
+  bool same = true;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = row0 + r < n ? mod[row0 + r] : mod[row0];
+    same = same && m[r] == m[0];
+  }
+  // Writes row r's vector c given the table vectors of its modality.
+  auto emit = [&](int r, int i, const float* shv, const float* scv) {
+    const int c = lane + 64 * i;
+    float f[E], o[E];
+    unpack(raw[r][i], f, T());
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = fmaf((f[e] - mean[r]) * rstd[r], 1.0f + scv[e], shv[e]);
+    st_stream(reinterpret_cast<uint4*>(y + (row0 + r) * ld_y) + c, pack(o, T()));
+  };
+  auto load_table = [&](int mm, int c, float* shv, float* scv) {
+    const float4* shift = reinterpret_cast<const float4*>(table + (size_t)(3 * mm + 0) * d);
+    const float4* scale = reinterpret_cast<const float4*>(table + (size_t)(3 * mm + 1) * d);
+#pragma unroll
+    for (int e4 = 0; e4 < E / 4; ++e4) {
+      const float4 sh = shift[c * (E / 4) + e4];
+      const float4 sc = scale[c * (E / 4) + e4];
+      shv[4 * e4 + 0] = sh.x; shv[4 * e4 + 1] = sh.y; shv[4 * e4 + 2] = sh.z; shv[4 * e4 + 3] = sh.w;
+      scv[4 * e4 + 0] = sc.x; scv[4 * e4 + 1] = sc.y; scv[4 * e4 + 2] = sc.z; scv[4 * e4 + 3] = sc.w;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
-    if (c < nvec) {
-      float f[E], o[E];
-      unpack(raw[i], f, T());
+    if (c >= nvec) continue;
+    float shv[E], scv[E];
+    if (same) {
+      load_table(m[0], c, shv, scv);
 #pragma unroll
-      for (int e4 = 0; e4 < E / 4; ++e4) {
-        const float4 sh = shift[c * (E / 4) + e4];
-        const float4 sc = scale[c * (E / 4) + e4];
-        const float shv[4] = {sh.x, sh.y, sh.z, sh.w};
-        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+      for (int r = 0; r < R; ++r)
+        if (row0 + r < n) emit(r, i, shv, scv);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xh = (f[4 * e4 + e] - mean) * rstd;
-          o[4 * e4 + e] = fmaf(xh, 1.0f + scv[e], shv[e]);
-        }
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r >= n) continue;
+        load_table(m[r], c, shv, scv);
+        emit(r, i, shv, scv);
       }
-      yr[c] = pack(o, T());
     }
   }
 }
@@ -115,17 +151,20 @@ hipError_t dispatch(const void* x, int64_t ld_x, const uint8_t* mod, const float
                     int64_t ld_y, int64_t n, int d, float eps, hipStream_t s) {
   const int nvec = d / Vec<T>::N;
   const int need = (nvec + 63) / 64;
-  const dim3 grid((unsigned)((n + kWaves - 1) / kWaves)), block(64 * kWaves);
   const T* xp = static_cast<const T*>(x);
   T* yp = static_cast<T*>(y);
-#define DIT_ADALN_CASE(NVV)                                                                \
-  if (need <= NVV) {                                                                       \
-    adaln_kernel<T, NVV><<<grid, block, 0, s>>>(xp, ld_x, mod, table, yp, ld_y, n, d, eps); \
-    return hipGetLastError();                                                              \
+  // Rows per wave: enough to share table loads, few enough to keep the raw
+  // rows (R * NV * 4 registers) in registers.
+#define DIT_ADALN_CASE(NVV, RR)                                                                 \
+  if (need <= NVV) {                                                                            \
+    const dim3 grid((unsigned)((n + kWaves * RR - 1) / (kWaves * RR))), block(64 * kWaves);     \
+    adaln_kernel<T, NVV, RR><<<grid, block, 0, s>>>(xp, ld_x, mod, table, yp, ld_y, n, d, eps); \
+    return hipGetLastError();                                                                   \
   }
-  DIT_ADALN_CASE(1) DIT_ADALN_CASE(2) DIT_ADALN_CASE(3) DIT_ADALN_CASE(4) DIT_ADALN_CASE(5)
-  DIT_ADALN_CASE(6) DIT_ADALN_CASE(8) DIT_ADALN_CASE(10) DIT_ADALN_CASE(12) DIT_ADALN_CASE(16)
-  DIT_ADALN_CASE(20) DIT_ADALN_CASE(24) DIT_ADALN_CASE(32)
+  DIT_ADALN_CASE(1, 2) DIT_ADALN_CASE(2, 2) DIT_ADALN_CASE(3, 2) DIT_ADALN_CASE(4, 2)
+  DIT_ADALN_CASE(5, 2) DIT_ADALN_CASE(6, 2) DIT_ADALN_CASE(8, 2) DIT_ADALN_CASE(10, 2)
+  DIT_ADALN_CASE(12, 1)
+  DIT_ADALN_CASE(16, 1) DIT_ADALN_CASE(20, 1) DIT_ADALN_CASE(24, 1) DIT_ADALN_CASE(32, 1)
 #undef DIT_ADALN_CASE
   return hipErrorInvalidValue;
 }

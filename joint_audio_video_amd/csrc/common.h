@@ -11,6 +11,19 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte global access (non-temporal hint) for data touched once:
+// rows that are read or written exactly once per launch should not displace
+// reused lines (tables, weights) from the caches.
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+}
 
 // bf16 storage is raw 16-bit patterns; widening is exact.
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -44,7 +44,13 @@ __device__ __forceinline__ uint4 store_vec(const float* f, float) {
 
 constexpr int kThreads = 256;
 
-template <typename T, int DH>
+// Workgroup = TOK tokens.  Thread tid handles vector tid + kThreads*j of each
+// of the 2*TOK rows (q and k of every token); since kThreads*E is a multiple
+// of DH, its pairs p0..p0+E/2-1 within the head are the same for every j.
+// Rows wider than kThreads*NJ vectors are walked in chunks.  The loads do not
+// depend on the angles, so the first chunk's loads are issued before the
+// angle table is computed.
+template <typename T, int DH, int NJ>
 __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ q, int64_t ld_q,
                                                          T* __restrict__ k, int64_t ld_k,
                                                          const int32_t* __restrict__ pos,
@@ -53,55 +59,92 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ q, int64
   constexpr int P = DH / 2;             // pairs per head
   constexpr int TOK = kThreads / P;     // tokens per workgroup
   constexpr int E = VecE<T>::N;         // elements per 16-byte vector
+  static_assert((kThreads * E) % DH == 0, "a thread's pairs must not depend on j");
   __shared__ float2 cs[TOK][P];
 
   const int64_t t0 = (int64_t)blockIdx.x * TOK;
-  {
-    const int tok = threadIdx.x / P, p = threadIdx.x % P;
-    const int64_t row = t0 + tok;
-    float c = 1.0f, s = 0.0f;
-    if (row < n) {
-      const int col = 2 * p;
-      const int axis = col < s_t ? 0 : (col < s_t + s_h ? 1 : 2);
-      const int32_t ps = pos[3 * row + axis];
-      if (ps != 0) {
-        double sd, cd;
-        sincos((double)ps * fr.f[p], &sd, &cd);
-        s = (float)sd;
-        c = (float)cd;
-      }
-    }
-    cs[tok][p] = make_float2(c, s);
-  }
-  __syncthreads();
-
-  const int nv = n_heads * DH / E;                  // vectors per q (or k) row
-  const int items = TOK * 2 * nv;
-  for (int it = threadIdx.x; it < items; it += kThreads) {
-    const int tok = it / (2 * nv);
-    const int rem = it - tok * 2 * nv;
-    const int which = rem / nv;                     // 0: q, 1: k
-    const int v = rem - which * nv;
-    const int64_t row = t0 + tok;
-    if (row >= n) continue;
-    if (which == 1 && k == nullptr) continue;
-    T* base = which == 0 ? q + row * ld_q : k + row * ld_k;
-    uint4* ptr = reinterpret_cast<uint4*>(base) + v;
-    const uint4 raw = *ptr;
-    float f[E];
-    load_vec(raw, f, T());
-    const int p0 = ((v * E) % DH) / 2;
+  const int nv = n_heads * DH / E;      // vectors per q (or k) row
+  const int p0 = ((threadIdx.x * E) % DH) / 2;
+  T* base[TOK][2];
+  bool live[TOK][2];
 #pragma unroll
-    for (int j = 0; j < E / 2; ++j) {
-      const float2 r = cs[tok][p0 + j];
-      const float u = f[2 * j], w = f[2 * j + 1];
-      if (r.y != 0.0f) {
-        f[2 * j] = fmaf(u, r.x, -w * r.y);
-        f[2 * j + 1] = fmaf(u, r.y, w * r.x);
-      }
-    }
-    *ptr = store_vec(f, T());
+  for (int tk = 0; tk < TOK; ++tk) {
+    const int64_t row = t0 + tk;
+    base[tk][0] = q + row * ld_q;
+    base[tk][1] = k + row * ld_k;
+    live[tk][0] = row < n;
+    live[tk][1] = row < n && k != nullptr;
   }
+
+  for (int vb = 0; vb < nv; vb += kThreads * NJ) {
+    uint4 raw[TOK][2][NJ];
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk)
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int v = vb + threadIdx.x + kThreads * j;
+          raw[tk][w][j] = live[tk][w] && v < nv
+                              ? ld_stream(reinterpret_cast<const uint4*>(base[tk][w]) + v)
+                              : make_uint4(0, 0, 0, 0);
+        }
+
+    if (vb == 0) {
+      // Angle table: thread (tk, p) computes pair p of token t0 + tk.
+      const int tk = threadIdx.x / P, p = threadIdx.x % P;
+      const int64_t row = t0 + tk;
+      float c = 1.0f, sn = 0.0f;
+      if (row < n) {
+        const int col = 2 * p;
+        const int axis = col < s_t ? 0 : (col < s_t + s_h ? 1 : 2);
+        const int32_t ps = pos[3 * row + axis];
+        if (ps != 0) {
+          double sd, cd;
+          sincos((double)ps * fr.f[p], &sd, &cd);
+          sn = (float)sd;
+          c = (float)cd;
+        }
+      }
+      cs[tk][p] = make_float2(c, sn);
+      __syncthreads();
+    }
+
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk)
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int v = vb + threadIdx.x + kThreads * j;
+          if (!live[tk][w] || v >= nv) continue;
+          float f[E];
+          load_vec(raw[tk][w][j], f, T());
+#pragma unroll
+          for (int jj = 0; jj < E / 2; ++jj) {
+            const float2 r = cs[tk][p0 + jj];
+            const float u = f[2 * jj], x = f[2 * jj + 1];
+            if (r.y != 0.0f) {
+              f[2 * jj] = fmaf(u, r.x, -x * r.y);
+              f[2 * jj + 1] = fmaf(u, r.y, x * r.x);
+            }
+          }
+          st_stream(reinterpret_cast<uint4*>(base[tk][w]) + v, store_vec(f, T()));
+        }
+  }
+}
+
+template <typename T, int DH>
+hipError_t launch_dh(T* q, int64_t ld_q, T* k, int64_t ld_k, const int32_t* pos, int64_t n,
+                     int n_heads, int s_t, int s_h, const Freqs& fr, hipStream_t s) {
+  constexpr int TOK = kThreads / (DH / 2);
+  const int nv = n_heads * DH / VecE<T>::N;
+  const int nj = (nv + kThreads - 1) / kThreads;     // vectors per thread per row
+  const dim3 grid((unsigned)((n + TOK - 1) / TOK)), block(kThreads);
+  if (nj <= 1) rope_kernel<T, DH, 1><<<grid, block, 0, s>>>(q, ld_q, k, ld_k, pos, n, n_heads, s_t, s_h, fr);
+  else if (nj <= 2) rope_kernel<T, DH, 2><<<grid, block, 0, s>>>(q, ld_q, k, ld_k, pos, n, n_heads, s_t, s_h, fr);
+  else rope_kernel<T, DH, 3><<<grid, block, 0, s>>>(q, ld_q, k, ld_k, pos, n, n_heads, s_t, s_h, fr);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -112,18 +155,9 @@ hipError_t dispatch(void* q, int64_t ld_q, void* k, int64_t ld_k, const int32_t*
   for (int p = 0; p < 64; ++p) fr.f[p] = p < head_dim / 2 ? freq[p] : 0.0;
   T* qp = static_cast<T*>(q);
   T* kp = static_cast<T*>(k);
-  if (head_dim == 128) {
-    constexpr int TOK = kThreads / 64;
-    rope_kernel<T, 128><<<dim3((unsigned)((n + TOK - 1) / TOK)), dim3(kThreads), 0, s>>>(
-        qp, ld_q, kp, ld_k, pos, n, n_heads, s_t, s_h, fr);
-  } else if (head_dim == 64) {
-    constexpr int TOK = kThreads / 32;
-    rope_kernel<T, 64><<<dim3((unsigned)((n + TOK - 1) / TOK)), dim3(kThreads), 0, s>>>(
-        qp, ld_q, kp, ld_k, pos, n, n_heads, s_t, s_h, fr);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (head_dim == 128) return launch_dh<T, 128>(qp, ld_q, kp, ld_k, pos, n, n_heads, s_t, s_h, fr, s);
+  if (head_dim == 64) return launch_dh<T, 64>(qp, ld_q, kp, ld_k, pos, n, n_heads, s_t, s_h, fr, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
