@@ -8,13 +8,19 @@
 // Workgroup tile 256x256x64, four waves in a 2x2 arrangement, each owning a
 // 128x128 sub-tile as 4x4 MFMA blocks (256 accumulators per lane, held in the
 // AGPR half of the register file).  A and B tiles are staged through LDS
-// (double-buffered, 128 KB) with an XOR swizzle of the 16-byte chunk index so
-// the 32 rows an MFMA fragment read touches fall in distinct banks.  Both
-// operands are K-contiguous ([rows][K]), so every fragment is one 16-byte LDS
-// read.  Tiles are handed out XCD-aware: the hardware deals workgroups to the
-// 8 XCDs round-robin, so the launch index is remapped so that each XCD works
-// through a contiguous range of an M-grouped tile order and its L2 sees
-// neighbouring A and B panels.
+// (double-buffered, 128 KB) by buffer loads that write straight into LDS,
+// with an XOR swizzle of the 16-byte chunk index so the rows an MFMA fragment
+// read touches spread over the banks.  Both operands are K-contiguous
+// ([rows][K]), so every fragment is one 16-byte LDS read.
+// With one wave per SIMD nothing else hides latency, so each k-step is laid
+// out by hand as 16 fenced groups of four independent MFMAs; the fragment
+// reads of the next sub-step and the next tile's global loads ride in the
+// groups' shadows (the loads in the first half, so they land before the
+// step's closing barrier).
+// Tile order: workgroups in launch order walk groups of kGroupM M-tiles
+// column by column.  The hardware deals consecutive workgroups to the 8 XCDs
+// round-robin, so each XCD sees one A panel of the group (kept in its L2)
+// against every other B panel.
 //
 // float32 path: a plain LDS-tiled VALU kernel (the tiny float32 workload only
 // needs to be exact, not fast).
@@ -25,7 +31,7 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 4;
 
 struct EpiArgs {
   int kind;
@@ -39,18 +45,14 @@ struct EpiArgs {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-// Logical tile id for this workgroup: XCD-contiguous ranges, then M-grouping.
+// Tile of this workgroup: groups of kGroupM M-tiles, walked column by column.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
   const int pid = blockIdx.x;
-  const int xcd = pid & 7, idx = pid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   const int group_span = kGroupM * tiles_n;
-  const int group = logical / group_span;
+  const int group = pid / group_span;
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = logical - group * group_span;
+  const int in_group = pid - group * group_span;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
 }
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
 
@@ -100,49 +103,62 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     aoff[i] = ((uint32_t)min(32 * i + lrow, rows_a - 1) * (uint32_t)lda + lchunk * 8) * 2u;
     boff[i] = ((uint32_t)min(32 * i + lrow, rows_b - 1) * (uint32_t)K + lchunk * 8) * 2u;
   }
-  auto issue = [&](uint16_t* adst, uint16_t* bdst, int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  // One 16-byte load of slot i (0..15: A rows 32i.., then B) into the stage buffers.
+  auto load1 = [&](uint16_t* adst, uint16_t* bdst, int k0, int i) {
+    if (i < 8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, adst + (256 * i + 64 * wave) * 8, 16, aoff[i],
                                                k0 * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, bdst + (256 * i + 64 * wave) * 8, 16, boff[i],
-                                               k0 * 2, 0, 0);
-    }
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, bdst + (256 * (i - 8) + 64 * wave) * 8, 16,
+                                               boff[i - 8], k0 * 2, 0, 0);
+  };
+  auto issue = [&](uint16_t* adst, uint16_t* bdst, int k0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) load1(adst, bdst, k0, i);
   };
 
   f32x16 acc[4][4];
   const f32x16 zero16 = {};
 
-  // One k-step of BK: prefetch step kt+1 into (an, bn), multiply from (as, bs).
-  // Fragments of sub-step ks+1 are read while the MFMAs of ks run.
+  // One k-step of BK: multiply from (as, bs) while the next step's tile is
+  // loaded into (an, bn).  The step is written as 16 fenced groups of 4
+  // independent MFMAs; after each come 2 fragment reads for the next
+  // sub-step and, in the first 8 groups, 2 of the 16 global loads, so every
+  // read and load issues while an MFMA runs and the compiler cannot regroup
+  // them (left alone it sinks the reads next to their uses and bunches the
+  // loads, exposing both latencies).
   const int nk = K / BK;
-  // The first step starts every accumulator from an inline zero operand.
+  auto frag = [&](const uint16_t* base, int row, int ks) {
+    return *reinterpret_cast<const bf16x8*>(&base[row * BK + swz(row, 2 * ks + g) * 8]);
+  };
   auto k_step = [&](const uint16_t* as, const uint16_t* bs, uint16_t* an, uint16_t* bn, int kt,
                     bool first) {
-    if (kt + 1 < nk) issue(an, bn, (kt + 1) * BK);
-    auto frag = [&](const uint16_t* base, int row, int ks) {
-      return *reinterpret_cast<const bf16x8*>(&base[row * BK + swz(row, 2 * ks + g) * 8]);
-    };
-    bf16x8 af[4], bfr[4];
+    const int kload = min(kt + 1, nk - 1) * BK;   // last step: reload into the idle buffer
+    bf16x8 af[4], bfr[4], an_[4], bn_[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) af[mb] = frag(as, wm * 128 + mb * 32 + l32, 0);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(bs, wn * 128 + nb * 32 + l32, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 an_[4], bn_[4];
-      if (ks + 1 < BK / 16) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) an_[mb] = frag(as, wm * 128 + mb * 32 + l32, ks + 1);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) bn_[nb] = frag(bs, wn * 128 + nb * 32 + l32, ks + 1);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               bfr[nb], af[mb], (first && ks == 0) ? zero16 : acc[mb][nb], 0, 0, 0);
+        if (ks + 1 < BK / 16) {
+          // reads for sub-step ks+1: A block mb and B block mb
+          an_[mb] = frag(as, wm * 128 + mb * 32 + l32, ks + 1);
+          bn_[mb] = frag(bs, wn * 128 + mb * 32 + l32, ks + 1);
+        }
+        if (ks < 2) {                   // the 16 loads: two per group, first half
+          load1(an, bn, kload, 2 * (4 * ks + mb));
+          load1(an, bn, kload, 2 * (4 * ks + mb) + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (ks + 1 < BK / 16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
