@@ -86,13 +86,17 @@ def summarize_profile(kind: str, out_dir: str) -> int:
     per = {}
     for r in csv.DictReader(open(files[0])):
         name = r["Kernel_Name"]
-        key = (ATTN_KERNEL if ATTN_KERNEL in name else
-               "copy" if "copy" in name.lower() else None)
-        if key is None:
+        if "dit::" in name:
+            key = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("void ", ""))
+        elif "copy" in name.lower():
+            key = "copy"
+        else:
             continue
         per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    print("| kernel | counter | dispatches | mean per dispatch |")
+    print("|---|---|---|---|")
     for (k, c), vals in sorted(per.items()):
-        print(f"{k} {c} KiB/dispatch: " + ", ".join(f"{v:.0f}" for v in vals))
+        print(f"| {k[:60]} | {c} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
     return 0
 
 
@@ -233,6 +237,40 @@ def main() -> int:
     print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}",
           file=sys.stderr, flush=True)
 
+    # Each stage again on its own (fresh buffers, same inputs), so its rate can be
+    # read apart from its neighbours in the block (the block's stage times include
+    # the event brackets and the power state the previous kernel left behind).
+    print("# isolated stages ...", file=sys.stderr, flush=True)
+    y = torch.empty_like(x)
+    qkv = torch.empty((n, 3 * d), dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(x)
+    jav.adaln_modulate(x, mod, table, wl.eps, out=y, stream=stream)
+    jav.qkv_project(y, w_qkv, out=qkv, stream=stream)
+    q_v, k_v, v_v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    iso_ops = {
+        "adaln": (20, lambda: jav.adaln_modulate(x, mod, table, wl.eps, out=y, stream=stream)),
+        "qkv": (5, lambda: jav.qkv_project(y, w_qkv, out=qkv, stream=stream)),
+        "rope": (20, lambda: jav.rope3d_apply(q_v, k_v, pos, H, Dh, wl.sections, wl.theta,
+                                              stream=stream)),
+        "attn": (3, lambda: jav.attn_packed(q_v, k_v, v_v, cu, ms_len, H, Dh,
+                                            causal=args.causal, out=o, stream=stream)),
+        "out": (5, lambda: jav.out_proj_gated(o, w_o, x, mod, table, out=out, stream=stream)),
+    }
+    iso_ms = {}
+    for name, (reps, fn) in iso_ops.items():
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        iso_ms[name] = e0.elapsed_time(e1) / reps
+    del y, qkv, o, q_v, k_v, v_v
+    print(f"# isolated: {iso_ms}", file=sys.stderr, flush=True)
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -270,6 +308,16 @@ def main() -> int:
         "out_proj_tflops": round(out_f / (stage_ms["out"] * 1e-3) / 1e12, 2),
         "adaln_gbs": round(adaln_b / (stage_ms["adaln"] * 1e-3) / 1e9, 1),
         "rope_gbs": round(rope_b / (stage_ms["rope"] * 1e-3) / 1e9, 1),
+        "isolated_ms": {k: round(v, 4) for k, v in iso_ms.items()},
+        "isolated": {
+            "attention_tflops": round(attn_f / (iso_ms["attn"] * 1e-3) / 1e12, 2),
+            "qkv_tflops": round(qkv_f / (iso_ms["qkv"] * 1e-3) / 1e12, 2),
+            "out_proj_tflops": round(out_f / (iso_ms["out"] * 1e-3) / 1e12, 2),
+            "adaln_gbs": round(adaln_b / (iso_ms["adaln"] * 1e-3) / 1e9, 1),
+            "adaln_frac_of_hbm": round(adaln_b / (iso_ms["adaln"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "rope_gbs": round(rope_b / (iso_ms["rope"] * 1e-3) / 1e9, 1),
+            "rope_frac_of_hbm": round(rope_b / (iso_ms["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        },
         "roofline": {
             "kernel": "attn_bf16_kernel",
             "bound": "mfma",
