@@ -72,10 +72,13 @@ def test_adaln_parity(jav, name):
     check(got, ref, wl.dtype, f"adaln[{name}]")
 
 
-def test_adaln_strided_rows_and_trim(jav):
-    """Rows inside wider buffers; only n_tokens rows are touched."""
+@pytest.mark.parametrize("n", [1000, 999])
+def test_adaln_strided_rows_and_trim(jav, n):
+    """Rows inside wider buffers; only n_tokens rows are touched.  Modalities are
+    drawn per row, so neighbouring rows (one wave's pair) often differ; an odd
+    n leaves the last wave a single row."""
     import torch
-    d, n, rows_alloc = 1536, 1000, 1040
+    d, rows_alloc = 1536, 1040
     x_full = synth.normal_array((rows_alloc, d + 64), seed=70, dtype="bf16")
     table = synth.normal_array((3, 3, d), seed=71, std=0.1)
     mod = synth.uniform_ints((rows_alloc,), 0, 3, seed=72).astype(np.uint8)
@@ -89,11 +92,25 @@ def test_adaln_strided_rows_and_trim(jav):
     assert torch.isnan(y[n:]).all() and torch.isnan(y[:, d:]).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_adaln_wide_rows(jav, dtype):
+    """d_model 8192: rows longer than the two-rows-per-wave register budget (one
+    row per wave), with per-row modalities and an odd row count."""
+    import torch
+    d, n = 8192, 37
+    x_h = synth.normal_array((n, d), seed=73, dtype=dtype)
+    table = synth.normal_array((3, 3, d), seed=74, std=0.1)
+    mod = synth.uniform_ints((n,), 0, 3, seed=75).astype(np.uint8)
+    y = jav.adaln_modulate(dev(x_h, dtype), dev_int(mod, torch.uint8), dev_f32(table))
+    _sync()
+    check(host(y), oracle.adaln_modulate(x_h, mod, table), dtype, f"adaln wide {dtype}")
+
+
 # ---------------------------------------------------------------------------
 # rope3d_apply
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "small", "full"])
+@pytest.mark.parametrize("name", ["tiny", "small", "medium", "full"])
 def test_rope_parity_on_fused_qkv(jav, name):
     import torch
     wl = synth.WORKLOADS[name]
@@ -122,6 +139,26 @@ def test_rope_parity_on_fused_qkv(jav, name):
         b = before[:, sl].view(n, H, Dh)[at][:, :, s_t:]
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_rope_wide_rows_in_chunks(jav):
+    """56 heads x 128 (896 vectors per row): rows wider than one pass of the
+    kernel, walked in chunks; 37 tokens (not a multiple of the 4 per
+    workgroup), positions drawn at random with zeros included."""
+    import torch
+    n, H, Dh, sections = 37, 56, 128, (32, 48, 48)
+    d = H * Dh
+    qkv_h = synth.normal_array((n, 3 * d), seed=111, dtype="bf16")
+    pos = synth.uniform_ints((n, 3), 0, 40, seed=112).astype(np.int32)
+    pos[::5] = 0
+    qkv = dev(qkv_h, "bf16")
+    before = qkv.clone()
+    jav.rope3d_apply(qkv[:, :d], qkv[:, d:2 * d], dev_int(pos, torch.int32), H, Dh, sections)
+    _sync()
+    for which, sl in (("q", slice(0, d)), ("k", slice(d, 2 * d))):
+        ref = oracle.rope3d(qkv_h[:, sl], pos, H, Dh, sections, 1e4)
+        check(host(qkv[:, sl]), ref, "bf16", f"rope wide.{which}")
+    assert torch.equal(qkv[:, 2 * d:], before[:, 2 * d:])
 
 
 def test_rope_q_only_and_zero_positions(jav):
