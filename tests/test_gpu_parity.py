@@ -263,6 +263,29 @@ def test_qkv_project_parity(jav, name, bias):
     check(got, ref, wl.dtype, f"qkv[{name}]")
 
 
+@pytest.mark.parametrize("d,n", [(64, 300), (1600, 777)])
+def test_gemm_odd_depths_and_ragged_tiles(jav, d, n):
+    """d_model 64 (a single k-step) and 1600 (25 k-steps, an odd count); token
+    and feature counts that leave partial 256-wide tiles; bias and the gated
+    residual with per-row modalities."""
+    import torch
+    print(f"gemm d={d} n={n}", flush=True)
+    y_h = synth.normal_array((n, d), seed=310 + d, dtype="bf16")
+    w_qkv = synth.normal_array((3 * d, d), seed=311 + d, std=0.02, dtype="bf16")
+    b_qkv = synth.normal_array((3 * d,), seed=312 + d, std=0.1, dtype="bf16")
+    out = jav.qkv_project(dev(y_h, "bf16"), dev(w_qkv, "bf16"), dev(b_qkv, "bf16"))
+    _sync()
+    check(host(out), oracle.qkv_project(y_h, w_qkv, b_qkv), "bf16", f"qkv d={d}")
+    w_o = synth.normal_array((d, d), seed=313 + d, std=0.02, dtype="bf16")
+    x_h = synth.normal_array((n, d), seed=314 + d, dtype="bf16")
+    table = synth.normal_array((3, 3, d), seed=315 + d, std=0.1)
+    mod = synth.uniform_ints((n,), 0, 3, seed=316 + d).astype(np.uint8)
+    res = jav.out_proj_gated(dev(y_h, "bf16"), dev(w_o, "bf16"), dev(x_h, "bf16"),
+                             dev_int(mod, torch.uint8), dev_f32(table))
+    _sync()
+    check(host(res), oracle.out_proj_gated(y_h, w_o, x_h, mod, table), "bf16", f"out d={d}")
+
+
 @pytest.mark.parametrize("name,bias,inplace", [("tiny", True, False), ("small", False, False),
                                                ("small", True, True), ("full", False, True)])
 def test_out_proj_gated_parity(jav, name, bias, inplace):
