@@ -24,18 +24,21 @@ Readings where those pages leave a step open are listed in each function's
 docstring.  Pins for every function live in ``tests/test_oracle_*.py``.
 Parity of the pack order and of the RoPE pair convention is pinned by the
 stated readings only (the pages fix neither), see ``oracle.layout`` and
-``oracle.block.rope3d``.
+``oracle.block.rope3d``; so are the feed-forward half's activation (tanh
+GELU) and width (4 x d_model), see ``oracle.block.gelu_tanh`` and
+``oracle.block.ffn_forward``.
 """
 from .layout import (MOD_AUDIO, MOD_TEXT, MOD_VIDEO, SAMPLES_PER_AUDIO_TOKEN,
                      SPATIAL_DOWNSAMPLE, TEMPORAL_DOWNSAMPLE, grid_from_media,
                      pack_layout, request_length)
 from .block import (adaln_modulate, attention, attention_probs, block_forward,
-                    out_proj_gated, qkv_project, rope3d, rope_frequencies)
+                    ffn_forward, ffn_up, gelu_tanh, out_proj_gated, qkv_project, rope3d,
+                    rope_frequencies)
 
 __all__ = [
     "MOD_VIDEO", "MOD_AUDIO", "MOD_TEXT", "SAMPLES_PER_AUDIO_TOKEN",
     "SPATIAL_DOWNSAMPLE", "TEMPORAL_DOWNSAMPLE", "grid_from_media",
     "pack_layout", "request_length", "adaln_modulate", "qkv_project",
     "rope3d", "rope_frequencies", "attention", "attention_probs",
-    "out_proj_gated", "block_forward",
+    "out_proj_gated", "block_forward", "gelu_tanh", "ffn_up", "ffn_forward",
 ]

@@ -263,3 +263,60 @@ def block_forward(x, modality, pos, cu_seqlens, table, w_qkv, w_o, *,
     o = attention(q_rot, k_rot, v, cu_seqlens, n_heads, head_dim, causal, scale, rows)
     out = out_proj_gated(o, w_o, x, modality, table, b_o, rows)
     return dict(y=y, q=q, k=k, v=v, q_rot=q_rot, k_rot=k_rot, o=o, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Feed-forward half of the block
+# ---------------------------------------------------------------------------
+
+_GELU_C = math.sqrt(2.0 / math.pi)
+
+
+def gelu_tanh(z) -> np.ndarray:
+    """GELU in its tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+
+    Reading.  [H3-NFT] (section "How VeRL-Omni's Adapter Architecture Keeps
+    H3-Specific Logic Contained") names the feed-forward weights ff.net.0.proj
+    and ff.net.2 but not the activation.  A projection called `proj` inside the
+    first element of the feed-forward stack is the layout of a GELU module
+    that owns its input projection, and the DiT family uses the tanh form of
+    GELU; that is the reading.  The pages do not pin it.
+    """
+    z = _f64(z)
+    return 0.5 * z * (1.0 + np.tanh(_GELU_C * (z + 0.044715 * z * z * z)))
+
+
+def ffn_up(y, w1, b1=None) -> np.ndarray:
+    """First feed-forward projection and activation: gelu_tanh(y W1^T + b1).
+
+    W1 is ff.net.0.proj, [d_ff][d_model] ([out][in]).
+    """
+    y = np.asarray(y)
+    w = _f64(w1)
+    out = np.empty((y.shape[0], w.shape[0]), dtype=np.float64)
+    for s in range(0, y.shape[0], _ROW_CHUNK):
+        z = _f64(y[s:s + _ROW_CHUNK]) @ w.T
+        if b1 is not None:
+            z += _f64(b1)
+        out[s:s + z.shape[0]] = gelu_tanh(z)
+    return out
+
+
+def ffn_forward(x, modality, table_mlp, w1, w2, b1=None, b2=None, eps: float = 1e-6,
+                rows=None) -> np.ndarray:
+    """Feed-forward half of one DiT block for every token (or the given rows).
+
+    [vLLM-Omni] section 3 (the DiT stage of the packed data flow): every block
+    runs attention and then an MLP over the packed rows.  [H3-NFT] (adapter
+    section) names its weights ff.net.0.proj and ff.net.2.  The half mirrors
+    the attention half (readings): AdaLN with the MLP rows of the cached
+    per-modality table (shift, scale, gate), the two projections with the
+    activation between, and the gated residual:
+
+        out = x + gate_mlp[m] * (gelu_tanh(AdaLN_mlp(x) W1^T + b1) W2^T + b2)
+
+    table_mlp is [3 modalities][shift, scale, gate][d_model]; W2 is [d_model][d_ff].
+    """
+    y = adaln_modulate(x, modality, table_mlp, eps, rows=rows)
+    h = ffn_up(y, w1, b1)
+    return out_proj_gated(h, w2, x, modality, table_mlp, b2, rows=rows)

@@ -98,3 +98,17 @@ def block(x, modality, pos, cu_seqlens, table, w_qkv, w_o, n_heads, head_dim,
     z = linear(o, w_o, b_o)
     return [[x[i][c] + table[modality[i]][2][c] * z[i][c] for c in range(d)]
             for i in range(len(x))]
+
+
+def gelu_tanh(z: float) -> float:
+    """0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))."""
+    return 0.5 * z * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def ffn(x, modality, table, w1, w2, b1=None, b2=None, eps: float = 1e-6):
+    """x + gate[m] * (gelu(AdaLN(x) W1^T + b1) W2^T + b2), row by row."""
+    y = adaln(x, modality, table, eps)
+    h = [[gelu_tanh(v) for v in row] for row in linear(y, w1, b1)]
+    z = linear(h, w2, b2)
+    return [[x[i][j] + table[modality[i]][2][j] * z[i][j] for j in range(len(x[i]))]
+            for i in range(len(x))]

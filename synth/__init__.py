@@ -70,6 +70,11 @@ class Workload:
     def n_tokens(self) -> int:
         return self.expected_tokens
 
+    @property
+    def d_ff(self) -> int:
+        """Feed-forward width: 4 x d_model (a reading; the pages give none)."""
+        return 4 * self.d_model
+
 
 def _req(grid, media) -> Request:
     return Request(*grid, *media[:4])
@@ -176,6 +181,36 @@ def block_inputs(wl: Workload, n_tokens: Optional[int] = None,
         if with_bias:
             b_qkv, b_o = round_to_bf16(b_qkv), round_to_bf16(b_o)
     return BlockInputs(x, table, w_qkv, w_o, b_qkv, b_o)
+
+
+@dataclasses.dataclass
+class FfnInputs:
+    """Float32 host arrays for the feed-forward half; bf16-exact for bf16 workloads."""
+    table: np.ndarray      # [3][3][D], N(0, 0.1): MLP rows shift, scale, gate per modality
+    w1: np.ndarray         # [F][D], N(0, 0.02)   (ff.net.0.proj)
+    w2: np.ndarray         # [D][F], N(0, 0.02)   (ff.net.2)
+    b1: Optional[np.ndarray] = None   # [F], N(0, 0.02) when drawn
+    b2: Optional[np.ndarray] = None   # [D]
+
+
+def ffn_inputs(wl: Workload, with_bias: bool = False, seed: Optional[int] = None) -> FfnInputs:
+    """Draw the MLP table, W1, W2 (then biases) in that order from PCG64(seed), a stream of
+    its own (default wl.seed + 1000) so the attention-half draws are unchanged; the
+    half's input x is the block's x."""
+    d, f = wl.d_model, wl.d_ff
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 1000 if seed is None else seed))
+    table = _normal(rng, (3, 3, d), 0.1)
+    w1 = _normal(rng, (f, d), 0.02)
+    w2 = _normal(rng, (d, f), 0.02)
+    b1 = b2 = None
+    if with_bias:
+        b1 = _normal(rng, (f,), 0.02)
+        b2 = _normal(rng, (d,), 0.02)
+    if wl.dtype == BF16:
+        w1, w2 = round_to_bf16(w1), round_to_bf16(w2)
+        if with_bias:
+            b1, b2 = round_to_bf16(b1), round_to_bf16(b2)
+    return FfnInputs(table, w1, w2, b1, b2)
 
 
 def normal_array(shape, seed: int, std: float = 1.0, dtype: str = F32) -> np.ndarray:
