@@ -206,6 +206,64 @@ dit_status out_proj_gated(dit_dtype dt, const void* o, int64_t ld_o, const void*
                           int64_t ld_out, int64_t n_tokens, int32_t d_model, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Feed-forward half: ff.net.0.proj -> GELU -> ff.net.2                       */
+/* ------------------------------------------------------------------------ */
+
+/* [H3-NFT] section "How VeRL-Omni's Adapter Architecture Keeps H3-Specific
+ * Logic Contained" names the feed-forward weights ff.net.0.proj and ff.net.2;
+ * [vLLM-Omni] section 3 (DiT stage of the packed data flow) runs attention and
+ * an MLP in every block.  The activation is tanh-form GELU and the half is
+ * modulated by its own per-modality AdaLN rows (readings; the pages give
+ * neither).
+ *
+ * ffn_up_gelu: h = gelu_tanh(y W1^T + b1), gelu_tanh(z) =
+ * 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).  y: [n_tokens][ld_y] (first
+ * d_model columns used); w1: [d_ff][d_model] contiguous ([out][in]); b1:
+ * [d_ff] or NULL; h: [n_tokens][ld_h], must not overlap y.  Computed in float32,
+ * h rounded once (bf16: RNE).
+ * Errors: DIT_EINVAL for a null pointer, d_model or d_ff < 1, ld too small;
+ * DIT_EUNSUPPORTED when d_model or d_ff is not a multiple of 64 or a pointer,
+ * bias or ld is not 16-byte aligned; DIT_EHIP on a launch failure. */
+dit_status ffn_up_gelu(dit_dtype dt, const void* y, int64_t ld_y, const void* w1,
+                       const void* b1, void* h, int64_t ld_h, int64_t n_tokens,
+                       int32_t d_model, int32_t d_ff, void* stream);
+
+/* ffn_down_gated: out = x + table[m][GATE] * (h W2^T + b2), with the gate row of
+ * the feed-forward half's own AdaLN table.  h: [n_tokens][ld_h] (first d_ff
+ * columns); w2: [d_model][d_ff] contiguous; b2: [d_model] or NULL; x, out:
+ * [n_tokens][ld]; out may be x itself (in place) but must not otherwise overlap
+ * x or h; modality: device uint8 [n_tokens]; table: device f32 [3][3][d_model].
+ * Errors as ffn_up_gelu. */
+dit_status ffn_down_gated(dit_dtype dt, const void* h, int64_t ld_h, const void* w2,
+                          const void* b2, const void* x, int64_t ld_x,
+                          const uint8_t* modality, const float* table, void* out,
+                          int64_t ld_out, int64_t n_tokens, int32_t d_model, int32_t d_ff,
+                          void* stream);
+
+typedef struct {
+  dit_dtype dtype;
+  int32_t d_model, d_ff;   /* d_ff: 4 * d_model in the workloads here */
+  float ln_eps;            /* 1e-6 */
+} dit_ffn_desc;
+
+/* Bytes of scratch dit_ffn_forward needs: y [N][D] + h [N][d_ff] elements, each
+ * region rounded up to 256 bytes.  0 for a bad descriptor. */
+size_t dit_ffn_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens);
+
+/* The whole feed-forward half: y = AdaLN(x) with the half's table (shift,
+ * scale rows), h = ffn_up_gelu(y), out = ffn_down_gated(h, x) (gate row).
+ * x, out: [n_tokens][d_model] contiguous (out may equal x); modality: device
+ * uint8 [n_tokens]; ada_table: device f32 [3][3][d_model] (the MLP rows);
+ * w1 [d_ff][d_model]; w2 [d_model][d_ff]; biases nullable; workspace: device, at
+ * least dit_ffn_workspace_bytes() bytes, 256-byte aligned.  Enqueues
+ * adaln_modulate -> ffn_up_gelu -> ffn_down_gated on stream, after validating
+ * all three.  Errors: those of the stages, plus DIT_EWORKSPACE. */
+dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void* out,
+                           const uint8_t* modality, int64_t n_tokens, const float* ada_table,
+                           const void* w1, const void* b1, const void* w2, const void* b2,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* The whole attention half of the block                                      */
 /* ------------------------------------------------------------------------ */
 

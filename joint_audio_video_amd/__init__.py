@@ -31,6 +31,7 @@ EXPORTED = (
     "dit_abi_version", "dit_last_error", "dit_grid_from_media", "dit_pack_layout",
     "adaln_modulate", "rope3d_apply", "attn_packed", "qkv_project", "out_proj_gated",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
+    "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
 )
 
 
@@ -59,6 +60,11 @@ class BlockDesc(ctypes.Structure):
                 ("causal", ctypes.c_int32)]
 
 
+class FfnDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m joint_audio_video_amd.build`")
@@ -82,6 +88,12 @@ def _load() -> ctypes.CDLL:
         "dit_block_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
         "dit_block_forward": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32, I32,
                                              I64, P, P, P, P, P, P, SZ, P]),
+        "ffn_up_gelu": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, I32, P]),
+        "ffn_down_gated": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, P, P, P, I64, I64,
+                                          I32, I32, P]),
+        "dit_ffn_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
+        "dit_ffn_forward": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P, P,
+                                           P, SZ, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -276,6 +288,61 @@ def block_forward(desc: BlockDesc, x, modality, pos, cu_seqlens, max_seqlen: int
                                   cu_seqlens.numel() - 1, int(max_seqlen), n, table.data_ptr(),
                                   w_qkv.data_ptr(), _ptr(b_qkv), w_o.data_ptr(), _ptr(b_o),
                                   workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+def ffn_up_gelu(y, w1, b1=None, out=None, n_tokens=None, stream=None):
+    """h = gelu_tanh(y W1^T + b1) (libdit ffn_up_gelu)."""
+    torch = _torch()
+    n = y.shape[0] if n_tokens is None else int(n_tokens)
+    d, f = y.shape[1], w1.shape[0]
+    if out is None:
+        out = torch.empty((y.shape[0], f), dtype=y.dtype, device=y.device)
+    py, ldy = _rows(y)
+    ph, ldh = _rows(out)
+    _check(_lib.ffn_up_gelu(_dtype_code(y), py, ldy, w1.data_ptr(), _ptr(b1), ph, ldh, n, d, f,
+                            _stream(stream)))
+    return out
+
+
+def ffn_down_gated(h, w2, x, modality, table, b2=None, out=None, n_tokens=None, stream=None):
+    """out = x + table[m][2] * (h W2^T + b2) (libdit ffn_down_gated)."""
+    torch = _torch()
+    n = h.shape[0] if n_tokens is None else int(n_tokens)
+    d, f = w2.shape
+    if out is None:
+        out = torch.empty((x.shape[0], d), dtype=x.dtype, device=x.device)
+    ph, ldh = _rows(h)
+    px, ldx = _rows(x)
+    pout, ldout = _rows(out)
+    _check(_lib.ffn_down_gated(_dtype_code(h), ph, ldh, w2.data_ptr(), _ptr(b2), px, ldx,
+                               modality.data_ptr(), table.data_ptr(), pout, ldout, n, d, f,
+                               _stream(stream)))
+    return out
+
+
+def ffn_desc(dtype_code: int, d_model: int, d_ff: int, eps: float = 1e-6) -> FfnDesc:
+    return FfnDesc(dtype_code, d_model, d_ff, eps)
+
+
+def ffn_workspace_bytes(desc: FfnDesc, n_tokens: int) -> int:
+    return int(_lib.dit_ffn_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def ffn_forward(desc: FfnDesc, x, modality, table, w1, w2, b1=None, b2=None, out=None,
+                workspace=None, n_tokens=None, stream=None):
+    """The feed-forward half of one DiT block (libdit dit_ffn_forward)."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    if out is None:
+        out = torch.empty_like(x)
+    need = ffn_workspace_bytes(desc, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(_lib.dit_ffn_forward(ctypes.byref(desc), x.data_ptr(), out.data_ptr(),
+                                modality.data_ptr(), n, table.data_ptr(), w1.data_ptr(), _ptr(b1),
+                                w2.data_ptr(), _ptr(b2), workspace.data_ptr(), workspace.numel(),
+                                _stream(stream)))
     return out
 
 

@@ -204,16 +204,20 @@ extern "C" dit_status attn_packed(dit_dtype dt, const void* q, int64_t ld_q, con
 
 // ---------------------------------------------------------------------------
 
+// C [n_tokens][width_out] = A [n_tokens][k_in] W^T: inner width k_in (a
+// multiple of the 64-deep k-step), output width a multiple of 4 (the
+// epilogue stores four features at a time).
 static dit_status proj_check(const char* who, dit_dtype dt, const void* a, int64_t lda,
                              const void* w, void* c, int64_t ldc, int64_t n_tokens,
-                             int32_t d_model, int64_t width_out) {
+                             int32_t k_in, int64_t width_out) {
   if (!dtype_ok(dt)) return fail(DIT_EINVAL, "%s: unknown dtype %d", who, (int)dt);
   if (!a || !w || !c) return fail(DIT_EINVAL, "%s: null pointer", who);
-  if (d_model < 1) return fail(DIT_EINVAL, "%s: d_model < 1", who);
-  if (lda < d_model || ldc < width_out) return fail(DIT_EINVAL, "%s: ld too small", who);
+  if (k_in < 1 || width_out < 1) return fail(DIT_EINVAL, "%s: width < 1", who);
+  if (lda < k_in || ldc < width_out) return fail(DIT_EINVAL, "%s: ld too small", who);
   if (dit_status st = check_stream_rows(n_tokens)) return st;
-  if (d_model % 64 != 0)
-    return fail(DIT_EUNSUPPORTED, "%s: d_model %d is not a multiple of 64", who, d_model);
+  if (k_in % 64 != 0 || width_out % 4 != 0 || width_out > INT32_MAX)
+    return fail(DIT_EUNSUPPORTED, "%s: inner width %d must be a multiple of 64, output width "
+                "%lld of 4", who, k_in, (long long)width_out);
   if (!aligned16(a) || !aligned16(w) || !aligned16(c) || !ld_aligned(dt, lda) ||
       !ld_aligned(dt, ldc))
     return fail(DIT_EUNSUPPORTED, "%s: pointers/ld must be 16-byte aligned", who);
@@ -257,8 +261,123 @@ extern "C" dit_status out_proj_gated(dit_dtype dt, const void* o, int64_t ld_o, 
 }
 
 // ---------------------------------------------------------------------------
+// Feed-forward half
+
+extern "C" dit_status ffn_up_gelu(dit_dtype dt, const void* y, int64_t ld_y, const void* w1,
+                                  const void* b1, void* h, int64_t ld_h, int64_t n_tokens,
+                                  int32_t d_model, int32_t d_ff, void* stream) {
+  clear_error();
+  if (d_model < 1 || d_ff < 1) return fail(DIT_EINVAL, "ffn_up_gelu: d_model/d_ff < 1");
+  if (dit_status st = proj_check("ffn_up_gelu", dt, y, ld_y, w1, h, ld_h, n_tokens, d_model,
+                                 d_ff))
+    return st;
+  if (d_ff % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "ffn_up_gelu: d_ff %d is not a multiple of 64", d_ff);
+  if (b1 && !aligned16(b1)) return fail(DIT_EUNSUPPORTED, "ffn_up_gelu: b1 not 16-byte aligned");
+  if (n_tokens == 0) return DIT_OK;
+  GemmEpilogue ep{2, b1, nullptr, 0, nullptr, nullptr};
+  hipError_t e = launch_gemm(dt == DIT_BF16, y, ld_y, w1, h, ld_h, n_tokens, d_ff, d_model, ep,
+                             (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "ffn_up_gelu launch");
+}
+
+static dit_status down_check(dit_dtype dt, const void* h, int64_t ld_h, const void* w2,
+                             const void* x, int64_t ld_x, const uint8_t* modality,
+                             const float* table, void* out, int64_t ld_out, int64_t n_tokens,
+                             int32_t d_model, int32_t d_ff) {
+  if (d_model < 1 || d_ff < 1) return fail(DIT_EINVAL, "ffn_down_gated: d_model/d_ff < 1");
+  if (dit_status st = proj_check("ffn_down_gated", dt, h, ld_h, w2, out, ld_out, n_tokens, d_ff,
+                                 d_model))
+    return st;
+  if (!x || !modality || !table) return fail(DIT_EINVAL, "ffn_down_gated: null pointer");
+  if (ld_x < d_model) return fail(DIT_EINVAL, "ffn_down_gated: ld_x too small");
+  if (d_model % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "ffn_down_gated: d_model %d is not a multiple of 64", d_model);
+  if (!aligned16(x) || !ld_aligned(dt, ld_x))
+    return fail(DIT_EUNSUPPORTED, "ffn_down_gated: pointers/ld must be 16-byte aligned");
+  if (x == out && ld_x != ld_out)
+    return fail(DIT_EINVAL, "ffn_down_gated: in-place needs ld_x == ld_out");
+  return DIT_OK;
+}
+
+extern "C" dit_status ffn_down_gated(dit_dtype dt, const void* h, int64_t ld_h, const void* w2,
+                                     const void* b2, const void* x, int64_t ld_x,
+                                     const uint8_t* modality, const float* table, void* out,
+                                     int64_t ld_out, int64_t n_tokens, int32_t d_model,
+                                     int32_t d_ff, void* stream) {
+  clear_error();
+  if (dit_status st = down_check(dt, h, ld_h, w2, x, ld_x, modality, table, out, ld_out,
+                                 n_tokens, d_model, d_ff))
+    return st;
+  if (b2 && !aligned16(b2)) return fail(DIT_EUNSUPPORTED, "ffn_down_gated: b2 not 16-byte aligned");
+  if (n_tokens == 0) return DIT_OK;
+  GemmEpilogue ep{1, b2, x, ld_x, modality, table + 2 * (size_t)d_model};
+  hipError_t e = launch_gemm(dt == DIT_BF16, h, ld_h, w2, out, ld_out, n_tokens, d_model, d_ff,
+                             ep, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "ffn_down_gated launch");
+}
+
+// ---------------------------------------------------------------------------
 
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+extern "C" size_t dit_ffn_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens) {
+  if (!d || !dtype_ok(d->dtype) || d->d_model < 1 || d->d_ff < 1 || n_tokens < 0) return 0;
+  const size_t es = elt_size(d->dtype), n = (size_t)n_tokens;
+  return round256(n * (size_t)d->d_model * es) + round256(n * (size_t)d->d_ff * es);
+}
+
+extern "C" dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void* out,
+                                      const uint8_t* modality, int64_t n_tokens,
+                                      const float* ada_table, const void* w1, const void* b1,
+                                      const void* w2, const void* b2, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!d) return fail(DIT_EINVAL, "dit_ffn_forward: null descriptor");
+  const dit_dtype dt = d->dtype;
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "dit_ffn_forward: unknown dtype %d", (int)dt);
+  const int32_t D = d->d_model, F = d->d_ff;
+  if (D < 1 || F < 1) return fail(DIT_EINVAL, "dit_ffn_forward: d_model/d_ff < 1");
+  if (!x || !out || !modality || !ada_table || !w1 || !w2)
+    return fail(DIT_EINVAL, "dit_ffn_forward: null pointer");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  const size_t need = dit_ffn_workspace_bytes(d, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "dit_ffn_forward: workspace %zu bytes, need %zu",
+                workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "dit_ffn_forward: workspace must be 256-byte aligned");
+  const size_t es = elt_size(dt), n = (size_t)n_tokens;
+  char* ws = static_cast<char*>(workspace);
+  void* y = ws;
+  void* h = ws + round256(n * (size_t)D * es);
+
+  // Validate every stage before enqueuing any of them.
+  if (dit_status st = adaln_check(dt, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps))
+    return st;
+  if (dit_status st = proj_check("ffn_up_gelu", dt, y, D, w1, h, F, n_tokens, D, F)) return st;
+  if (dit_status st = down_check(dt, h, F, w2, x, D, modality, ada_table, out, D, n_tokens, D, F))
+    return st;
+  if (F % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "dit_ffn_forward: d_ff %d is not a multiple of 64", F);
+  if ((b1 && !aligned16(b1)) || (b2 && !aligned16(b2)) || !aligned16(out))
+    return fail(DIT_EUNSUPPORTED, "dit_ffn_forward: pointers must be 16-byte aligned");
+  if (n_tokens == 0) return DIT_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_adaln(dt == DIT_BF16, x, D, modality, ada_table, y, D, n_tokens, D,
+                              d->ln_eps, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward: adaln launch");
+  GemmEpilogue ep_up{2, b1, nullptr, 0, nullptr, nullptr};
+  e = launch_gemm(dt == DIT_BF16, y, D, w1, h, F, n_tokens, F, D, ep_up, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward: up-projection launch");
+  GemmEpilogue ep_down{1, b2, x, D, modality, ada_table + 2 * (size_t)D};
+  e = launch_gemm(dt == DIT_BF16, h, F, w2, out, D, n_tokens, D, F, ep_down, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward: down-projection launch");
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------------------
 
 extern "C" size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens) {
   if (!d || !dtype_ok(d->dtype) || d->d_model < 1 || n_tokens < 0) return 0;

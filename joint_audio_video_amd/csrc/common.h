@@ -84,9 +84,9 @@ hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int
                        int n_heads, int head_dim, float scale, int causal, hipStream_t s);
 
 // C = A B^T (+ bias), A [M][K], B [N][K]; epilogue 0: store C; 1: gated residual
-// out = x + table[mod][GATE] * C.
+// out = x + table[mod][GATE] * C; 2: store gelu_tanh(C).
 struct GemmEpilogue {
-  int kind;                 // 0 plain, 1 gated residual
+  int kind;                 // 0 plain, 1 gated residual, 2 GELU
   const void* bias;         // [N] or null
   const void* x;            // residual input (kind 1)
   int64_t ld_x;

@@ -1,8 +1,12 @@
-// Projections of the block: C = A B^T (+ bias), with two epilogues.
+// Projections of the block: C = A B^T (+ bias), with three epilogues.
 //   plain:          qkv = y W_qkv^T + b          (fused to_q | to_k | to_v)
-//   gated residual: out = x + gate[m] * (o W_o^T + b)   (to_out.0)
+//   gated residual: out = x + gate[m] * (o W_o^T + b)   (to_out.0, ff.net.2)
+//   GELU:           h = gelu_tanh(y W_1^T + b)   (ff.net.0.proj)
 // [VeRL-Omni] section 5.2 (Q, K, V packed into one matrix on the rollout
-// side); [H3-NFT] (projection names to_q, to_k, to_v, to_out.0).
+// side); [H3-NFT] section "How VeRL-Omni's Adapter Architecture Keeps
+// H3-Specific Logic Contained" (projection names to_q, to_k, to_v, to_out.0,
+// ff.net.0.proj, ff.net.2); the feed-forward activation, tanh-form GELU, is a
+// reading (the pages name none).
 //
 // bf16 path: CDNA4 bf16 MFMA (v_mfma_f32_32x32x16_bf16), float32 accumulate.
 // Workgroup tile 256x256x64, four waves in a 2x2 arrangement, each owning a
@@ -44,6 +48,18 @@ struct EpiArgs {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// tanh-form GELU: 0.5 z (1 + tanh u) with u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated as z / (1 + exp(-2u)) (the same function; one exp and one
+// reciprocal).  Large |z| saturate to z and -0.
+__device__ __forceinline__ float gelu_tanh_fast(float z) {
+  const float u2 = 1.5957691216057308f * fmaf(0.044715f * z, z * z, z);   // 2u
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-u2));
+}
+__device__ __forceinline__ float gelu_tanh_exact(float z) {
+  const float u2 = 1.5957691216057308f * fmaf(0.044715f * z, z * z, z);
+  return z / (1.0f + expf(-u2));
+}
 
 // Tile of this workgroup: groups of kGroupM M-tiles, walked column by column.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -204,6 +220,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
           const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
           v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
         }
+        if constexpr (KIND == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
+        }
         if constexpr (KIND == 1) {
           const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
           const float4 gt = *reinterpret_cast<const float4*>(grow + col);
@@ -257,6 +277,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       const int col = n0 + tx * 4 + j;
       if (col >= N) continue;
       float v = acc[i][j] + (bias ? bias[col] : 0.0f);
+      if (kind == 2) v = gelu_tanh_exact(v);
       if (kind == 1) v = fmaf(gate[mod[row] * gate_stride + col], v, x[(int64_t)row * ld_x + col]);
       C[(int64_t)row * ldc + col] = v;
     }
@@ -276,6 +297,10 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
               ep.ld_x, ep.mod, ep.gate, gate_stride};
     if (ep.kind == 1)
       gemm_bf16_kernel<1><<<dim3(tiles), dim3(kThreads), 0, s>>>(
+          static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
+          static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
+    else if (ep.kind == 2)
+      gemm_bf16_kernel<2><<<dim3(tiles), dim3(kThreads), 0, s>>>(
           static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
           static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
     else

@@ -118,13 +118,21 @@ FULL_ALIGNED_TOKENS = 58816
 # bf16 storage helpers (input formatting: round-to-nearest-even, done once)
 # ---------------------------------------------------------------------------
 
+def _bf16_rounded_words(a: np.ndarray) -> np.ndarray:
+    """float32 bit patterns rounded to bfloat16 (nearest, ties to even) in the high
+    half.  In uint32 the sum wraps only for NaN inputs, which callers replace."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    return r
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = (_bf16_rounded_words(a) >> 16).astype(np.uint16)
     nan = np.isnan(a)
-    out = rounded.astype(np.uint16)
     if nan.any():
         out[nan] = 0x7FC0
     return out
@@ -137,7 +145,13 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """float32 array whose values are exactly representable in bfloat16."""
-    return bf16_bits_to_f32(f32_to_bf16_bits(a))
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    r = _bf16_rounded_words(a)
+    r &= np.uint32(0xFFFF0000)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = np.uint32(0x7FC00000)
+    return r.view(np.float32)
 
 
 # ---------------------------------------------------------------------------

@@ -142,3 +142,41 @@ def test_block_workspace_and_descriptor_checks():
     st = jav._lib.dit_block_forward(ctypes.byref(bad), *args, fake, 1 << 40, None)
     assert st == jav.DIT_EINVAL
     assert jav.block_workspace_bytes(jav.block_desc(9, 64, 1, 64, (16, 24, 24)), 10) == 0
+
+
+def test_ffn_entry_points_validate_before_enqueue():
+    fake = 1 << 20            # never dereferenced: validation fails first
+    B = jav.DIT_BF16
+    # ffn_up_gelu(dt, y, ld_y, w1, b1, h, ld_h, n, d_model, d_ff, stream)
+    assert _call("ffn_up_gelu", B, None, 5120, fake, None, fake, 20480, 10, 5120, 20480, None) == jav.DIT_EINVAL
+    assert _call("ffn_up_gelu", B, fake, 5120, fake, None, fake, 20000, 10, 5120, 20480, None) == jav.DIT_EINVAL   # ld_h
+    assert _call("ffn_up_gelu", B, fake, 5120, fake, None, fake, 20480, 10, 5120, 0, None) == jav.DIT_EINVAL       # d_ff
+    assert _call("ffn_up_gelu", B, fake, 5120, fake, None, fake, 20480, 10, 5120, 20420, None) == jav.DIT_EUNSUPPORTED  # d_ff % 64
+    assert _call("ffn_up_gelu", B, fake, 5120, fake, fake + 8, fake, 20480, 10, 5120, 20480, None) == jav.DIT_EUNSUPPORTED  # b1 align
+    assert _call("ffn_up_gelu", B, fake, 5120, fake, None, fake, 20480, 0, 5120, 20480, None) == jav.DIT_OK      # no rows
+    # ffn_down_gated(dt, h, ld_h, w2, b2, x, ld_x, mod, table, out, ld_out, n, d_model, d_ff, stream)
+    D = [B, fake, 20480, fake, None]
+    assert _call("ffn_down_gated", *D, None, 5120, fake, fake, fake, 5120, 10, 5120, 20480, None) == jav.DIT_EINVAL   # x
+    assert _call("ffn_down_gated", *D, fake, 5120, fake, fake, fake, 5120, 10, 5064, 20480, None) == jav.DIT_EUNSUPPORTED  # d_model % 64
+    assert _call("ffn_down_gated", *D, fake, 5120, fake, fake, fake, 5184, 10, 5120, 20480, None) == jav.DIT_EINVAL   # in place, ld differs
+    assert _call("ffn_down_gated", *D, fake, 5120, fake, fake, fake + 16, 5120, 0, 5120, 20480, None) == jav.DIT_OK
+
+
+def test_ffn_workspace_and_descriptor_checks():
+    desc = jav.ffn_desc(jav.DIT_BF16, 5120, 20480)
+    n = 58758
+    want = sum(((n * w * 2 + 255) // 256) * 256 for w in (5120, 20480))
+    assert jav.ffn_workspace_bytes(desc, n) == want
+    fake = 1 << 20
+    # (desc, x, out, mod, n, table, w1, b1, w2, b2, ws, ws_bytes, stream)
+    st = jav._lib.dit_ffn_forward(ctypes.byref(desc), fake, fake, fake, 100, fake, fake, None,
+                                  fake, None, fake, 10, None)
+    assert st == jav.DIT_EWORKSPACE
+    st = jav._lib.dit_ffn_forward(ctypes.byref(desc), fake, fake, fake, 100, fake, fake, None,
+                                  fake, None, fake + 128, 1 << 40, None)
+    assert st == jav.DIT_EUNSUPPORTED           # workspace not 256-byte aligned
+    bad = jav.ffn_desc(jav.DIT_BF16, 5120, 20420)
+    st = jav._lib.dit_ffn_forward(ctypes.byref(bad), fake, fake, fake, 100, fake, fake, None,
+                                  fake, None, fake, 1 << 40, None)
+    assert st == jav.DIT_EUNSUPPORTED           # d_ff not a multiple of 64
+    assert jav.ffn_workspace_bytes(jav.ffn_desc(9, 64, 256), 10) == 0
