@@ -8,8 +8,10 @@ with float32 accumulation, inputs resident in HBM before timing starts.
 Prints ONE JSON line.  ``value`` is the block's algorithmic TFLOP/s; the
 attention kernel (85% of the block's FLOPs) is the dominant kernel for the
 roofline entry, timed with HIP events recorded by the library around each
-stage on the stream the kernels run on.  ``cpu_baseline`` times the float64
-oracle on a bounded row sample of the same workload on the host cores.
+stage on the stream the kernels run on.  ``ffn_half`` times the block's
+feed-forward half (d_ff = 4 d_model) on its own; it is not part of ``value``.
+``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
+workload on the host cores.
 """
 from __future__ import annotations
 
@@ -161,6 +163,8 @@ def main() -> int:
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ffn", action="store_true",
+                    help="skip timing the feed-forward half (d_ff = 4 d_model)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
@@ -271,6 +275,51 @@ def main() -> int:
     del y, qkv, o, q_v, k_v, v_v
     print(f"# isolated: {iso_ms}", file=sys.stderr, flush=True)
 
+    # The feed-forward half of the same block (d_ff = 4 d_model), timed on its own:
+    # the whole half, then each of its GEMMs.
+    ffn_rec = None
+    if not args.no_ffn:
+        print("# feed-forward half ...", file=sys.stderr, flush=True)
+        fi = synth.ffn_inputs(wl)
+        F = wl.d_ff
+        w1, w2 = bf(fi.w1), bf(fi.w2)
+        table2 = torch.from_numpy(fi.table).to(dev)
+        fdesc = jav.ffn_desc(jav.DIT_BF16, d, F, wl.eps)
+        fws = torch.empty(jav.ffn_workspace_bytes(fdesc, n), dtype=torch.uint8, device=dev)
+        y2 = torch.empty_like(x)
+        h2 = torch.empty((n, F), dtype=torch.bfloat16, device=dev)
+        jav.adaln_modulate(x, mod, table2, wl.eps, out=y2, stream=stream)
+        ffn_ops = {
+            "ffn": (5, lambda: jav.ffn_forward(fdesc, x, mod, table2, w1, w2, out=out,
+                                               workspace=fws, stream=stream)),
+            "ffn_up": (5, lambda: jav.ffn_up_gelu(y2, w1, out=h2, stream=stream)),
+            "ffn_down": (5, lambda: jav.ffn_down_gated(h2, w2, x, mod, table2, out=out,
+                                                       stream=stream)),
+        }
+        for name, (reps, fn) in ffn_ops.items():
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            iso_ms[name] = e0.elapsed_time(e1) / reps
+        gemm_f = 2.0 * n * d * F
+        ffn_rec = {
+            "d_ff": F,
+            "ffn_ms": round(iso_ms["ffn"], 4),
+            "ffn_tflops": round(2 * gemm_f / (iso_ms["ffn"] * 1e-3) / 1e12, 2),
+            "ffn_frac_of_bf16_peak": round(2 * gemm_f / (iso_ms["ffn"] * 1e-3) / 1e12
+                                           / PEAK_BF16_TFLOPS, 4),
+            "up_gelu_tflops": round(gemm_f / (iso_ms["ffn_up"] * 1e-3) / 1e12, 2),
+            "down_gated_tflops": round(gemm_f / (iso_ms["ffn_down"] * 1e-3) / 1e12, 2),
+        }
+        del fws, y2, h2, w1, w2
+        print(f"# ffn: {ffn_rec}", file=sys.stderr, flush=True)
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -328,6 +377,8 @@ def main() -> int:
             "traffic": recorded_traffic() if (wl.name == "full" and not args.causal) else None,
         },
     }
+    if ffn_rec is not None:
+        rec["ffn_half"] = ffn_rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle
