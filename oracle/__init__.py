@@ -26,7 +26,9 @@ Parity of the pack order and of the RoPE pair convention is pinned by the
 stated readings only (the pages fix neither), see ``oracle.layout`` and
 ``oracle.block.rope3d``; so are the feed-forward half's activation (tanh
 GELU) and width (4 x d_model), see ``oracle.block.gelu_tanh`` and
-``oracle.block.ffn_forward``.
+``oracle.block.ffn_forward``.  ``oracle.denoise`` holds the denoising step
+around the block (Rectified Flow X0, Euler with eta = 0, dual schedules,
+anchor re-pinning, H3's timestep and velocity conventions).
 """
 from .layout import (MOD_AUDIO, MOD_TEXT, MOD_VIDEO, SAMPLES_PER_AUDIO_TOKEN,
                      SPATIAL_DOWNSAMPLE, TEMPORAL_DOWNSAMPLE, grid_from_media,
@@ -34,6 +36,8 @@ from .layout import (MOD_AUDIO, MOD_TEXT, MOD_VIDEO, SAMPLES_PER_AUDIO_TOKEN,
 from .block import (adaln_modulate, attention, attention_probs, block_forward,
                     ffn_forward, ffn_up, gelu_tanh, out_proj_gated, qkv_project, rope3d,
                     rope_frequencies)
+from .denoise import (VIDEO_LATENT_CHANNELS, clean_estimate, denoise_loop, denoise_step,
+                      euler_step, standard_velocity, timestep_from_sigma)
 
 __all__ = [
     "MOD_VIDEO", "MOD_AUDIO", "MOD_TEXT", "SAMPLES_PER_AUDIO_TOKEN",
@@ -41,4 +45,6 @@ __all__ = [
     "pack_layout", "request_length", "adaln_modulate", "qkv_project",
     "rope3d", "rope_frequencies", "attention", "attention_probs",
     "out_proj_gated", "block_forward", "gelu_tanh", "ffn_up", "ffn_forward",
+    "VIDEO_LATENT_CHANNELS", "timestep_from_sigma", "standard_velocity", "clean_estimate",
+    "euler_step", "denoise_step", "denoise_loop",
 ]

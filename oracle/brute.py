@@ -112,3 +112,27 @@ def ffn(x, modality, table, w1, w2, b1=None, b2=None, eps: float = 1e-6):
     z = linear(h, w2, b2)
     return [[x[i][j] + table[modality[i]][2][j] * z[i][j] for j in range(len(x[i]))]
             for i in range(len(x))]
+
+
+def denoise_step(z, v, modality, sigmas, anchor=None, anchor_vals=None, velocity_sign=1.0):
+    """Loop version of oracle.denoise.denoise_step (None where a row is not advanced)."""
+    z_next, x0 = [], []
+    for i, row in enumerate(z):
+        m = modality[i]
+        if m not in (0, 1):
+            z_next.append(list(row))
+            x0.append([None] * len(row))
+            continue
+        if anchor is not None and anchor[i]:
+            z_next.append(list(anchor_vals[i]))
+            x0.append(list(anchor_vals[i]))
+            continue
+        s, s_next = sigmas[m]
+        zr, xr = [], []
+        for c in range(len(row)):
+            vs = velocity_sign * v[i][c]
+            xr.append(row[c] - s * vs)
+            zr.append(row[c] + (s_next - s) * vs)
+        z_next.append(zr)
+        x0.append(xr)
+    return z_next, x0
