@@ -10,6 +10,9 @@ attention kernel (85% of the block's FLOPs) is the dominant kernel for the
 roofline entry, timed with HIP events recorded by the library around each
 stage on the stream the kernels run on.  ``ffn_half`` times the block's
 feed-forward half (d_ff = 4 d_model) on its own; it is not part of ``value``.
+``denoise_step`` times the denoising step around the block (one streaming
+pass over the packed latent state), at the workload's size and on a 16-pack
+batch large enough to stream from HBM.
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
 workload on the host cores.
 """
@@ -121,6 +124,27 @@ def elementwise_bytes(n_tokens, d, elt=2):
     return adaln, rope
 
 
+DENOISE_CHANNELS = 96        # 24 latent channels x the 1x2x2 patch of a video token
+
+
+def denoise_anchors(mod, pos):
+    """Anchor rows of the synthetic recipe: the first video frame (t = 0) and the first
+    8 audio tokens of each channel."""
+    return (((mod == 0) & (pos[:, 0] == 0)) | ((mod == 1) & (pos[:, 0] < 8))).astype(np.uint8)
+
+
+def denoise_bytes(mod, anchor, channels, v_elt=2):
+    """Algorithmic bytes of one denoise_step with an X0 output: every row reads its id;
+    latent rows read their anchor flag; free latent rows read z and v and write z and
+    X0; anchor rows read their anchor value and write z and X0; text rows nothing more."""
+    lat = mod != 2
+    pin = lat & (anchor != 0)
+    free = lat & ~pin
+    c = channels
+    return int(mod.size + lat.sum() + free.sum() * (4 * c + v_elt * c + 8 * c)
+               + pin.sum() * 12 * c)
+
+
 def cpu_baseline(wl, inp, lay, rows_n: int):
     """Oracle (float64 NumPy) on a bounded sample: every stage for `rows_n` query rows,
     attention of those rows against all keys of their segment (synthetic k, v)."""
@@ -165,6 +189,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip timing the feed-forward half (d_ff = 4 d_model)")
+    ap.add_argument("--no-denoise", action="store_true",
+                    help="skip timing the denoising step around the block")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
@@ -320,6 +346,45 @@ def main() -> int:
         del fws, y2, h2, w1, w2
         print(f"# ffn: {ffn_rec}", file=sys.stderr, flush=True)
 
+    # The denoising step around the block: one streaming pass over the packed latent
+    # state (float32 z, bf16 velocity, float32 X0), at the workload's size (79 MB, held
+    # in the Infinity Cache between launches) and on 16 packs (1.27 GB from HBM).
+    den_rec = None
+    if not args.no_denoise:
+        print("# denoise step ...", file=sys.stderr, flush=True)
+        C = DENOISE_CHANNELS
+        sig = (0.62, 0.6, 0.5, 0.47)
+        mod_h = np.asarray(lay["modality"])
+        an_h = denoise_anchors(mod_h, np.asarray(lay["pos"]))
+        den_rec = {"channels": C, "sigmas": list(sig), "anchor_rows": int(an_h.sum())}
+        for label, packs, reps in (("pack", 1, 50), ("16_packs", 16, 20)):
+            di = synth.denoise_inputs(wl, C, n_rows=n * packs)
+            m_h, a_h = np.tile(mod_h, packs), np.tile(an_h, packs)
+            z_d = torch.from_numpy(di.z).to(dev)
+            v_d = bf(di.v)
+            av_d = torch.from_numpy(di.anchor_vals).to(dev)
+            x0_d = torch.empty_like(z_d)
+            m_d, a_d = torch.from_numpy(m_h).to(dev), torch.from_numpy(a_h).to(dev)
+            fn = (lambda z_d=z_d, v_d=v_d, m_d=m_d, x0_d=x0_d, a_d=a_d, av_d=av_d:
+                  jav.denoise_step(z_d, v_d, m_d, sig, x0=x0_d, anchor=a_d, anchor_vals=av_d,
+                                   stream=stream))
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_ms = e0.elapsed_time(e1) / reps
+            b = denoise_bytes(m_h, a_h, C)
+            den_rec[label] = {"rows": int(m_h.size), "us": round(t_ms * 1e3, 2), "bytes": b,
+                              "gbs": round(b / (t_ms * 1e-3) / 1e9, 1),
+                              "frac_of_hbm": round(b / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del z_d, v_d, av_d, x0_d, m_d, a_d, di
+        print(f"# denoise: {den_rec}", file=sys.stderr, flush=True)
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -379,6 +444,8 @@ def main() -> int:
     }
     if ffn_rec is not None:
         rec["ffn_half"] = ffn_rec
+    if den_rec is not None:
+        rec["denoise_step"] = den_rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle

@@ -13,7 +13,9 @@
  *
  * The block: per-modality AdaLN -> fused QKV projection -> 3D (t, h, w) RoPE on
  * q and k -> softmax attention inside cu_seqlens segments -> output projection
- * -> gated residual.  The FFN half of the layer is not part of this library.
+ * -> gated residual; then the feed-forward half (AdaLN -> ff.net.0.proj ->
+ * GELU -> ff.net.2 -> gated residual).  Around the block: the denoising step
+ * that advances the packed audio-video latent state after each DiT forward.
  *
  * Conventions shared by every device entry point
  * ----------------------------------------------
@@ -262,6 +264,52 @@ dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void* out,
                            const uint8_t* modality, int64_t n_tokens, const float* ada_table,
                            const void* w1, const void* b1, const void* w2, const void* b2,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The denoising step around the block                                        */
+/* ------------------------------------------------------------------------ */
+
+/* [vLLM-Omni] section 4, "Joint Audio-Video Denoising Execution Flow" (runtime
+ * loop, stages 4-7): the DiT's packed output is split by modality into a video
+ * and an audio velocity; the Rectified Flow parameterisation turns it into a
+ * clean estimate X0; a deterministic Euler step (eta = 0) advances each
+ * modality with its own schedule (sigma_video, sigma_audio), written back
+ * together; anchor rows are then re-pinned to their original values.
+ * [VeRL-Omni] section 5.1: H3's DiT takes data-progress time t = 1 - sigma
+ * (sigma = 1 pure noise, 0 clean) and emits the negated velocity.
+ *
+ * denoise_step: for each row r of the packed latent state, with modality
+ * m = modality[r]:
+ *   m == VIDEO or AUDIO, anchor absent or anchor[r] == 0:
+ *     v_std = velocity_sign * v[r];   (s, s') = the sigmas of modality m
+ *     x0[r] = z[r] - s * v_std        (Rectified Flow: z = (1-s) x0 + s eps,
+ *     z[r]  = z[r] + (s' - s) * v_std  v_std = eps - x0; Euler in sigma)
+ *   m == VIDEO or AUDIO, anchor[r] != 0:  z[r] = x0[r] = anchor_vals[r]
+ *   m == TEXT: nothing is read or written (text rows condition the DiT but
+ *   are not latent state).
+ * z: device float32 [n_rows][ld_z], updated in place; v: [n_rows][ld_v] of
+ * v_dtype (bf16 or f32, the DiT's output head); x0: float32 [n_rows][ld_x0]
+ * or NULL (not written); modality: device uint8 [n_rows] (the block's ids);
+ * anchor: device uint8 [n_rows] or NULL (no anchors); anchor_vals: float32
+ * [n_rows][ld_a], read on anchor rows only (required when anchor is given).
+ * The first `channels` columns of each row are the state (96 = 24 latent
+ * channels x the 1x2x2 patch of a video token, [H3-NFT]).  sigmas: host
+ * float[4] = {sigma_video, sigma_video_next, sigma_audio, sigma_audio_next},
+ * each in [0, 1]; the step is sigma_next - sigma in float32, exactly -sigma
+ * when sigma_next is 0, so the last step leaves z == x0.  velocity_sign: +1
+ * when v is eps - x0 (generic schedulers), -1 for H3's own output.
+ * x0 must not overlap z, v or anchor_vals; z must not overlap v.
+ * Errors: DIT_EINVAL for a null z / v / modality / sigmas, anchor without
+ * anchor_vals, channels < 1, an ld below channels, n_rows < 0, a sigma that
+ * is not finite or outside [0, 1], velocity_sign not +-1, an unknown dtype;
+ * DIT_EUNSUPPORTED when channels is not a multiple of 4, n_rows * channels / 4
+ * exceeds 2^31 - 1, or a pointer or ld breaks the 16-byte rule; DIT_EHIP on
+ * a launch failure. */
+dit_status denoise_step(dit_dtype v_dtype, float* z, int64_t ld_z, const void* v, int64_t ld_v,
+                        float* x0, int64_t ld_x0, const uint8_t* modality,
+                        const uint8_t* anchor, const float* anchor_vals, int64_t ld_a,
+                        int64_t n_rows, int32_t channels, const float sigmas[4],
+                        int32_t velocity_sign, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* The whole attention half of the block                                      */

@@ -32,6 +32,7 @@ EXPORTED = (
     "adaln_modulate", "rope3d_apply", "attn_packed", "qkv_project", "out_proj_gated",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
     "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
+    "denoise_step",
 )
 
 
@@ -94,6 +95,8 @@ def _load() -> ctypes.CDLL:
         "dit_ffn_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
         "dit_ffn_forward": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P, P,
                                            P, SZ, P]),
+        "denoise_step": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, P, P, I64, I64,
+                                        I32, ctypes.POINTER(F32), I32, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -356,3 +359,32 @@ def profile_read() -> Tuple[List[float], int]:
     n = ctypes.c_int32(0)
     _check(_lib.dit_profile_read(ms, ctypes.byref(n)))
     return list(ms), n.value
+
+
+# ---------------------------------------------------------------------------
+# denoising step around the block
+# ---------------------------------------------------------------------------
+
+def timestep_from_sigma(sigma: float) -> float:
+    """H3's data-progress time for a scheduler noise level: t = 1 - sigma."""
+    return 1.0 - float(sigma)
+
+
+def denoise_step(z, v, modality, sigmas: Sequence[float], x0=None, anchor=None,
+                 anchor_vals=None, velocity_sign: int = 1, n_rows=None, stream=None):
+    """One step of the joint loop in place on z (libdit denoise_step).
+
+    sigmas = (sigma_video, sigma_video_next, sigma_audio, sigma_audio_next);
+    x0, if given, receives the clean estimate of every video/audio row.
+    """
+    n = z.shape[0] if n_rows is None else int(n_rows)
+    c = z.shape[1]
+    pz, ldz = _rows(z)
+    pv, ldv = _rows(v)
+    px, ldx = (0, 0) if x0 is None else _rows(x0)
+    pa, lda = (0, 0) if anchor_vals is None else _rows(anchor_vals)
+    sig = (ctypes.c_float * 4)(*[float(x) for x in sigmas])
+    _check(_lib.denoise_step(_dtype_code(v), pz, ldz, pv, ldv, px, ldx, modality.data_ptr(),
+                             _ptr(anchor), pa, lda, n, c, sig, int(velocity_sign),
+                             _stream(stream)))
+    return z

@@ -32,7 +32,8 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-SOURCES = ["abi.cpp", "layout.cpp", "adaln.hip", "rope.hip", "gemm.hip", "attn.hip"]
+SOURCES = ["abi.cpp", "layout.cpp", "adaln.hip", "rope.hip", "gemm.hip", "attn.hip",
+           "denoise.hip"]
 
 
 def _compile(src: str) -> str:

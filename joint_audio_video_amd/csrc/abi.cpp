@@ -318,6 +318,57 @@ extern "C" dit_status ffn_down_gated(dit_dtype dt, const void* h, int64_t ld_h, 
 }
 
 // ---------------------------------------------------------------------------
+// Denoising step
+
+static dit_status denoise_check(dit_dtype dt, const float* z, int64_t ld_z, const void* v,
+                                int64_t ld_v, const float* x0, int64_t ld_x0,
+                                const uint8_t* modality, const uint8_t* anchor,
+                                const float* anchor_vals, int64_t ld_a, int64_t n_rows,
+                                int32_t channels, const float* sigmas, int32_t sign) {
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "denoise_step: unknown dtype %d", (int)dt);
+  if (!z || !v || !modality || !sigmas) return fail(DIT_EINVAL, "denoise_step: null pointer");
+  if (anchor && !anchor_vals)
+    return fail(DIT_EINVAL, "denoise_step: anchor flags given without anchor_vals");
+  if (channels < 1) return fail(DIT_EINVAL, "denoise_step: channels < 1");
+  if (ld_z < channels || ld_v < channels || (x0 && ld_x0 < channels) ||
+      (anchor && ld_a < channels))
+    return fail(DIT_EINVAL, "denoise_step: ld < channels");
+  if (n_rows < 0) return fail(DIT_EINVAL, "denoise_step: n_rows < 0");
+  for (int i = 0; i < 4; ++i)
+    if (!(sigmas[i] >= 0.0f && sigmas[i] <= 1.0f))
+      return fail(DIT_EINVAL, "denoise_step: sigma[%d] = %g is not in [0, 1]", i,
+                  (double)sigmas[i]);
+  if (sign != 1 && sign != -1)
+    return fail(DIT_EINVAL, "denoise_step: velocity_sign %d is not +1 or -1", sign);
+  if (channels % 4 != 0)
+    return fail(DIT_EUNSUPPORTED, "denoise_step: channels %d is not a multiple of 4", channels);
+  if (n_rows * (int64_t)(channels / 4) > INT32_MAX)
+    return fail(DIT_EUNSUPPORTED, "denoise_step: more than 2^31-1 groups of 4 channels");
+  if (!aligned16(z) || !aligned16(v) || (x0 && !aligned16(x0)) ||
+      (anchor && !aligned16(anchor_vals)) || !ld_aligned(DIT_F32, ld_z) || !ld_aligned(dt, ld_v) ||
+      (x0 && !ld_aligned(DIT_F32, ld_x0)) || (anchor && !ld_aligned(DIT_F32, ld_a)))
+    return fail(DIT_EUNSUPPORTED, "denoise_step: pointers/ld must be 16-byte aligned");
+  return DIT_OK;
+}
+
+extern "C" dit_status denoise_step(dit_dtype v_dtype, float* z, int64_t ld_z, const void* v,
+                                   int64_t ld_v, float* x0, int64_t ld_x0,
+                                   const uint8_t* modality, const uint8_t* anchor,
+                                   const float* anchor_vals, int64_t ld_a, int64_t n_rows,
+                                   int32_t channels, const float sigmas[4],
+                                   int32_t velocity_sign, void* stream) {
+  clear_error();
+  if (dit_status st = denoise_check(v_dtype, z, ld_z, v, ld_v, x0, ld_x0, modality, anchor,
+                                    anchor_vals, ld_a, n_rows, channels, sigmas, velocity_sign))
+    return st;
+  if (n_rows == 0) return DIT_OK;
+  hipError_t e = launch_denoise(v_dtype == DIT_BF16, z, ld_z, v, ld_v, x0, ld_x0, modality,
+                                anchor, anchor_vals, ld_a, n_rows, channels, sigmas,
+                                (float)velocity_sign, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "denoise_step launch");
+}
+
+// ---------------------------------------------------------------------------
 
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 

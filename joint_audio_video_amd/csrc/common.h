@@ -97,4 +97,10 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
                        int64_t ldc, int64_t m, int n, int k, const GemmEpilogue& ep,
                        hipStream_t s);
 
+// sigmas: host {video, video_next, audio, audio_next}; sign +1 or -1.
+hipError_t launch_denoise(int bf16, float* z, int64_t ld_z, const void* v, int64_t ld_v,
+                          float* x0, int64_t ld_x0, const uint8_t* mod, const uint8_t* anchor,
+                          const float* anchor_vals, int64_t ld_a, int64_t n_rows, int channels,
+                          const float sigmas[4], float sign, hipStream_t s);
+
 }  // namespace dit

@@ -248,3 +248,34 @@ def random_segments(n_tokens: int, n_segs: int, seed: int, min_len: int = 1) -> 
         cuts.add(c)
     offs = [0] + sorted(cuts) + [n_tokens]
     return offs
+
+
+@dataclasses.dataclass
+class DenoiseInputs:
+    """Float32 host arrays for one denoising step over a packed latent state."""
+    z: np.ndarray            # [N][C] state, N(0, 1)
+    v: np.ndarray            # [N][C] predicted velocity, N(0, 1); bf16-exact for bf16 workloads
+    anchor_vals: np.ndarray  # [N][C] original values of anchor rows, N(0, 1)
+
+
+def denoise_inputs(wl: Workload, channels: int = 96, n_rows: Optional[int] = None,
+                   seed: Optional[int] = None) -> DenoiseInputs:
+    """Draw z, v, anchor values in that order from PCG64(seed) (default wl.seed + 2000).
+
+    The state stays float32 (it carries 50 steps of updates); the velocity has
+    the workload's dtype, as the DiT's output head would produce it."""
+    n = wl.n_tokens if n_rows is None else n_rows
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 2000 if seed is None else seed))
+    z = _normal(rng, (n, channels), 1.0)
+    v = _normal(rng, (n, channels), 1.0)
+    a = _normal(rng, (n, channels), 1.0)
+    if wl.dtype == BF16:
+        v = round_to_bf16(v)
+    return DenoiseInputs(z, v, a)
+
+
+def sigma_schedule(n_steps: int, power: float = 1.0) -> np.ndarray:
+    """A synthetic decreasing schedule sigma_i = (1 - i / n_steps) ** power, i = 0..n_steps,
+    in float32 (the pages give no sigma values)."""
+    i = np.arange(n_steps + 1, dtype=np.float64)
+    return ((1.0 - i / n_steps) ** power).astype(np.float32)

@@ -180,3 +180,35 @@ def test_ffn_workspace_and_descriptor_checks():
                                   fake, None, fake, 1 << 40, None)
     assert st == jav.DIT_EUNSUPPORTED           # d_ff not a multiple of 64
     assert jav.ffn_workspace_bytes(jav.ffn_desc(9, 64, 256), 10) == 0
+
+
+def test_denoise_step_validates_before_enqueue():
+    fake = 1 << 20            # never dereferenced: validation fails first
+    B, F = jav.DIT_BF16, jav.DIT_F32
+    sig = (ctypes.c_float * 4)(0.8, 0.6, 0.7, 0.5)
+
+    def call(dt=B, z=fake, ldz=96, v=fake, ldv=96, x0=fake, ldx=96, mod=fake, anchor=None,
+             av=None, lda=0, n=10, c=96, sigmas=sig, sign=1):
+        return _call("denoise_step", dt, z, ldz, v, ldv, x0, ldx, mod, anchor, av, lda, n, c,
+                     sigmas, sign, None)
+
+    assert call(dt=5) == jav.DIT_EINVAL
+    assert call(z=None) == jav.DIT_EINVAL
+    assert call(mod=None) == jav.DIT_EINVAL
+    assert call(sigmas=None) == jav.DIT_EINVAL
+    assert call(anchor=fake) == jav.DIT_EINVAL              # flags without values
+    assert call(ldv=64) == jav.DIT_EINVAL
+    assert call(anchor=fake, av=fake, lda=32) == jav.DIT_EINVAL
+    assert call(n=-1) == jav.DIT_EINVAL
+    assert call(c=0) == jav.DIT_EINVAL
+    assert call(sign=0) == jav.DIT_EINVAL
+    for bad in ((1.5, 0.6, 0.7, 0.5), (0.8, -0.1, 0.7, 0.5), (0.8, 0.6, float("nan"), 0.5)):
+        assert call(sigmas=(ctypes.c_float * 4)(*bad)) == jav.DIT_EINVAL
+    assert "sigma" in jav.last_error()
+    assert call(c=94, ldz=96, ldv=96, ldx=96) == jav.DIT_EUNSUPPORTED     # channels % 4
+    assert call(z=fake + 8) == jav.DIT_EUNSUPPORTED
+    assert call(dt=F, ldv=98) == jav.DIT_EUNSUPPORTED                     # f32 rows of 392 B
+    assert call(n=(1 << 31) // 24 + 1) == jav.DIT_EUNSUPPORTED
+    assert call(n=0) == jav.DIT_OK                                        # no rows: no-op
+    assert call(x0=None, ldx=0, n=0) == jav.DIT_OK
+    assert jav.timestep_from_sigma(1.0) == 0.0 and jav.timestep_from_sigma(0.0) == 1.0
