@@ -271,12 +271,16 @@ def main() -> int:
     # read apart from its neighbours in the block (the block's stage times include
     # the event brackets and the power state the previous kernel left behind).
     print("# isolated stages ...", file=sys.stderr, flush=True)
+    # q, k, v as three [N][D] planes, the layout dit_block_forward's workspace uses
     y = torch.empty_like(x)
     qkv = torch.empty((n, 3 * d), dtype=torch.bfloat16, device=dev)
+    planes = torch.empty((3, n, d), dtype=torch.bfloat16, device=dev)
     o = torch.empty_like(x)
     jav.adaln_modulate(x, mod, table, wl.eps, out=y, stream=stream)
     jav.qkv_project(y, w_qkv, out=qkv, stream=stream)
-    q_v, k_v, v_v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    for i in range(3):
+        planes[i].copy_(qkv[:, i * d:(i + 1) * d])
+    q_v, k_v, v_v = planes[0], planes[1], planes[2]
     iso_ops = {
         "adaln": (20, lambda: jav.adaln_modulate(x, mod, table, wl.eps, out=y, stream=stream)),
         "qkv": (5, lambda: jav.qkv_project(y, w_qkv, out=qkv, stream=stream)),
@@ -298,7 +302,7 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         iso_ms[name] = e0.elapsed_time(e1) / reps
-    del y, qkv, o, q_v, k_v, v_v
+    del y, qkv, planes, o, q_v, k_v, v_v
     print(f"# isolated: {iso_ms}", file=sys.stderr, flush=True)
 
     # The feed-forward half of the same block (d_ff = 4 d_model), timed on its own:

@@ -325,8 +325,9 @@ typedef struct {
   int32_t causal;             /* 0: bidirectional inside each segment */
 } dit_block_desc;
 
-/* Bytes of scratch dit_block_forward needs: y [N][D] + qkv [N][3D] + o [N][D]
- * elements, each region rounded up to 256 bytes.  0 for a bad descriptor. */
+/* Bytes of scratch dit_block_forward needs: five [N][D] planes y, q, k, v, o
+ * (q, k, v are the fused projection's output split by column), each rounded
+ * up to 256 bytes.  0 for a bad descriptor. */
 size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
 
 /* x, out: [n_tokens][d_model] contiguous (out may equal x); modality, pos_thw,

@@ -430,10 +430,13 @@ extern "C" dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void
 
 // ---------------------------------------------------------------------------
 
+// Block workspace: five [N][D] planes, y | q | k | v | o, each rounded up to
+// 256 bytes.  q, k and v are separate planes (not one [N][3D] array): the
+// in-place RoPE pass and the attention K/V loads then stream contiguous rows.
 extern "C" size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens) {
   if (!d || !dtype_ok(d->dtype) || d->d_model < 1 || n_tokens < 0) return 0;
   const size_t es = elt_size(d->dtype), n = (size_t)n_tokens, D = (size_t)d->d_model;
-  return round256(n * D * es) + round256(n * 3 * D * es) + round256(n * D * es);
+  return 5 * round256(n * D * es);
 }
 
 extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
@@ -461,26 +464,24 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
     return fail(DIT_EUNSUPPORTED, "dit_block_forward: workspace must be 256-byte aligned");
 
   const size_t es = elt_size(dt), n = (size_t)n_tokens;
+  const size_t plane_bytes = round256(n * D * es);
   char* ws = static_cast<char*>(workspace);
   void* y = ws;
-  char* qkv = ws + round256(n * D * es);
-  void* o = qkv + round256(n * 3 * (size_t)D * es);
-  void* q = qkv;
-  void* k = qkv + (size_t)D * es;
-  void* v = qkv + 2 * (size_t)D * es;
+  char* q = ws + plane_bytes;
+  char* k = q + plane_bytes;
+  char* v = k + plane_bytes;
+  void* o = v + plane_bytes;
 
   // Validate every stage before enqueuing any of them.
   if (dit_status st = adaln_check(dt, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps))
     return st;
-  if (dit_status st = proj_check("qkv_project", dt, y, D, w_qkv, qkv, 3 * (int64_t)D, n_tokens,
-                                 D, 3 * (int64_t)D))
+  if (dit_status st = proj_check("qkv_project", dt, y, D, w_qkv, q, D, n_tokens, D, D))
     return st;
-  if (dit_status st = rope_check(dt, q, 3 * (int64_t)D, k, 3 * (int64_t)D, pos_thw, n_tokens, H,
-                                 Dh, d->rope_sections, d->rope_theta))
+  if (dit_status st = rope_check(dt, q, D, k, D, pos_thw, n_tokens, H, Dh, d->rope_sections,
+                                 d->rope_theta))
     return st;
-  if (dit_status st = attn_check(dt, q, 3 * (int64_t)D, k, 3 * (int64_t)D, v, 3 * (int64_t)D, o,
-                                 D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
-                                 d->softmax_scale))
+  if (dit_status st = attn_check(dt, q, D, k, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
+                                 n_tokens, H, Dh, d->softmax_scale))
     return st;
   if (dit_status st = proj_check("out_proj_gated", dt, o, D, w_o, out, D, n_tokens, D, D))
     return st;
@@ -498,19 +499,20 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   e = launch_adaln(dt == DIT_BF16, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: adaln launch");
   mark(1);
-  GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr};
-  e = launch_gemm(dt == DIT_BF16, y, D, w_qkv, qkv, 3 * (int64_t)D, n_tokens, 3 * D, D, ep_qkv, s);
+  // One GEMM over the fused W_qkv [3D][D], its output split into the q, k, v planes.
+  GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr, D, (int64_t)(plane_bytes / es)};
+  e = launch_gemm(dt == DIT_BF16, y, D, w_qkv, q, D, n_tokens, 3 * D, D, ep_qkv, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: qkv launch");
   mark(2);
   double freq[64];
   rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
-  e = launch_rope(dt == DIT_BF16, q, 3 * (int64_t)D, k, 3 * (int64_t)D, pos_thw, n_tokens, H, Dh,
-                  d->rope_sections[0], d->rope_sections[1], freq, s);
+  e = launch_rope(dt == DIT_BF16, q, D, k, D, pos_thw, n_tokens, H, Dh, d->rope_sections[0],
+                  d->rope_sections[1], freq, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope launch");
   mark(3);
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
-  e = launch_attn(dt == DIT_BF16, q, 3 * (int64_t)D, k, 3 * (int64_t)D, v, 3 * (int64_t)D, o, D,
-                  cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh, scale, d->causal != 0, s);
+  e = launch_attn(dt == DIT_BF16, q, D, k, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
+                  n_tokens, H, Dh, scale, d->causal != 0, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: attention launch");
   mark(4);
   GemmEpilogue ep_out{1, b_o, x, D, modality, ada_table + 2 * (size_t)D};

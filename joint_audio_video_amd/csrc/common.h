@@ -85,6 +85,9 @@ hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int
 
 // C = A B^T (+ bias), A [M][K], B [N][K]; epilogue 0: store C; 1: gated residual
 // out = x + table[mod][GATE] * C; 2: store gelu_tanh(C).
+// Planes (kind 0 only): with plane_cols > 0, output column j goes to plane
+// j / plane_cols, column j % plane_cols, planes plane_stride elements apart
+// (row stride ldc inside a plane); plane_cols must be a multiple of 32.
 struct GemmEpilogue {
   int kind;                 // 0 plain, 1 gated residual, 2 GELU
   const void* bias;         // [N] or null
@@ -92,6 +95,8 @@ struct GemmEpilogue {
   int64_t ld_x;
   const uint8_t* mod;       // modality ids (kind 1)
   const float* gate;        // table + GATE row offset; row stride 3*N floats (kind 1)
+  int plane_cols = 0;       // 0: one [M][ldc] output
+  int64_t plane_stride = 0;
 };
 hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c,
                        int64_t ldc, int64_t m, int n, int k, const GemmEpilogue& ep,

@@ -45,6 +45,8 @@ struct EpiArgs {
   const uint8_t* mod;
   const float* gate;
   int64_t gate_stride;      // floats between the gate rows of two modalities
+  int plane_cols;           // kind 0: output split into planes of this many columns (0: none)
+  int64_t plane_stride;     // elements between planes
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
@@ -209,6 +211,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
+      // A 32-column block never straddles two planes (plane_cols is a multiple of 32).
+      uint16_t* cbase = crow;
+      int cshift = 0;
+      if (KIND == 0 && ep.plane_cols > 0) {
+        const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
+        cbase = crow + plane * ep.plane_stride;
+        cshift = plane * ep.plane_cols;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
           v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
           v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
         }
-        *reinterpret_cast<uint2*>(crow + col) =
+        *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
@@ -248,7 +258,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                         int N, int K, const float* bias,
                                                         int kind, const float* x, int64_t ld_x,
                                                         const uint8_t* mod, const float* gate,
-                                                        int64_t gate_stride) {
+                                                        int64_t gate_stride, int plane_cols,
+                                                        int64_t plane_stride) {
   __shared__ float As[FK][FT + 1];
   __shared__ float Bs[FK][FT + 1];
   const int m0 = blockIdx.y * FT, n0 = blockIdx.x * FT;
@@ -279,7 +290,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       float v = acc[i][j] + (bias ? bias[col] : 0.0f);
       if (kind == 2) v = gelu_tanh_exact(v);
       if (kind == 1) v = fmaf(gate[mod[row] * gate_stride + col], v, x[(int64_t)row * ld_x + col]);
-      C[(int64_t)row * ldc + col] = v;
+      const int plane = plane_cols > 0 ? col / plane_cols : 0;
+      C[plane * plane_stride + (int64_t)row * ldc + (col - plane * plane_cols)] = v;
     }
   }
 }
@@ -289,12 +301,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c, int64_t ldc,
                        int64_t m, int n, int k, const GemmEpilogue& ep, hipStream_t s) {
   if (k % BK != 0 || m > INT32_MAX) return hipErrorInvalidValue;
+  if (ep.plane_cols < 0 || ep.plane_cols % 32 != 0 || (ep.plane_cols > 0 && ep.kind != 0))
+    return hipErrorInvalidValue;
   // gate rows of the table are 3*N floats apart (table [3][3][N], N = d_model)
   const int64_t gate_stride = 3 * (int64_t)n;
   if (bf16) {
     const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
-              ep.ld_x, ep.mod, ep.gate, gate_stride};
+              ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride};
     if (ep.kind == 1)
       gemm_bf16_kernel<1><<<dim3(tiles), dim3(kThreads), 0, s>>>(
           static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
@@ -312,7 +326,8 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
     gemm_f32_kernel<<<grid, dim3(256), 0, s>>>(
         static_cast<const float*>(a), lda, static_cast<const float*>(b), static_cast<float*>(c),
         ldc, (int)m, n, k, static_cast<const float*>(ep.bias), ep.kind,
-        static_cast<const float*>(ep.x), ep.ld_x, ep.mod, ep.gate, gate_stride);
+        static_cast<const float*>(ep.x), ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols,
+        ep.plane_stride);
   }
   return hipGetLastError();
 }
