@@ -25,6 +25,9 @@
 //     wave's softmax (exp, convert: plain VALU) overlaps the other's MFMAs.
 //     Row sums are fp32 adds, not v_dot2 (which shares the matrix pipe and
 //     would serialise with the other wave's MFMAs).
+//   * Softmax without a per-tile max: the first key tile sets each row's
+//     reference max and later tiles exponentiate against it; only a tile whose
+//     probabilities would leave range moves the reference (rare).
 //   * exp2 with log2(e) folded into the scale; P is rounded to bf16 for the
 //     PV product, its row sum is taken over the fp32 values; accumulation in
 //     float32.
@@ -69,9 +72,9 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const lds_u16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
 }
 
-// Reference max moves only when a row's running max grows by more than this
-// (log2 units), so the O rescale is rare; p <= 2^kLazyLog2 meanwhile.
-constexpr float kLazyLog2 = 8.0f;
+// Bound on a lane's partial row sum of one tile (so on every p) before the
+// reference max is moved: 2^32.
+constexpr float kRefBound = 4294967296.0f;
 
 // LDS fragment reads are issued this many k-steps (S^T) or MFMAs (PV) ahead of
 // the MFMA that consumes them; scheduling fences keep the compiler from
@@ -200,7 +203,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
-  const float lazy_raw = kLazyLog2 / scale_log2;   // threshold in raw score units
   const f32x16 zero16 = {};
 
   // Ping-pong: the two waves sharing a SIMD (w and w + kWaves/2) are half a
@@ -243,6 +245,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
   // Online softmax of tile j (scores in sacc) into the bf16 operand pf.
   // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.
+  // The first key tile sets each row's reference max; later tiles exponentiate
+  // against it without taking their own max.  Only when a tile's probabilities
+  // could leave range (a lane's partial row sum above 2^kRefLog2, or not finite)
+  // does the rare path take that tile's max, move the reference and rescale
+  // O and l.  o = sum p v / sum p does not depend on the reference.
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kb = seg0 + j * KB;
     if ((kb + KB > seg1) || (causal && kb + KB - 1 > qw0)) {
@@ -254,37 +261,43 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
           if (key >= seg1 || (causal && key > qrow)) sacc[b][e] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int b = 0; b < NKB; ++b)
+      for (int b = 0; b < NKB; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[b][e]);
-    mx = half_swap_max(mx);
-    // Lazy rescale: move the reference max (and rescale O, l) only when some
-    // row's max grew by more than the threshold; o/l is unchanged either way.
-    const bool grow = mx > m_run + lazy_raw;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.0f;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[b][e]);
+      return half_swap_max(mx);
+    };
+    auto exps = [&]() __attribute__((always_inline)) {
+      const float nms = -(m_run == -INFINITY ? 0.0f : m_run) * scale_log2;
+      float rs = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e + 1], scale_log2, nms));
+          rs += p0 + p1;
+          pf[2 * b + (e >> 3)][e & 7] = (__bf16)p0;
+          pf[2 * b + (e >> 3)][(e & 7) + 1] = (__bf16)p1;
+        }
+      return rs;
+    };
+    if (j == 0) m_run = tile_max();
+    float rs = exps();
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kRefBound)) != 0) {
+      const float m_new = fmaxf(m_run, tile_max());
+      const float alpha = m_run == -INFINITY ? 0.0f
+                                             : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
       m_run = m_new;
+      rs = exps();
     }
-    const float nms = -(m_run == -INFINITY ? 0.0f : m_run) * scale_log2;
-    float rs = 0.0f;
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e + 1], scale_log2, nms));
-        rs += p0 + p1;
-        pf[2 * b + (e >> 3)][e & 7] = (__bf16)p0;
-        pf[2 * b + (e >> 3)][(e & 7) + 1] = (__bf16)p1;
-      }
     l_run += rs;
   };
 
