@@ -68,7 +68,7 @@ class FfnDesc(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m joint_audio_video_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python joint_audio_video_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)

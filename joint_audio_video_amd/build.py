@@ -1,6 +1,8 @@
 """Build libdit.so in-tree with hipcc for gfx950.
 
-Usage: python -m joint_audio_video_amd.build   (or build() from Python)
+Usage: python joint_audio_video_amd/build.py   (or __graft_entry__.build()); run
+as a file, not with -m: the package's __init__ loads the built library and
+refuses to import without it.
 
 Every source under csrc/ is compiled to an object in _build/ and linked into
 joint_audio_video_amd/libdit.so.  The build always recompiles (it is the
