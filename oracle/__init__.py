@@ -28,7 +28,8 @@ stated readings only (the pages fix neither), see ``oracle.layout`` and
 GELU) and width (4 x d_model), see ``oracle.block.gelu_tanh`` and
 ``oracle.block.ffn_forward``.  ``oracle.denoise`` holds the denoising step
 around the block (Rectified Flow X0, Euler with eta = 0, dual schedules,
-anchor re-pinning, H3's timestep and velocity conventions).
+anchor re-pinning, H3's timestep and velocity conventions); ``oracle.nft`` the
+DiffusionNFT loss and its gradient.
 """
 from .layout import (MOD_AUDIO, MOD_TEXT, MOD_VIDEO, SAMPLES_PER_AUDIO_TOKEN,
                      SPATIAL_DOWNSAMPLE, TEMPORAL_DOWNSAMPLE, grid_from_media,
@@ -38,6 +39,7 @@ from .block import (adaln_modulate, attention, attention_probs, block_forward,
                     rope_frequencies)
 from .denoise import (VIDEO_LATENT_CHANNELS, clean_estimate, denoise_loop, denoise_step,
                       euler_step, standard_velocity, timestep_from_sigma)
+from .nft import implicit_policies, nft_loss
 
 __all__ = [
     "MOD_VIDEO", "MOD_AUDIO", "MOD_TEXT", "SAMPLES_PER_AUDIO_TOKEN",
@@ -46,5 +48,5 @@ __all__ = [
     "rope3d", "rope_frequencies", "attention", "attention_probs",
     "out_proj_gated", "block_forward", "gelu_tanh", "ffn_up", "ffn_forward",
     "VIDEO_LATENT_CHANNELS", "timestep_from_sigma", "standard_velocity", "clean_estimate",
-    "euler_step", "denoise_step", "denoise_loop",
+    "euler_step", "denoise_step", "denoise_loop", "implicit_policies", "nft_loss",
 ]

@@ -136,3 +136,34 @@ def denoise_step(z, v, modality, sigmas, anchor=None, anchor_vals=None, velocity
         z_next.append(zr)
         x0.append(xr)
     return z_next, x0
+
+
+def nft_loss(v_theta, v_old, v_target, cu, reward, beta, loss_mask=None, velocity_sign=1.0,
+             grad_scale=None):
+    """Loop version of oracle.nft.nft_loss: (loss, mse_pos, mse_neg, grad) as lists."""
+    n_s = len(cu) - 1
+    scale = 1.0 / n_s if grad_scale is None else grad_scale
+    n, c = len(v_theta), len(v_theta[0])
+    grad = [[0.0] * c for _ in range(n)]
+    loss, mp, mn = [], [], []
+    for s in range(n_s):
+        rows = [i for i in range(cu[s], cu[s + 1]) if loss_mask is None or loss_mask[i]]
+        if not rows:
+            loss.append(0.0), mp.append(0.0), mn.append(0.0)
+            continue
+        cnt = len(rows) * c
+        sp = sn = 0.0
+        for i in rows:
+            for j in range(c):
+                vt = velocity_sign * v_theta[i][j]
+                vo = velocity_sign * v_old[i][j]
+                ep = beta * vt + (1.0 - beta) * vo - v_target[i][j]
+                en = (1.0 + beta) * vo - beta * vt - v_target[i][j]
+                sp += ep * ep
+                sn += en * en
+                g = 2.0 / cnt * (reward[s] * beta * ep - (1.0 - reward[s]) * beta * en)
+                grad[i][j] = scale * velocity_sign * g
+        mp.append(sp / cnt)
+        mn.append(sn / cnt)
+        loss.append(reward[s] * mp[-1] + (1.0 - reward[s]) * mn[-1])
+    return loss, mp, mn, grad
