@@ -12,7 +12,8 @@ stage on the stream the kernels run on.  ``ffn_half`` times the block's
 feed-forward half (d_ff = 4 d_model) on its own; it is not part of ``value``.
 ``denoise_step`` times the denoising step around the block (one streaming
 pass over the packed latent state), at the workload's size and on a 16-pack
-batch large enough to stream from HBM.
+batch large enough to stream from HBM; ``nft_loss`` does the same for the
+DiffusionNFT loss and its gradient (one sample per request).
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
 workload on the host cores.
 """
@@ -145,6 +146,25 @@ def denoise_bytes(mod, anchor, channels, v_elt=2):
                + pin.sum() * 12 * c)
 
 
+def nft_loss_mask(mod, pos, cu, t_last):
+    """Loss-bearing rows of the synthetic recipe: video and audio rows except the first
+    and last video frame of each request (condition frames of a first/last-frame task)."""
+    keep = np.zeros(mod.size, dtype=np.uint8)
+    for (a, b), tl in zip(zip(cu, cu[1:]), t_last):
+        m, p = mod[a:b], pos[a:b]
+        cond = (m == 0) & ((p[:, 0] == 0) | (p[:, 0] == tl))
+        keep[a:b] = ((m != 2) & ~cond).astype(np.uint8)
+    return keep
+
+
+def nft_bytes(keep, channels, v_elt=2):
+    """Algorithmic bytes of one nft_loss with a gradient: every row reads its mask byte
+    and writes its gradient row; loss-bearing rows also read v_theta, v_old (v_elt each)
+    and the float32 target."""
+    c = channels
+    return int(keep.size * (1 + 4 * c) + int((keep != 0).sum()) * (2 * v_elt * c + 4 * c))
+
+
 def cpu_baseline(wl, inp, lay, rows_n: int):
     """Oracle (float64 NumPy) on a bounded sample: every stage for `rows_n` query rows,
     attention of those rows against all keys of their segment (synthetic k, v)."""
@@ -191,6 +211,8 @@ def main() -> int:
                     help="skip timing the feed-forward half (d_ff = 4 d_model)")
     ap.add_argument("--no-denoise", action="store_true",
                     help="skip timing the denoising step around the block")
+    ap.add_argument("--no-nft", action="store_true",
+                    help="skip timing the DiffusionNFT loss")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
@@ -389,6 +411,51 @@ def main() -> int:
             del z_d, v_d, av_d, x0_d, m_d, a_d, di
         print(f"# denoise: {den_rec}", file=sys.stderr, flush=True)
 
+    # The DiffusionNFT loss and its gradient over the same latent rows, one sample per
+    # request, at the pack's size and on 16 packs.
+    nft_rec = None
+    if not args.no_nft:
+        print("# nft loss ...", file=sys.stderr, flush=True)
+        C = DENOISE_CHANNELS
+        mod_h, pos_h = np.asarray(lay["modality"]), np.asarray(lay["pos"])
+        cu_h = lay["cu_seqlens"].tolist()
+        keep_h = nft_loss_mask(mod_h, pos_h, cu_h, [r.t - 1 for r in wl.requests])
+        nft_rec = {"channels": C, "beta": 0.5, "kept_rows": int(keep_h.sum())}
+        for label, packs, reps in (("pack", 1, 50), ("16_packs", 16, 20)):
+            S = (len(cu_h) - 1) * packs
+            ni = synth.nft_inputs(wl, S, C, n_rows=n * packs)
+            k_h = np.tile(keep_h, packs)
+            cu_p = np.concatenate([[0]] + [np.asarray(cu_h[1:]) + i * n for i in range(packs)])
+            vt_d, vo_d = bf(ni.v_theta), bf(ni.v_old)
+            tg_d = torch.from_numpy(ni.v_target).to(dev)
+            g_d = torch.empty_like(tg_d)
+            out_d = torch.empty((S, 3), dtype=torch.float32, device=dev)
+            k_d = torch.from_numpy(k_h).to(dev)
+            cu_d = torch.from_numpy(cu_p.astype(np.int32)).to(dev)
+            r_d = torch.from_numpy(ni.reward).to(dev)
+            max_rows = int(np.max(np.diff(cu_p)))
+            nws = torch.empty(jav.nft_workspace_bytes(S, max_rows), dtype=torch.uint8, device=dev)
+            fn = (lambda vt_d=vt_d, vo_d=vo_d, tg_d=tg_d, cu_d=cu_d, max_rows=max_rows, r_d=r_d,
+                  k_d=k_d, g_d=g_d, out_d=out_d, nws=nws:
+                  jav.nft_loss(vt_d, vo_d, tg_d, cu_d, max_rows, r_d, 0.5, loss_mask=k_d,
+                               grad=g_d, loss_out=out_d, workspace=nws, stream=stream))
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_ms = e0.elapsed_time(e1) / reps
+            b = nft_bytes(k_h, C)
+            nft_rec[label] = {"rows": int(k_h.size), "samples": S, "us": round(t_ms * 1e3, 2),
+                              "bytes": b, "gbs": round(b / (t_ms * 1e-3) / 1e9, 1),
+                              "frac_of_hbm": round(b / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del vt_d, vo_d, tg_d, g_d, out_d, k_d, cu_d, r_d, nws, ni
+        print(f"# nft: {nft_rec}", file=sys.stderr, flush=True)
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -450,6 +517,8 @@ def main() -> int:
         rec["ffn_half"] = ffn_rec
     if den_rec is not None:
         rec["denoise_step"] = den_rec
+    if nft_rec is not None:
+        rec["nft_loss"] = nft_rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle

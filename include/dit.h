@@ -312,6 +312,50 @@ dit_status denoise_step(dit_dtype v_dtype, float* z, int64_t ld_z, const void* v
                         int32_t velocity_sign, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The DiffusionNFT loss on the block's velocity output                       */
+/* ------------------------------------------------------------------------ */
+
+/* [VeRL-Omni] section 4 (DiffusionNFT with a scalar optimality reward): the
+ * current policy's velocity v_theta and the frozen old adapter's v_old define
+ * v_pos = beta v_theta + (1 - beta) v_old and v_neg = (1 + beta) v_old -
+ * beta v_theta; a sample with reward r in [0, 1] has the loss
+ * L = r MSE(v_pos, v_target) + (1 - r) MSE(v_neg, v_target).  [H3-NFT]
+ * section "FL2VA: First-Frame Conditioning With Shared Infrastructure":
+ * condition-frame latents are masked out of the loss.  [VeRL-Omni] section
+ * 5.1: H3's velocity is sign-reversed (velocity_sign = -1 converts it).
+ *
+ * nft_loss: samples are row ranges [cu_samples[s], cu_samples[s+1]) of a
+ * packed batch (device int32 [n_samples + 1], the cu_seqlens contract, every
+ * range at most max_rows long).  For each sample, MSE is the mean over the
+ * rows whose loss_mask flag is non-zero (all rows when loss_mask is NULL),
+ * every one of their `channels` columns.  loss_out (device float32
+ * [n_samples][3]) receives (L_s, MSE(v_pos), MSE(v_neg)); a sample with no
+ * loss-bearing row gets zeros.  grad (device float32 [n_rows][ld_g], or NULL
+ * for the loss alone) receives d(grad_scale * sum_s L_s)/d v_theta for every
+ * row of every sample (zero on masked rows), with respect to the raw output
+ * (so it carries velocity_sign); grad_scale = 1/n_samples is the mean over
+ * samples.  v_theta, v_old: [n_rows][ld] of v_dtype (bf16 or f32); v_target:
+ * float32 [n_rows][ld_t] in the standard convention (eps - x0); reward:
+ * device float32 [n_samples]; beta, grad_scale: host.  grad must not overlap
+ * the inputs.  Accumulation: per 32-row chunk in float32, across chunks in
+ * float64, in a fixed order (deterministic, no atomics).
+ * workspace: device, at least dit_nft_workspace_bytes(n_samples, max_rows)
+ * bytes, 256-byte aligned.  Three launches on stream; with n_rows == 0 they
+ * still write zero losses (the outputs are per sample).
+ * Errors: DIT_EINVAL for a null required pointer, n_samples < 1, max_rows < 1
+ * with n_rows > 0, channels < 1, an ld below channels, non-finite beta or
+ * grad_scale, velocity_sign not +-1, an unknown dtype; DIT_EUNSUPPORTED when
+ * channels is not a multiple of 4, n_samples > 65535, or a pointer or ld
+ * breaks the 16-byte rule; DIT_EWORKSPACE; DIT_EHIP on a launch failure. */
+size_t dit_nft_workspace_bytes(int32_t n_samples, int32_t max_rows);
+dit_status nft_loss(dit_dtype v_dtype, const void* v_theta, int64_t ld_vt, const void* v_old,
+                    int64_t ld_vo, const float* v_target, int64_t ld_t, const uint8_t* loss_mask,
+                    const int32_t* cu_samples, int32_t n_samples, int32_t max_rows,
+                    int64_t n_rows, int32_t channels, const float* reward, float beta,
+                    int32_t velocity_sign, float grad_scale, float* grad, int64_t ld_g,
+                    float* loss_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* The whole attention half of the block                                      */
 /* ------------------------------------------------------------------------ */
 

@@ -32,7 +32,7 @@ EXPORTED = (
     "adaln_modulate", "rope3d_apply", "attn_packed", "qkv_project", "out_proj_gated",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
     "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
-    "denoise_step",
+    "denoise_step", "dit_nft_workspace_bytes", "nft_loss",
 )
 
 
@@ -97,6 +97,9 @@ def _load() -> ctypes.CDLL:
                                            P, SZ, P]),
         "denoise_step": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, P, P, I64, I64,
                                         I32, ctypes.POINTER(F32), I32, P]),
+        "dit_nft_workspace_bytes": (SZ, [I32, I32]),
+        "nft_loss": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, P, I32, I32, I64, I32,
+                                    P, F32, I32, F32, P, I64, P, P, SZ, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -388,3 +391,41 @@ def denoise_step(z, v, modality, sigmas: Sequence[float], x0=None, anchor=None,
                              _ptr(anchor), pa, lda, n, c, sig, int(velocity_sign),
                              _stream(stream)))
     return z
+
+
+# ---------------------------------------------------------------------------
+# DiffusionNFT loss
+# ---------------------------------------------------------------------------
+
+def nft_workspace_bytes(n_samples: int, max_rows: int) -> int:
+    return int(_lib.dit_nft_workspace_bytes(int(n_samples), int(max_rows)))
+
+
+def nft_loss(v_theta, v_old, v_target, cu_samples, max_rows: int, reward, beta: float,
+             loss_mask=None, velocity_sign: int = 1, grad_scale=None, grad=None,
+             loss_out=None, workspace=None, want_grad: bool = True, n_rows=None, stream=None):
+    """DiffusionNFT loss per sample and its gradient (libdit nft_loss).
+
+    Returns (loss_out [S][3] = (loss, mse_pos, mse_neg), grad or None)."""
+    torch = _torch()
+    n_s = cu_samples.numel() - 1
+    n = v_theta.shape[0] if n_rows is None else int(n_rows)
+    c = v_theta.shape[1]
+    dev = v_theta.device
+    if loss_out is None:
+        loss_out = torch.empty((n_s, 3), dtype=torch.float32, device=dev)
+    if grad is None and want_grad:
+        grad = torch.empty((v_theta.shape[0], c), dtype=torch.float32, device=dev)
+    need = nft_workspace_bytes(n_s, max(int(max_rows), 1))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    pt, ldt = _rows(v_theta)
+    po, ldo = _rows(v_old)
+    pg, ldg = (0, 0) if grad is None else _rows(grad)
+    ptg, ldtg = _rows(v_target)
+    scale = 1.0 / n_s if grad_scale is None else float(grad_scale)
+    _check(_lib.nft_loss(_dtype_code(v_theta), pt, ldt, po, ldo, ptg, ldtg, _ptr(loss_mask),
+                         cu_samples.data_ptr(), n_s, int(max_rows), n, c, reward.data_ptr(),
+                         float(beta), int(velocity_sign), scale, pg, ldg, loss_out.data_ptr(),
+                         workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return loss_out, grad

@@ -369,6 +369,57 @@ extern "C" dit_status denoise_step(dit_dtype v_dtype, float* z, int64_t ld_z, co
 }
 
 // ---------------------------------------------------------------------------
+// DiffusionNFT loss
+
+extern "C" size_t dit_nft_workspace_bytes(int32_t n_samples, int32_t max_rows) {
+  if (n_samples < 1 || max_rows < 1) return 0;
+  return nft_workspace_layout(n_samples, max_rows, nullptr);
+}
+
+extern "C" dit_status nft_loss(dit_dtype v_dtype, const void* v_theta, int64_t ld_vt,
+                               const void* v_old, int64_t ld_vo, const float* v_target,
+                               int64_t ld_t, const uint8_t* loss_mask, const int32_t* cu_samples,
+                               int32_t n_samples, int32_t max_rows, int64_t n_rows,
+                               int32_t channels, const float* reward, float beta,
+                               int32_t velocity_sign, float grad_scale, float* grad, int64_t ld_g,
+                               float* loss_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  clear_error();
+  const dit_dtype dt = v_dtype;
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "nft_loss: unknown dtype %d", (int)dt);
+  if (!v_theta || !v_old || !v_target || !cu_samples || !reward || !loss_out)
+    return fail(DIT_EINVAL, "nft_loss: null pointer");
+  if (n_samples < 1) return fail(DIT_EINVAL, "nft_loss: n_samples < 1");
+  if (dit_status st = check_stream_rows(n_rows)) return st;
+  if (n_rows > 0 && max_rows < 1) return fail(DIT_EINVAL, "nft_loss: max_rows < 1");
+  if (channels < 1) return fail(DIT_EINVAL, "nft_loss: channels < 1");
+  if (ld_vt < channels || ld_vo < channels || ld_t < channels || (grad && ld_g < channels))
+    return fail(DIT_EINVAL, "nft_loss: ld < channels");
+  if (!std::isfinite(beta) || !std::isfinite(grad_scale))
+    return fail(DIT_EINVAL, "nft_loss: beta and grad_scale must be finite");
+  if (velocity_sign != 1 && velocity_sign != -1)
+    return fail(DIT_EINVAL, "nft_loss: velocity_sign %d is not +1 or -1", velocity_sign);
+  if (channels % 4 != 0)
+    return fail(DIT_EUNSUPPORTED, "nft_loss: channels %d is not a multiple of 4", channels);
+  if (n_samples > 65535) return fail(DIT_EUNSUPPORTED, "nft_loss: more than 65535 samples");
+  if (!aligned16(v_theta) || !aligned16(v_old) || !aligned16(v_target) ||
+      (grad && !aligned16(grad)) || !ld_aligned(dt, ld_vt) || !ld_aligned(dt, ld_vo) ||
+      !ld_aligned(DIT_F32, ld_t) || (grad && !ld_aligned(DIT_F32, ld_g)))
+    return fail(DIT_EUNSUPPORTED, "nft_loss: pointers/ld must be 16-byte aligned");
+  if (n_rows == 0) max_rows = std::max(max_rows, 1);
+  const size_t need = dit_nft_workspace_bytes(n_samples, max_rows);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "nft_loss: workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "nft_loss: workspace must be 256-byte aligned");
+  hipError_t e = launch_nft_loss(dt == DIT_BF16, v_theta, ld_vt, v_old, ld_vo, v_target, ld_t,
+                                 loss_mask, cu_samples, n_samples, max_rows, channels, reward,
+                                 beta, (float)velocity_sign, grad_scale, grad, ld_g, loss_out,
+                                 workspace, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "nft_loss launch");
+}
+
+// ---------------------------------------------------------------------------
 
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 

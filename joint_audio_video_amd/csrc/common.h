@@ -102,6 +102,17 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
                        int64_t ldc, int64_t m, int n, int k, const GemmEpilogue& ep,
                        hipStream_t s);
 
+// Workspace of launch_nft_loss: a loss-bearing row count per sample (int32)
+// and two squared-error sums (float) per (sample, 32-row chunk), each region
+// 256-byte aligned.
+size_t nft_workspace_layout(int n_samples, int max_rows, size_t* partials_offset);
+hipError_t launch_nft_loss(int bf16, const void* v_theta, int64_t ld_vt, const void* v_old,
+                           int64_t ld_vo, const float* v_target, int64_t ld_t,
+                           const uint8_t* mask, const int32_t* cu, int n_samples, int max_rows,
+                           int channels, const float* reward, float beta, float sign,
+                           float scale, float* grad, int64_t ld_g, float* loss_out,
+                           void* workspace, hipStream_t s);
+
 // sigmas: host {video, video_next, audio, audio_next}; sign +1 or -1.
 hipError_t launch_denoise(int bf16, float* z, int64_t ld_z, const void* v, int64_t ld_v,
                           float* x0, int64_t ld_x0, const uint8_t* mod, const uint8_t* anchor,

@@ -279,3 +279,30 @@ def sigma_schedule(n_steps: int, power: float = 1.0) -> np.ndarray:
     in float32 (the pages give no sigma values)."""
     i = np.arange(n_steps + 1, dtype=np.float64)
     return ((1.0 - i / n_steps) ** power).astype(np.float32)
+
+
+@dataclasses.dataclass
+class NftInputs:
+    """Float32 host arrays for the DiffusionNFT loss over a packed batch."""
+    v_theta: np.ndarray     # [N][C] current policy's velocity: v_old + N(0, 0.05^2)
+    v_old: np.ndarray       # [N][C] frozen adapter's velocity, N(0, 1)
+    v_target: np.ndarray    # [N][C] eps - x0 with eps, x0 ~ N(0, 1)
+    reward: np.ndarray      # [S] uniform in [0, 1)
+
+
+def nft_inputs(wl: Workload, n_samples: int, channels: int = 96, n_rows: Optional[int] = None,
+               seed: Optional[int] = None) -> NftInputs:
+    """Draw v_old, the policy's drift, eps, x0 and the rewards in that order from
+    PCG64(seed) (default wl.seed + 3000).  Velocities are bf16-exact for bf16 workloads
+    (network outputs); the target stays float32."""
+    n = wl.n_tokens if n_rows is None else n_rows
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 3000 if seed is None else seed))
+    v_old = _normal(rng, (n, channels), 1.0)
+    drift = _normal(rng, (n, channels), 0.05)
+    eps = _normal(rng, (n, channels), 1.0)
+    x0 = _normal(rng, (n, channels), 1.0)
+    reward = rng.random(n_samples, dtype=np.float32)
+    v_theta = v_old + drift
+    if wl.dtype == BF16:
+        v_old, v_theta = round_to_bf16(v_old), round_to_bf16(v_theta)
+    return NftInputs(v_theta, v_old, (eps - x0).astype(np.float32), reward)

@@ -212,3 +212,38 @@ def test_denoise_step_validates_before_enqueue():
     assert call(n=0) == jav.DIT_OK                                        # no rows: no-op
     assert call(x0=None, ldx=0, n=0) == jav.DIT_OK
     assert jav.timestep_from_sigma(1.0) == 0.0 and jav.timestep_from_sigma(0.0) == 1.0
+
+
+def test_nft_loss_validates_before_enqueue():
+    fake = 1 << 20            # never dereferenced: validation fails first
+    B = jav.DIT_BF16
+    # 4 int32 row counts (16 -> 256 B) + 460 chunks of 32 rows x 4 samples x 2 floats
+    # (14,720 -> 14,848 B)
+    assert jav.nft_workspace_bytes(4, 14690) == 256 + 14848
+    assert jav.nft_workspace_bytes(0, 10) == 0 and jav.nft_workspace_bytes(2, 0) == 0
+
+    def call(dt=B, vt=fake, ldvt=96, vo=fake, ldvo=96, tg=fake, ldt=96, mask=None, cu=fake,
+             ns=4, mr=14690, n=58758, c=96, rew=fake, beta=0.5, sign=1, scale=0.25, g=fake,
+             ldg=96, out=fake, ws=fake, wsb=1 << 30):
+        return _call("nft_loss", dt, vt, ldvt, vo, ldvo, tg, ldt, mask, cu, ns, mr, n, c, rew,
+                     beta, sign, scale, g, ldg, out, ws, wsb, None)
+
+    assert call(dt=3) == jav.DIT_EINVAL
+    assert call(vt=None) == jav.DIT_EINVAL
+    assert call(out=None) == jav.DIT_EINVAL
+    assert call(rew=None) == jav.DIT_EINVAL
+    assert call(ns=0) == jav.DIT_EINVAL
+    assert call(mr=0) == jav.DIT_EINVAL
+    assert call(c=0) == jav.DIT_EINVAL
+    assert call(ldt=64) == jav.DIT_EINVAL
+    assert call(beta=float("inf")) == jav.DIT_EINVAL
+    assert call(scale=float("nan")) == jav.DIT_EINVAL
+    assert call(sign=2) == jav.DIT_EINVAL
+    assert call(c=94, ldvt=96, ldvo=96, ldt=96, ldg=96) == jav.DIT_EUNSUPPORTED
+    assert call(ns=70000) == jav.DIT_EUNSUPPORTED
+    assert call(vo=fake + 4) == jav.DIT_EUNSUPPORTED
+    assert call(ldvt=100) == jav.DIT_EUNSUPPORTED        # bf16 rows of 200 B
+    assert call(wsb=16) == jav.DIT_EWORKSPACE
+    assert call(ws=None) == jav.DIT_EWORKSPACE
+    assert call(ws=fake + 64) == jav.DIT_EUNSUPPORTED
+    assert "nft_loss" in jav.last_error()
