@@ -67,23 +67,36 @@ def recorded_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def _short_kernel(name: str) -> str:
+    short = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", short)
+
+
 def summarize_profile(kind: str, out_dir: str) -> int:
-    """Print a markdown summary of rocprofv3 CSV output (committed under profiles/)."""
+    """Print a markdown summary of rocprofv3 CSV output (committed under profiles/).
+
+    Kernels are grouped by name and grid size, so launches of one kernel at
+    different sizes (and the calibration copy) are reported apart."""
     if kind == "stats":
-        files = glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True)
+        files = glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True)
         if not files:
-            print(f"no kernel_stats.csv under {out_dir}", file=sys.stderr)
+            print(f"no kernel_trace.csv under {out_dir}", file=sys.stderr)
             return 1
-        rows = list(csv.DictReader(open(files[0])))
-        print("| kernel | calls | avg ms | min ms | max ms | total % |")
-        print("|---|---|---|---|---|---|")
-        for r in rows:
-            name = r["Name"]
-            short = name.replace("(anonymous namespace)::", "").replace("void ", "")
-            short = re.sub(r"\(.*", "", short)
-            print(f"| {short[:60]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
-                  f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | "
-                  f"{float(r['Percentage']):.2f} |")
+        per = {}
+        for r in csv.DictReader(open(files[0])):
+            name = r["Kernel_Name"]
+            if "dit::" not in name and "copyBuffer" not in name:
+                continue
+            key = (_short_kernel(name), int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+                   * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+            per.setdefault(key, []).append(dur)
+        total = sum(sum(v) for v in per.values())
+        print("| kernel | grid (work-items) | calls | avg ms | min ms | max ms | total % |")
+        print("|---|---|---|---|---|---|---|")
+        for (k, grid), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            print(f"| {k[:60]} | {grid} | {len(v)} | {sum(v) / len(v):.4f} | {min(v):.4f} | "
+                  f"{max(v):.4f} | {100 * sum(v) / total:.2f} |")
         return 0
     files = glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -92,17 +105,16 @@ def summarize_profile(kind: str, out_dir: str) -> int:
     per = {}
     for r in csv.DictReader(open(files[0])):
         name = r["Kernel_Name"]
-        if "dit::" in name:
-            key = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("void ", ""))
-        elif "copy" in name.lower():
-            key = "copy"
-        else:
+        if "dit::" not in name and "copyBuffer" not in name:
             continue
+        key = f"{_short_kernel(name)} [grid {r['Grid_Size']}]"
         per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     print("| kernel | counter | dispatches | mean per dispatch |")
     print("|---|---|---|---|")
     for (k, c), vals in sorted(per.items()):
-        print(f"| {k[:60]} | {c} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
+        if "copyBuffer" in k and max(vals) < 1024:
+            continue   # small runtime copies
+        print(f"| {k[:72]} | {c} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
     return 0
 
 
