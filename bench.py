@@ -315,11 +315,15 @@ def main() -> int:
     for i in range(3):
         planes[i].copy_(qkv[:, i * d:(i + 1) * d])
     q_v, k_v, v_v = planes[0], planes[1], planes[2]
+    spare = torch.empty_like(x)
     iso_ops = {
         "adaln": (20, lambda: jav.adaln_modulate(x, mod, table, wl.eps, out=y, stream=stream)),
         "qkv": (5, lambda: jav.qkv_project(y, w_qkv, out=qkv, stream=stream)),
         "rope": (20, lambda: jav.rope3d_apply(q_v, k_v, pos, H, Dh, wl.sections, wl.theta,
                                               stream=stream)),
+        # the block's form: rotated q into a spare plane, rotated k over q's plane
+        "rope_to": (20, lambda: jav.rope3d_apply_to(q_v, k_v, spare, q_v, pos, H, Dh,
+                                                    wl.sections, wl.theta, stream=stream)),
         "attn": (3, lambda: jav.attn_packed(q_v, k_v, v_v, cu, ms_len, H, Dh,
                                             causal=args.causal, out=o, stream=stream)),
         "out": (5, lambda: jav.out_proj_gated(o, w_o, x, mod, table, out=out, stream=stream)),
@@ -336,7 +340,7 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         iso_ms[name] = e0.elapsed_time(e1) / reps
-    del y, qkv, planes, o, q_v, k_v, v_v
+    del y, qkv, planes, spare, o, q_v, k_v, v_v
     print(f"# isolated: {iso_ms}", file=sys.stderr, flush=True)
 
     # The feed-forward half of the same block (d_ff = 4 d_model), timed on its own:
@@ -514,6 +518,9 @@ def main() -> int:
             "adaln_frac_of_hbm": round(adaln_b / (iso_ms["adaln"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "rope_gbs": round(rope_b / (iso_ms["rope"] * 1e-3) / 1e9, 1),
             "rope_frac_of_hbm": round(rope_b / (iso_ms["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "rope_to_gbs": round(rope_b / (iso_ms["rope_to"] * 1e-3) / 1e9, 1),
+            "rope_to_frac_of_hbm": round(rope_b / (iso_ms["rope_to"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                         4),
         },
         "roofline": {
             "kernel": "attn_bf16_kernel",

@@ -168,6 +168,20 @@ dit_status rope3d_apply(dit_dtype dt, void* q, int64_t ld_q, void* k, int64_t ld
                         int32_t head_dim, const int32_t sections[3], float theta,
                         void* stream);
 
+/* rope3d_apply_to: the same rotation written to separate outputs: q_out gets
+ * the rotated q and k_out the rotated k (k and k_out both NULL: q only).
+ * Out of place, each line is read once and written once elsewhere, with no
+ * read-modify-write of the same lines.  An output may be its own input (in
+ * place) or the other input with the same pointer and ld (k_out = q: each
+ * vector is read before it is overwritten); any other overlap between an
+ * output and an input, or between the outputs, is DIT_EINVAL.  Errors as
+ * rope3d_apply, plus DIT_EINVAL for a missing output or an output ld below
+ * n_heads * head_dim. */
+dit_status rope3d_apply_to(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                           int64_t ld_k, void* q_out, int64_t ld_qo, void* k_out, int64_t ld_ko,
+                           const int32_t* pos_thw, int64_t n_tokens, int32_t n_heads,
+                           int32_t head_dim, const int32_t sections[3], float theta, void* stream);
+
 /* Softmax attention over a packed sequence ([vLLM-Omni] section 3: the
  * kernel derives its mask from cu_seqlens, so a token attends only to keys of
  * its own segment; section 1: audio and video share one attention context;

@@ -32,7 +32,7 @@ EXPORTED = (
     "adaln_modulate", "rope3d_apply", "attn_packed", "qkv_project", "out_proj_gated",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
     "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
-    "denoise_step", "dit_nft_workspace_bytes", "nft_loss",
+    "denoise_step", "dit_nft_workspace_bytes", "nft_loss", "rope3d_apply_to",
 )
 
 
@@ -81,6 +81,8 @@ def _load() -> ctypes.CDLL:
         "adaln_modulate": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, F32, P]),
         "rope3d_apply": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, I32, I32,
                                         ctypes.POINTER(I32), F32, P]),
+        "rope3d_apply_to": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P, I64,
+                                           I32, I32, ctypes.POINTER(I32), F32, P]),
         "attn_packed": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P, I32, I32,
                                        I64, I32, I32, F32, I32, P]),
         "qkv_project": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, P]),
@@ -216,6 +218,20 @@ def rope3d_apply(q, k, pos, n_heads: int, head_dim: int, sections: Sequence[int]
     sec = (ctypes.c_int32 * 3)(*[int(s) for s in sections])
     _check(_lib.rope3d_apply(_dtype_code(q), pq, ldq, pk, ldk, pos.data_ptr(), n, n_heads,
                              head_dim, sec, float(theta), _stream(stream)))
+
+
+def rope3d_apply_to(q, k, q_out, k_out, pos, n_heads: int, head_dim: int,
+                    sections: Sequence[int], theta: float = 10000.0, n_tokens=None, stream=None):
+    """Rotate q into q_out and k into k_out (libdit rope3d_apply_to)."""
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    pq, ldq = _rows(q)
+    pqo, ldqo = _rows(q_out)
+    pk, ldk = (0, 0) if k is None else _rows(k)
+    pko, ldko = (0, 0) if k_out is None else _rows(k_out)
+    sec = (ctypes.c_int32 * 3)(*[int(s) for s in sections])
+    _check(_lib.rope3d_apply_to(_dtype_code(q), pq, ldq, pk, ldk, pqo, ldqo, pko, ldko,
+                                pos.data_ptr(), n, n_heads, head_dim, sec, float(theta),
+                                _stream(stream)))
 
 
 def attn_packed(q, k, v, cu_seqlens, max_seqlen: int, n_heads: int, head_dim: int,

@@ -149,9 +149,62 @@ extern "C" dit_status rope3d_apply(dit_dtype dt, void* q, int64_t ld_q, void* k,
   if (n_tokens == 0) return DIT_OK;
   double freq[64];
   rope_freqs(sections, (double)theta, head_dim, freq);
-  hipError_t e = launch_rope(dt == DIT_BF16, q, ld_q, k, ld_k, pos_thw, n_tokens, n_heads,
-                             head_dim, sections[0], sections[1], freq, (hipStream_t)stream);
+  hipError_t e = launch_rope(dt == DIT_BF16, q, ld_q, k, ld_k, q, ld_q, k, ld_k, pos_thw,
+                             n_tokens, n_heads, head_dim, sections[0], sections[1], freq,
+                             (hipStream_t)stream);
   return e == hipSuccess ? DIT_OK : hip_fail(e, "rope3d_apply launch");
+}
+
+// Rows [p, p + n*ld) and [o, o + n*ld_o) in bytes overlap only if the spans do.
+static bool spans_overlap(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t n,
+                          int64_t width, size_t es) {
+  if (!a || !b || n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, a1 = a0 + ((n - 1) * lda + width) * es;
+  const uintptr_t b0 = (uintptr_t)b, b1 = b0 + ((n - 1) * ldb + width) * es;
+  return a0 < b1 && b0 < a1;
+}
+
+extern "C" dit_status rope3d_apply_to(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                                      int64_t ld_k, void* q_out, int64_t ld_qo, void* k_out,
+                                      int64_t ld_ko, const int32_t* pos_thw, int64_t n_tokens,
+                                      int32_t n_heads, int32_t head_dim,
+                                      const int32_t sections[3], float theta, void* stream) {
+  clear_error();
+  if (dit_status st = rope_check(dt, const_cast<void*>(q), ld_q, const_cast<void*>(k), ld_k,
+                                 pos_thw, n_tokens, n_heads, head_dim, sections, theta))
+    return st;
+  if (!q_out || (k && !k_out) || (!k && k_out))
+    return fail(DIT_EINVAL, "rope3d_apply_to: an output is missing (or k_out without k)");
+  const int64_t width = (int64_t)n_heads * head_dim;
+  if (ld_qo < width || (k_out && ld_ko < width))
+    return fail(DIT_EINVAL, "rope3d_apply_to: output ld too small");
+  if (!aligned16(q_out) || !ld_aligned(dt, ld_qo) ||
+      (k_out && (!aligned16(k_out) || !ld_aligned(dt, ld_ko))))
+    return fail(DIT_EUNSUPPORTED, "rope3d_apply_to: pointers/ld must be 16-byte aligned");
+  // An output may be its own input or the other input with the same rows and
+  // ld; any other overlap is refused.
+  const size_t es = elt_size(dt);
+  auto same = [](const void* a, int64_t la, const void* b, int64_t lb) {
+    return a == b && la == lb;
+  };
+  const void* ins[2] = {q, k};
+  const int64_t ins_ld[2] = {ld_q, ld_k};
+  void* outs[2] = {q_out, k_out};
+  const int64_t outs_ld[2] = {ld_qo, ld_ko};
+  for (int o = 0; o < 2; ++o)
+    for (int i = 0; i < 2; ++i)
+      if (outs[o] && ins[i] && !same(outs[o], outs_ld[o], ins[i], ins_ld[i]) &&
+          spans_overlap(outs[o], outs_ld[o], ins[i], ins_ld[i], n_tokens, width, es))
+        return fail(DIT_EINVAL, "rope3d_apply_to: an output partly overlaps an input");
+  if (k_out && spans_overlap(q_out, ld_qo, k_out, ld_ko, n_tokens, width, es))
+    return fail(DIT_EINVAL, "rope3d_apply_to: the outputs overlap");
+  if (n_tokens == 0) return DIT_OK;
+  double freq[64];
+  rope_freqs(sections, (double)theta, head_dim, freq);
+  hipError_t e = launch_rope(dt == DIT_BF16, q, ld_q, k, ld_k, q_out, ld_qo, k_out, ld_ko,
+                             pos_thw, n_tokens, n_heads, head_dim, sections[0], sections[1],
+                             freq, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "rope3d_apply_to launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -531,7 +584,13 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   if (dit_status st = rope_check(dt, q, D, k, D, pos_thw, n_tokens, H, Dh, d->rope_sections,
                                  d->rope_theta))
     return st;
-  if (dit_status st = attn_check(dt, q, D, k, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
+  // RoPE writes the rotated q into the y plane (dead after the QKV GEMM) and
+  // the rotated k over q's plane (each vector is read before it is
+  // overwritten): an out-of-place pass with no extra memory.  Attention then
+  // reads q' = y, k' = q's plane, v.
+  void* qr = y;
+  void* kr = q;
+  if (dit_status st = attn_check(dt, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
                                  n_tokens, H, Dh, d->softmax_scale))
     return st;
   if (dit_status st = proj_check("out_proj_gated", dt, o, D, w_o, out, D, n_tokens, D, D))
@@ -557,12 +616,12 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   mark(2);
   double freq[64];
   rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
-  e = launch_rope(dt == DIT_BF16, q, D, k, D, pos_thw, n_tokens, H, Dh, d->rope_sections[0],
-                  d->rope_sections[1], freq, s);
+  e = launch_rope(dt == DIT_BF16, q, D, k, D, qr, D, kr, D, pos_thw, n_tokens, H, Dh,
+                  d->rope_sections[0], d->rope_sections[1], freq, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope launch");
   mark(3);
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
-  e = launch_attn(dt == DIT_BF16, q, D, k, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
+  e = launch_attn(dt == DIT_BF16, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
                   n_tokens, H, Dh, scale, d->causal != 0, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: attention launch");
   mark(4);

@@ -74,7 +74,11 @@ hipError_t launch_adaln(int bf16, const void* x, int64_t ld_x, const uint8_t* mo
                         float eps, hipStream_t s);
 
 // freq_d: host array of head_dim/2 pair frequencies theta^(-2j/s_axis), in double.
-hipError_t launch_rope(int bf16, void* q, int64_t ld_q, void* k, int64_t ld_k,
+// Rotates q into q_out and k into k_out (k, k_out null: q only); in place when
+// the outputs are the inputs; k_out may be q (each vector is loaded before the
+// same thread stores over it).
+hipError_t launch_rope(int bf16, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                       void* q_out, int64_t ld_qo, void* k_out, int64_t ld_ko,
                        const int32_t* pos, int64_t n, int n_heads, int head_dim,
                        int s_t, int s_h, const double* freq_d, hipStream_t s);
 

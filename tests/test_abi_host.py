@@ -247,3 +247,26 @@ def test_nft_loss_validates_before_enqueue():
     assert call(ws=None) == jav.DIT_EWORKSPACE
     assert call(ws=fake + 64) == jav.DIT_EUNSUPPORTED
     assert "nft_loss" in jav.last_error()
+
+
+def test_rope3d_apply_to_overlap_rules():
+    fake = 1 << 24            # never dereferenced: validation fails first
+    sec = (ctypes.c_int32 * 3)(32, 48, 48)
+    B, n, w = jav.DIT_BF16, 10, 5120
+    row = w * 2
+
+    def call(q, k, qo, ko, ldq=w, ldk=w, ldqo=w, ldko=w, n=n):
+        return _call("rope3d_apply_to", B, q, ldq, k, ldk, qo, ldqo, ko, ldko, fake, n, 40, 128,
+                     sec, 1e4, None)
+
+    q, k = fake, fake + 64 * row
+    assert call(q, k, None, fake + 128 * row) == jav.DIT_EINVAL          # missing output
+    assert call(q, None, fake + 128 * row, fake + 160 * row) == jav.DIT_EINVAL   # k_out without k
+    assert call(q, k, fake + 128 * row, fake + 160 * row, ldko=4000) == jav.DIT_EINVAL
+    assert call(q, k, q + 4 * row, fake + 160 * row) == jav.DIT_EINVAL   # output shifted into q
+    assert call(q, k, fake + 128 * row, fake + 133 * row) == jav.DIT_EINVAL   # outputs overlap
+    assert call(q, k, fake + 128 * row, fake + 160 * row + 8) == jav.DIT_EUNSUPPORTED
+    # allowed: separate outputs, in place, and k_out = q (the block's arrangement)
+    assert call(q, k, fake + 128 * row, fake + 160 * row, n=0) == jav.DIT_OK
+    assert call(q, k, q, k, n=0) == jav.DIT_OK
+    assert call(q, k, fake + 128 * row, q, n=0) == jav.DIT_OK

@@ -141,6 +141,42 @@ def test_rope_parity_on_fused_qkv(jav, name):
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
+@pytest.mark.parametrize("name", ["tiny", "small", "full"])
+def test_rope_apply_to_out_of_place_and_crossed(jav, name):
+    """rope3d_apply_to: separate outputs (inputs untouched), and the block's own
+    arrangement, rotated q into a spare plane and rotated k over q's plane, with the
+    same bits as the in-place entry point."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    d, H, Dh = wl.d_model, wl.n_heads, wl.head_dim
+    lay = _layout(name)
+    _, pos_d, _, _ = _dev_layout(jav, name)
+    n = wl.n_tokens
+    print(f"rope_to {name} N={n}", flush=True)
+    qh = synth.normal_array((n, d), seed=120 + wl.seed, dtype=wl.dtype)
+    kh = synth.normal_array((n, d), seed=121 + wl.seed, dtype=wl.dtype)
+    q, k = dev(qh, wl.dtype), dev(kh, wl.dtype)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    jav.rope3d_apply_to(q, k, qo, ko, pos_d, H, Dh, wl.sections, wl.theta)
+    _sync()
+    assert torch.equal(q, dev(qh, wl.dtype)) and torch.equal(k, dev(kh, wl.dtype))
+    rows = None if n < 20000 else sample_rows(lay["cu_seqlens"], n, limit=3000)
+    for which, src, out in (("q", qh, qo), ("k", kh, ko)):
+        ref = oracle.rope3d(src, lay["pos"], H, Dh, wl.sections, wl.theta, rows=rows)
+        got = host(out) if rows is None else host(out[torch.from_numpy(rows).cuda()])
+        check(got, ref, wl.dtype, f"rope_to[{name}].{which}")
+    # in place, for the bit comparison
+    qi, ki = q.clone(), k.clone()
+    jav.rope3d_apply(qi, ki, pos_d, H, Dh, wl.sections, wl.theta)
+    # the block's arrangement: q -> spare plane, k -> over q's plane
+    spare = torch.empty_like(q)
+    q2, k2 = q.clone(), k.clone()
+    jav.rope3d_apply_to(q2, k2, spare, q2, pos_d, H, Dh, wl.sections, wl.theta)
+    _sync()
+    assert torch.equal(qo, qi) and torch.equal(ko, ki)
+    assert torch.equal(spare, qi) and torch.equal(q2, ki) and torch.equal(k2, k)
+
+
 def test_rope_wide_rows_in_chunks(jav):
     """56 heads x 128 (896 vectors per row): rows wider than one pass of the
     kernel, walked in chunks; 37 tokens (not a multiple of the 4 per
