@@ -16,7 +16,9 @@
 namespace dit {
 namespace {
 
-constexpr int kWaves = 4;   // rows per workgroup
+// Waves per workgroup: measured best of 1, 2, 4, 8 (2 rows per wave at d_model
+// 5120: 205.5 us = 73.2% of 8 TB/s against 208.8 us for 4 waves).
+constexpr int kWaves = 2;
 
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int N = 8; };   // bf16 bits

@@ -1,0 +1,116 @@
+"""FP8 (e4m3, OCP "fn" variant) quantization and FP8 projections in float64.
+
+Test infrastructure only (see the package docstring).
+
+[vLLM-Omni] section 5 ("Distributed Layerwise Offload") runs the active DiT
+layers in FP8; the pages give no scaling recipe.  Readings:
+
+* Format: e4m3 with 1 sign, 4 exponent (bias 7) and 3 mantissa bits,
+  subnormals, no infinities, codes 0x7F / 0xFF for NaN, largest finite 448.
+* Rounding: to the nearest representable value, ties to the even code
+  (mantissa LSB 0); finite values beyond +-448 saturate to +-448 (beyond the
+  rounding midpoint 464 the e4m3fn format has no code, so a saturating
+  conversion is the plainest choice for a quantizer).
+* Scaling: one float32 scale per row (per token for activations, per output
+  channel for weights), scale = amax(|row|) / 448 computed in float32; a zero
+  row has scale 1.  Codes are e4m3(fp32(x) / scale) with an IEEE float32
+  division, the precision in which the GPU takes the same decision.
+* A projection C = (dequant(A) dequant(B)^T) with dequant(q) = decode(q) *
+  scale of its row, evaluated here in float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_NAN = 0x7F
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of one e4m3fn code, from the format definition."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+def e4m3_table() -> np.ndarray:
+    """float64 [256]: the value of every code (NaN for the two NaN codes)."""
+    return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+_POS = e4m3_table()[:0x7F]          # codes 0x00..0x7E: 0 and the positive finite values
+
+
+def _apply_sign(v, code: int) -> int:
+    return code | 0x80 if (v < 0 or (v == 0 and np.signbit(v))) else code
+
+
+def e4m3_encode_bruteforce(x) -> np.ndarray:
+    """uint8 codes of float values: nearest finite e4m3 value, ties to the even
+    code, saturating beyond +-448; NaN -> 0x7F.  A search over the 127
+    non-negative finite values, one value at a time (for tiny inputs)."""
+    a = np.asarray(x, dtype=np.float64)
+    flat = a.ravel()
+    out = np.empty(flat.size, dtype=np.uint8)
+    for i, v in enumerate(flat):
+        if np.isnan(v):
+            out[i] = E4M3_NAN
+            continue
+        mag = min(abs(v), E4M3_MAX)
+        d = np.abs(_POS - mag)
+        best = np.flatnonzero(d == d.min())
+        code = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+        out[i] = _apply_sign(v, code)
+    return out.reshape(a.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """The same rounding as e4m3_encode_bruteforce, vectorised: the two finite
+    neighbours of |x| (clamped to 448) in the sorted value table, the nearer
+    one, the even code on a tie."""
+    a = np.asarray(x, dtype=np.float64)
+    mag = np.minimum(np.abs(a), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_POS, mag, side="left"), 0, _POS.size - 1)
+    lo = np.clip(hi - 1, 0, _POS.size - 1)
+    d_lo, d_hi = mag - _POS[lo], _POS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    neg = (a < 0) | ((a == 0) & np.signbit(a))
+    code = np.where(neg, code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(a), np.uint8(E4M3_NAN), code).astype(np.uint8)
+
+
+def row_scales(x) -> np.ndarray:
+    """float32 per-row scales amax / 448 (1 for an all-zero row), computed in float32."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s[amax == 0] = np.float32(1.0)
+    return s
+
+
+def quantize_rows(x):
+    """Per-row e4m3 quantization: (codes uint8 [N][D], scales float32 [N])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    s = row_scales(x32)
+    q = (x32 / s[:, None]).astype(np.float32)        # IEEE float32 division, one rounding
+    return e4m3_encode(q), s
+
+
+def dequantize_rows(codes, scales) -> np.ndarray:
+    """float64 decode(code) * scale of the row."""
+    return e4m3_table()[np.asarray(codes, dtype=np.uint8)] * np.asarray(scales, np.float64)[:, None]
+
+
+def linear_fp8(a_codes, a_scales, w_codes, w_scales, bias=None) -> np.ndarray:
+    """float64 C = dequant(A) dequant(W)^T (+ bias): A [N][K], W [F][K] ([out][in])."""
+    c = dequantize_rows(a_codes, a_scales) @ dequantize_rows(w_codes, w_scales).T
+    if bias is not None:
+        c = c + np.asarray(bias, np.float64)[None, :]
+    return c
