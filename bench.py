@@ -13,7 +13,9 @@ feed-forward half (d_ff = 4 d_model) on its own; it is not part of ``value``.
 ``denoise_step`` times the denoising step around the block (one streaming
 pass over the packed latent state), at the workload's size and on a 16-pack
 batch large enough to stream from HBM; ``nft_loss`` does the same for the
-DiffusionNFT loss and its gradient (one sample per request).
+DiffusionNFT loss and its gradient (one sample per request); ``fp8`` times the
+block's four projections in FP8 (e4m3 codes, per-row scales) against the
+e4m3 MFMA peak, and the row quantization against HBM.
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
 workload on the host cores.
 """
@@ -37,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DiT-block ms + attention TFLOP/s at 58,758 tokens; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6       # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0        # dense e4m3 MFMA, twice the bf16 rate
 ATTN_KERNEL = "attn_bf16_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_full_hbm_traffic.md")
 KERNEL_SOURCES = ("joint_audio_video_amd/csrc/attn.hip", "joint_audio_video_amd/csrc/common.h")
@@ -225,6 +228,8 @@ def main() -> int:
                     help="skip timing the denoising step around the block")
     ap.add_argument("--no-nft", action="store_true",
                     help="skip timing the DiffusionNFT loss")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip timing the FP8 projections")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
@@ -472,6 +477,69 @@ def main() -> int:
             del vt_d, vo_d, tg_d, g_d, out_d, k_d, cu_d, r_d, nws, ni
         print(f"# nft: {nft_rec}", file=sys.stderr, flush=True)
 
+    # The block's projections in FP8: activations and weights quantized per row on the
+    # GPU, then the four products (QKV into planes, to_out.0 gated, ff.net.0.proj with
+    # GELU, ff.net.2 gated) timed on their own.
+    fp8_rec = None
+    if not args.no_fp8:
+        print("# fp8 projections ...", file=sys.stderr, flush=True)
+        F = wl.d_ff
+        fi = synth.ffn_inputs(wl)
+        wq, wqs = jav.quantize_rows_fp8(w_qkv)
+        wo, wos = jav.quantize_rows_fp8(w_o)
+        w1 = bf(fi.w1)
+        w1q, w1s = jav.quantize_rows_fp8(w1)
+        del w1
+        w2 = bf(fi.w2)
+        w2q, w2s = jav.quantize_rows_fp8(w2)
+        del w2
+        xq = torch.empty((n, d), dtype=torch.uint8, device=dev)
+        xs = torch.empty(n, dtype=torch.float32, device=dev)
+        hq = torch.empty((n, F), dtype=torch.uint8, device=dev)
+        hs = torch.empty(n, dtype=torch.float32, device=dev)
+        jav.quantize_rows_fp8(x, codes=xq, scales=xs, stream=stream)
+        hq.random_(0, 120)                 # finite codes, magnitudes up to 240
+        hs.fill_(1.0 / 64)
+        qkv8 = torch.empty((n, 3 * d), dtype=torch.bfloat16, device=dev)
+        h8 = torch.empty((n, F), dtype=torch.bfloat16, device=dev)
+        out8 = torch.empty_like(x)
+        ops8 = {
+            "quant_x": (20, lambda: jav.quantize_rows_fp8(x, codes=xq, scales=xs, stream=stream)),
+            "qkv": (5, lambda: jav.linear_fp8(xq, xs, wq, wqs, out=qkv8, stream=stream)),
+            "out": (5, lambda: jav.linear_fp8(xq, xs, wo, wos, epilogue="gated", x=x,
+                                              modality=mod, table=table, out=out8,
+                                              stream=stream)),
+            "ffn_up": (5, lambda: jav.linear_fp8(xq, xs, w1q, w1s, epilogue="gelu", out=h8,
+                                                 stream=stream)),
+            "ffn_down": (5, lambda: jav.linear_fp8(hq, hs, w2q, w2s, epilogue="gated", x=x,
+                                                   modality=mod, table=table, out=out8,
+                                                   stream=stream)),
+        }
+        t8 = {}
+        for name, (reps, fn) in ops8.items():
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t8[name] = e0.elapsed_time(e1) / reps
+        fl = {"qkv": 6.0 * n * d * d, "out": 2.0 * n * d * d, "ffn_up": 2.0 * n * d * F,
+              "ffn_down": 2.0 * n * d * F}
+        fp8_rec = {"format": "e4m3, per-row float32 scales", "ms": {k: round(v, 4) for k, v in t8.items()}}
+        for k, f in fl.items():
+            tf = f / (t8[k] * 1e-3) / 1e12
+            fp8_rec[f"{k}_tflops"] = round(tf, 1)
+            fp8_rec[f"{k}_frac_of_fp8_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
+        qb = n * (d * 2 + d + 4)
+        fp8_rec["quant_x_gbs"] = round(qb / (t8["quant_x"] * 1e-3) / 1e9, 1)
+        fp8_rec["quant_x_frac_of_hbm"] = round(qb / (t8["quant_x"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        del wq, wo, w1q, w2q, xq, hq, qkv8, h8, out8
+        print(f"# fp8: {fp8_rec}", file=sys.stderr, flush=True)
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -538,6 +606,8 @@ def main() -> int:
         rec["denoise_step"] = den_rec
     if nft_rec is not None:
         rec["nft_loss"] = nft_rec
+    if fp8_rec is not None:
+        rec["fp8_projections"] = fp8_rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle

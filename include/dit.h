@@ -280,6 +280,48 @@ dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* FP8 projections                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* [vLLM-Omni] section 5 ("Distributed Layerwise Offload") runs the active DiT
+ * layers in FP8; the pages give no scaling recipe.  Here: OCP e4m3 ("fn")
+ * codes, one float32 scale per row (per token for activations, per output
+ * channel for weights), scale = amax(|row|) / 448 (1 for an all-zero row),
+ * code = e4m3(x * (1 / scale)) rounded to nearest with ties to the even code
+ * and saturated at +-448; the two divisions are IEEE float32, once per row,
+ * and the product one float32 rounding.  On gfx950 the e4m3 MFMA
+ * runs at twice the bf16 rate. */
+
+/* quantize_rows_fp8: x [n_rows][ld_x] of dt (bf16 or f32), first d columns ->
+ * q uint8 [n_rows][ld_q] e4m3 codes and scales float32 [n_rows] (device).
+ * Errors: DIT_EINVAL for a null pointer, d < 1, ld_x < d, ld_q < d, n_rows <
+ * 0, an unknown dtype; DIT_EUNSUPPORTED for d not a multiple of 8 or above
+ * 20480 (bf16; 10240 f32), or pointers / ld off the 16-byte rule (ld_q in
+ * bytes); DIT_EHIP on a launch failure. */
+dit_status quantize_rows_fp8(dit_dtype dt, const void* x, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                             float* scales, int64_t n_rows, int32_t d, void* stream);
+
+typedef enum { DIT_EPI_PLAIN = 0, DIT_EPI_GATED = 1, DIT_EPI_GELU = 2 } dit_epilogue;
+
+/* linear_fp8: out = epi((decode(a) * a_scales[row]) (decode(w) * w_scales[col])^T
+ * + bias), float32 accumulation, bf16 output (RNE).  a: e4m3 codes
+ * [n_tokens][ld_a] (first k_in used); w: codes [n_out][k_in] contiguous
+ * ([out][in]); a_scales [n_tokens], w_scales [n_out] float32; bias bf16
+ * [n_out] or NULL.  epi PLAIN stores the product; GELU stores its tanh-form
+ * GELU; GATED stores x + table[modality[row]][GATE] * product with x bf16
+ * [n_tokens][ld_x], modality uint8 [n_tokens] and table float32 [3][3][n_out]
+ * (out may be x, in place).  All pointers device.  Errors: DIT_EINVAL for a
+ * null required pointer, an unknown epilogue, k_in or n_out < 1, an ld too
+ * small, n_tokens < 0; DIT_EUNSUPPORTED when k_in is not a multiple of 128,
+ * n_out not a multiple of 4, or a pointer / ld breaks the 16-byte rule;
+ * DIT_EHIP on a launch failure. */
+dit_status linear_fp8(const uint8_t* a, int64_t ld_a, const float* a_scales, const uint8_t* w,
+                      const float* w_scales, const void* bias, dit_epilogue epi, const void* x,
+                      int64_t ld_x, const uint8_t* modality, const float* table, void* out,
+                      int64_t ld_out, int64_t n_tokens, int32_t k_in, int32_t n_out,
+                      void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* The denoising step around the block                                        */
 /* ------------------------------------------------------------------------ */
 

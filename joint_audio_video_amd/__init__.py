@@ -33,6 +33,7 @@ EXPORTED = (
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
     "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
     "denoise_step", "dit_nft_workspace_bytes", "nft_loss", "rope3d_apply_to",
+    "quantize_rows_fp8", "linear_fp8",
 )
 
 
@@ -102,6 +103,9 @@ def _load() -> ctypes.CDLL:
         "dit_nft_workspace_bytes": (SZ, [I32, I32]),
         "nft_loss": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, P, I32, I32, I64, I32,
                                     P, F32, I32, F32, P, I64, P, P, SZ, P]),
+        "quantize_rows_fp8": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, I32, P]),
+        "linear_fp8": (ctypes.c_int, [P, I64, P, P, P, P, ctypes.c_int, P, I64, P, P, P, I64, I64,
+                                      I32, I32, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -445,3 +449,44 @@ def nft_loss(v_theta, v_old, v_target, cu_samples, max_rows: int, reward, beta: 
                          float(beta), int(velocity_sign), scale, pg, ldg, loss_out.data_ptr(),
                          workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return loss_out, grad
+
+
+# ---------------------------------------------------------------------------
+# FP8 projections
+# ---------------------------------------------------------------------------
+
+DIT_EPI_PLAIN, DIT_EPI_GATED, DIT_EPI_GELU = 0, 1, 2
+_EPI = {"plain": DIT_EPI_PLAIN, "gated": DIT_EPI_GATED, "gelu": DIT_EPI_GELU}
+
+
+def quantize_rows_fp8(x, codes=None, scales=None, n_rows=None, stream=None):
+    """Per-row e4m3 codes and float32 scales of x (libdit quantize_rows_fp8)."""
+    torch = _torch()
+    n = x.shape[0] if n_rows is None else int(n_rows)
+    d = x.shape[1]
+    if codes is None:
+        codes = torch.empty((x.shape[0], d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    px, ldx = _rows(x)
+    pq, ldq = _rows(codes)
+    _check(_lib.quantize_rows_fp8(_dtype_code(x), px, ldx, pq, ldq, scales.data_ptr(), n, d,
+                                  _stream(stream)))
+    return codes, scales
+
+
+def linear_fp8(a_codes, a_scales, w_codes, w_scales, bias=None, epilogue: str = "plain", x=None,
+               modality=None, table=None, out=None, n_tokens=None, stream=None):
+    """out = epilogue(dequant(A) dequant(W)^T + bias) in bf16 (libdit linear_fp8)."""
+    torch = _torch()
+    n = a_codes.shape[0] if n_tokens is None else int(n_tokens)
+    f, k = w_codes.shape
+    if out is None:
+        out = torch.empty((a_codes.shape[0], f), dtype=torch.bfloat16, device=a_codes.device)
+    pa, lda = _rows(a_codes)
+    po, ldo = _rows(out)
+    px, ldx = (0, 0) if x is None else _rows(x)
+    _check(_lib.linear_fp8(pa, lda, a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
+                           _ptr(bias), _EPI[epilogue], px, ldx, _ptr(modality), _ptr(table), po,
+                           ldo, n, k, f, _stream(stream)))
+    return out

@@ -371,6 +371,63 @@ extern "C" dit_status ffn_down_gated(dit_dtype dt, const void* h, int64_t ld_h, 
 }
 
 // ---------------------------------------------------------------------------
+// FP8 projections
+
+extern "C" dit_status quantize_rows_fp8(dit_dtype dt, const void* x, int64_t ld_x, uint8_t* q,
+                                        int64_t ld_q, float* scales, int64_t n_rows, int32_t d,
+                                        void* stream) {
+  clear_error();
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "quantize_rows_fp8: unknown dtype %d", (int)dt);
+  if (!x || !q || !scales) return fail(DIT_EINVAL, "quantize_rows_fp8: null pointer");
+  if (d < 1) return fail(DIT_EINVAL, "quantize_rows_fp8: d < 1");
+  if (ld_x < d || ld_q < d) return fail(DIT_EINVAL, "quantize_rows_fp8: ld < d");
+  if (dit_status st = check_stream_rows(n_rows)) return st;
+  if (d % 8 != 0 || d > (dt == DIT_BF16 ? 20480 : 10240))
+    return fail(DIT_EUNSUPPORTED, "quantize_rows_fp8: d %d unsupported", d);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !ld_aligned(dt, ld_x) ||
+      ld_q % 16 != 0)
+    return fail(DIT_EUNSUPPORTED, "quantize_rows_fp8: pointers/ld must be 16-byte aligned");
+  if (n_rows == 0) return DIT_OK;
+  hipError_t e = launch_quant_rows_fp8(dt == DIT_BF16, x, ld_x, q, ld_q, scales, n_rows, d,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "quantize_rows_fp8 launch");
+}
+
+extern "C" dit_status linear_fp8(const uint8_t* a, int64_t ld_a, const float* a_scales,
+                                 const uint8_t* w, const float* w_scales, const void* bias,
+                                 dit_epilogue epi, const void* x, int64_t ld_x,
+                                 const uint8_t* modality, const float* table, void* out,
+                                 int64_t ld_out, int64_t n_tokens, int32_t k_in, int32_t n_out,
+                                 void* stream) {
+  clear_error();
+  if (!a || !a_scales || !w || !w_scales || !out) return fail(DIT_EINVAL, "linear_fp8: null pointer");
+  if (epi != DIT_EPI_PLAIN && epi != DIT_EPI_GATED && epi != DIT_EPI_GELU)
+    return fail(DIT_EINVAL, "linear_fp8: unknown epilogue %d", (int)epi);
+  if (epi == DIT_EPI_GATED && (!x || !modality || !table))
+    return fail(DIT_EINVAL, "linear_fp8: the gated epilogue needs x, modality and table");
+  if (k_in < 1 || n_out < 1) return fail(DIT_EINVAL, "linear_fp8: width < 1");
+  if (ld_a < k_in || ld_out < n_out || (epi == DIT_EPI_GATED && ld_x < n_out))
+    return fail(DIT_EINVAL, "linear_fp8: ld too small");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (k_in % 128 != 0 || n_out % 4 != 0)
+    return fail(DIT_EUNSUPPORTED, "linear_fp8: k_in %d must be a multiple of 128, n_out %d of 4",
+                k_in, n_out);
+  if (!aligned16(a) || ld_a % 16 != 0 || !aligned16(w) || !aligned16(w_scales) ||
+      !aligned16(out) || !ld_aligned(DIT_BF16, ld_out) || (bias && !aligned16(bias)) ||
+      (epi == DIT_EPI_GATED && (!aligned16(x) || !ld_aligned(DIT_BF16, ld_x) || !aligned16(table))))
+    return fail(DIT_EUNSUPPORTED, "linear_fp8: pointers/ld must be 16-byte aligned");
+  if (epi == DIT_EPI_GATED && x == out && ld_x != ld_out)
+    return fail(DIT_EINVAL, "linear_fp8: in-place needs ld_x == ld_out");
+  if (n_tokens == 0) return DIT_OK;
+  GemmEpilogue ep{(int)epi, bias, epi == DIT_EPI_GATED ? x : nullptr, ld_x,
+                  epi == DIT_EPI_GATED ? modality : nullptr,
+                  epi == DIT_EPI_GATED ? table + 2 * (size_t)n_out : nullptr};
+  hipError_t e = launch_gemm_fp8(a, ld_a, a_scales, w, w_scales, out, ld_out, n_tokens, n_out,
+                                 k_in, ep, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "linear_fp8 launch");
+}
+
+// ---------------------------------------------------------------------------
 // Denoising step
 
 static dit_status denoise_check(dit_dtype dt, const float* z, int64_t ld_z, const void* v,

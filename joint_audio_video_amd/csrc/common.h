@@ -106,6 +106,15 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
                        int64_t ldc, int64_t m, int n, int k, const GemmEpilogue& ep,
                        hipStream_t s);
 
+// FP8 projection: a, w e4m3 codes [m][k] / [n][k] (row strides lda, k bytes),
+// sa [m], sw [n] float32 row scales; c bf16; epilogues as launch_gemm.
+hipError_t launch_gemm_fp8(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,
+                           const float* sw, void* c, int64_t ldc, int64_t m, int n, int k,
+                           const GemmEpilogue& ep, hipStream_t s);
+// Per-row e4m3 quantization of bf16 (or float32) rows: codes [n][ld_q], scales [n].
+hipError_t launch_quant_rows_fp8(int bf16, const void* x, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                                 float* scales, int64_t n, int d, hipStream_t s);
+
 // Workspace of launch_nft_loss: a loss-bearing row count per sample (int32)
 // and two squared-error sums (float) per (sample, 32-row chunk), each region
 // 256-byte aligned.

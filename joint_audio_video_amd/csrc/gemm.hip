@@ -249,6 +249,264 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   }
 }
 
+// ---- FP8 path: e4m3 codes with one float32 scale per row of A and of W ----
+//
+// C = (decode(A) decode(W)^T) * sa[row] * sw[col] (+ bias), then the same
+// three epilogues.  v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
+// accumulate) at twice the bf16 rate.  The tile and the LDS layout are the
+// bf16 kernel's in bytes: a 64-element bf16 k-step is a 128-byte row, and so
+// is a 128-code FP8 k-step, so the 256x256 tiles, the XOR-swizzled 16-byte
+// chunks and the direct global -> LDS loads carry over unchanged.  A k-step
+// is 2 sub-steps of 64 codes; a fragment (32 codes of one row) is two chunks,
+// two 16-byte LDS reads.  Each sub-step is written as 4 fenced groups of 4
+// independent MFMAs, each group followed by the next sub-step's reads of one
+// A and one B block and, in the first sub-step, 4 of the next tile's 16
+// global loads.
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+constexpr int BK8 = 128;   // codes per k-step
+
+struct EpiArgs8 {
+  const float* sa;          // [M] row scales of A
+  const float* sw;          // [N] row scales of W (output channels)
+};
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B,
+    uint16_t* C, int64_t ldc, int M, int N, int K, EpiArgs ep, EpiArgs8 sc) {
+  __shared__ __attribute__((aligned(16))) uint8_t As0[BM * BK8];
+  __shared__ __attribute__((aligned(16))) uint8_t As1[BM * BK8];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs0[BN * BK8];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs1[BN * BK8];
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // Global -> LDS exactly as the bf16 kernel, with 128-byte rows of codes.
+  const int lrow = tid >> 3;
+  const int lchunk = (tid & 7) ^ ((tid >> 3) & 7);
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(A + (int64_t)m0 * lda), 0, (int)((uint32_t)rows_a * (uint32_t)lda),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(B + (int64_t)n0 * K), 0, (int)((uint32_t)rows_b * (uint32_t)K),
+      0x00020000);
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    aoff[i] = (uint32_t)min(32 * i + lrow, rows_a - 1) * (uint32_t)lda + lchunk * 16;
+    boff[i] = (uint32_t)min(32 * i + lrow, rows_b - 1) * (uint32_t)K + lchunk * 16;
+  }
+  auto load1 = [&](uint8_t* adst, uint8_t* bdst, int k0, int i) {
+    if (i < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, adst + (256 * i + 64 * wave) * 16, 16, aoff[i],
+                                               k0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, bdst + (256 * (i - 8) + 64 * wave) * 16, 16,
+                                               boff[i - 8], k0, 0, 0);
+  };
+  auto issue = [&](uint8_t* adst, uint8_t* bdst, int k0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) load1(adst, bdst, k0, i);
+  };
+
+  f32x16 acc[4][4];
+  const f32x16 zero16 = {};
+  const int nk = K / BK8;
+  // Fragment of sub-step ks for a row: codes 64ks + 32g .. +31 = chunks
+  // 4ks + 2g and 4ks + 2g + 1 of the row.
+  auto frag = [&](const uint8_t* base, int row, int ks) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(&base[row * BK8 + swz(row, 4 * ks + 2 * g) * 16]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&base[row * BK8 + swz(row, 4 * ks + 2 * g + 1) * 16]);
+    return v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                 (int)hi.w};
+  };
+  auto k_step = [&](const uint8_t* as, const uint8_t* bs, uint8_t* an, uint8_t* bn, int kt,
+                    bool first) {
+    const int kload = min(kt + 1, nk - 1) * BK8;   // last step: reload into the idle buffer
+    v8i32 af[4], bfr[4], an_[4], bn_[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) af[mb] = frag(as, wm * 128 + mb * 32 + l32, 0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(bs, wn * 128 + nb * 32 + l32, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < BK8 / 64; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bfr[nb], af[mb], (first && ks == 0) ? zero16 : acc[mb][nb], 0, 0, 0, 0, 0, 0);
+        if (ks + 1 < BK8 / 64) {
+          an_[mb] = frag(as, wm * 128 + mb * 32 + l32, ks + 1);
+          bn_[mb] = frag(bs, wn * 128 + mb * 32 + l32, ks + 1);
+        }
+        if (ks == 0) {                   // the 16 loads: four per group, first sub-step
+#pragma unroll
+          for (int j = 0; j < 4; ++j) load1(an, bn, kload, 4 * mb + j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ks + 1 < BK8 / 64) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[i] = an_[i];
+          bfr[i] = bn_[i];
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  issue(As0, Bs0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  k_step(As0, Bs0, As1, Bs1, 0, true);
+  for (int kt = 1; kt < nk; kt += 2) {
+    k_step(As1, Bs1, As0, Bs0, kt, false);
+    if (kt + 1 < nk) k_step(As0, Bs0, As1, Bs1, kt + 1, false);
+  }
+
+  // Epilogue: acc^T as in the bf16 kernel, times the row scale of A and the
+  // column scales of W, then the bias and the epilogue kind.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int row = m0 + wm * 128 + mb * 32 + l32;
+    if (row >= M) continue;
+    const float sa = sc.sa[row];
+    uint16_t* crow = C + (int64_t)row * ldc;
+    const uint16_t* xrow = KIND == 1 ? ep.x + (int64_t)row * ep.ld_x : nullptr;
+    const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      uint16_t* cbase = crow;
+      int cshift = 0;
+      if (KIND == 0 && ep.plane_cols > 0) {
+        const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
+        cbase = crow + plane * ep.plane_stride;
+        cshift = plane * ep.plane_cols;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
+        if (col >= N) continue;
+        const float4 sw = *reinterpret_cast<const float4*>(sc.sw + col);
+        float v[4] = {acc[mb][nb][4 * r + 0] * sa * sw.x, acc[mb][nb][4 * r + 1] * sa * sw.y,
+                      acc[mb][nb][4 * r + 2] * sa * sw.z, acc[mb][nb][4 * r + 3] * sa * sw.w};
+        if (ep.bias) {
+          const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
+          v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
+        }
+        if constexpr (KIND == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
+        }
+        if constexpr (KIND == 1) {
+          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
+          const float4 gt = *reinterpret_cast<const float4*>(grow + col);
+          v[0] = fmaf(gt.x, v[0], bf16lo(xv.x));
+          v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
+          v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
+          v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
+        }
+        *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+}
+
+// Four e4m3 codes of four float32 values in one word (value j in byte j):
+// nearest, ties to the even code (v_cvt_pk_fp8_f32, which rounds exactly so
+// for |v| <= 464: checked against the float64 oracle on every code, every
+// midpoint and its float32 neighbours and 2e5 random values), saturating at
+// +-448 (the conversion gives NaN beyond 464, so values are clamped first),
+// NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_pack4(float f0, float f1, float f2, float f3) {
+  auto clamp = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f0), clamp(f1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f2), clamp(f3), w, true);
+  uint32_t u = (uint32_t)w;
+  if (__builtin_isnan(f0) | __builtin_isnan(f1) | __builtin_isnan(f2) | __builtin_isnan(f3)) {
+    if (__builtin_isnan(f0)) u = (u & 0xffffff00u) | 0x7fu;
+    if (__builtin_isnan(f1)) u = (u & 0xffff00ffu) | 0x7f00u;
+    if (__builtin_isnan(f2)) u = (u & 0xff00ffffu) | 0x7f0000u;
+    if (__builtin_isnan(f3)) u = (u & 0x00ffffffu) | 0x7f000000u;
+  }
+  return u;
+}
+
+// Per-row quantization: one wave per row, the row held in registers (NV
+// 16-byte vectors per lane), scale = amax / 448 and inv = 1 / scale (IEEE
+// divisions, once per row), codes of x * inv (one float32 product per value),
+// 4-code stores.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x, int64_t ld_x,
+                                                         uint8_t* __restrict__ q, int64_t ld_q,
+                                                         float* __restrict__ scales, int64_t n,
+                                                         int d) {
+  constexpr int E = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int nvec = d / E;
+  uint4 raw[NV];
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld_x);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    raw[i] = c < nvec ? ld_stream(xr + c) : make_uint4(0, 0, 0, 0);
+  }
+  auto unpack = [&](const uint4& r, float* f) {
+    if constexpr (E == 8) {
+      f[0] = bf16lo(r.x); f[1] = bf16hi(r.x); f[2] = bf16lo(r.y); f[3] = bf16hi(r.y);
+      f[4] = bf16lo(r.z); f[5] = bf16hi(r.z); f[6] = bf16lo(r.w); f[7] = bf16hi(r.w);
+    } else {
+      f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+      f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+    }
+  };
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float f[E];
+    unpack(raw[i], f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  }
+  amax = wave_max(amax);
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const float inv = 1.0f / s;
+  if (lane == 0) scales[row] = s;
+  uint8_t* qr = q + row * ld_q;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nvec) continue;
+    float f[E];
+    unpack(raw[i], f);
+    uint32_t w[E / 4];
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j)
+      w[j] = e4m3_pack4(f[4 * j] * inv, f[4 * j + 1] * inv, f[4 * j + 2] * inv, f[4 * j + 3] * inv);
+    if constexpr (E == 8)
+      *reinterpret_cast<uint2*>(qr + c * E) = make_uint2(w[0], w[1]);
+    else
+      *reinterpret_cast<uint32_t*>(qr + c * E) = w[0];
+  }
+}
+
 // ---- float32 path ----
 constexpr int FT = 64, FK = 16;
 
@@ -330,6 +588,50 @@ hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void
         ep.plane_stride);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,
+                           const float* sw, void* c, int64_t ldc, int64_t m, int n, int k,
+                           const GemmEpilogue& ep, hipStream_t s) {
+  if (k % BK8 != 0 || m > INT32_MAX) return hipErrorInvalidValue;
+  if (ep.plane_cols < 0 || ep.plane_cols % 32 != 0 || (ep.plane_cols > 0 && ep.kind != 0))
+    return hipErrorInvalidValue;
+  const int64_t gate_stride = 3 * (int64_t)n;
+  const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
+            ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride};
+  EpiArgs8 e8{sa, sw};
+  uint16_t* cp = static_cast<uint16_t*>(c);
+  if (ep.kind == 1)
+    gemm_fp8_kernel<1><<<dim3(tiles), dim3(kThreads), 0, s>>>(a, lda, w, cp, ldc, (int)m, n, k, e, e8);
+  else if (ep.kind == 2)
+    gemm_fp8_kernel<2><<<dim3(tiles), dim3(kThreads), 0, s>>>(a, lda, w, cp, ldc, (int)m, n, k, e, e8);
+  else
+    gemm_fp8_kernel<0><<<dim3(tiles), dim3(kThreads), 0, s>>>(a, lda, w, cp, ldc, (int)m, n, k, e, e8);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_fp8(int bf16, const void* x, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                                 float* scales, int64_t n, int d, hipStream_t s) {
+  const int e = bf16 ? 8 : 4;
+  if (d % e != 0) return hipErrorInvalidValue;
+  const int need = (d / e + 63) / 64;
+  const dim3 grid((unsigned)((n + 3) / 4)), block(256);
+#define DIT_QUANT_CASE(NVV)                                                                     \
+  if (need <= NVV) {                                                                            \
+    if (bf16)                                                                                   \
+      quant_rows_kernel<uint16_t, NVV><<<grid, block, 0, s>>>(                                  \
+          static_cast<const uint16_t*>(x), ld_x, q, ld_q, scales, n, d);                        \
+    else                                                                                        \
+      quant_rows_kernel<float, NVV><<<grid, block, 0, s>>>(static_cast<const float*>(x), ld_x,  \
+                                                           q, ld_q, scales, n, d);              \
+    return hipGetLastError();                                                                   \
+  }
+  DIT_QUANT_CASE(1) DIT_QUANT_CASE(2) DIT_QUANT_CASE(4) DIT_QUANT_CASE(8) DIT_QUANT_CASE(10)
+  DIT_QUANT_CASE(12)
+  DIT_QUANT_CASE(16) DIT_QUANT_CASE(24) DIT_QUANT_CASE(32) DIT_QUANT_CASE(40)
+#undef DIT_QUANT_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dit

@@ -13,8 +13,11 @@ layers in FP8; the pages give no scaling recipe.  Readings:
   conversion is the plainest choice for a quantizer).
 * Scaling: one float32 scale per row (per token for activations, per output
   channel for weights), scale = amax(|row|) / 448 computed in float32; a zero
-  row has scale 1.  Codes are e4m3(fp32(x) / scale) with an IEEE float32
-  division, the precision in which the GPU takes the same decision.
+  row has scale 1.  Codes are e4m3(fp32(x) * inv) with inv = 1 / scale, one
+  IEEE float32 division per row and one float32 product per value: the
+  precision in which the GPU takes the same decision (a multiply by the
+  reciprocal, not a division per value, which would dominate the
+  quantization pass).
 * A projection C = (dequant(A) dequant(B)^T) with dequant(q) = decode(q) *
   scale of its row, evaluated here in float64.
 """
@@ -99,7 +102,8 @@ def quantize_rows(x):
     """Per-row e4m3 quantization: (codes uint8 [N][D], scales float32 [N])."""
     x32 = np.asarray(x, dtype=np.float32)
     s = row_scales(x32)
-    q = (x32 / s[:, None]).astype(np.float32)        # IEEE float32 division, one rounding
+    inv = (np.float32(1.0) / s).astype(np.float32)   # IEEE float32 division, once per row
+    q = (x32 * inv[:, None]).astype(np.float32)      # one float32 rounding per value
     return e4m3_encode(q), s
 
 
