@@ -15,7 +15,9 @@ pass over the packed latent state), at the workload's size and on a 16-pack
 batch large enough to stream from HBM; ``nft_loss`` does the same for the
 DiffusionNFT loss and its gradient (one sample per request); ``fp8`` times the
 block's four projections in FP8 (e4m3 codes, per-row scales) against the
-e4m3 MFMA peak, and the row quantization against HBM.
+e4m3 MFMA peak, the row quantization and the FP8-output AdaLN against HBM,
+and the two halves of the block with FP8 projections (``block_fp8``,
+``ffn_fp8``, ms per call).
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
 workload on the host cores.
 """
@@ -503,8 +505,21 @@ def main() -> int:
         qkv8 = torch.empty((n, 3 * d), dtype=torch.bfloat16, device=dev)
         h8 = torch.empty((n, F), dtype=torch.bfloat16, device=dev)
         out8 = torch.empty_like(x)
+        table8 = torch.from_numpy(fi.table).to(dev)
+        ws_b8 = torch.empty(jav.block_fp8_workspace_bytes(desc, n), dtype=torch.uint8, device=dev)
+        fdesc8 = jav.ffn_desc(jav.DIT_BF16, d, F, wl.eps)
+        ws_f8 = torch.empty(jav.ffn_fp8_workspace_bytes(fdesc8, n), dtype=torch.uint8,
+                            device=dev)
         ops8 = {
             "quant_x": (20, lambda: jav.quantize_rows_fp8(x, codes=xq, scales=xs, stream=stream)),
+            "adaln_fp8": (20, lambda: jav.adaln_modulate_fp8(x, mod, table, wl.eps, codes=xq,
+                                                             scales=xs, stream=stream)),
+            "block_fp8": (3, lambda: jav.block_forward_fp8(desc, x, mod, pos, cu, ms_len, table,
+                                                           wq, wqs, wo, wos, out=out8,
+                                                           workspace=ws_b8, stream=stream)),
+            "ffn_fp8": (3, lambda: jav.ffn_forward_fp8(fdesc8, x, mod, table8, w1q, w1s, w2q,
+                                                       w2s, out=out8, workspace=ws_f8,
+                                                       stream=stream)),
             "qkv": (5, lambda: jav.linear_fp8(xq, xs, wq, wqs, out=qkv8, stream=stream)),
             "out": (5, lambda: jav.linear_fp8(xq, xs, wo, wos, epilogue="gated", x=x,
                                               modality=mod, table=table, out=out8,
@@ -537,7 +552,11 @@ def main() -> int:
         qb = n * (d * 2 + d + 4)
         fp8_rec["quant_x_gbs"] = round(qb / (t8["quant_x"] * 1e-3) / 1e9, 1)
         fp8_rec["quant_x_frac_of_hbm"] = round(qb / (t8["quant_x"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        del wq, wo, w1q, w2q, xq, hq, qkv8, h8, out8
+        # AdaLN with FP8 output: reads x (bf16), writes codes and scales
+        fp8_rec["adaln_fp8_gbs"] = round(qb / (t8["adaln_fp8"] * 1e-3) / 1e9, 1)
+        fp8_rec["adaln_fp8_frac_of_hbm"] = round(qb / (t8["adaln_fp8"] * 1e-3) / 1e9
+                                                 / PEAK_HBM_GBS, 4)
+        del wq, wo, w1q, w2q, xq, hq, qkv8, h8, out8, ws_b8, ws_f8, table8
         print(f"# fp8: {fp8_rec}", file=sys.stderr, flush=True)
 
     cu_list = lay["cu_seqlens"].tolist()

@@ -301,6 +301,16 @@ dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void* out,
 dit_status quantize_rows_fp8(dit_dtype dt, const void* x, int64_t ld_x, uint8_t* q, int64_t ld_q,
                              float* scales, int64_t n_rows, int32_t d, void* stream);
 
+/* adaln_modulate_fp8: adaln_modulate whose output y (float32, never rounded
+ * to dt) leaves as per-row e4m3 codes q uint8 [n_tokens][ld_q] and scales
+ * float32 [n_tokens], quantized by the rule above from y's float32 values.
+ * Arguments and errors as adaln_modulate (prefix adaln_modulate_fp8), with
+ * ld_q in bytes, a multiple of 16. */
+dit_status adaln_modulate_fp8(dit_dtype dt, const void* x, int64_t ld_x,
+                              const uint8_t* modality, const float* table, uint8_t* q,
+                              int64_t ld_q, float* scales, int64_t n_tokens, int32_t d_model,
+                              float eps, void* stream);
+
 typedef enum { DIT_EPI_PLAIN = 0, DIT_EPI_GATED = 1, DIT_EPI_GELU = 2 } dit_epilogue;
 
 /* linear_fp8: out = epi((decode(a) * a_scales[row]) (decode(w) * w_scales[col])^T
@@ -443,6 +453,53 @@ dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
                              const void* w_qkv, const void* b_qkv,
                              const void* w_o, const void* b_o,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* FP8 block halves                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* The attention and feed-forward halves with their projections in FP8
+ * ([vLLM-Omni] section 5: the active layers run in FP8), with the
+ * quantization rule of the FP8 projections: each projection's operand (the
+ * AdaLN output, the attention output, the activated hidden state) is
+ * quantized per row, weights come as e4m3 codes [out][in] contiguous with
+ * float32 scales [out] (device, 16-byte aligned).  Activations, q, k, v,
+ * attention and the output stay bf16 (d->dtype must be DIT_BF16, else
+ * DIT_EUNSUPPORTED); widths must be multiples of 128. */
+
+/* Bytes of scratch dit_block_forward_fp8 needs: five bf16 [N][D] planes and
+ * N float32 row scales, each region rounded up to 256 bytes.  0 for a bad
+ * descriptor (also for a dtype other than DIT_BF16). */
+size_t dit_block_fp8_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
+
+/* As dit_block_forward, with w_qkv codes [3D][D] and w_qkv_scales [3D],
+ * w_o codes [D][D] and w_o_scales [D].  Enqueues adaln_modulate_fp8 ->
+ * linear_fp8 (QKV, split into planes) -> rope3d_apply_to -> attn_packed ->
+ * quantize_rows_fp8 -> linear_fp8 (gated) on stream, after validating all.
+ * Errors: those of the stages, plus DIT_EWORKSPACE. */
+dit_status dit_block_forward_fp8(const dit_block_desc* d, const void* x, void* out,
+                                 const uint8_t* modality, const int32_t* pos_thw,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                                 int64_t n_tokens, const float* ada_table, const uint8_t* w_qkv,
+                                 const float* w_qkv_scales, const void* b_qkv,
+                                 const uint8_t* w_o, const float* w_o_scales, const void* b_o,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch dit_ffn_forward_fp8 needs: codes [N][max(d_ff, d_model)]
+ * bytes, h bf16 [N][d_ff] and N float32 row scales, each region rounded up to
+ * 256 bytes.  0 for a bad descriptor (also for a dtype other than DIT_BF16). */
+size_t dit_ffn_fp8_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens);
+
+/* As dit_ffn_forward, with w1 codes [d_ff][d_model] and w1_scales [d_ff], w2
+ * codes [d_model][d_ff] and w2_scales [d_model]; d_ff at most 20480.
+ * Enqueues adaln_modulate_fp8 -> linear_fp8 (GELU) -> quantize_rows_fp8 ->
+ * linear_fp8 (gated) on stream.  Errors: those of the stages, plus
+ * DIT_EWORKSPACE. */
+dit_status dit_ffn_forward_fp8(const dit_ffn_desc* d, const void* x, void* out,
+                               const uint8_t* modality, int64_t n_tokens, const float* ada_table,
+                               const uint8_t* w1, const float* w1_scales, const void* b1,
+                               const uint8_t* w2, const float* w2_scales, const void* b2,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Optional stage timing of dit_block_forward (measurement plumbing)         */

@@ -33,7 +33,8 @@ EXPORTED = (
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
     "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
     "denoise_step", "dit_nft_workspace_bytes", "nft_loss", "rope3d_apply_to",
-    "quantize_rows_fp8", "linear_fp8",
+    "quantize_rows_fp8", "linear_fp8", "adaln_modulate_fp8", "dit_block_fp8_workspace_bytes",
+    "dit_block_forward_fp8", "dit_ffn_fp8_workspace_bytes", "dit_ffn_forward_fp8",
 )
 
 
@@ -106,6 +107,14 @@ def _load() -> ctypes.CDLL:
         "quantize_rows_fp8": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, I32, P]),
         "linear_fp8": (ctypes.c_int, [P, I64, P, P, P, P, ctypes.c_int, P, I64, P, P, P, I64, I64,
                                       I32, I32, P]),
+        "adaln_modulate_fp8": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, P, I64, I32, F32,
+                                              P]),
+        "dit_block_fp8_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
+        "dit_block_forward_fp8": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32,
+                                                 I32, I64, P, P, P, P, P, P, P, P, SZ, P]),
+        "dit_ffn_fp8_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
+        "dit_ffn_forward_fp8": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P,
+                                               P, P, P, P, SZ, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -489,4 +498,68 @@ def linear_fp8(a_codes, a_scales, w_codes, w_scales, bias=None, epilogue: str = 
     _check(_lib.linear_fp8(pa, lda, a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
                            _ptr(bias), _EPI[epilogue], px, ldx, _ptr(modality), _ptr(table), po,
                            ldo, n, k, f, _stream(stream)))
+    return out
+
+
+def adaln_modulate_fp8(x, modality, table, eps: float = 1e-6, codes=None, scales=None,
+                       n_tokens=None, stream=None):
+    """AdaLN with its output as per-row e4m3 codes and float32 scales (libdit
+    adaln_modulate_fp8)."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    d = x.shape[1]
+    if codes is None:
+        codes = torch.empty((x.shape[0], d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    px, ldx = _rows(x)
+    pq, ldq = _rows(codes)
+    _check(_lib.adaln_modulate_fp8(_dtype_code(x), px, ldx, modality.data_ptr(), table.data_ptr(),
+                                   pq, ldq, scales.data_ptr(), n, d, float(eps), _stream(stream)))
+    return codes, scales
+
+
+def block_fp8_workspace_bytes(desc: BlockDesc, n_tokens: int) -> int:
+    return int(_lib.dit_block_fp8_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def block_forward_fp8(desc: BlockDesc, x, modality, pos, cu_seqlens, max_seqlen: int, table,
+                      w_qkv_codes, w_qkv_scales, w_o_codes, w_o_scales, b_qkv=None, b_o=None,
+                      out=None, workspace=None, n_tokens=None, stream=None):
+    """The attention half with FP8 projections (libdit dit_block_forward_fp8)."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    if out is None:
+        out = torch.empty_like(x)
+    need = block_fp8_workspace_bytes(desc, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(_lib.dit_block_forward_fp8(
+        ctypes.byref(desc), x.data_ptr(), out.data_ptr(), modality.data_ptr(), pos.data_ptr(),
+        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), n, table.data_ptr(),
+        w_qkv_codes.data_ptr(), w_qkv_scales.data_ptr(), _ptr(b_qkv), w_o_codes.data_ptr(),
+        w_o_scales.data_ptr(), _ptr(b_o), workspace.data_ptr(), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+def ffn_fp8_workspace_bytes(desc: FfnDesc, n_tokens: int) -> int:
+    return int(_lib.dit_ffn_fp8_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def ffn_forward_fp8(desc: FfnDesc, x, modality, table, w1_codes, w1_scales, w2_codes, w2_scales,
+                    b1=None, b2=None, out=None, workspace=None, n_tokens=None, stream=None):
+    """The feed-forward half with FP8 projections (libdit dit_ffn_forward_fp8)."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    if out is None:
+        out = torch.empty_like(x)
+    need = ffn_fp8_workspace_bytes(desc, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(_lib.dit_ffn_forward_fp8(
+        ctypes.byref(desc), x.data_ptr(), out.data_ptr(), modality.data_ptr(), n,
+        table.data_ptr(), w1_codes.data_ptr(), w1_scales.data_ptr(), _ptr(b1),
+        w2_codes.data_ptr(), w2_scales.data_ptr(), _ptr(b2), workspace.data_ptr(),
+        workspace.numel(), _stream(stream)))
     return out

@@ -113,6 +113,42 @@ extern "C" dit_status adaln_modulate(dit_dtype dt, const void* x, int64_t ld_x,
   return e == hipSuccess ? DIT_OK : hip_fail(e, "adaln_modulate launch");
 }
 
+static dit_status adaln_fp8_check(dit_dtype dt, const void* x, int64_t ld_x,
+                                  const uint8_t* modality, const float* table, const uint8_t* q,
+                                  int64_t ld_q, const float* scales, int64_t n_tokens,
+                                  int32_t d_model, float eps) {
+  if (!dtype_ok(dt)) return fail(DIT_EINVAL, "adaln_modulate_fp8: unknown dtype %d", (int)dt);
+  if (!x || !modality || !table || !q || !scales)
+    return fail(DIT_EINVAL, "adaln_modulate_fp8: null pointer");
+  if (d_model < 1) return fail(DIT_EINVAL, "adaln_modulate_fp8: d_model < 1");
+  if (ld_x < d_model || ld_q < d_model)
+    return fail(DIT_EINVAL, "adaln_modulate_fp8: ld < d_model");
+  if (!(eps > 0.0f)) return fail(DIT_EINVAL, "adaln_modulate_fp8: eps must be > 0");
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  const int per_vec = dt == DIT_BF16 ? 8 : 4;
+  const int max_d = dt == DIT_BF16 ? 16384 : 8192;
+  if (d_model % per_vec != 0 || d_model > max_d)
+    return fail(DIT_EUNSUPPORTED, "adaln_modulate_fp8: d_model %d unsupported", d_model);
+  if (!aligned16(x) || !aligned16(table) || !aligned16(q) || !aligned16(scales) ||
+      !ld_aligned(dt, ld_x) || ld_q % 16 != 0)
+    return fail(DIT_EUNSUPPORTED, "adaln_modulate_fp8: pointers/ld must be 16-byte aligned");
+  return DIT_OK;
+}
+
+extern "C" dit_status adaln_modulate_fp8(dit_dtype dt, const void* x, int64_t ld_x,
+                                         const uint8_t* modality, const float* table, uint8_t* q,
+                                         int64_t ld_q, float* scales, int64_t n_tokens,
+                                         int32_t d_model, float eps, void* stream) {
+  clear_error();
+  if (dit_status st = adaln_fp8_check(dt, x, ld_x, modality, table, q, ld_q, scales, n_tokens,
+                                      d_model, eps))
+    return st;
+  if (n_tokens == 0) return DIT_OK;
+  hipError_t e = launch_adaln_fp8(dt == DIT_BF16, x, ld_x, modality, table, q, ld_q, scales,
+                                  n_tokens, d_model, eps, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "adaln_modulate_fp8 launch");
+}
+
 // ---------------------------------------------------------------------------
 
 static dit_status rope_check(dit_dtype dt, void* q, int64_t ld_q, void* k, int64_t ld_k,
@@ -533,6 +569,19 @@ extern "C" dit_status nft_loss(dit_dtype v_dtype, const void* v_theta, int64_t l
 
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// An FP8 projection inside a block: W [n_out][k_in] codes with per-row
+// scales, optional bf16 bias [n_out].
+static dit_status fp8_weight_check(const char* who, const uint8_t* w, const float* w_scales,
+                                   const void* bias, int32_t k_in, int32_t n_out) {
+  if (!w || !w_scales) return fail(DIT_EINVAL, "%s: null weight pointer", who);
+  if (k_in % 128 != 0 || n_out % 32 != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: widths %d x %d (multiples of 128 and 32 only)", who,
+                n_out, k_in);
+  if (!aligned16(w) || !aligned16(w_scales) || (bias && !aligned16(bias)))
+    return fail(DIT_EUNSUPPORTED, "%s: weight pointers must be 16-byte aligned", who);
+  return DIT_OK;
+}
+
 extern "C" size_t dit_ffn_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens) {
   if (!d || !dtype_ok(d->dtype) || d->d_model < 1 || d->d_ff < 1 || n_tokens < 0) return 0;
   const size_t es = elt_size(d->dtype), n = (size_t)n_tokens;
@@ -586,6 +635,66 @@ extern "C" dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void
   GemmEpilogue ep_down{1, b2, x, D, modality, ada_table + 2 * (size_t)D};
   e = launch_gemm(dt == DIT_BF16, h, F, w2, out, D, n_tokens, D, F, ep_down, s);
   if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward: down-projection launch");
+  return DIT_OK;
+}
+
+// FP8 feed-forward workspace: codes [N][d_ff] (the AdaLN output's codes
+// [N][d_model] first, then h's) | h bf16 [N][d_ff] | row scales [N] float32.
+extern "C" size_t dit_ffn_fp8_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens) {
+  if (!d || d->dtype != DIT_BF16 || d->d_model < 1 || d->d_ff < 1 || n_tokens < 0) return 0;
+  const size_t n = (size_t)n_tokens, F = (size_t)d->d_ff;
+  return round256(n * std::max(F, (size_t)d->d_model)) + round256(n * F * 2) + round256(n * 4);
+}
+
+extern "C" dit_status dit_ffn_forward_fp8(const dit_ffn_desc* d, const void* x, void* out,
+                                          const uint8_t* modality, int64_t n_tokens,
+                                          const float* ada_table, const uint8_t* w1,
+                                          const float* w1_scales, const void* b1,
+                                          const uint8_t* w2, const float* w2_scales,
+                                          const void* b2, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "dit_ffn_forward_fp8";
+  if (!d) return fail(DIT_EINVAL, "%s: null descriptor", who);
+  if (d->dtype != DIT_BF16)
+    return fail(DIT_EUNSUPPORTED, "%s: bf16 activations only (dtype %d)", who, (int)d->dtype);
+  const int32_t D = d->d_model, F = d->d_ff;
+  if (D < 1 || F < 1) return fail(DIT_EINVAL, "%s: d_model/d_ff < 1", who);
+  if (!x || !out || !modality || !ada_table) return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  const size_t need = dit_ffn_fp8_workspace_bytes(d, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", who);
+  const size_t n = (size_t)n_tokens;
+  char* ws = static_cast<char*>(workspace);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws);
+  void* h = ws + round256(n * std::max((size_t)F, (size_t)D));
+  float* scales = reinterpret_cast<float*>(static_cast<char*>(h) + round256(n * (size_t)F * 2));
+
+  if (dit_status st = adaln_fp8_check(DIT_BF16, x, D, modality, ada_table, codes, D, scales,
+                                      n_tokens, D, d->ln_eps))
+    return st;
+  if (dit_status st = fp8_weight_check(who, w1, w1_scales, b1, D, F)) return st;
+  if (dit_status st = fp8_weight_check(who, w2, w2_scales, b2, F, D)) return st;
+  if (F > 20480) return fail(DIT_EUNSUPPORTED, "%s: d_ff %d > 20480", who, F);
+  if (!aligned16(out)) return fail(DIT_EUNSUPPORTED, "%s: out must be 16-byte aligned", who);
+  if (n_tokens == 0) return DIT_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_adaln_fp8(1, x, D, modality, ada_table, codes, D, scales, n_tokens, D,
+                                  d->ln_eps, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward_fp8: adaln launch");
+  GemmEpilogue ep_up{2, b1, nullptr, 0, nullptr, nullptr};
+  e = launch_gemm_fp8(codes, D, scales, w1, w1_scales, h, F, n_tokens, F, D, ep_up, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward_fp8: up-projection launch");
+  // h's codes replace the AdaLN codes (consumed by the up-projection).
+  e = launch_quant_rows_fp8(1, h, F, codes, F, scales, n_tokens, F, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward_fp8: quantization launch");
+  GemmEpilogue ep_down{1, b2, x, D, modality, ada_table + 2 * (size_t)D};
+  e = launch_gemm_fp8(codes, F, scales, w2, w2_scales, out, D, n_tokens, D, F, ep_down, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_forward_fp8: down-projection launch");
   return DIT_OK;
 }
 
@@ -685,6 +794,101 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   GemmEpilogue ep_out{1, b_o, x, D, modality, ada_table + 2 * (size_t)D};
   e = launch_gemm(dt == DIT_BF16, o, D, w_o, out, D, n_tokens, D, D, ep_out, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: out-proj launch");
+  mark(5);
+  return DIT_OK;
+}
+
+// FP8 block workspace: the five bf16 planes of the bf16 block, then row
+// scales [N] float32.  Plane 0 holds the AdaLN codes, then the rotated q,
+// then the attention output's codes.
+extern "C" size_t dit_block_fp8_workspace_bytes(const dit_block_desc* d, int64_t n_tokens) {
+  if (!d || d->dtype != DIT_BF16 || d->d_model < 1 || n_tokens < 0) return 0;
+  const size_t n = (size_t)n_tokens, D = (size_t)d->d_model;
+  return 5 * round256(n * D * 2) + round256(n * 4);
+}
+
+extern "C" dit_status dit_block_forward_fp8(
+    const dit_block_desc* d, const void* x, void* out, const uint8_t* modality,
+    const int32_t* pos_thw, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+    int64_t n_tokens, const float* ada_table, const uint8_t* w_qkv, const float* w_qkv_scales,
+    const void* b_qkv, const uint8_t* w_o, const float* w_o_scales, const void* b_o,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "dit_block_forward_fp8";
+  if (!d) return fail(DIT_EINVAL, "%s: null descriptor", who);
+  if (d->dtype != DIT_BF16)
+    return fail(DIT_EUNSUPPORTED, "%s: bf16 activations only (dtype %d)", who, (int)d->dtype);
+  const int32_t D = d->d_model, H = d->n_heads, Dh = d->head_dim;
+  if (D < 1 || H < 1 || Dh < 1 || (int64_t)H * Dh != D)
+    return fail(DIT_EINVAL, "%s: d_model %d != n_heads %d * head_dim %d", who, D, H, Dh);
+  if (!x || !out || !modality || !pos_thw || !cu_seqlens || !ada_table)
+    return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  const size_t need = dit_block_fp8_workspace_bytes(d, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", who);
+
+  const size_t n = (size_t)n_tokens;
+  const size_t plane_bytes = round256(n * D * 2);
+  char* ws = static_cast<char*>(workspace);
+  char* p0 = ws;
+  char* q = ws + plane_bytes;
+  char* k = q + plane_bytes;
+  char* v = k + plane_bytes;
+  char* o = v + plane_bytes;
+  float* scales = reinterpret_cast<float*>(o + plane_bytes);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(p0);
+  // Stage by stage: AdaLN codes -> p0; QKV -> q, k, v planes; RoPE: q' -> p0
+  // (the codes are consumed), k' -> over q; attention -> o; o's codes -> p0
+  // (q' is consumed); output projection -> out.
+  void* qr = p0;
+  void* kr = q;
+  if (dit_status st = adaln_fp8_check(DIT_BF16, x, D, modality, ada_table, codes, D, scales,
+                                      n_tokens, D, d->ln_eps))
+    return st;
+  if (dit_status st = fp8_weight_check(who, w_qkv, w_qkv_scales, b_qkv, D, 3 * D)) return st;
+  if (dit_status st = rope_check(DIT_BF16, q, D, k, D, pos_thw, n_tokens, H, Dh,
+                                 d->rope_sections, d->rope_theta))
+    return st;
+  if (dit_status st = attn_check(DIT_BF16, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs,
+                                 max_seqlen, n_tokens, H, Dh, d->softmax_scale))
+    return st;
+  if (dit_status st = fp8_weight_check(who, w_o, w_o_scales, b_o, D, D)) return st;
+  if (!aligned16(out)) return fail(DIT_EUNSUPPORTED, "%s: out must be 16-byte aligned", who);
+  if (n_tokens == 0) return DIT_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+  };
+  hipError_t e;
+  mark(0);
+  e = launch_adaln_fp8(1, x, D, modality, ada_table, codes, D, scales, n_tokens, D, d->ln_eps, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: adaln launch");
+  mark(1);
+  GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr, D, (int64_t)(plane_bytes / 2)};
+  e = launch_gemm_fp8(codes, D, scales, w_qkv, w_qkv_scales, q, D, n_tokens, 3 * D, D, ep_qkv, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: qkv launch");
+  mark(2);
+  double freq[64];
+  rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
+  e = launch_rope(1, q, D, k, D, qr, D, kr, D, pos_thw, n_tokens, H, Dh, d->rope_sections[0],
+                  d->rope_sections[1], freq, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: rope launch");
+  mark(3);
+  const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
+  e = launch_attn(1, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
+                  scale, d->causal != 0, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: attention launch");
+  mark(4);
+  e = launch_quant_rows_fp8(1, o, D, codes, D, scales, n_tokens, D, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: quantization launch");
+  GemmEpilogue ep_out{1, b_o, x, D, modality, ada_table + 2 * (size_t)D};
+  e = launch_gemm_fp8(codes, D, scales, w_o, w_o_scales, out, D, n_tokens, D, D, ep_out, s);
+  if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: out-proj launch");
   mark(5);
   return DIT_OK;
 }

@@ -46,11 +46,13 @@ __device__ __forceinline__ uint4 pack(const float* f, float) {
 // reduction, and when the R rows share one modality (the common case in a
 // pack, whose modalities come in long runs) each table vector is loaded once
 // for all of them, dividing the table's L2 traffic by R.
-template <typename T, int NV, int R>
+// Q8: instead of y, write its per-row e4m3 codes (q, row stride ld_y bytes)
+// and float32 scales (qs), scale = amax(|y|) / 448 of the float32 y.
+template <typename T, int NV, int R, bool Q8 = false>
 __global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
     const T* __restrict__ x, int64_t ld_x, const uint8_t* __restrict__ mod,
     const float* __restrict__ table, T* __restrict__ y, int64_t ld_y, int64_t n, int d,
-    float eps) {
+    float eps, uint8_t* __restrict__ q = nullptr, float* __restrict__ qs = nullptr) {
   constexpr int E = Vec<T>::N;
   const int lane = threadIdx.x & 63;
   const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float q = 0.0f;
+    float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       if (lane + 64 * i < nvec) {
@@ -93,11 +95,11 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float t = f[e] - mean[r];
-          q = fmaf(t, t, q);
+          ss = fmaf(t, t, ss);
         }
       }
     }
-    rstd[r] = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+    rstd[r] = 1.0f / sqrtf(wave_sum(ss) * inv_d + eps);
   }
 
   int m[R];
@@ -107,14 +109,12 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
     m[r] = row0 + r < n ? mod[row0 + r] : mod[row0];
     same = same && m[r] == m[0];
   }
-  // Writes row r's vector c given the table vectors of its modality.
-  auto emit = [&](int r, int i, const float* shv, const float* scv) {
-    const int c = lane + 64 * i;
-    float f[E], o[E];
+  // Modulated values of row r's vector i given the table vectors of its modality.
+  auto modulate = [&](int r, int i, const float* shv, const float* scv, float* o) {
+    float f[E];
     unpack(raw[r][i], f, T());
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = fmaf((f[e] - mean[r]) * rstd[r], 1.0f + scv[e], shv[e]);
-    st_stream(reinterpret_cast<uint4*>(y + (row0 + r) * ld_y) + c, pack(o, T()));
   };
   auto load_table = [&](int mm, int c, float* shv, float* scv) {
     const float4* shift = reinterpret_cast<const float4*>(table + (size_t)(3 * mm + 0) * d);
@@ -127,40 +127,91 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_kernel(
       scv[4 * e4 + 0] = sc.x; scv[4 * e4 + 1] = sc.y; scv[4 * e4 + 2] = sc.z; scv[4 * e4 + 3] = sc.w;
     }
   };
+  if constexpr (!Q8) {
+    // Writes row r's vector i given the table vectors of its modality.
+    auto emit = [&](int r, int i, const float* shv, const float* scv) {
+      float o[E];
+      modulate(r, i, shv, scv, o);
+      st_stream(reinterpret_cast<uint4*>(y + (row0 + r) * ld_y) + lane + 64 * i, pack(o, T()));
+    };
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= nvec) continue;
-    float shv[E], scv[E];
-    if (same) {
-      load_table(m[0], c, shv, scv);
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+      if (c >= nvec) continue;
+      float shv[E], scv[E];
+      if (same) {
+        load_table(m[0], c, shv, scv);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (row0 + r < n) emit(r, i, shv, scv);
-    } else {
+        for (int r = 0; r < R; ++r)
+          if (row0 + r < n) emit(r, i, shv, scv);
+      } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (row0 + r >= n) continue;
-        load_table(m[r], c, shv, scv);
-        emit(r, i, shv, scv);
+        for (int r = 0; r < R; ++r) {
+          if (row0 + r >= n) continue;
+          load_table(m[r], c, shv, scv);
+          emit(r, i, shv, scv);
+        }
       }
+    }
+  } else {
+    // FP8 output (one row per wave): the modulated row stays in registers
+    // while the wave reduces its amax, then leaves as codes of y * (1 / scale).
+    static_assert(!Q8 || R == 1, "the FP8 output takes one row per wave");
+    float yv[NV][E];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+#pragma unroll
+      for (int e = 0; e < E; ++e) yv[i][e] = 0.0f;
+      if (c >= nvec) continue;
+      float shv[E], scv[E];
+      load_table(m[0], c, shv, scv);
+      modulate(0, i, shv, scv, yv[i]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(yv[i][e]));
+    }
+    const float a = wave_max(amax);
+    const float sc = a > 0.0f ? a / 448.0f : 1.0f;
+    const float inv = 1.0f / sc;
+    if (lane == 0) qs[row0] = sc;
+    uint8_t* qrow = q + row0 * ld_y;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+      if (c >= nvec) continue;
+      uint32_t w[E / 4];
+#pragma unroll
+      for (int j = 0; j < E / 4; ++j)
+        w[j] = e4m3_pack4(yv[i][4 * j] * inv, yv[i][4 * j + 1] * inv, yv[i][4 * j + 2] * inv,
+                          yv[i][4 * j + 3] * inv);
+      if constexpr (E == 8)
+        *reinterpret_cast<uint2*>(qrow + c * E) = make_uint2(w[0], w[1]);
+      else
+        *reinterpret_cast<uint32_t*>(qrow + c * E) = w[0];
     }
   }
 }
 
-template <typename T>
+template <typename T, bool Q8>
 hipError_t dispatch(const void* x, int64_t ld_x, const uint8_t* mod, const float* table, void* y,
-                    int64_t ld_y, int64_t n, int d, float eps, hipStream_t s) {
+                    int64_t ld_y, int64_t n, int d, float eps, uint8_t* q, float* qs,
+                    hipStream_t s) {
   const int nvec = d / Vec<T>::N;
   const int need = (nvec + 63) / 64;
   const T* xp = static_cast<const T*>(x);
   T* yp = static_cast<T*>(y);
   // Rows per wave: enough to share table loads, few enough to keep the raw
   // rows (R * NV * 4 registers) in registers.
+  // The FP8 output keeps the modulated row in registers between its two
+  // passes: one row per wave keeps the register count (and occupancy) of the
+  // bf16 output's two rows.
 #define DIT_ADALN_CASE(NVV, RR)                                                                 \
   if (need <= NVV) {                                                                            \
-    const dim3 grid((unsigned)((n + kWaves * RR - 1) / (kWaves * RR))), block(64 * kWaves);     \
-    adaln_kernel<T, NVV, RR><<<grid, block, 0, s>>>(xp, ld_x, mod, table, yp, ld_y, n, d, eps); \
+    constexpr int RQ = Q8 ? 1 : RR;                                                             \
+    const dim3 grid((unsigned)((n + kWaves * RQ - 1) / (kWaves * RQ))), block(64 * kWaves);     \
+    adaln_kernel<T, NVV, RQ, Q8><<<grid, block, 0, s>>>(xp, ld_x, mod, table, yp, ld_y, n, d,   \
+                                                        eps, q, qs);                            \
     return hipGetLastError();                                                                   \
   }
   DIT_ADALN_CASE(1, 2) DIT_ADALN_CASE(2, 2) DIT_ADALN_CASE(3, 2) DIT_ADALN_CASE(4, 2)
@@ -176,8 +227,18 @@ hipError_t dispatch(const void* x, int64_t ld_x, const uint8_t* mod, const float
 hipError_t launch_adaln(int bf16, const void* x, int64_t ld_x, const uint8_t* mod,
                         const float* table, void* y, int64_t ld_y, int64_t n, int d, float eps,
                         hipStream_t s) {
-  return bf16 ? dispatch<uint16_t>(x, ld_x, mod, table, y, ld_y, n, d, eps, s)
-              : dispatch<float>(x, ld_x, mod, table, y, ld_y, n, d, eps, s);
+  return bf16 ? dispatch<uint16_t, false>(x, ld_x, mod, table, y, ld_y, n, d, eps, nullptr,
+                                         nullptr, s)
+              : dispatch<float, false>(x, ld_x, mod, table, y, ld_y, n, d, eps, nullptr, nullptr,
+                                       s);
+}
+
+hipError_t launch_adaln_fp8(int bf16, const void* x, int64_t ld_x, const uint8_t* mod,
+                            const float* table, uint8_t* q, int64_t ld_q, float* scales,
+                            int64_t n, int d, float eps, hipStream_t s) {
+  return bf16 ? dispatch<uint16_t, true>(x, ld_x, mod, table, nullptr, ld_q, n, d, eps, q, scales,
+                                         s)
+              : dispatch<float, true>(x, ld_x, mod, table, nullptr, ld_q, n, d, eps, q, scales, s);
 }
 
 }  // namespace dit

@@ -64,6 +64,26 @@ __device__ __forceinline__ float half_swap_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Four e4m3 codes of four float32 values in one word (value j in byte j):
+// nearest, ties to the even code (v_cvt_pk_fp8_f32, which rounds exactly so
+// for |v| <= 464: checked against the float64 oracle on every code, every
+// midpoint and its float32 neighbours and 2e5 random values), saturating at
+// +-448 (the conversion gives NaN beyond 464, so values are clamped first),
+// NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_pack4(float f0, float f1, float f2, float f3) {
+  auto clamp = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f0), clamp(f1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f2), clamp(f3), w, true);
+  uint32_t u = (uint32_t)w;
+  if (__builtin_isnan(f0) | __builtin_isnan(f1) | __builtin_isnan(f2) | __builtin_isnan(f3)) {
+    if (__builtin_isnan(f0)) u = (u & 0xffffff00u) | 0x7fu;
+    if (__builtin_isnan(f1)) u = (u & 0xffff00ffu) | 0x7f00u;
+    if (__builtin_isnan(f2)) u = (u & 0xff00ffffu) | 0x7f0000u;
+    if (__builtin_isnan(f3)) u = (u & 0x00ffffffu) | 0x7f000000u;
+  }
+  return u;
+}
+
 }  // namespace dit
 
 // Launchers implemented in the .hip files; all return hipGetLastError() of the launch.
@@ -112,6 +132,10 @@ hipError_t launch_gemm_fp8(const uint8_t* a, int64_t lda, const float* sa, const
                            const float* sw, void* c, int64_t ldc, int64_t m, int n, int k,
                            const GemmEpilogue& ep, hipStream_t s);
 // Per-row e4m3 quantization of bf16 (or float32) rows: codes [n][ld_q], scales [n].
+// launch_adaln_fp8: AdaLN whose output is written as such codes and scales.
+hipError_t launch_adaln_fp8(int bf16, const void* x, int64_t ld_x, const uint8_t* mod,
+                            const float* table, uint8_t* q, int64_t ld_q, float* scales,
+                            int64_t n, int d, float eps, hipStream_t s);
 hipError_t launch_quant_rows_fp8(int bf16, const void* x, int64_t ld_x, uint8_t* q, int64_t ld_q,
                                  float* scales, int64_t n, int d, hipStream_t s);
 

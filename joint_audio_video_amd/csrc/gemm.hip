@@ -427,26 +427,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
   }
 }
 
-// Four e4m3 codes of four float32 values in one word (value j in byte j):
-// nearest, ties to the even code (v_cvt_pk_fp8_f32, which rounds exactly so
-// for |v| <= 464: checked against the float64 oracle on every code, every
-// midpoint and its float32 neighbours and 2e5 random values), saturating at
-// +-448 (the conversion gives NaN beyond 464, so values are clamped first),
-// NaN -> 0x7F.
-__device__ __forceinline__ uint32_t e4m3_pack4(float f0, float f1, float f2, float f3) {
-  auto clamp = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f0), clamp(f1), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f2), clamp(f3), w, true);
-  uint32_t u = (uint32_t)w;
-  if (__builtin_isnan(f0) | __builtin_isnan(f1) | __builtin_isnan(f2) | __builtin_isnan(f3)) {
-    if (__builtin_isnan(f0)) u = (u & 0xffffff00u) | 0x7fu;
-    if (__builtin_isnan(f1)) u = (u & 0xffff00ffu) | 0x7f00u;
-    if (__builtin_isnan(f2)) u = (u & 0xff00ffffu) | 0x7f0000u;
-    if (__builtin_isnan(f3)) u = (u & 0x00ffffffu) | 0x7f000000u;
-  }
-  return u;
-}
-
 // Per-row quantization: one wave per row, the row held in registers (NV
 // 16-byte vectors per lane), scale = amax / 448 and inv = 1 / scale (IEEE
 // divisions, once per row), codes of x * inv (one float32 product per value),

@@ -20,10 +20,19 @@ layers in FP8; the pages give no scaling recipe.  Readings:
   quantization pass).
 * A projection C = (dequant(A) dequant(B)^T) with dequant(q) = decode(q) *
   scale of its row, evaluated here in float64.
+* The FP8 block: the attention half and the feed-forward half of the block
+  with every projection in FP8.  The operand of each projection (the AdaLN
+  output, the attention output, the activated hidden state) is quantized per
+  row from its float32 value; rotary embedding, attention, the activation
+  and the gated residual stay in the plain oracle's float64 arithmetic.
 """
 from __future__ import annotations
 
+from typing import Dict, Optional, Sequence
+
 import numpy as np
+
+from .block import (adaln_modulate, attention, ffn_up, out_proj_gated, qkv_project, rope3d)
 
 E4M3_MAX = 448.0
 E4M3_NAN = 0x7F
@@ -118,3 +127,58 @@ def linear_fp8(a_codes, a_scales, w_codes, w_scales, bias=None) -> np.ndarray:
     if bias is not None:
         c = c + np.asarray(bias, np.float64)[None, :]
     return c
+
+
+# ---------------------------------------------------------------------------
+# FP8 block
+# ---------------------------------------------------------------------------
+
+def adaln_modulate_fp8(x, modality, table, eps: float = 1e-6, rows=None):
+    """AdaLN (oracle.block.adaln_modulate) quantized per row: (codes, scales)
+    of the float32 value of its output."""
+    return quantize_rows(adaln_modulate(x, modality, table, eps, rows=rows))
+
+
+def block_forward_fp8(x, modality, pos, cu_seqlens, table, wq_codes, wq_scales, wo_codes,
+                      wo_scales, *, n_heads: int, head_dim: int, sections: Sequence[int],
+                      theta: float = 10000.0, eps: float = 1e-6, causal: bool = False,
+                      scale: Optional[float] = None, b_qkv=None, b_o=None,
+                      rows=None) -> Dict[str, np.ndarray]:
+    """The attention half of the block (oracle.block.block_forward) with both
+    projections in FP8: the AdaLN output and the attention output are
+    quantized per row, W_qkv [3D][D] and W_o [D][D] are given as per-row codes
+    and scales.  Returns y_codes, y_scales, q, k, v, o, o_codes, o_scales and
+    out (float64); with ``rows``, o, its codes and out hold those rows only.
+    """
+    x = np.asarray(x)
+    n, d = x.shape
+    yc, ys = adaln_modulate_fp8(x, modality, table, eps)
+    y = dequantize_rows(yc, ys)
+    w = dequantize_rows(wq_codes, wq_scales)
+    bias = [None] * 3 if b_qkv is None else [np.asarray(b_qkv)[i * d:(i + 1) * d] for i in range(3)]
+    k = qkv_project(y, w[d:2 * d], bias[1])
+    v = qkv_project(y, w[2 * d:], bias[2])
+    k_rot = rope3d(k, pos, n_heads, head_dim, sections, theta)
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = np.zeros((n, d))
+    q[idx] = qkv_project(y[idx], w[:d], bias[0])
+    q_rot = np.zeros((n, d))
+    q_rot[idx] = rope3d(q[idx], np.asarray(pos)[idx], n_heads, head_dim, sections, theta)
+    o = attention(q_rot, k_rot, v, cu_seqlens, n_heads, head_dim, causal, scale, rows)
+    oc, os_ = quantize_rows(o)
+    out = out_proj_gated(dequantize_rows(oc, os_), dequantize_rows(wo_codes, wo_scales), x,
+                         modality, table, b_o, rows)
+    return dict(y_codes=yc, y_scales=ys, q=q, k=k, v=v, o=o, o_codes=oc, o_scales=os_, out=out)
+
+
+def ffn_forward_fp8(x, modality, table_mlp, w1_codes, w1_scales, w2_codes, w2_scales,
+                    b1=None, b2=None, eps: float = 1e-6, rows=None) -> Dict[str, np.ndarray]:
+    """The feed-forward half (oracle.block.ffn_forward) with both projections
+    in FP8: the AdaLN output and the activated hidden state h are quantized
+    per row.  Returns y_codes, y_scales, h, h_codes, h_scales and out."""
+    yc, ys = adaln_modulate_fp8(x, modality, table_mlp, eps, rows=rows)
+    h = ffn_up(dequantize_rows(yc, ys), dequantize_rows(w1_codes, w1_scales), b1)
+    hc, hs = quantize_rows(h)
+    out = out_proj_gated(dequantize_rows(hc, hs), dequantize_rows(w2_codes, w2_scales), x,
+                         modality, table_mlp, b2, rows=rows)
+    return dict(y_codes=yc, y_scales=ys, h=h, h_codes=hc, h_scales=hs, out=out)

@@ -270,3 +270,55 @@ def test_rope3d_apply_to_overlap_rules():
     assert call(q, k, fake + 128 * row, fake + 160 * row, n=0) == jav.DIT_OK
     assert call(q, k, q, k, n=0) == jav.DIT_OK
     assert call(q, k, fake + 128 * row, q, n=0) == jav.DIT_OK
+
+
+def test_fp8_block_halves_validate_before_enqueue():
+    fake = 1 << 24            # never dereferenced: validation fails first
+    B, F32 = jav.DIT_BF16, jav.DIT_F32
+    # adaln_modulate_fp8(dt, x, ld_x, mod, table, q, ld_q, scales, n, d, eps, stream)
+    assert _call("adaln_modulate_fp8", B, fake, 5120, fake, fake, None, 5120, fake, 10, 5120, 1e-6, None) == jav.DIT_EINVAL
+    assert _call("adaln_modulate_fp8", B, fake, 5120, fake, fake, fake, 5000, fake, 10, 5120, 1e-6, None) == jav.DIT_EINVAL
+    assert _call("adaln_modulate_fp8", B, fake, 5120, fake, fake, fake, 5128, fake, 10, 5120, 1e-6, None) == jav.DIT_EUNSUPPORTED
+    assert _call("adaln_modulate_fp8", B, fake, 5120, fake, fake, fake, 5120, fake + 4, 10, 5120, 1e-6, None) == jav.DIT_EUNSUPPORTED
+    assert "adaln_modulate_fp8" in jav.last_error()
+    assert _call("adaln_modulate_fp8", F32, fake, 256, fake, fake, fake, 256, fake, 0, 256, 1e-6, None) == jav.DIT_OK
+
+    desc = jav.block_desc(B, 5120, 40, 128, (32, 48, 48))
+    n = 58758
+    plane = ((n * 5120 * 2 + 255) // 256) * 256
+    assert jav.block_fp8_workspace_bytes(desc, n) == 5 * plane + ((n * 4 + 255) // 256) * 256
+    assert jav.block_fp8_workspace_bytes(jav.block_desc(F32, 256, 4, 64, (16, 24, 24)), 10) == 0
+    # (desc, x, out, mod, pos, cu, n_seqs, max_seqlen, n, table, wq, wqs, bq, wo, wos, bo, ws, bytes, s)
+    args = [fake, fake, fake, fake, fake, 1, 100, 100, fake, fake, fake, None, fake, fake, None]
+    st = jav._lib.dit_block_forward_fp8(ctypes.byref(desc), *args, fake, 10, None)
+    assert st == jav.DIT_EWORKSPACE
+    f32 = jav.block_desc(F32, 256, 4, 64, (16, 24, 24))
+    st = jav._lib.dit_block_forward_fp8(ctypes.byref(f32), *args, fake, 1 << 40, None)
+    assert st == jav.DIT_EUNSUPPORTED            # bf16 activations only
+    a2 = list(args)
+    a2[10] = fake + 8                            # w_qkv scales misaligned
+    st = jav._lib.dit_block_forward_fp8(ctypes.byref(desc), *a2, fake, 1 << 40, None)
+    assert st == jav.DIT_EUNSUPPORTED
+    a2 = list(args)
+    a2[9] = None                                 # no w_qkv
+    st = jav._lib.dit_block_forward_fp8(ctypes.byref(desc), *a2, fake, 1 << 40, None)
+    assert st == jav.DIT_EINVAL
+    odd = jav.block_desc(B, 192, 3, 64, (16, 24, 24))   # d_model not a multiple of 128
+    st = jav._lib.dit_block_forward_fp8(ctypes.byref(odd), *args, fake, 1 << 40, None)
+    assert st == jav.DIT_EUNSUPPORTED
+    st = jav._lib.dit_block_forward_fp8(ctypes.byref(desc), *args[:7], 0, *args[8:], fake,
+                                        1 << 40, None)
+    assert st == jav.DIT_OK                      # no rows: nothing enqueued
+
+    fdesc = jav.ffn_desc(B, 5120, 20480)
+    want = (((n * 20480 + 255) // 256) * 256 + ((n * 20480 * 2 + 255) // 256) * 256
+            + ((n * 4 + 255) // 256) * 256)
+    assert jav.ffn_fp8_workspace_bytes(fdesc, n) == want
+    # (desc, x, out, mod, n, table, w1, w1s, b1, w2, w2s, b2, ws, bytes, s)
+    fargs = [fake, fake, fake, 100, fake, fake, fake, None, fake, fake, None]
+    assert jav._lib.dit_ffn_forward_fp8(ctypes.byref(fdesc), *fargs, fake, 10, None) == jav.DIT_EWORKSPACE
+    wide = jav.ffn_desc(B, 5120, 20480 + 128)
+    assert jav._lib.dit_ffn_forward_fp8(ctypes.byref(wide), *fargs, fake, 1 << 40, None) == jav.DIT_EUNSUPPORTED
+    narrow = jav.ffn_desc(B, 5120, 20480 - 64)
+    assert jav._lib.dit_ffn_forward_fp8(ctypes.byref(narrow), *fargs, fake, 1 << 40, None) == jav.DIT_EUNSUPPORTED
+    assert jav.ffn_fp8_workspace_bytes(jav.ffn_desc(F32, 256, 1024), 10) == 0

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check, dev, dev_f32, dev_int, host, sample_rows
+from gpu_util import check, dev, dev_f32, dev_int, host, rel_l2, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +136,278 @@ def test_fp8_projection_error_against_bf16(jav):
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     print(f"  fp8 vs exact bf16 product: rel_l2={rel:.3e}", flush=True)
     assert rel <= 5e-2
+
+
+# ---------------------------------------------------------------------------
+# FP8 block halves
+# ---------------------------------------------------------------------------
+
+def _round256(b):
+    return (b + 255) // 256 * 256
+
+
+def _spacing(v):
+    """e4m3 spacing at |v| (code units, before scaling)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6)))
+    return 2.0 ** (e - 3)
+
+
+def _check_codes(got, ref, what, max_frac):
+    """Codes equal, except where the two sides' float32 values straddle a rounding
+    boundary: there the codes must be neighbours (one e4m3 step apart)."""
+    tab = oracle.e4m3_table()
+    got = np.asarray(got, np.uint8)
+    ref = np.asarray(ref, np.uint8)
+    bad = got != ref
+    frac = float(bad.mean()) if bad.size else 0.0
+    print(f"  {what}: code mismatches {frac:.2e}", flush=True)
+    if bad.any():
+        vg, vr = tab[got[bad]], tab[ref[bad]]
+        assert np.all(np.isfinite(vg))
+        assert np.all(np.abs(vg - vr) <= _spacing(np.maximum(np.abs(vg), np.abs(vr))) * (1 + 1e-9))
+    assert frac <= max_frac, (what, frac)
+
+
+# Output tolerance of an FP8 half against the oracle's FP8 half: the two sides
+# quantize intermediates (o, h) that differ by their bf16 error, so about 2% of
+# the codes sit one e4m3 step (2^-3 relative) apart.  Over K = 20480 operands
+# that gives the branch an RMS error of sqrt(0.02 K) 2^-3 rms(h) rms(w) ~ 0.05,
+# times |gate| <= 0.4 and 4.5 sigma over the sampled outputs: max-abs 0.1.  The
+# rel-L2 bound stays the bf16 one.
+FP8_HALF_MAX_ABS = 1e-1
+
+
+def _check_fp8_out(got, ref, what):
+    r = rel_l2(got, ref)
+    m = float(np.max(np.abs(np.asarray(got) - np.asarray(ref))))
+    print(f"  {what}: rel_l2={r:.3e} max_abs={m:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert r <= 1e-2 and m <= FP8_HALF_MAX_ABS, (what, r, m)
+
+
+def _check_quantized(codes, scales, vals, ref_codes, what, max_frac):
+    """Codes and scales the library wrote for its own bf16 values: each scale is the
+    row's float32 amax / 448 and each code a nearest rounding of value / scale (within
+    half an e4m3 step).  Against the oracle's codes of its float64 values, only the
+    fraction that differs is bounded: the two sides round values that differ by the
+    bf16 error of the attention (or projection) output, often across a rounding
+    boundary near zero, where the e4m3 steps are finest."""
+    tab = oracle.e4m3_table()
+    vals = np.asarray(vals, np.float32)
+    amax = np.abs(vals).max(axis=1)
+    want = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+    np.testing.assert_array_equal(scales, want)
+    s = scales.astype(np.float64)[:, None]
+    u = vals.astype(np.float64) / s
+    assert np.all(np.abs(tab[codes] - u) <= 0.5 * _spacing(u) * (1 + 1e-6) + 1e-12), what
+    frac = float(np.mean(codes != ref_codes))
+    print(f"  {what}: codes differing from the oracle's {frac:.2e}", flush=True)
+    assert frac <= max_frac, (what, frac)
+
+
+def _fp8_layout(jav, name, n=None, cu=None):
+    """Device and oracle layouts of a workload, optionally cut to the first n rows with
+    the segment offsets cu."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    grids = [r.grid for r in wl.requests]
+    lay_d = jav.pack_layout(grids)
+    lay = oracle.pack_layout(grids)
+    n = wl.n_tokens if n is None else n
+    cu = list(lay["cu_seqlens"]) if cu is None else list(cu)
+    mod, pos = np.asarray(lay["modality"])[:n], np.asarray(lay["pos"])[:n]
+    dev_lay = (dev_int(np.asarray(lay_d["modality"])[:n], torch.uint8),
+               dev_int(np.asarray(lay_d["pos"])[:n], torch.int32),
+               dev_int(np.asarray(cu), torch.int32), int(max(b - a for a, b in zip(cu, cu[1:]))))
+    return mod, pos, cu, dev_lay
+
+
+@pytest.mark.parametrize("name,n", [("tiny", None), ("small", 1000), ("full", None)])
+def test_adaln_fp8_codes_and_scales(jav, name, n):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, n_tokens=n)
+    mod, _, _, (mod_d, _, _, _) = _fp8_layout(jav, name, n=inp.x.shape[0],
+                                              cu=[0, inp.x.shape[0]])
+    print(f"adaln_fp8 {name} n={inp.x.shape[0]}", flush=True)
+    codes, scales = jav.adaln_modulate_fp8(dev(inp.x, wl.dtype), mod_d, dev_f32(inp.table),
+                                           eps=wl.eps)
+    _sync()
+    rows = None if inp.x.shape[0] <= 4096 else sample_rows([0, inp.x.shape[0]], inp.x.shape[0],
+                                                           limit=3000)
+    ref_c, ref_s = oracle.adaln_modulate_fp8(inp.x, mod, inp.table, wl.eps, rows=rows)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    if rows is not None:
+        got_c, got_s = got_c[rows], got_s[rows]
+    np.testing.assert_allclose(got_s, ref_s, rtol=1e-5)
+    _check_codes(got_c, ref_c, f"adaln_fp8[{name}]", 1e-3)
+
+
+def _block_fp8(jav, name, n=None, cu=None, rows=None, with_bias=False, causal=False,
+               inplace=False):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, n_tokens=n, with_bias=with_bias)
+    n = inp.x.shape[0]
+    mod, pos, cu, (mod_d, pos_d, cu_d, ms) = _fp8_layout(jav, name, n=n, cu=cu)
+    wq = oracle.quantize_rows(inp.w_qkv)
+    wo = oracle.quantize_rows(inp.w_o)
+    desc = jav.block_desc(jav.DIT_BF16, wl.d_model, wl.n_heads, wl.head_dim, wl.sections,
+                          wl.theta, wl.eps, causal=causal)
+    ws = torch.empty(jav.block_fp8_workspace_bytes(desc, n), dtype=torch.uint8, device="cuda")
+    print(f"block_fp8 {name} n={n} segs={len(cu) - 1} bias={with_bias} causal={causal} "
+          f"inplace={inplace}", flush=True)
+    x = dev(inp.x, "bf16")
+    out = jav.block_forward_fp8(desc, x, mod_d, pos_d, cu_d, ms, dev_f32(inp.table),
+                                _codes_dev(wq[0]), dev_f32(wq[1]), _codes_dev(wo[0]),
+                                dev_f32(wo[1]),
+                                b_qkv=dev(inp.b_qkv, "bf16") if with_bias else None,
+                                b_o=dev(inp.b_o, "bf16") if with_bias else None,
+                                out=x if inplace else None, workspace=ws)
+    _sync()
+    ref = oracle.block_forward_fp8(inp.x, mod, pos, cu, inp.table, *wq, *wo, n_heads=wl.n_heads,
+                                   head_dim=wl.head_dim, sections=wl.sections, theta=wl.theta,
+                                   eps=wl.eps, causal=causal,
+                                   b_qkv=inp.b_qkv if with_bias else None,
+                                   b_o=inp.b_o if with_bias else None, rows=rows)
+    idx = np.arange(n) if rows is None else rows
+    d = wl.d_model
+    plane = _round256(n * d * 2)
+    # after the call the workspace holds o (plane 4), o's codes (plane 0) and o's scales
+    o = ws[4 * plane:4 * plane + n * d * 2].view(torch.bfloat16).view(n, d)
+    o_codes = ws[:n * d].view(n, d).cpu().numpy()[idx]
+    o_scales = ws[5 * plane:5 * plane + 4 * n].view(torch.float32).cpu().numpy()[idx]
+    o_h = host(o)[idx]
+    check(o_h, ref["o"], "bf16", f"block_fp8[{name}].o")
+    np.testing.assert_allclose(o_scales, ref["o_scales"], rtol=1e-2)
+    _check_quantized(o_codes, o_scales, o_h, ref["o_codes"], f"block_fp8[{name}].o_codes", 0.1)
+    _check_fp8_out(host(out)[idx], ref["out"], f"block_fp8[{name}].out")
+    return out
+
+
+def test_block_fp8_small(jav):
+    _block_fp8(jav, "small")
+
+
+def test_block_fp8_ragged_segments_bias_causal_inplace(jav):
+    _block_fp8(jav, "small", n=1000, cu=[0, 617, 1000], with_bias=True, causal=True,
+               inplace=True)
+
+
+def _weights(f, k, seed):
+    """Weight codes and scales of a per-row quantization of N(0, 0.02^2) rows."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    return _codes((f, k), seed), (rng.uniform(0.95, 1.05, f) * 0.02 * 4.5 / 448).astype(np.float32)
+
+
+def test_block_fp8_full_shape_equals_its_stages(jav):
+    """At the full shape (a 3 GB workspace) the fused entry point gives bit for bit
+    what its stages give when called one by one on separate buffers; each stage
+    has its own full-shape parity test against the oracle.  (The oracle needs
+    every row's keys and values for one query, minutes of float64 work here.)"""
+    import torch
+    wl = synth.WORKLOADS["full"]
+    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
+    _, _, cu, (mod_d, pos_d, cu_d, ms) = _fp8_layout(jav, "full")
+    print(f"block_fp8 full n={n}: fused vs stages", flush=True)
+    x = dev(synth.normal_array((n, d), seed=900, dtype="bf16"), "bf16")
+    table = dev_f32(synth.normal_array((3, 3, d), seed=901, std=0.1))
+    wqc, wqs = _weights(3 * d, d, 902)
+    woc, wos = _weights(d, d, 903)
+    b_qkv = dev(synth.normal_array((3 * d,), seed=904, std=0.02, dtype="bf16"), "bf16")
+    b_o = dev(synth.normal_array((d,), seed=905, std=0.02, dtype="bf16"), "bf16")
+    wqc, wqs, woc, wos = _codes_dev(wqc), dev_f32(wqs), _codes_dev(woc), dev_f32(wos)
+    desc = jav.block_desc(jav.DIT_BF16, d, H, Dh, wl.sections, wl.theta, wl.eps)
+    fused = jav.block_forward_fp8(desc, x, mod_d, pos_d, cu_d, ms, table, wqc, wqs, woc, wos,
+                                  b_qkv=b_qkv, b_o=b_o)
+    _sync()
+    yc, ys = jav.adaln_modulate_fp8(x, mod_d, table, eps=wl.eps)
+    qkv = jav.linear_fp8(yc, ys, wqc, wqs, bias=b_qkv)
+    q_r = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    k_r = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    jav.rope3d_apply_to(qkv[:, :d], qkv[:, d:2 * d], q_r, k_r, pos_d, H, Dh, wl.sections,
+                        wl.theta)
+    o = jav.attn_packed(q_r, k_r, qkv[:, 2 * d:], cu_d, ms, H, Dh)
+    oc, os_ = jav.quantize_rows_fp8(o)
+    staged = jav.linear_fp8(oc, os_, woc, wos, bias=b_o, epilogue="gated", x=x, modality=mod_d,
+                            table=table)
+    _sync()
+    assert torch.isfinite(fused.float()).all()
+    assert torch.equal(fused, staged)
+
+
+def _ffn_fp8(jav, name, n=None, rows=None, with_bias=False, pool_weights=False):
+    import torch
+    wl = synth.WORKLOADS[name]
+    f = synth.ffn_inputs(wl, with_bias=with_bias)
+    x_h = synth.normal_array((wl.n_tokens, wl.d_model), seed=500 + wl.seed, dtype=wl.dtype)
+    if n is not None:
+        x_h = x_h[:n]
+    n = x_h.shape[0]
+    mod, _, _, (mod_d, _, _, _) = _fp8_layout(jav, name, n=n, cu=[0, n])
+    if pool_weights:
+        w1, w2 = _weights(wl.d_ff, wl.d_model, 906), _weights(wl.d_model, wl.d_ff, 907)
+    else:
+        w1, w2 = oracle.quantize_rows(f.w1), oracle.quantize_rows(f.w2)
+    desc = jav.ffn_desc(jav.DIT_BF16, wl.d_model, wl.d_ff, wl.eps)
+    ws = torch.empty(jav.ffn_fp8_workspace_bytes(desc, n), dtype=torch.uint8, device="cuda")
+    print(f"ffn_fp8 {name} n={n} bias={with_bias}", flush=True)
+    out = jav.ffn_forward_fp8(desc, dev(x_h, "bf16"), mod_d, dev_f32(f.table), _codes_dev(w1[0]),
+                              dev_f32(w1[1]), _codes_dev(w2[0]), dev_f32(w2[1]),
+                              b1=dev(f.b1, "bf16") if with_bias else None,
+                              b2=dev(f.b2, "bf16") if with_bias else None, workspace=ws)
+    _sync()
+    ref = oracle.ffn_forward_fp8(x_h, mod, f.table, *w1, *w2, b1=f.b1 if with_bias else None,
+                                 b2=f.b2 if with_bias else None, eps=wl.eps, rows=rows)
+    idx = np.arange(n) if rows is None else rows
+    F = wl.d_ff
+    c0 = _round256(n * max(F, wl.d_model))
+    # after the call the workspace holds h's codes, h and h's scales
+    h = ws[c0:c0 + n * F * 2].view(torch.bfloat16).view(n, F)
+    h_h = host(h)[idx]
+    check(h_h, ref["h"], "bf16", f"ffn_fp8[{name}].h")
+    sc0 = c0 + _round256(n * F * 2)
+    h_scales = ws[sc0:sc0 + 4 * n].view(torch.float32).cpu().numpy()[idx]
+    np.testing.assert_allclose(h_scales, ref["h_scales"], rtol=1e-2)
+    _check_quantized(ws[:n * F].view(n, F).cpu().numpy()[idx], h_scales, h_h, ref["h_codes"],
+                     f"ffn_fp8[{name}].h_codes", 0.1)
+    _check_fp8_out(host(out)[idx], ref["out"], f"ffn_fp8[{name}].out")
+
+
+def test_ffn_fp8_small_ragged_bias(jav):
+    _ffn_fp8(jav, "small", n=1000, with_bias=True)
+
+
+def test_ffn_fp8_full_shape_sampled(jav):
+    """The half is row-local, so sampled rows of the oracle are cheap; the weights
+    come as codes of a per-row quantization drawn from a pool (3e8 codes)."""
+    wl = synth.WORKLOADS["full"]
+    _ffn_fp8(jav, "full", rows=sample_rows([0, wl.n_tokens], wl.n_tokens, limit=200),
+             pool_weights=True)
+
+
+def test_ffn_fp8_equals_its_stages(jav):
+    """The fused feed-forward half gives bit for bit what its stages give when called
+    one by one (ragged rows, biases)."""
+    import torch
+    wl = synth.WORKLOADS["small"]
+    n, d, F = 1000, wl.d_model, wl.d_ff
+    f = synth.ffn_inputs(wl, with_bias=True)
+    _, _, _, (mod_d, _, _, _) = _fp8_layout(jav, "small", n=n, cu=[0, n])
+    print(f"ffn_fp8 small n={n}: fused vs stages", flush=True)
+    x = dev(synth.normal_array((n, d), seed=910, dtype="bf16"), "bf16")
+    table = dev_f32(f.table)
+    w1c, w1s = oracle.quantize_rows(f.w1)
+    w2c, w2s = oracle.quantize_rows(f.w2)
+    w1c, w1s, w2c, w2s = _codes_dev(w1c), dev_f32(w1s), _codes_dev(w2c), dev_f32(w2s)
+    b1, b2 = dev(f.b1, "bf16"), dev(f.b2, "bf16")
+    desc = jav.ffn_desc(jav.DIT_BF16, d, F, wl.eps)
+    fused = jav.ffn_forward_fp8(desc, x, mod_d, table, w1c, w1s, w2c, w2s, b1=b1, b2=b2)
+    yc, ys = jav.adaln_modulate_fp8(x, mod_d, table, eps=wl.eps)
+    h = jav.linear_fp8(yc, ys, w1c, w1s, bias=b1, epilogue="gelu")
+    hc, hs = jav.quantize_rows_fp8(h)
+    staged = jav.linear_fp8(hc, hs, w2c, w2s, bias=b2, epilogue="gated", x=x, modality=mod_d,
+                            table=table)
+    _sync()
+    assert torch.isfinite(fused.float()).all()
+    assert torch.equal(fused, staged)

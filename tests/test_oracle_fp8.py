@@ -105,3 +105,134 @@ def test_exactly_representable_inputs_give_an_exact_product():
     b = rng.standard_normal(7)
     np.testing.assert_allclose(oracle.linear_fp8(ac, asc, wc, wsc, b), a @ w.T + b, rtol=1e-13,
                                atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# FP8 block halves
+# ---------------------------------------------------------------------------
+
+def _e4m3_grid_rows(rng, shape, top):
+    """Rows of e4m3 values times 2^-6 whose largest magnitude is ``top`` = 448 * 2^-6
+    (so the per-row scale is exactly 2^-6 and quantization is lossless)."""
+    tab = oracle.e4m3_table()
+    fin = tab[np.isfinite(tab) & (np.abs(tab) <= 448)]
+    a = rng.choice(fin, size=shape) * 2.0 ** -6
+    a[..., 0] = top
+    return a
+
+
+def _half_steps(v, s):
+    """Half the e4m3 spacing at each |v| / s (per-row scale s), times s: the largest
+    error of a nearest rounding of an unsaturated value."""
+    u = np.abs(v) / s[:, None]
+    e = np.floor(np.log2(np.maximum(u, 2.0 ** -6)))
+    return s[:, None] * 2.0 ** (e - 4)
+
+
+def _lossless_block(seed, d=16, h=2, n=12, with_bias=True):
+    """Inputs whose AdaLN output is exactly representable: unit-free modulation
+    (scale row -1, so y = shift[m]) with shift rows on the e4m3 grid."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((n, d))
+    table = rng.standard_normal((3, 3, d)) * 0.3
+    table[:, 1, :] = -1.0
+    table[:, 0, :] = _e4m3_grid_rows(rng, (3, d), 7.0)
+    mod = rng.integers(0, 3, n)
+    pos = rng.integers(0, 9, (n, 3))
+    wq = oracle.quantize_rows(rng.standard_normal((3 * d, d)) * 0.3)
+    wo = oracle.quantize_rows(rng.standard_normal((d, d)) * 0.3)
+    b_qkv = rng.standard_normal(3 * d) * 0.1 if with_bias else None
+    b_o = rng.standard_normal(d) * 0.1 if with_bias else None
+    return x, table, mod, pos, wq, wo, b_qkv, b_o
+
+
+def test_fp8_adaln_of_a_grid_shift_is_exact():
+    """y = shift[m] on the e4m3 grid: the codes are the shift's own codes, the scale 2^-6."""
+    x, table, mod, _, _, _, _, _ = _lossless_block(71)
+    codes, s = oracle.adaln_modulate_fp8(x, mod, table)
+    np.testing.assert_array_equal(s, np.full(x.shape[0], 2.0 ** -6, np.float32))
+    np.testing.assert_array_equal(codes, oracle.e4m3_encode(table[mod, 0, :] * 64.0))
+    np.testing.assert_array_equal(oracle.dequantize_rows(codes, s), table[mod, 0, :])
+
+
+def test_fp8_adaln_codes_are_within_half_a_step_of_the_modulated_rows():
+    rng = np.random.Generator(np.random.PCG64(72))
+    x = rng.standard_normal((40, 64)) * 3 + 1
+    table = rng.standard_normal((3, 3, 64)) * 0.2
+    mod = rng.integers(0, 3, 40)
+    y = oracle.adaln_modulate(x, mod, table)
+    codes, s = oracle.adaln_modulate_fp8(x, mod, table)
+    np.testing.assert_array_equal(s, (np.abs(y.astype(np.float32)).max(1) / np.float32(448)))
+    err = np.abs(oracle.dequantize_rows(codes, s) - y)
+    assert np.all(err <= _half_steps(y, s.astype(np.float64)) * (1 + 1e-6) + 1e-12)
+    big = np.abs(y).argmax(1)
+    assert np.all(oracle.e4m3_table()[codes[np.arange(40), big] & 0x7F] == 448.0)
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_fp8_block_with_a_lossless_adaln_output_matches_the_plain_block(with_bias):
+    """With y exactly representable, q, k, v and o equal the plain oracle's with the
+    dequantized weights, and out differs from it only by the rounding of o, which is
+    bounded by half an e4m3 step per element of o."""
+    x, table, mod, pos, wq, wo, b_qkv, b_o = _lossless_block(73, with_bias=with_bias)
+    kw = dict(n_heads=2, head_dim=8, sections=(2, 2, 4), theta=100.0)
+    cu = [0, 5, 12]
+    f8 = oracle.block_forward_fp8(x, mod, pos, cu, table, *wq, *wo, b_qkv=b_qkv, b_o=b_o, **kw)
+    w_qkv, w_o = oracle.dequantize_rows(*wq), oracle.dequantize_rows(*wo)
+    ref = oracle.block_forward(x, mod, pos, cu, table, w_qkv, w_o, b_qkv=b_qkv, b_o=b_o, **kw)
+    for key in ("q", "k", "v", "o"):
+        np.testing.assert_allclose(f8[key], ref[key], rtol=1e-12, atol=1e-12)
+    o = ref["o"]
+    s = oracle.row_scales(o).astype(np.float64)
+    bound = np.abs(table[mod, 2, :]) * (_half_steps(o, s) @ np.abs(w_o).T)
+    diff = np.abs(f8["out"] - ref["out"])
+    assert np.all(diff <= bound * (1 + 1e-6) + 1e-12)
+    assert diff.max() > 0                     # o is not on the grid: its rounding shows
+
+
+def test_fp8_ffn_with_a_lossless_adaln_output_matches_the_plain_half():
+    x, table, mod, _, _, _, _, _ = _lossless_block(74, d=32, n=20)
+    rng = np.random.Generator(np.random.PCG64(75))
+    w1 = oracle.quantize_rows(rng.standard_normal((128, 32)) * 0.3)
+    w2 = oracle.quantize_rows(rng.standard_normal((32, 128)) * 0.3)
+    b1, b2 = rng.standard_normal(128) * 0.1, rng.standard_normal(32) * 0.1
+    f8 = oracle.ffn_forward_fp8(x, mod, table, *w1, *w2, b1=b1, b2=b2)
+    W1, W2 = oracle.dequantize_rows(*w1), oracle.dequantize_rows(*w2)
+    y = oracle.adaln_modulate(x, mod, table)
+    h = oracle.ffn_up(y, W1, b1)
+    np.testing.assert_array_equal(f8["h"], h)
+    ref = oracle.ffn_forward(x, mod, table, W1, W2, b1, b2)
+    s = oracle.row_scales(h).astype(np.float64)
+    bound = np.abs(table[mod, 2, :]) * (_half_steps(h, s) @ np.abs(W2).T)
+    diff = np.abs(f8["out"] - ref)
+    assert np.all(diff <= bound * (1 + 1e-6) + 1e-12) and diff.max() > 0
+
+
+def test_fp8_block_rows_subset_matches_every_row():
+    x, table, mod, pos, wq, wo, b_qkv, b_o = _lossless_block(76)
+    table[:, 1, :] = 0.1                      # a general (lossy) modulation
+    kw = dict(n_heads=2, head_dim=8, sections=(2, 2, 4), b_qkv=b_qkv, b_o=b_o)
+    full = oracle.block_forward_fp8(x, mod, pos, [0, 5, 12], table, *wq, *wo, **kw)
+    rows = np.array([0, 4, 5, 11])
+    part = oracle.block_forward_fp8(x, mod, pos, [0, 5, 12], table, *wq, *wo, rows=rows, **kw)
+    np.testing.assert_allclose(part["out"], full["out"][rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(part["o_codes"], full["o_codes"][rows])
+
+
+def test_fp8_block_tiny_workload_is_close_to_the_unquantized_block():
+    """The tiny workload with weights quantized per row: the branch out - x within
+    rel-L2 8e-2 of the plain oracle's (four e4m3 roundings in series, each about 2.6%
+    RMS), the output itself within the bf16 output tolerance."""
+    wl = synth.WORKLOADS["tiny"]
+    lay = oracle.pack_layout([r.grid for r in wl.requests])
+    inp = synth.block_inputs(wl)
+    kw = dict(n_heads=wl.n_heads, head_dim=wl.head_dim, sections=wl.sections)
+    args = (inp.x, lay["modality"], lay["pos"], lay["cu_seqlens"], inp.table)
+    f8 = oracle.block_forward_fp8(*args, *oracle.quantize_rows(inp.w_qkv),
+                                  *oracle.quantize_rows(inp.w_o), **kw)
+    ref = oracle.block_forward(*args, inp.w_qkv, inp.w_o, **kw)
+    x = inp.x.astype(np.float64)
+    rel = np.linalg.norm((f8["out"] - x) - (ref["out"] - x)) / np.linalg.norm(ref["out"] - x)
+    assert 5e-3 < rel < 8e-2
+    assert np.abs(f8["out"] - ref["out"]).max() <= 3e-2
+    assert np.linalg.norm(f8["out"] - ref["out"]) <= 1e-2 * np.linalg.norm(ref["out"])
