@@ -30,7 +30,8 @@ GELU) and width (4 x d_model), see ``oracle.block.gelu_tanh`` and
 around the block (Rectified Flow X0, Euler with eta = 0, dual schedules,
 anchor re-pinning, H3's timestep and velocity conventions); ``oracle.nft`` the
 DiffusionNFT loss and its gradient; ``oracle.fp8`` the e4m3 quantization and the
-FP8 projections and the FP8 block halves.
+FP8 projections and the FP8 block halves; ``oracle.backward`` the gradients
+of the attention half (the chain rule through the forward definitions).
 """
 from .layout import (MOD_AUDIO, MOD_TEXT, MOD_VIDEO, SAMPLES_PER_AUDIO_TOKEN,
                      SPATIAL_DOWNSAMPLE, TEMPORAL_DOWNSAMPLE, grid_from_media,
@@ -41,6 +42,7 @@ from .block import (adaln_modulate, attention, attention_probs, block_forward,
 from .denoise import (VIDEO_LATENT_CHANNELS, clean_estimate, denoise_loop, denoise_step,
                       euler_step, standard_velocity, timestep_from_sigma)
 from .nft import implicit_policies, nft_loss
+from .backward import adaln_backward, attention_backward, block_backward, rope3d_backward
 from .fp8 import (E4M3_MAX, adaln_modulate_fp8, block_forward_fp8, dequantize_rows, e4m3_decode,
                   e4m3_encode, e4m3_encode_bruteforce, e4m3_table, ffn_forward_fp8, linear_fp8,
                   quantize_rows, row_scales)
@@ -55,5 +57,6 @@ __all__ = [
     "euler_step", "denoise_step", "denoise_loop", "implicit_policies", "nft_loss",
     "E4M3_MAX", "e4m3_decode", "e4m3_table", "e4m3_encode", "e4m3_encode_bruteforce",
     "row_scales", "quantize_rows", "dequantize_rows", "linear_fp8", "adaln_modulate_fp8",
-    "block_forward_fp8", "ffn_forward_fp8",
+    "block_forward_fp8", "ffn_forward_fp8", "attention_backward", "rope3d_backward",
+    "adaln_backward", "block_backward",
 ]

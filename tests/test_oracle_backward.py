@@ -1,0 +1,134 @@
+"""Pins of the oracle's backward pass of the attention half (CPU only).
+
+The backward pass is the chain rule through the forward definitions; it is
+pinned by (a) central differences of the oracle's own float64 forward along
+random directions (no derivative is retyped), (b) torch autograd in float64
+(a library) through torch's layer norm and scaled-dot-product attention, (c)
+the adjoint and inverse identities of the rotation, and (d) special cases.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+
+def _setup(n=14, d=16, h=2, seed=80, bias=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((n, d)) * 1.5 + 0.3
+    table = rng.standard_normal((3, 3, d)) * 0.3
+    w_qkv = rng.standard_normal((3 * d, d)) * 0.4
+    w_o = rng.standard_normal((d, d)) * 0.4
+    b_qkv = rng.standard_normal(3 * d) * 0.1 if bias else None
+    b_o = rng.standard_normal(d) * 0.1 if bias else None
+    mod = rng.integers(0, 3, n)
+    pos = rng.integers(0, 7, (n, 3))
+    dout = rng.standard_normal((n, d))
+    return x, table, w_qkv, w_o, b_qkv, b_o, mod, pos, dout
+
+
+KW = dict(n_heads=2, head_dim=8, sections=(2, 2, 4), theta=50.0)
+
+
+def _objective(x, table, w_qkv, w_o, b_qkv, b_o, mod, pos, dout, cu, causal):
+    out = oracle.block_forward(x, mod, pos, cu, table, w_qkv, w_o, b_qkv=b_qkv, b_o=b_o,
+                               causal=causal, **KW)["out"]
+    return float(np.sum(dout * out))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_backward_directional_derivatives(causal):
+    """<grad, delta> equals the central difference of sum(dout * out) along delta for every
+    input group (x, table, W_qkv, b_qkv, W_o, b_o)."""
+    x, table, w_qkv, w_o, b_qkv, b_o, mod, pos, dout = _setup()
+    cu = [0, 6, 14]
+    g = oracle.block_backward(x, mod, pos, cu, table, w_qkv, w_o, dout, b_qkv=b_qkv, b_o=b_o,
+                              causal=causal, **KW)
+    args = dict(x=x, table=table, w_qkv=w_qkv, w_o=w_o, b_qkv=b_qkv, b_o=b_o)
+    grads = dict(x=g["dx"], table=g["dtable"], w_qkv=g["dw_qkv"], w_o=g["dw_o"],
+                 b_qkv=g["db_qkv"], b_o=g["db_o"])
+    rng = np.random.Generator(np.random.PCG64(81))
+    eps = 1e-5
+    for name, val in args.items():
+        delta = rng.standard_normal(val.shape)
+        plus = dict(args, **{name: val + eps * delta})
+        minus = dict(args, **{name: val - eps * delta})
+        fd = (_objective(**plus, mod=mod, pos=pos, dout=dout, cu=cu, causal=causal)
+              - _objective(**minus, mod=mod, pos=pos, dout=dout, cu=cu, causal=causal)) / (2 * eps)
+        an = float(np.sum(grads[name] * delta))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_attention_backward_matches_torch_autograd():
+    """torch's scaled_dot_product_attention (float64, block-diagonal / causal masks)
+    differentiated by autograd gives the same dq, dk, dv."""
+    rng = np.random.Generator(np.random.PCG64(82))
+    n, H, Dh = 23, 3, 8
+    q, k, v, do = (rng.standard_normal((n, H * Dh)) for _ in range(4))
+    cu = [0, 9, 9, 23]
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, cu, H, Dh, causal=causal, scale=0.4)
+        tq, tk, tv = (torch.tensor(a.reshape(n, H, Dh).transpose(1, 0, 2), requires_grad=True)
+                      for a in (q, k, v))
+        seg = np.searchsorted(np.asarray(cu[1:]), np.arange(n), side="right")
+        mask = seg[:, None] == seg[None, :]
+        if causal:
+            mask &= np.arange(n)[None, :] <= np.arange(n)[:, None]
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(mask), scale=0.4)
+        o.backward(torch.tensor(do.reshape(n, H, Dh).transpose(1, 0, 2).copy()))
+        for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+            ref = t.grad.numpy().transpose(1, 0, 2).reshape(n, H * Dh)
+            np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_adaln_backward_matches_torch_autograd():
+    x, table, *_ , mod, _, dout = _setup(n=11, d=24, seed=83)
+    dx, dsh, dsc = oracle.adaln_backward(x, mod, table, dout, eps=1e-6)
+    tx = torch.tensor(x, requires_grad=True)
+    tt = torch.tensor(table, requires_grad=True)
+    m = torch.tensor(mod)
+    y = F.layer_norm(tx, (x.shape[1],), eps=1e-6) * (1 + tt[m, 1]) + tt[m, 0]
+    y.backward(torch.tensor(dout))
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dsh, tt.grad[:, 0].numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dsc, tt.grad[:, 1].numpy(), rtol=1e-10, atol=1e-12)
+    assert np.all(tt.grad[:, 2].numpy() == 0)
+
+
+def test_rope_backward_is_the_adjoint_and_the_inverse():
+    rng = np.random.Generator(np.random.PCG64(84))
+    n, H, Dh, sec = 9, 2, 16, (4, 6, 6)
+    pos = rng.integers(0, 50, (n, 3))
+    a, b = rng.standard_normal((n, H * Dh)), rng.standard_normal((n, H * Dh))
+    ra = oracle.rope3d(a, pos, H, Dh, sec, 100.0)
+    rb_t = oracle.rope3d_backward(b, pos, H, Dh, sec, 100.0)
+    assert abs(np.sum(ra * b) - np.sum(a * rb_t)) <= 1e-10 * np.abs(ra * b).sum()
+    np.testing.assert_allclose(oracle.rope3d(rb_t, pos, H, Dh, sec, 100.0), b, atol=1e-12)
+    # position 0 leaves the gradient as it is
+    np.testing.assert_array_equal(oracle.rope3d_backward(b, np.zeros((n, 3), int), H, Dh, sec),
+                                  b)
+
+
+def test_zero_gate_passes_the_gradient_straight_through():
+    """A zero gate cuts the branch: dx = dout exactly, every weight gradient and the shift
+    and scale rows vanish, and the gate row collects dout * z per modality."""
+    x, table, w_qkv, w_o, b_qkv, b_o, mod, pos, dout = _setup(seed=85)
+    table[:, 2, :] = 0.0
+    g = oracle.block_backward(x, mod, pos, [0, 14], table, w_qkv, w_o, dout, b_qkv=b_qkv,
+                              b_o=b_o, **KW)
+    np.testing.assert_array_equal(g["dx"], dout)
+    for key in ("dw_qkv", "db_qkv", "dw_o", "db_o"):
+        assert not np.any(g[key]), key
+    assert not np.any(g["dtable"][:, :2, :])
+    for m in range(3):
+        np.testing.assert_allclose(g["dtable"][m, 2], (dout * g["z"])[mod == m].sum(0))
+
+
+def test_value_gradient_of_a_single_key_segment():
+    """A one-token segment attends only to itself: o = v, so dv = do and dq = dk = 0."""
+    rng = np.random.Generator(np.random.PCG64(86))
+    q, k, v, do = (rng.standard_normal((5, 16)) for _ in range(4))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, [0, 1, 5], 2, 8)
+    np.testing.assert_allclose(dv[0], do[0], atol=1e-15)
+    assert not np.any(dq[0]) and not np.any(dk[0])
