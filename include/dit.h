@@ -280,6 +280,48 @@ dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Attention backward                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* The gradient of attn_packed: the chain rule through softmax(q k^T scale) v
+ * per segment and head (the pages print no backward pass; the DiffusionNFT
+ * objective of [H3-NFT] section "DiffusionNFT: Skipping the Reverse Chain
+ * Entirely" trains the DiT through it).  bf16, head_dim 128 only. */
+
+/* attn_packed_lse: attn_packed that also writes lse float32
+ * [n_heads][n_tokens] (device), lse[h][i] = log sum_j exp(q_i k_j^T scale)
+ * over row i's keys.  Arguments and errors as attn_packed, plus DIT_EINVAL for
+ * a null lse and DIT_EUNSUPPORTED for a dtype other than DIT_BF16. */
+dit_status attn_packed_lse(dit_dtype dt, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                           const void* v, int64_t ld_v, void* o, int64_t ld_o, float* lse,
+                           const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                           int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                           float softmax_scale, int32_t causal, void* stream);
+
+/* Bytes of scratch attn_packed_backward needs: n_heads * n_tokens floats
+ * (delta = rowsum(dout * o) per head), rounded up to 256.  0 for bad sizes. */
+size_t dit_attn_backward_workspace_bytes(int64_t n_tokens, int32_t n_heads);
+
+/* attn_packed_backward: given q, k, v, the forward's o and lse and
+ * dout = dL/do (all [n_tokens][ld] bf16 rows, lse as above), writes
+ * dq = dL/dq, dk, dv ([n_tokens][ld] bf16, device; they must not overlap the
+ * inputs).  P = exp(q k^T scale - lse) is recomputed; dv = P^T dout,
+ * dS = P * (dout v^T - rowsum(dout * o)), dq = scale dS k, dk = scale dS^T q,
+ * float32 accumulation.  Deterministic (no atomics).  Rows past a segment's
+ * end are never read; rows outside every segment are not written.  Errors:
+ * those of attn_packed (prefix attn_packed or attn_packed_backward), DIT_EINVAL
+ * for a null dout / lse / dq / dk / dv or an ld below n_heads * head_dim,
+ * DIT_EUNSUPPORTED for a dtype other than DIT_BF16, DIT_EWORKSPACE. */
+dit_status attn_packed_backward(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                                int64_t ld_k, const void* v, int64_t ld_v, const void* o,
+                                int64_t ld_o, const void* dout, int64_t ld_do, const float* lse,
+                                void* dq, int64_t ld_dq, void* dk, int64_t ld_dk, void* dv,
+                                int64_t ld_dv, const int32_t* cu_seqlens, int32_t n_seqs,
+                                int32_t max_seqlen, int64_t n_tokens, int32_t n_heads,
+                                int32_t head_dim, float softmax_scale, int32_t causal,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* FP8 projections                                                            */
 /* ------------------------------------------------------------------------ */
 

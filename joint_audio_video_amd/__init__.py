@@ -35,6 +35,7 @@ EXPORTED = (
     "denoise_step", "dit_nft_workspace_bytes", "nft_loss", "rope3d_apply_to",
     "quantize_rows_fp8", "linear_fp8", "adaln_modulate_fp8", "dit_block_fp8_workspace_bytes",
     "dit_block_forward_fp8", "dit_ffn_fp8_workspace_bytes", "dit_ffn_forward_fp8",
+    "attn_packed_lse", "dit_attn_backward_workspace_bytes", "attn_packed_backward",
 )
 
 
@@ -115,6 +116,12 @@ def _load() -> ctypes.CDLL:
         "dit_ffn_fp8_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
         "dit_ffn_forward_fp8": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P,
                                                P, P, P, P, SZ, P]),
+        "attn_packed_lse": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P, P,
+                                           I32, I32, I64, I32, I32, F32, I32, P]),
+        "dit_attn_backward_workspace_bytes": (SZ, [I64, I32]),
+        "attn_packed_backward": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P,
+                                                I64, P, P, I64, P, I64, P, I64, P, I32, I32, I64,
+                                                I32, I32, F32, I32, P, SZ, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -264,6 +271,59 @@ def attn_packed(q, k, v, cu_seqlens, max_seqlen: int, n_heads: int, head_dim: in
                             cu_seqlens.data_ptr(), n_seqs, int(max_seqlen), n, n_heads,
                             head_dim, float(softmax_scale), int(bool(causal)), _stream(stream)))
     return out
+
+
+def attn_packed_lse(q, k, v, cu_seqlens, max_seqlen: int, n_heads: int, head_dim: int,
+                    softmax_scale: float = 0.0, causal: bool = False, out=None, lse=None,
+                    n_tokens=None, stream=None):
+    """attn_packed that also writes lse [n_heads][n_tokens] float32, each row's
+    log-sum-exp of the scaled scores (libdit attn_packed_lse)."""
+    torch = _torch()
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    if out is None:
+        out = torch.empty((q.shape[0], n_heads * head_dim), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((n_heads, n), dtype=torch.float32, device=q.device)
+    pq, ldq = _rows(q)
+    pk, ldk = _rows(k)
+    pv, ldv = _rows(v)
+    po, ldo = _rows(out)
+    _check(_lib.attn_packed_lse(_dtype_code(q), pq, ldq, pk, ldk, pv, ldv, po, ldo,
+                                lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                int(max_seqlen), n, n_heads, head_dim, float(softmax_scale),
+                                int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def attn_backward_workspace_bytes(n_tokens: int, n_heads: int) -> int:
+    return int(_lib.dit_attn_backward_workspace_bytes(int(n_tokens), int(n_heads)))
+
+
+def attn_packed_backward(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, n_heads: int,
+                         head_dim: int, softmax_scale: float = 0.0, causal: bool = False,
+                         dq=None, dk=None, dv=None, workspace=None, n_tokens=None, stream=None):
+    """(dq, dk, dv) of attn_packed given dout and the forward's o and lse
+    (libdit attn_packed_backward)."""
+    torch = _torch()
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    w = n_heads * head_dim
+    dq = torch.empty((q.shape[0], w), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((q.shape[0], w), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((q.shape[0], w), dtype=q.dtype, device=q.device) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(attn_backward_workspace_bytes(n, n_heads), 1),
+                                dtype=torch.uint8, device=q.device)
+    args = []
+    for t in (q, k, v, o, dout):
+        args += list(_rows(t))
+    args.append(lse.data_ptr())
+    for t in (dq, dk, dv):
+        args += list(_rows(t))
+    _check(_lib.attn_packed_backward(_dtype_code(q), *args, cu_seqlens.data_ptr(),
+                                     cu_seqlens.numel() - 1, int(max_seqlen), n, n_heads,
+                                     head_dim, float(softmax_scale), int(bool(causal)),
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
 
 
 def qkv_project(y, w_qkv, b_qkv=None, out=None, n_tokens=None, stream=None):

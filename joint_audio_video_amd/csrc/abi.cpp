@@ -24,6 +24,7 @@ char* error_buffer() {
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t elt_size(dit_dtype dt) { return dt == DIT_BF16 ? 2 : 4; }
 
@@ -287,8 +288,69 @@ extern "C" dit_status attn_packed(dit_dtype dt, const void* q, int64_t ld_q, con
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   hipError_t e = launch_attn(dt == DIT_BF16, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens,
                              n_seqs, max_seqlen, n_tokens, n_heads, head_dim, scale,
-                             causal != 0, (hipStream_t)stream);
+                             causal != 0, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_packed launch");
+}
+
+extern "C" dit_status attn_packed_lse(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                                      int64_t ld_k, const void* v, int64_t ld_v, void* o,
+                                      int64_t ld_o, float* lse, const int32_t* cu_seqlens,
+                                      int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
+                                      int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                      int32_t causal, void* stream) {
+  clear_error();
+  if (dit_status st = attn_check(dt, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens, n_seqs,
+                                 max_seqlen, n_tokens, n_heads, head_dim, softmax_scale))
+    return st;
+  if (!lse) return fail(DIT_EINVAL, "attn_packed_lse: null lse");
+  if (dt != DIT_BF16) return fail(DIT_EUNSUPPORTED, "attn_packed_lse: bf16 only");
+  if (n_tokens == 0) return DIT_OK;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  hipError_t e = launch_attn(1, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens, n_seqs,
+                             max_seqlen, n_tokens, n_heads, head_dim, scale, causal != 0, lse,
+                             (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_packed_lse launch");
+}
+
+extern "C" size_t dit_attn_backward_workspace_bytes(int64_t n_tokens, int32_t n_heads) {
+  if (n_tokens < 0 || n_heads < 1) return 0;
+  return round256((size_t)n_tokens * (size_t)n_heads * 4);
+}
+
+extern "C" dit_status attn_packed_backward(
+    dit_dtype dt, const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
+    int64_t ld_v, const void* o, int64_t ld_o, const void* dout, int64_t ld_do, const float* lse,
+    void* dq, int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
+    const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
+    int32_t n_heads, int32_t head_dim, float softmax_scale, int32_t causal, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "attn_packed_backward";
+  if (dit_status st = attn_check(dt, q, ld_q, k, ld_k, v, ld_v, const_cast<void*>(o), ld_o,
+                                 cu_seqlens, n_seqs, max_seqlen, n_tokens, n_heads, head_dim,
+                                 softmax_scale))
+    return st;
+  if (!dout || !lse || !dq || !dk || !dv) return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (dt != DIT_BF16) return fail(DIT_EUNSUPPORTED, "%s: bf16 only", who);
+  const int64_t width = (int64_t)n_heads * head_dim;
+  if (ld_do < width || ld_dq < width || ld_dk < width || ld_dv < width)
+    return fail(DIT_EINVAL, "%s: ld too small", who);
+  if ((double)max_seqlen * (double)std::max(ld_q, ld_do) * 2.0 >= 4294967296.0)
+    return fail(DIT_EUNSUPPORTED, "%s: a segment's rows span 4 GiB or more", who);
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !ld_aligned(dt, ld_do) || !ld_aligned(dt, ld_dq) || !ld_aligned(dt, ld_dk) ||
+      !ld_aligned(dt, ld_dv))
+    return fail(DIT_EUNSUPPORTED, "%s: pointers/ld must be 16-byte aligned", who);
+  const size_t need = dit_attn_backward_workspace_bytes(n_tokens, n_heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
+  if (n_tokens == 0) return DIT_OK;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  hipError_t e = launch_attn_bwd(q, ld_q, k, ld_k, v, ld_v, o, ld_o, dout, ld_do, lse, dq, ld_dq,
+                                 dk, ld_dk, dv, ld_dv, cu_seqlens, n_seqs, max_seqlen, n_tokens,
+                                 n_heads, scale, causal != 0, static_cast<float*>(workspace),
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_packed_backward launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -567,7 +629,6 @@ extern "C" dit_status nft_loss(dit_dtype v_dtype, const void* v_theta, int64_t l
 
 // ---------------------------------------------------------------------------
 
-static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // An FP8 projection inside a block: W [n_out][k_in] codes with per-row
 // scales, optional bf16 bias [n_out].
@@ -788,7 +849,7 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   mark(3);
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
   e = launch_attn(dt == DIT_BF16, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
-                  n_tokens, H, Dh, scale, d->causal != 0, s);
+                  n_tokens, H, Dh, scale, d->causal != 0, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: attention launch");
   mark(4);
   GemmEpilogue ep_out{1, b_o, x, D, modality, ada_table + 2 * (size_t)D};
@@ -881,7 +942,7 @@ extern "C" dit_status dit_block_forward_fp8(
   mark(3);
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
   e = launch_attn(1, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
-                  scale, d->causal != 0, s);
+                  scale, d->causal != 0, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: attention launch");
   mark(4);
   e = launch_quant_rows_fp8(1, o, D, codes, D, scales, n_tokens, D, s);

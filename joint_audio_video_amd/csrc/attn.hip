@@ -36,6 +36,8 @@
 //     holding NaN cannot leak in.  Causal launches longest q-tiles first.
 //   * Grid = (q-tiles of the longest segment, segments, heads): consecutive
 //     workgroups share one head's K/V, which stays hot in L2 / MALL.
+//   * Optionally each row's log-sum-exp, lse[h][row] = log sum_j exp(s_j
+//     scale), for the backward pass.
 //
 // f32 path: one wave per (query, head), online softmax in float32 over key
 // chunks of 64 (exactness for the small float32 workload, not speed).
@@ -101,7 +103,8 @@ __device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (2 * (row & 
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, uint16_t* __restrict__ o, int64_t ld_o,
-    const int32_t* __restrict__ cu, float scale_log2, int causal) {
+    const int32_t* __restrict__ cu, float scale_log2, int causal, float* __restrict__ lse,
+    int64_t ld_lse) {
   // Two LDS buffers per tensor as distinct objects: with the key loop unrolled
   // by two, every access names its buffer at compile time, so the compiler can
   // tell the prefetch into one buffer from the reads of the other and does not
@@ -350,6 +353,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
   const float l_tot = half_swap_sum(l_run);
   const float inv = 1.0f / l_tot;
+  // log sum_j exp(s_j scale) = ln2 (m scale_log2 + log2 l), m the row's reference max
+  if (lse != nullptr && g == 0 && qrow < seg1)
+    lse[(int64_t)h * ld_lse + qrow] = (m_run * scale_log2 + log2f(l_tot)) * 0.69314718055994531f;
   if (qrow < seg1) {
     uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
 #pragma unroll
@@ -424,15 +430,16 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
                        const void* v, int64_t ld_v, void* o, int64_t ld_o, const int32_t* cu,
                        int n_seqs, int max_seqlen, int64_t n_tokens, int n_heads, int head_dim,
-                       float scale, int causal, hipStream_t s) {
+                       float scale, int causal, float* lse, hipStream_t s) {
   if (n_seqs > 65535 || n_heads > 65535 || n_tokens > INT32_MAX) return hipErrorInvalidValue;
+  if (lse != nullptr && !bf16) return hipErrorInvalidValue;
   if (bf16) {
     if (head_dim != DH) return hipErrorInvalidValue;
     const dim3 grid((max_seqlen + QBLK - 1) / QBLK, n_seqs, n_heads);
     attn_bf16_kernel<<<grid, dim3(kAttnThreads), 0, s>>>(
         static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
         static_cast<const uint16_t*>(v), ld_v, static_cast<uint16_t*>(o), ld_o, cu,
-        scale * 1.4426950408889634f, causal);
+        scale * 1.4426950408889634f, causal, lse, n_tokens);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)n_tokens, n_heads);

@@ -1,0 +1,416 @@
+// Backward pass of the packed softmax attention (bf16, head_dim 128).
+//
+// The gradient of o = softmax(q k^T scale) v inside each cu_seqlens segment
+// (the chain rule through the forward of this library's attention; the
+// pages print no backward pass, the DiffusionNFT objective of [H3-NFT]
+// section "DiffusionNFT: Skipping the Reverse Chain Entirely" trains the
+// DiT through it).  With P = exp(s scale - lse) recomputed from the
+// forward's per-row log-sum-exp and delta = rowsum(do * o):
+//   dv = P^T do,  dS = P * (do v^T - delta),  dq = scale dS k,  dk = scale dS^T q.
+//
+// Three launches, no atomics, deterministic:
+//   * attn_delta_kernel: delta[h][row], one thread per (row, head).
+//   * attn_bwd_dkdv_kernel: a workgroup owns 128 keys of one (segment,
+//     head) (32 per wave, their K and V in registers) and streams the
+//     segment's queries in tiles of 64 (q, do, lse, delta double-buffered in
+//     LDS).  Per tile a wave computes S = q k^T and dP = do v^T (rows =
+//     queries, so the 32x32 accumulator gives each lane one key column), P
+//     and dS elementwise, then dv^T += do^T P and dk^T += q^T dS with the
+//     transposed operand read from LDS by ds_read_b64_tr_b16 and P / dS as
+//     the bf16 B operand in the accumulator's own row order (the k index of
+//     a product can be permuted as long as both operands agree).
+//   * attn_bwd_dq_kernel: a workgroup owns 128 queries (q, do, lse, delta of
+//     its 32 per wave in registers) and streams the keys in tiles of 64:
+//     S^T = k q^T and dP^T = v do^T (rows = keys), dS^T, then
+//     dq^T += k^T dS^T, as the forward kernel computes O^T.
+// All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P
+// and dS are rounded to bf16 as MFMA operands.  Rows past a segment's end
+// load as zeros (buffer range checks) and get P = 0.
+#include <cmath>
+
+#include "common.h"
+
+namespace dit {
+namespace {
+
+constexpr int DH = 128;
+constexpr int kWavesB = 4;
+constexpr int kThreadsB = 64 * kWavesB;
+constexpr int BLK = 32 * kWavesB;                        // keys (dk, dv) or queries (dq) per workgroup
+constexpr int TB = 64;                                   // streamed rows per tile
+constexpr int kLoads = TB * DH * 2 / 16 / kThreadsB;     // 16-byte loads per thread per tile
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// LDS tiles are [row][d] with 256-byte rows; 16-byte chunk c of row r sits at
+// physical chunk c ^ (r & 7).
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+
+// Fragment whose 32 rows are tile rows: lane (l32, g) holds row r, d = 16 ks + 8 g .. +7.
+__device__ __forceinline__ bf16x8 row_frag(const uint16_t* t, int r, int ks, int g) {
+  return *reinterpret_cast<const bf16x8*>(t + r * DH + swz(r, 2 * ks + g) * 8);
+}
+
+// Fragment whose 32 rows are d = 32 db + l32 and whose 8 k values are tile
+// rows b0 + 4g + {0..3} and b0 + 4g + 8 + {0..3} (transposing reads: in each
+// 16-lane group, lane i supplies row b0 + 4g + (i >> 2), columns
+// 32 db + 16 ((lane >> 4) & 1) + 4 (i & 3) .. +3, and receives column
+// 32 db + l32 of the four rows).
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* t, int b0, int db, int lane) {
+  const int i = lane & 15, g = lane >> 5;
+  const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  const int r0 = b0 + 4 * g + (i >> 2), r1 = r0 + 8;
+  const lds_u16* p0 = (const lds_u16*)t + r0 * DH + swz(r0, col >> 3) * 8 + (col & 7);
+  const lds_u16* p1 = (const lds_u16*)t + r1 * DH + swz(r1, col >> 3) * 8 + (col & 7);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Accumulator element e of a 32x32 block lies in row 8 (e / 4) + 4 g + e % 4.
+__device__ __forceinline__ int acc_row(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
+
+// Global -> LDS tile loader: slot s = threads * i + tid is tile row s / 16,
+// physical chunk s % 16 (the swizzle applied on the global side).
+struct TileLoader {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[kLoads];
+  uint32_t tstep;
+  __device__ void init(const uint16_t* base, int64_t ld, uint32_t rows, int tid) {
+    rs = make_rsrc(base, rows * (uint32_t)ld * 2u);
+    const int srow = tid >> 4, pch = tid & 15;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int row = (kThreadsB / 16) * i + srow;
+      off[i] = (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)swz(row, pch) * 16u;
+    }
+    tstep = (uint32_t)TB * (uint32_t)ld * 2u;
+  }
+  __device__ void issue(uint16_t* dst, int tile, int wave) const {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + (kThreadsB * i + 64 * wave) * 8, 16,
+                                               off[i], (int)(tile * tstep), 0, 0);
+  }
+};
+
+// delta[h][row] = sum_d do[row][h d] o[row][h d]
+__global__ __launch_bounds__(256) void attn_delta_kernel(const uint16_t* __restrict__ o,
+                                                         int64_t ld_o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         int64_t ld_do, float* __restrict__ delta,
+                                                         int64_t n, int n_heads) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n * n_heads) return;
+  const int64_t row = idx / n_heads;
+  const int h = (int)(idx - row * n_heads);
+  const uint4* op = reinterpret_cast<const uint4*>(o + row * ld_o + h * DH);
+  const uint4* dp = reinterpret_cast<const uint4*>(dout + row * ld_do + h * DH);
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < DH / 8; ++c) {
+    const uint4 a = op[c], b = dp[c];
+    s = fmaf(bf16lo(a.x), bf16lo(b.x), s); s = fmaf(bf16hi(a.x), bf16hi(b.x), s);
+    s = fmaf(bf16lo(a.y), bf16lo(b.y), s); s = fmaf(bf16hi(a.y), bf16hi(b.y), s);
+    s = fmaf(bf16lo(a.z), bf16lo(b.z), s); s = fmaf(bf16hi(a.z), bf16hi(b.z), s);
+    s = fmaf(bf16lo(a.w), bf16lo(b.w), s); s = fmaf(bf16hi(a.w), bf16hi(b.w), s);
+  }
+  delta[(int64_t)h * n + row] = s;
+}
+
+// Stores a 32x32 accumulator block transposed into rows of out: lane (key or
+// query l32) writes d = 32 db + 8 j + 4 g .. +3 for j = 0..3.
+__device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16& acc, int db, int g,
+                                           float mul) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = 32 * db + 8 * j + 4 * g;
+    *reinterpret_cast<uint2*>(rowp + d) =
+        make_uint2(pack_bf16x2(acc[4 * j] * mul, acc[4 * j + 1] * mul),
+                   pack_bf16x2(acc[4 * j + 2] * mul, acc[4 * j + 3] * mul));
+  }
+}
+
+__global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
+    const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
+    int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dk, int64_t ld_dk, uint16_t* __restrict__ dv, int64_t ld_dv,
+    const int32_t* __restrict__ cu, int64_t n, float scale, float scale_log2, int causal) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs0[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs1[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds0[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds1[TB * DH];
+  __shared__ float Ls0[TB], Ls1[TB], Es0[TB], Es1[TB];   // lse * log2(e), delta
+
+  const int h = blockIdx.z, seq = blockIdx.y;
+  const int seg0 = cu[seq], seg1 = cu[seq + 1];
+  const int kb0 = seg0 + (int)blockIdx.x * BLK;
+  if (kb0 >= seg1) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int key = kb0 + 32 * wave + l32;
+
+  // K and V^T operands of this wave's 32 keys: lane (key l32, half g) holds
+  // d = 16 ks + 8 g .. +7.
+  bf16x8 kf[DH / 16], vf[DH / 16];
+  {
+    const bool live = key < seg1;
+    const uint16_t* kp = k + (int64_t)key * ld_k + h * DH + 8 * g;
+    const uint16_t* vp = v + (int64_t)key * ld_v + h * DH + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      const uint4 a = live ? *reinterpret_cast<const uint4*>(kp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      const uint4 b = live ? *reinterpret_cast<const uint4*>(vp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      kf[ks] = __builtin_bit_cast(bf16x8, a);
+      vf[ks] = __builtin_bit_cast(bf16x8, b);
+    }
+  }
+
+  // Query tiles: causal attention reaches this block's keys only from queries >= kb0.
+  const int qt0 = causal ? (kb0 - seg0) / TB : 0;
+  const int nqt = (seg1 - seg0 + TB - 1) / TB;
+  const uint32_t seg_rows = (uint32_t)(seg1 - seg0);
+  TileLoader lq, ld;
+  lq.init(q + (int64_t)seg0 * ld_q + h * DH, ld_q, seg_rows, tid);
+  ld.init(dout + (int64_t)seg0 * ld_do + h * DH, ld_do, seg_rows, tid);
+  const float* lse_h = lse + (int64_t)h * n;
+  const float* del_h = delta + (int64_t)h * n;
+  // lse / delta of a tile: threads 0..63 fetch lse, 64..127 delta (registers,
+  // stored to LDS after the current tile's reads).
+  auto fetch_ld = [&](int t) -> float {
+    const int r = seg0 + t * TB + (tid & 63);
+    if (tid < 64) return r < seg1 ? lse_h[r] * 1.4426950408889634f : INFINITY;
+    if (tid < 128) return r < seg1 ? del_h[r] : 0.0f;
+    return 0.0f;
+  };
+  auto put_ld = [&](float* L, float* E, float val) {
+    if (tid < 64) L[tid] = val;
+    else if (tid < 128) E[tid - 64] = val;
+  };
+
+  f32x16 dka[DH / 32], dva[DH / 32];
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dka[db][e] = 0.0f, dva[db][e] = 0.0f;
+  const f32x16 zero16 = {};
+
+  auto step = [&](const uint16_t* Qs, const uint16_t* Ds, const float* Ls, const float* Es,
+                  uint16_t* Qn, uint16_t* Dn, float* Ln, float* En, int t)
+      __attribute__((always_inline)) {
+    float nxt = 0.0f;
+    if (t + 1 < nqt) {
+      lq.issue(Qn, t + 1, wave);
+      ld.issue(Dn, t + 1, wave);
+      nxt = fetch_ld(t + 1);
+    }
+    const int qbase = seg0 + t * TB;
+    bf16x8 pf[4], sf[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sacc = zero16, pacc = zero16;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qs, 32 * qb + l32, ks, g), kf[ks],
+                                                       sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ds, 32 * qb + l32, ks, g), vf[ks],
+                                                       pacc, 0, 0, 0);
+      }
+      const bool diag = causal && qbase + 32 * qb < key;   // some query of the block precedes this key
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * qb + acc_row(e, g);
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -Ls[r]));
+        if (diag && qbase + r < key) p = 0.0f;
+        const float ds = p * (pacc[e] - Es[r]);
+        pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
+        sf[2 * qb + (e >> 3)][e & 7] = (__bf16)ds;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int b0 = 16 * s;   // = 32 qb + 16 u for s = 2 qb + u
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Ds, b0, db, lane), pf[s], dva[db],
+                                                          0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Qs, b0, db, lane), sf[s], dka[db],
+                                                          0, 0, 0);
+      }
+    }
+    if (t + 1 < nqt) put_ld(Ln, En, nxt);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  if (qt0 < nqt) {
+    lq.issue(Qs0, qt0, wave);
+    ld.issue(Ds0, qt0, wave);
+    put_ld(Ls0, Es0, fetch_ld(qt0));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = qt0; t < nqt; t += 2) {
+    step(Qs0, Ds0, Ls0, Es0, Qs1, Ds1, Ls1, Es1, t);
+    if (t + 1 < nqt) step(Qs1, Ds1, Ls1, Es1, Qs0, Ds0, Ls0, Es0, t + 1);
+  }
+
+  if (key < seg1) {
+    uint16_t* kr = dk + (int64_t)key * ld_dk + h * DH;
+    uint16_t* vr = dv + (int64_t)key * ld_dv + h * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db) {
+      store_rows(kr, dka[db], db, g, scale);
+      store_rows(vr, dva[db], db, g, 1.0f);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
+    const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
+    int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dq, int64_t ld_dq, const int32_t* __restrict__ cu, int64_t n,
+    float scale, float scale_log2, int causal) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[TB * DH];
+
+  const int h = blockIdx.z, seq = blockIdx.y;
+  const int seg0 = cu[seq], seg1 = cu[seq + 1];
+  const int q0 = seg0 + (int)blockIdx.x * BLK;
+  if (q0 >= seg1) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int qrow = q0 + 32 * wave + l32;
+  const bool live = qrow < seg1;
+
+  // Q^T and dO^T operands (B of S^T = K Q^T and dP^T = V dO^T): lane (query
+  // l32, half g) holds d = 16 ks + 8 g .. +7.
+  bf16x8 qf[DH / 16], df[DH / 16];
+  {
+    const uint16_t* qp = q + (int64_t)qrow * ld_q + h * DH + 8 * g;
+    const uint16_t* dp = dout + (int64_t)qrow * ld_do + h * DH + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      const uint4 a = live ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      const uint4 b = live ? *reinterpret_cast<const uint4*>(dp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, a);
+      df[ks] = __builtin_bit_cast(bf16x8, b);
+    }
+  }
+  const float lse2 = live ? lse[(int64_t)h * n + qrow] * 1.4426950408889634f : INFINITY;
+  const float dlt = live ? delta[(int64_t)h * n + qrow] : 0.0f;
+
+  const int kend = causal ? min(seg1, q0 + BLK) : seg1;
+  const int nkt = (kend - seg0 + TB - 1) / TB;
+  const uint32_t seg_rows = (uint32_t)(seg1 - seg0);
+  TileLoader lk, lv;
+  lk.init(k + (int64_t)seg0 * ld_k + h * DH, ld_k, seg_rows, tid);
+  lv.init(v + (int64_t)seg0 * ld_v + h * DH, ld_v, seg_rows, tid);
+
+  f32x16 dqa[DH / 32];
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqa[db][e] = 0.0f;
+  const f32x16 zero16 = {};
+
+  auto step = [&](const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, int t)
+      __attribute__((always_inline)) {
+    if (t + 1 < nkt) {
+      lk.issue(Kn, t + 1, wave);
+      lv.issue(Vn, t + 1, wave);
+    }
+    const int kbase = seg0 + t * TB;
+    bf16x8 sf[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 sacc = zero16, pacc = zero16;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, 32 * b + l32, ks, g), qf[ks],
+                                                       sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Vs, 32 * b + l32, ks, g), df[ks],
+                                                       pacc, 0, 0, 0);
+      }
+      const int kb = kbase + 32 * b;
+      const bool edge = kb + 32 > seg1 || (causal && kb + 31 > q0 + 32 * wave);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -lse2));
+        if (edge) {
+          const int kk = kb + acc_row(e, g);
+          if (kk >= seg1 || (causal && kk > qrow)) p = 0.0f;
+        }
+        sf[2 * b + (e >> 3)][e & 7] = (__bf16)(p * (pacc[e] - dlt));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Ks, 16 * s, db, lane), sf[s],
+                                                          dqa[db], 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  if (nkt > 0) {
+    lk.issue(Ks0, 0, wave);
+    lv.issue(Vs0, 0, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < nkt; t += 2) {
+    step(Ks0, Vs0, Ks1, Vs1, t);
+    if (t + 1 < nkt) step(Ks1, Vs1, Ks0, Vs0, t + 1);
+  }
+
+  if (live) {
+    uint16_t* qr = dq + (int64_t)qrow * ld_dq + h * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db) store_rows(qr, dqa[db], db, g, scale);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                           const void* v, int64_t ld_v, const void* o, int64_t ld_o,
+                           const void* dout, int64_t ld_do, const float* lse, void* dq,
+                           int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
+                           const int32_t* cu, int n_seqs, int max_seqlen, int64_t n_tokens,
+                           int n_heads, float scale, int causal, float* delta, hipStream_t s) {
+  if (n_seqs > 65535 || n_heads > 65535 || n_tokens > INT32_MAX) return hipErrorInvalidValue;
+  // the buffer resources address a segment's rows with 32-bit byte offsets
+  for (int64_t ld : {ld_q, ld_k, ld_v, ld_do})
+    if ((uint64_t)max_seqlen * (uint64_t)ld * 2u > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  if (n_tokens == 0) return hipSuccess;
+  const int64_t pairs = n_tokens * n_heads;
+  attn_delta_kernel<<<dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<const uint16_t*>(o), ld_o, static_cast<const uint16_t*>(dout), ld_do, delta,
+      n_tokens, n_heads);
+  const dim3 grid((max_seqlen + BLK - 1) / BLK, n_seqs, n_heads);
+  const float sl2 = scale * 1.4426950408889634f;
+  attn_bwd_dkdv_kernel<<<grid, dim3(kThreadsB), 0, s>>>(
+      static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
+      static_cast<const uint16_t*>(v), ld_v, static_cast<const uint16_t*>(dout), ld_do, lse, delta,
+      static_cast<uint16_t*>(dk), ld_dk, static_cast<uint16_t*>(dv), ld_dv, cu, n_tokens, scale,
+      sl2, causal);
+  attn_bwd_dq_kernel<<<grid, dim3(kThreadsB), 0, s>>>(
+      static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
+      static_cast<const uint16_t*>(v), ld_v, static_cast<const uint16_t*>(dout), ld_do, lse, delta,
+      static_cast<uint16_t*>(dq), ld_dq, cu, n_tokens, scale, sl2, causal);
+  return hipGetLastError();
+}
+
+}  // namespace dit

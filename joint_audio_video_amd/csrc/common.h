@@ -102,10 +102,24 @@ hipError_t launch_rope(int bf16, const void* q, int64_t ld_q, const void* k, int
                        const int32_t* pos, int64_t n, int n_heads, int head_dim,
                        int s_t, int s_h, const double* freq_d, hipStream_t s);
 
+// lse (bf16 only, may be null): float [n_heads][n_tokens], the natural
+// log-sum-exp of each row's scaled scores.
 hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
                        const void* v, int64_t ld_v, void* o, int64_t ld_o,
                        const int32_t* cu, int n_seqs, int max_seqlen, int64_t n_tokens,
-                       int n_heads, int head_dim, float scale, int causal, hipStream_t s);
+                       int n_heads, int head_dim, float scale, int causal, float* lse,
+                       hipStream_t s);
+
+// Attention backward (bf16, head_dim 128): delta[h][row] = sum_d do * o, then
+// dk, dv (one pass over the queries per key block) and dq (one pass over the
+// keys per query block), recomputing P = exp(s scale - lse).  delta: float
+// [n_heads][n_tokens] scratch.
+hipError_t launch_attn_bwd(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                           const void* v, int64_t ld_v, const void* o, int64_t ld_o,
+                           const void* dout, int64_t ld_do, const float* lse, void* dq,
+                           int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
+                           const int32_t* cu, int n_seqs, int max_seqlen, int64_t n_tokens,
+                           int n_heads, float scale, int causal, float* delta, hipStream_t s);
 
 // C = A B^T (+ bias), A [M][K], B [N][K]; epilogue 0: store C; 1: gated residual
 // out = x + table[mod][GATE] * C; 2: store gelu_tanh(C).

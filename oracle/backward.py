@@ -56,6 +56,53 @@ def attention_backward(q, k, v, do, cu_seqlens, n_heads: int, head_dim: int,
     return dq, dk, dv
 
 
+def attention_lse(q, k, cu_seqlens, n_heads: int, head_dim: int, causal: bool = False,
+                  scale: Optional[float] = None, rows=None) -> np.ndarray:
+    """lse[h][i] = log sum_j exp(q_i k_j^T scale) over row i's keys (its segment, j <= i
+    when causal), float64 [n_heads][len(rows)] (every row when rows is None)."""
+    q, k = _f64(q), _f64(k)
+    n = q.shape[0]
+    sc = 1.0 / np.sqrt(head_dim) if scale is None else float(scale)
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    cu = [int(c) for c in cu_seqlens]
+    seg = np.searchsorted(np.asarray(cu[1:]), idx, side="right")
+    out = np.empty((n_heads, idx.size))
+    for s in np.unique(seg):
+        sel = np.flatnonzero(seg == s)
+        a, b = cu[s], cu[s + 1]
+        qi = idx[sel]
+        for h in range(n_heads):
+            cols = slice(h * head_dim, (h + 1) * head_dim)
+            z = (q[qi, cols] @ k[a:b, cols].T) * sc
+            if causal:
+                z = np.where(np.arange(a, b)[None, :] <= qi[:, None], z, -np.inf)
+            m = z.max(axis=1, keepdims=True)
+            out[h, sel] = m[:, 0] + np.log(np.sum(np.exp(z - m), axis=1))
+    return out
+
+
+def attention_backward_rows(q, k, v, do, cu_seqlens, n_heads: int, head_dim: int, rows,
+                            causal: bool = False, scale: Optional[float] = None) -> np.ndarray:
+    """dq at the given query rows only (each needs its own softmax row, not the
+    others'): dq_i = scale sum_j P_ij (do_i v_j - do_i o_i) k_j."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    sc = 1.0 / np.sqrt(head_dim) if scale is None else float(scale)
+    idx = np.asarray(rows, dtype=np.int64)
+    cu = [int(c) for c in cu_seqlens]
+    seg = np.searchsorted(np.asarray(cu[1:]), idx, side="right")
+    out = np.zeros((idx.size, q.shape[1]))
+    for t, (i, sgi) in enumerate(zip(idx, seg)):
+        a, b = cu[sgi], cu[sgi + 1]
+        for h in range(n_heads):
+            cols = slice(h * head_dim, (h + 1) * head_dim)
+            P = _probs(q[i:i + 1, cols], k[a:b, cols], np.array([i]), a, causal, sc)[0]
+            o_i = P @ v[a:b, cols]
+            dP = v[a:b, cols] @ do[i, cols]
+            dS = P * (dP - do[i, cols] @ o_i)
+            out[t, cols] = sc * (dS @ k[a:b, cols])
+    return out
+
+
 def rope3d_backward(g, pos, n_heads: int, head_dim: int, sections: Sequence[int],
                     theta: float = 10000.0) -> np.ndarray:
     """Gradient through oracle.block.rope3d: the transposed rotation R^T g.

@@ -132,3 +132,50 @@ def test_value_gradient_of_a_single_key_segment():
     dq, dk, dv = oracle.attention_backward(q, k, v, do, [0, 1, 5], 2, 8)
     np.testing.assert_allclose(dv[0], do[0], atol=1e-15)
     assert not np.any(dq[0]) and not np.any(dk[0])
+
+
+def test_attention_lse_matches_torch_logsumexp_and_closed_form():
+    rng = np.random.Generator(np.random.PCG64(87))
+    n, H, Dh = 17, 2, 8
+    q, k = rng.standard_normal((n, H * Dh)), rng.standard_normal((n, H * Dh))
+    cu = [0, 7, 17]
+    for causal in (False, True):
+        lse = oracle.attention_lse(q, k, cu, H, Dh, causal=causal, scale=0.3)
+        for i in range(n):
+            a = 0 if i < 7 else 7
+            b = i + 1 if causal else (7 if i < 7 else 17)
+            for h in range(H):
+                c = slice(h * Dh, (h + 1) * Dh)
+                ref = torch.logsumexp(torch.tensor(k[a:b, c] @ q[i, c] * 0.3), 0).item()
+                assert abs(lse[h, i] - ref) <= 1e-12 * max(1, abs(ref))
+    # equal keys: every score is the same, lse = s + log(segment length)
+    kk = np.tile(k[:1], (n, 1))
+    lse = oracle.attention_lse(q, kk, [0, n], H, Dh)
+    s0 = np.array([[q[i, h * Dh:(h + 1) * Dh] @ k[0, h * Dh:(h + 1) * Dh] / np.sqrt(Dh)
+                    for i in range(n)] for h in range(H)])
+    np.testing.assert_allclose(lse, s0 + np.log(n), rtol=1e-12, atol=1e-12)
+    # a subset of rows equals those rows of the whole
+    np.testing.assert_allclose(oracle.attention_lse(q, k, cu, H, Dh, rows=[3, 16]),
+                               oracle.attention_lse(q, k, cu, H, Dh)[:, [3, 16]])
+
+
+def test_attention_backward_rows_equals_the_full_backward():
+    rng = np.random.Generator(np.random.PCG64(88))
+    q, k, v, do = (rng.standard_normal((19, 16)) for _ in range(4))
+    for causal in (False, True):
+        dq, _, _ = oracle.attention_backward(q, k, v, do, [0, 8, 19], 2, 8, causal=causal)
+        rows = [0, 7, 8, 18]
+        got = oracle.attention_backward_rows(q, k, v, do, [0, 8, 19], 2, 8, rows, causal=causal)
+        np.testing.assert_allclose(got, dq[rows], rtol=1e-12, atol=1e-13)
+
+
+def test_attention_gradient_column_sums():
+    """Shift invariance of the softmax over keys: the key gradients of a segment sum
+    to zero per head and dimension; the value gradients sum to the output gradients."""
+    rng = np.random.Generator(np.random.PCG64(89))
+    q, k, v, do = (rng.standard_normal((21, 16)) for _ in range(4))
+    for causal in (False, True):
+        _, dk, dv = oracle.attention_backward(q, k, v, do, [0, 9, 21], 2, 8, causal=causal)
+        for a, b in ((0, 9), (9, 21)):
+            np.testing.assert_allclose(dk[a:b].sum(0), 0.0, atol=1e-12)
+            np.testing.assert_allclose(dv[a:b].sum(0), do[a:b].sum(0), rtol=1e-12, atol=1e-12)
