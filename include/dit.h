@@ -497,6 +497,44 @@ dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Backward pass of the attention half                                        */
+/* ------------------------------------------------------------------------ */
+
+/* The gradients of sum(dout * out) for out = dit_block_forward(x): the chain
+ * rule through the gated residual, the output projection, attention, the 3D
+ * rotation (its transpose is the rotation by the negated angle), the fused
+ * QKV projection and the per-modality AdaLN (the pages print no backward
+ * pass; the DiffusionNFT objective of [H3-NFT] section "DiffusionNFT:
+ * Skipping the Reverse Chain Entirely" trains the DiT through it).  The
+ * forward stages are recomputed inside the call (nothing is saved between
+ * calls).  bf16, head_dim 128, d_model a multiple of 64. */
+
+/* Bytes of scratch dit_block_backward needs: about 12 bf16 planes of
+ * [n_tokens rounded up to 64][d_model], plus 2 * n_heads * n_tokens floats,
+ * 3 * d_model^2 bf16 and small reduction buffers.  0 for a bad descriptor
+ * (also for a dtype other than DIT_BF16). */
+size_t dit_block_backward_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
+
+/* Inputs as dit_block_forward, plus dout = dL/d(out) [n_tokens][d_model] bf16.
+ * Outputs (device): dx [n_tokens][d_model] bf16 (may be dout, must not
+ * overlap x); dtable float32 [3][3][d_model] (the shift, scale and gate rows
+ * of every modality; modalities absent from the pack get zero rows);
+ * dw_qkv [3D][D] and dw_o [D][D] bf16 ([out][in], as the weights); db_qkv
+ * [3D] and db_o [D] float32, or NULL to skip them.  Sums over tokens are
+ * deterministic (fixed chunks, fixed order), accumulation float32.  Errors:
+ * those of the forward's stages, DIT_EINVAL for a null required pointer or
+ * dx overlapping x, DIT_EUNSUPPORTED for a dtype other than DIT_BF16,
+ * d_model not a multiple of 64 or a misaligned pointer, DIT_EWORKSPACE. */
+dit_status dit_block_backward(const dit_block_desc* d, const void* x, const void* dout,
+                              const uint8_t* modality, const int32_t* pos_thw,
+                              const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                              int64_t n_tokens, const float* ada_table, const void* w_qkv,
+                              const void* b_qkv, const void* w_o, const void* b_o, void* dx,
+                              float* dtable, void* dw_qkv, float* db_qkv, void* dw_o,
+                              float* db_o, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* FP8 block halves                                                           */
 /* ------------------------------------------------------------------------ */
 

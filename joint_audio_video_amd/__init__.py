@@ -36,6 +36,7 @@ EXPORTED = (
     "quantize_rows_fp8", "linear_fp8", "adaln_modulate_fp8", "dit_block_fp8_workspace_bytes",
     "dit_block_forward_fp8", "dit_ffn_fp8_workspace_bytes", "dit_ffn_forward_fp8",
     "attn_packed_lse", "dit_attn_backward_workspace_bytes", "attn_packed_backward",
+    "dit_block_backward_workspace_bytes", "dit_block_backward",
 )
 
 
@@ -122,6 +123,9 @@ def _load() -> ctypes.CDLL:
         "attn_packed_backward": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P,
                                                 I64, P, P, I64, P, I64, P, I64, P, I32, I32, I64,
                                                 I32, I32, F32, I32, P, SZ, P]),
+        "dit_block_backward_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
+        "dit_block_backward": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32, I32,
+                                              I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -623,3 +627,38 @@ def ffn_forward_fp8(desc: FfnDesc, x, modality, table, w1_codes, w1_scales, w2_c
         w2_codes.data_ptr(), w2_scales.data_ptr(), _ptr(b2), workspace.data_ptr(),
         workspace.numel(), _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the attention half
+# ---------------------------------------------------------------------------
+
+def block_backward_workspace_bytes(desc: BlockDesc, n_tokens: int) -> int:
+    return int(_lib.dit_block_backward_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def block_backward(desc: BlockDesc, x, dout, modality, pos, cu_seqlens, max_seqlen: int, table,
+                   w_qkv, w_o, b_qkv=None, b_o=None, bias_grads: bool = True, dx=None,
+                   workspace=None, n_tokens=None, stream=None) -> dict:
+    """Gradients of sum(dout * out) of the attention half (libdit dit_block_backward):
+    dict(dx, dtable [3][3][D] float32, dw_qkv, dw_o, db_qkv, db_o (float32 or None))."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    d = x.shape[1]
+    dev = x.device
+    dx = torch.empty_like(x) if dx is None else dx
+    dtable = torch.empty((3, 3, d), dtype=torch.float32, device=dev)
+    dw_qkv = torch.empty((3 * d, d), dtype=x.dtype, device=dev)
+    dw_o = torch.empty((d, d), dtype=x.dtype, device=dev)
+    db_qkv = torch.empty(3 * d, dtype=torch.float32, device=dev) if bias_grads else None
+    db_o = torch.empty(d, dtype=torch.float32, device=dev) if bias_grads else None
+    if workspace is None:
+        workspace = torch.empty(max(block_backward_workspace_bytes(desc, n), 1),
+                                dtype=torch.uint8, device=dev)
+    _check(_lib.dit_block_backward(
+        ctypes.byref(desc), x.data_ptr(), dout.data_ptr(), modality.data_ptr(), pos.data_ptr(),
+        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), n, table.data_ptr(),
+        w_qkv.data_ptr(), _ptr(b_qkv), w_o.data_ptr(), _ptr(b_o), dx.data_ptr(),
+        dtable.data_ptr(), dw_qkv.data_ptr(), _ptr(db_qkv), dw_o.data_ptr(), _ptr(db_o),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dict(dx=dx, dtable=dtable, dw_qkv=dw_qkv, dw_o=dw_o, db_qkv=db_qkv, db_o=db_o)

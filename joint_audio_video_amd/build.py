@@ -35,7 +35,7 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["abi.cpp", "layout.cpp", "adaln.hip", "rope.hip", "gemm.hip", "attn.hip",
-           "attn_bwd.hip", "denoise.hip", "nft.hip"]
+           "attn_bwd.hip", "grad.hip", "denoise.hip", "nft.hip"]
 
 
 def _compile(src: str) -> str:

@@ -955,6 +955,177 @@ extern "C" dit_status dit_block_forward_fp8(
 }
 
 // ---------------------------------------------------------------------------
+// Backward pass of the attention half.
+//
+// Workspace (each region 256-byte aligned; Np = n_tokens rounded up to 64,
+// PT = round256(D * Np * 2) bytes, one bf16 [N][D] or [D][Np] plane):
+//   Y | Q K V (3 PT; later dqkv^T [3D][Np]) | O (later dy) | ZD (z, then do) |
+//   DZ | T1 (dz^T, then y^T) | T2 (o^T) | DQKV [N][3D] (3 PT) | LSE, DELTA
+//   [H][N] float | WT (W_o^T, then W_qkv^T) | STATS [N] float2 | column-sum
+//   partials.
+namespace {
+struct BwdLayout {
+  size_t pt, y, qkv, o, zd, dz, t1, t2, dqkv, lse, delta, wt, stats, part, total;
+};
+BwdLayout bwd_layout(int64_t n, int32_t d, int32_t h) {
+  BwdLayout L{};
+  const size_t np = (size_t)((n + 63) / 64 * 64);
+  L.pt = round256((size_t)d * np * 2);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round256(bytes);
+    return at;
+  };
+  L.y = take(L.pt);
+  L.qkv = take(3 * L.pt);
+  L.o = take(L.pt);
+  L.zd = take(L.pt);
+  L.dz = take(L.pt);
+  L.t1 = take(L.pt);
+  L.t2 = take(L.pt);
+  L.dqkv = take(3 * L.pt);
+  L.lse = take((size_t)h * (size_t)n * 4);
+  L.delta = take((size_t)h * (size_t)n * 4);
+  L.wt = take((size_t)3 * d * d * 2);
+  L.stats = take((size_t)n * 8);
+  L.part = take(std::max(colsum_partial_bytes(n, 3 * d, 1), colsum_partial_bytes(n, d, 3)));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+extern "C" size_t dit_block_backward_workspace_bytes(const dit_block_desc* d, int64_t n_tokens) {
+  if (!d || d->dtype != DIT_BF16 || d->d_model < 1 || d->n_heads < 1 || n_tokens < 0) return 0;
+  return bwd_layout(n_tokens, d->d_model, d->n_heads).total;
+}
+
+extern "C" dit_status dit_block_backward(
+    const dit_block_desc* d, const void* x, const void* dout, const uint8_t* modality,
+    const int32_t* pos_thw, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+    int64_t n_tokens, const float* ada_table, const void* w_qkv, const void* b_qkv,
+    const void* w_o, const void* b_o, void* dx, float* dtable, void* dw_qkv, float* db_qkv,
+    void* dw_o, float* db_o, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "dit_block_backward";
+  if (!d) return fail(DIT_EINVAL, "%s: null descriptor", who);
+  if (d->dtype != DIT_BF16)
+    return fail(DIT_EUNSUPPORTED, "%s: bf16 only (dtype %d)", who, (int)d->dtype);
+  const int32_t D = d->d_model, H = d->n_heads, Dh = d->head_dim;
+  if (D < 1 || H < 1 || Dh < 1 || (int64_t)H * Dh != D)
+    return fail(DIT_EINVAL, "%s: d_model %d != n_heads %d * head_dim %d", who, D, H, Dh);
+  if (!x || !dout || !modality || !pos_thw || !cu_seqlens || !ada_table || !w_qkv || !w_o ||
+      !dx || !dtable || !dw_qkv || !dw_o)
+    return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (D % 64 != 0) return fail(DIT_EUNSUPPORTED, "%s: d_model %d not a multiple of 64", who, D);
+  const BwdLayout L = bwd_layout(n_tokens, D, H);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes,
+                L.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", who);
+  char* ws = static_cast<char*>(workspace);
+  char *Y = ws + L.y, *Q = ws + L.qkv, *K = Q + L.pt, *V = K + L.pt, *O = ws + L.o;
+  char *ZD = ws + L.zd, *DZ = ws + L.dz, *T1 = ws + L.t1, *T2 = ws + L.t2, *DQKV = ws + L.dqkv;
+  float* LSE = reinterpret_cast<float*>(ws + L.lse);
+  float* DELTA = reinterpret_cast<float*>(ws + L.delta);
+  char* WT = ws + L.wt;
+  float* STATS = reinterpret_cast<float*>(ws + L.stats);
+  float* PART = reinterpret_cast<float*>(ws + L.part);
+  const int64_t np = (n_tokens + 63) / 64 * 64;
+
+  // The stages' own checks, before anything is enqueued.
+  if (dit_status st = adaln_check(DIT_BF16, x, D, modality, ada_table, Y, D, n_tokens, D,
+                                  d->ln_eps))
+    return st;
+  if (dit_status st = proj_check("qkv_project", DIT_BF16, Y, D, w_qkv, Q, D, n_tokens, D, D))
+    return st;
+  if (dit_status st = rope_check(DIT_BF16, Q, D, K, D, pos_thw, n_tokens, H, Dh,
+                                 d->rope_sections, d->rope_theta))
+    return st;
+  if (dit_status st = attn_check(DIT_BF16, Q, D, K, D, V, D, O, D, cu_seqlens, n_seqs, max_seqlen,
+                                 n_tokens, H, Dh, d->softmax_scale))
+    return st;
+  if (!aligned16(x) || !aligned16(dout) || !aligned16(dx) || !aligned16(dw_qkv) ||
+      !aligned16(dw_o) || !aligned16(dtable) || (b_qkv && !aligned16(b_qkv)) ||
+      (b_o && !aligned16(b_o)) || !aligned16(w_o))
+    return fail(DIT_EUNSUPPORTED, "%s: pointers must be 16-byte aligned", who);
+  if (spans_overlap(dx, D, x, D, n_tokens, D, 2))
+    return fail(DIT_EINVAL, "%s: dx overlaps x", who);
+  if (n_tokens == 0) return DIT_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
+  double freq[64], nfreq[64];
+  rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
+  for (int i = 0; i < Dh / 2; ++i) nfreq[i] = -freq[i];
+  const int causal = d->causal != 0;
+  const int s_t = d->rope_sections[0], s_h = d->rope_sections[1];
+  hipError_t e;
+#define DIT_BWD(call, what)                                          \
+  e = (call);                                                        \
+  if (e != hipSuccess) return hip_fail(e, "dit_block_backward: " what)
+  // forward stages, recomputed (nothing is saved between the calls)
+  DIT_BWD(launch_adaln(1, x, D, modality, ada_table, Y, D, n_tokens, D, d->ln_eps, s), "adaln");
+  GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr, D, (int64_t)(L.pt / 2)};
+  DIT_BWD(launch_gemm(1, Y, D, w_qkv, Q, D, n_tokens, 3 * D, D, ep_qkv, s), "qkv");
+  DIT_BWD(launch_rope(1, Q, D, K, D, Q, D, K, D, pos_thw, n_tokens, H, Dh, s_t, s_h, freq, s),
+          "rope");
+  DIT_BWD(launch_attn(1, Q, D, K, D, V, D, O, D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
+                      scale, causal, LSE, s),
+          "attention");
+  GemmEpilogue ep_z{0, b_o, nullptr, 0, nullptr, nullptr};
+  DIT_BWD(launch_gemm(1, O, D, w_o, ZD, D, n_tokens, D, D, ep_z, s), "z");
+  // out = x + gate * z: dz, the gate rows, db_o
+  DIT_BWD(launch_gate_scale(dout, D, modality, ada_table, DZ, D, n_tokens, D, s), "gate");
+  DIT_BWD(launch_colsum(1, dout, D, ZD, D, nullptr, modality, n_tokens, D, PART, dtable + 2 * D,
+                        3 * D, s),
+          "gate rows");
+  if (db_o)
+    DIT_BWD(launch_colsum(0, DZ, D, nullptr, 0, nullptr, nullptr, n_tokens, D, PART, db_o, 0, s),
+            "db_o");
+  // z = o W_o^T + b_o: do = dz W_o, dW_o = dz^T o
+  GemmEpilogue plain{0, nullptr, nullptr, 0, nullptr, nullptr};
+  DIT_BWD(launch_transpose(w_o, D, D, D, WT, D, s), "W_o^T");
+  DIT_BWD(launch_gemm(1, DZ, D, WT, ZD, D, n_tokens, D, D, plain, s), "do");
+  DIT_BWD(launch_transpose(DZ, D, n_tokens, D, T1, np, s), "dz^T");
+  DIT_BWD(launch_transpose(O, D, n_tokens, D, T2, np, s), "o^T");
+  DIT_BWD(launch_gemm(1, T1, np, T2, dw_o, D, D, D, (int)np, plain, s), "dW_o");
+  // attention, then the rotation's transpose (the rotation by the negated angle)
+  DIT_BWD(launch_attn_bwd(Q, D, K, D, V, D, O, D, ZD, D, LSE, DQKV, 3 * D, DQKV + 2 * D, 3 * D,
+                          DQKV + 4 * D, 3 * D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, scale,
+                          causal, DELTA, s),
+          "attention backward");
+  DIT_BWD(launch_rope(1, DQKV, 3 * D, DQKV + 2 * D, 3 * D, DQKV, 3 * D, DQKV + 2 * D, 3 * D,
+                      pos_thw, n_tokens, H, Dh, s_t, s_h, nfreq, s),
+          "rope backward");
+  if (db_qkv)
+    DIT_BWD(launch_colsum(0, DQKV, 3 * D, nullptr, 0, nullptr, nullptr, n_tokens, 3 * D, PART,
+                          db_qkv, 0, s),
+            "db_qkv");
+  // [q k v] = y W_qkv^T + b: dy = dqkv W_qkv, dW_qkv = dqkv^T y
+  char* DY = O;
+  char* DQKVT = Q;
+  DIT_BWD(launch_transpose(w_qkv, D, 3 * D, D, WT, 3 * D, s), "W_qkv^T");
+  DIT_BWD(launch_gemm(1, DQKV, 3 * D, WT, DY, D, n_tokens, D, 3 * D, plain, s), "dy");
+  DIT_BWD(launch_transpose(DQKV, 3 * D, n_tokens, 3 * D, DQKVT, np, s), "dqkv^T");
+  DIT_BWD(launch_transpose(Y, D, n_tokens, D, T1, np, s), "y^T");
+  DIT_BWD(launch_gemm(1, DQKVT, np, T1, dw_qkv, D, 3 * D, D, (int)np, plain, s), "dW_qkv");
+  // AdaLN: dx, then the shift and scale rows
+  DIT_BWD(launch_adaln_bwd(x, D, DY, D, dout, D, modality, ada_table, dx, D, STATS, n_tokens, D,
+                           d->ln_eps, s),
+          "adaln backward");
+  DIT_BWD(launch_colsum(0, DY, D, nullptr, 0, nullptr, modality, n_tokens, D, PART, dtable, 3 * D,
+                        s),
+          "shift rows");
+  DIT_BWD(launch_colsum(2, DY, D, x, D, STATS, modality, n_tokens, D, PART, dtable + D, 3 * D, s),
+          "scale rows");
+#undef DIT_BWD
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------------------
 
 extern "C" dit_status dit_profile_enable(int32_t max_calls) {
   clear_error();

@@ -222,6 +222,96 @@ hipError_t dispatch(const void* x, int64_t ld_x, const uint8_t* mod, const float
   return hipErrorInvalidValue;
 }
 
+// Backward of y = xhat (1 + scale[m]) + shift[m] for one row per wave
+// (bf16): with dxh = dy (1 + scale[m]), dx = dres + rstd (dxh - mean(dxh) -
+// xhat mean(dxh xhat)); the row's mean and rstd go to stats for the table
+// gradients.  x and dy stay in registers between the two passes.
+template <int NV>
+__global__ __launch_bounds__(64 * kWaves) void adaln_bwd_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* __restrict__ dy, int64_t ld_dy,
+    const uint16_t* dres, int64_t ld_dres, const uint8_t* __restrict__ mod,
+    const float* __restrict__ table, uint16_t* dx, int64_t ld_dx, float2* __restrict__ stats,
+    int64_t n, int d, float eps) {
+  constexpr int E = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int nvec = d / E;
+  uint4 xr[NV], gr[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    xr[i] = c < nvec ? ld_stream(reinterpret_cast<const uint4*>(x + row * ld_x) + c)
+                     : make_uint4(0, 0, 0, 0);
+    gr[i] = c < nvec ? ld_stream(reinterpret_cast<const uint4*>(dy + row * ld_dy) + c)
+                     : make_uint4(0, 0, 0, 0);
+  }
+  const float inv_d = 1.0f / (float)d;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float f[E];
+    unpack(xr[i], f, uint16_t());
+#pragma unroll
+    for (int e = 0; e < E; ++e) s += f[e];
+  }
+  const float mean = wave_sum(s) * inv_d;
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i < nvec) {
+      float f[E];
+      unpack(xr[i], f, uint16_t());
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float t = f[e] - mean;
+        ss = fmaf(t, t, ss);
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(ss) * inv_d + eps);
+  const float* scale = table + (size_t)(3 * mod[row] + 1) * d;
+  // dxh and xhat of vector i
+  auto terms = [&](int i, float* xh, float* g) {
+    float f[E];
+    unpack(xr[i], f, uint16_t());
+    unpack(gr[i], g, uint16_t());
+    const float4* sc = reinterpret_cast<const float4*>(scale) + 2 * (lane + 64 * i);
+    const float4 s0 = sc[0], s1 = sc[1];
+    const float sv[E] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      xh[e] = (f[e] - mean) * rstd;
+      g[e] *= 1.0f + sv[e];
+    }
+  };
+  float a1 = 0.0f, a2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i >= nvec) continue;
+    float xh[E], g[E];
+    terms(i, xh, g);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      a1 += g[e];
+      a2 = fmaf(g[e], xh[e], a2);
+    }
+  }
+  const float m1 = wave_sum(a1) * inv_d, m2 = wave_sum(a2) * inv_d;
+  if (lane == 0) stats[row] = make_float2(mean, rstd);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nvec) continue;
+    float xh[E], g[E], r[E];
+    terms(i, xh, g);
+    unpack(*(reinterpret_cast<const uint4*>(dres + row * ld_dres) + c), r, uint16_t());
+#pragma unroll
+    for (int e = 0; e < E; ++e) r[e] += rstd * (g[e] - m1 - xh[e] * m2);
+    *(reinterpret_cast<uint4*>(dx + row * ld_dx) + c) = pack(r, uint16_t());
+  }
+}
+
 }  // namespace
 
 hipError_t launch_adaln(int bf16, const void* x, int64_t ld_x, const uint8_t* mod,
@@ -239,6 +329,36 @@ hipError_t launch_adaln_fp8(int bf16, const void* x, int64_t ld_x, const uint8_t
   return bf16 ? dispatch<uint16_t, true>(x, ld_x, mod, table, nullptr, ld_q, n, d, eps, q, scales,
                                          s)
               : dispatch<float, true>(x, ld_x, mod, table, nullptr, ld_q, n, d, eps, q, scales, s);
+}
+
+}  // namespace dit
+
+namespace dit {
+
+hipError_t launch_adaln_bwd(const void* x, int64_t ld_x, const void* dy, int64_t ld_dy,
+                            const void* dres, int64_t ld_dres, const uint8_t* mod,
+                            const float* table, void* dx, int64_t ld_dx, float* stats, int64_t n,
+                            int d, float eps, hipStream_t s) {
+  if (d % 8 != 0 || d > 16384) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  const int need = (d / 8 + 63) / 64;
+  const dim3 grid((unsigned)((n + kWaves - 1) / kWaves)), block(64 * kWaves);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* gp = static_cast<const uint16_t*>(dy);
+  const uint16_t* rp = static_cast<const uint16_t*>(dres);
+  uint16_t* op = static_cast<uint16_t*>(dx);
+  float2* st = reinterpret_cast<float2*>(stats);
+#define DIT_ADALN_BWD_CASE(NVV)                                                                 \
+  if (need <= NVV) {                                                                            \
+    adaln_bwd_kernel<NVV><<<grid, block, 0, s>>>(xp, ld_x, gp, ld_dy, rp, ld_dres, mod, table,  \
+                                                 op, ld_dx, st, n, d, eps);                     \
+    return hipGetLastError();                                                                   \
+  }
+  DIT_ADALN_BWD_CASE(1) DIT_ADALN_BWD_CASE(2) DIT_ADALN_BWD_CASE(4) DIT_ADALN_BWD_CASE(6)
+  DIT_ADALN_BWD_CASE(8) DIT_ADALN_BWD_CASE(10) DIT_ADALN_BWD_CASE(12) DIT_ADALN_BWD_CASE(16)
+  DIT_ADALN_BWD_CASE(24) DIT_ADALN_BWD_CASE(32)
+#undef DIT_ADALN_BWD_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dit

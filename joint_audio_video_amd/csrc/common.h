@@ -164,6 +164,30 @@ hipError_t launch_nft_loss(int bf16, const void* v_theta, int64_t ld_vt, const v
                            float scale, float* grad, int64_t ld_g, float* loss_out,
                            void* workspace, hipStream_t s);
 
+// Backward-pass helpers (bf16).  Transpose: dst [cols][ld_dst] = src^T, zero
+// in columns rows..ld_dst-1; cols, ld_dst multiples of 64.
+hipError_t launch_transpose(const void* src, int64_t ld_src, int64_t rows, int cols, void* dst,
+                            int64_t ld_dst, hipStream_t s);
+// out = table[mod][GATE] * g (row-wise), d a multiple of 8.
+hipError_t launch_gate_scale(const void* g, int64_t ld_g, const uint8_t* mod, const float* table,
+                             void* out, int64_t ld_out, int64_t n, int d, hipStream_t s);
+// Column sums over n rows (deterministic): mode 0 sums a, 1 a * b, 2
+// a * (b - mean) * rstd with stats float2 [n] (mean, rstd); per modality into
+// out[m * out_gstride + j] (m = 0..2) when mod is given, else into out[j].
+// partial: colsum_partial_bytes(n, c, groups) bytes of scratch.
+constexpr int kColsumRows = 256;
+size_t colsum_partial_bytes(int64_t n, int c, int groups);
+hipError_t launch_colsum(int mode, const void* a, int64_t lda, const void* b, int64_t ldb,
+                         const float* stats, const uint8_t* mod, int64_t n, int c, float* partial,
+                         float* out, int64_t out_gstride, hipStream_t s);
+// AdaLN backward: dx = dres + rstd (dxh - mean(dxh) - xhat mean(dxh xhat)) with
+// dxh = dy (1 + table[mod][SCALE]); stats float2 [n] (mean, rstd) out.
+// dx may be dres.
+hipError_t launch_adaln_bwd(const void* x, int64_t ld_x, const void* dy, int64_t ld_dy,
+                            const void* dres, int64_t ld_dres, const uint8_t* mod,
+                            const float* table, void* dx, int64_t ld_dx, float* stats, int64_t n,
+                            int d, float eps, hipStream_t s);
+
 // sigmas: host {video, video_next, audio, audio_next}; sign +1 or -1.
 hipError_t launch_denoise(int bf16, float* z, int64_t ld_z, const void* v, int64_t ld_v,
                           float* x0, int64_t ld_x0, const uint8_t* mod, const uint8_t* anchor,

@@ -144,3 +144,96 @@ def test_attention_backward_full_shape(jav):
     r = rel_l2(dv_sum, do_sum)
     print(f"  full: sum dv vs sum dout rel_l2={r:.2e}", flush=True)
     assert r <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# The attention half's backward
+# ---------------------------------------------------------------------------
+
+def _layout(jav, name, n, cu):
+    import torch
+    wl = synth.WORKLOADS[name]
+    grids = [r.grid for r in wl.requests]
+    lay_d, lay = jav.pack_layout(grids), oracle.pack_layout(grids)
+    cu = list(lay["cu_seqlens"]) if cu is None else list(cu)
+    mod, pos = np.asarray(lay["modality"])[:n], np.asarray(lay["pos"])[:n]
+    dev_lay = (dev_int(np.asarray(lay_d["modality"])[:n], torch.uint8),
+               dev_int(np.asarray(lay_d["pos"])[:n], torch.int32),
+               dev_int(np.asarray(cu), torch.int32), int(max(b - a for a, b in zip(cu, cu[1:]))))
+    return mod, pos, cu, dev_lay
+
+
+def _block_backward(jav, name, n=None, cu=None, causal=False, with_bias=False, inplace=False):
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, n_tokens=n, with_bias=with_bias)
+    n, d = inp.x.shape
+    mod, pos, cu, (mod_d, pos_d, cu_d, ms) = _layout(jav, name, n, cu)
+    dout = synth.normal_array((n, d), seed=1500 + n, dtype="bf16")
+    desc = jav.block_desc(jav.DIT_BF16, d, wl.n_heads, wl.head_dim, wl.sections, wl.theta,
+                          wl.eps, causal=causal)
+    print(f"block backward {name} n={n} segs={len(cu) - 1} causal={causal} bias={with_bias} "
+          f"inplace={inplace}", flush=True)
+    x_d, dout_d = dev(inp.x, "bf16"), dev(dout, "bf16")
+    args = (desc, x_d, dout_d, mod_d, pos_d, cu_d, ms, dev(inp.table, "f32"),
+            dev(inp.w_qkv, "bf16"), dev(inp.w_o, "bf16"))
+    kw = dict(b_qkv=dev(inp.b_qkv, "bf16") if with_bias else None,
+              b_o=dev(inp.b_o, "bf16") if with_bias else None)
+    again = jav.block_backward(*args, **kw)
+    got = jav.block_backward(*args, dx=dout_d if inplace else None, **kw)
+    _sync()
+    for key in ("dtable", "dw_qkv", "dw_o", "db_qkv", "db_o"):
+        assert torch.equal(got[key], again[key]), key          # deterministic
+    assert torch.equal(got["dx"], again["dx"])
+    ref = oracle.block_backward(inp.x, mod, pos, cu, inp.table, inp.w_qkv, inp.w_o, dout,
+                                n_heads=wl.n_heads, head_dim=wl.head_dim, sections=wl.sections,
+                                theta=wl.theta, eps=wl.eps, causal=causal,
+                                b_qkv=inp.b_qkv if with_bias else None,
+                                b_o=inp.b_o if with_bias else None)
+    check_grad(host(got["dx"]), ref["dx"], f"{name}.dx")
+    check_grad(host(got["dw_o"]), ref["dw_o"], f"{name}.dw_o")
+    check_grad(host(got["dw_qkv"]), ref["dw_qkv"], f"{name}.dw_qkv")
+    check_grad(host(got["db_o"]), ref["db_o"], f"{name}.db_o")
+    check_grad(host(got["db_qkv"]), ref["db_qkv"], f"{name}.db_qkv")
+    present = np.unique(mod)
+    for r, row in enumerate(("shift", "scale", "gate")):
+        check_grad(host(got["dtable"])[present, r], ref["dtable"][present, r],
+                   f"{name}.dtable.{row}")
+    absent = np.setdiff1d(np.arange(3), present)
+    assert not host(got["dtable"])[absent].any()
+
+
+def test_block_backward_small(jav):
+    _block_backward(jav, "small")
+
+
+def test_block_backward_ragged_causal_bias_inplace(jav):
+    _block_backward(jav, "small", n=1000, cu=[0, 617, 1000], causal=True, with_bias=True,
+                    inplace=True)
+
+
+def test_block_backward_full_shape(jav):
+    """58,758 tokens: finite and deterministic; db_o against the sum of gate * dout from the
+    inputs alone; absent modalities get zero table rows (the full pack has all three)."""
+    import torch
+    wl = synth.WORKLOADS["full"]
+    inp = synth.block_inputs(wl)
+    n, d = inp.x.shape
+    mod, _, cu, (mod_d, pos_d, cu_d, ms) = _layout(jav, "full", n, None)
+    dout = synth.normal_array((n, d), seed=1600, dtype="bf16")
+    desc = jav.block_desc(jav.DIT_BF16, d, wl.n_heads, wl.head_dim, wl.sections, wl.theta,
+                          wl.eps)
+    print(f"block backward full n={n}", flush=True)
+    args = (desc, dev(inp.x, "bf16"), dev(dout, "bf16"), mod_d, pos_d, cu_d, ms,
+            dev(inp.table, "f32"), dev(inp.w_qkv, "bf16"), dev(inp.w_o, "bf16"))
+    a = jav.block_backward(*args)
+    b = jav.block_backward(*args)
+    _sync()
+    for key in ("dx", "dtable", "dw_qkv", "dw_o", "db_qkv", "db_o"):
+        assert torch.isfinite(a[key].float()).all(), key
+        assert torch.equal(a[key], b[key]), key
+    gate = inp.table[mod, 2, :].astype(np.float64)
+    want = (gate * dout.astype(np.float64)).sum(0)
+    r = rel_l2(host(a["db_o"]), want)
+    print(f"  full.db_o: rel_l2={r:.2e}", flush=True)
+    assert r <= 1e-2
