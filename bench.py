@@ -17,7 +17,8 @@ DiffusionNFT loss and its gradient (one sample per request); ``fp8`` times the
 block's four projections in FP8 (e4m3 codes, per-row scales) against the
 e4m3 MFMA peak, the row quantization and the FP8-output AdaLN against HBM,
 and the two halves of the block with FP8 projections (``block_fp8``,
-``ffn_fp8``, ms per call).
+``ffn_fp8``, ms per call).  ``backward`` times the attention backward and the
+whole backward pass of the attention half (which recomputes its forward).
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
 workload on the host cores.
 """
@@ -232,6 +233,8 @@ def main() -> int:
                     help="skip timing the DiffusionNFT loss")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip timing the FP8 projections")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward pass of the attention half")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
@@ -559,6 +562,61 @@ def main() -> int:
         del wq, wo, w1q, w2q, xq, hq, qkv8, h8, out8, ws_b8, ws_f8, table8
         print(f"# fp8: {fp8_rec}", file=sys.stderr, flush=True)
 
+    # The backward pass of the attention half: the attention backward on its own
+    # (given q', k', v, o, lse and dout) and the whole dit_block_backward (which
+    # recomputes the forward).  Algorithmic FLOPs: attention backward = 2.5 x the
+    # forward's (five products of the same size, S recomputed); the block
+    # backward = its forward again + z + attention backward + four GEMMs (do,
+    # dW_o, dy, dW_qkv).
+    bwd_rec = None
+    if not args.no_backward:
+        print("# backward ...", file=sys.stderr, flush=True)
+        dout = bf(synth.normal_array((n, d), seed=wl.seed + 4000, dtype="bf16"))
+        q_r = bf(synth.normal_array((n, d), seed=wl.seed + 4001, dtype="bf16"))
+        k_r = bf(synth.normal_array((n, d), seed=wl.seed + 4002, dtype="bf16"))
+        v_r = bf(synth.normal_array((n, d), seed=wl.seed + 4003, dtype="bf16"))
+        o_r, lse_r = jav.attn_packed_lse(q_r, k_r, v_r, cu, ms_len, H, Dh, causal=args.causal)
+        dq_r, dk_r, dv_r = (torch.empty_like(q_r) for _ in range(3))
+        aws = torch.empty(jav.attn_backward_workspace_bytes(n, H), dtype=torch.uint8, device=dev)
+        bws = torch.empty(jav.block_backward_workspace_bytes(desc, n), dtype=torch.uint8,
+                          device=dev)
+        dx_b = torch.empty_like(x)
+        ops_b = {
+            "attn_bwd": (3, lambda: jav.attn_packed_backward(
+                q_r, k_r, v_r, o_r, dout, lse_r, cu, ms_len, H, Dh, causal=args.causal, dq=dq_r,
+                dk=dk_r, dv=dv_r, workspace=aws, stream=stream)),
+            "block_bwd": (2, lambda: jav.block_backward(
+                desc, x, dout, mod, pos, cu, ms_len, table, w_qkv, w_o, dx=dx_b, workspace=bws,
+                stream=stream)),
+        }
+        tb = {}
+        for name, (reps, fn) in ops_b.items():
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tb[name] = e0.elapsed_time(e1) / reps
+        a_f, q_f, o_f = block_flops(n, d, lay["cu_seqlens"].tolist(), args.causal)
+        attn_bwd_f = 2.5 * a_f
+        blk_bwd_f = (a_f + q_f + o_f) + o_f + attn_bwd_f + 2 * o_f + 2 * q_f
+        bwd_rec = {
+            "attention_backward_ms": round(tb["attn_bwd"], 3),
+            "attention_backward_tflops": round(attn_bwd_f / (tb["attn_bwd"] * 1e-3) / 1e12, 1),
+            "attention_backward_frac_of_bf16_peak": round(
+                attn_bwd_f / (tb["attn_bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "block_backward_ms": round(tb["block_bwd"], 3),
+            "block_backward_tflops": round(blk_bwd_f / (tb["block_bwd"] * 1e-3) / 1e12, 1),
+            "block_backward_frac_of_bf16_peak": round(
+                blk_bwd_f / (tb["block_bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+        del dout, q_r, k_r, v_r, o_r, lse_r, dq_r, dk_r, dv_r, aws, bws, dx_b
+        print(f"# backward: {bwd_rec}", file=sys.stderr, flush=True)
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -627,6 +685,8 @@ def main() -> int:
         rec["nft_loss"] = nft_rec
     if fp8_rec is not None:
         rec["fp8_projections"] = fp8_rec
+    if bwd_rec is not None:
+        rec["backward"] = bwd_rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle

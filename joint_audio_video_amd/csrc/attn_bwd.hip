@@ -10,8 +10,9 @@
 //
 // Three launches, no atomics, deterministic:
 //   * attn_delta_kernel: delta[h][row], one thread per (row, head).
-//   * attn_bwd_dkdv_kernel: a workgroup owns 128 keys of one (segment,
-//     head) (32 per wave, their K and V in registers) and streams the
+//   * attn_bwd_dkdv_kernel: a workgroup owns 256 keys of one (segment,
+//     head) (32 per wave, their K and V in registers; 8 waves, two per SIMD,
+//     share every streamed tile) and streams the
 //     segment's queries in tiles of 64 (q, do, lse, delta double-buffered in
 //     LDS).  Per tile a wave computes S = q k^T and dP = do v^T (rows =
 //     queries, so the 32x32 accumulator gives each lane one key column), P
@@ -20,7 +21,8 @@
 //     the bf16 B operand in the accumulator's own row order (the k index of
 //     a product can be permuted as long as both operands agree).
 //   * attn_bwd_dq_kernel: a workgroup owns 128 queries (q, do, lse, delta of
-//     its 32 per wave in registers) and streams the keys in tiles of 64:
+//     its 32 per wave in registers; two workgroups per CU) and streams the
+//     keys in tiles of 64:
 //     S^T = k q^T and dP^T = v do^T (rows = keys), dS^T, then
 //     dq^T += k^T dS^T, as the forward kernel computes O^T.
 // All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P
@@ -34,11 +36,14 @@ namespace dit {
 namespace {
 
 constexpr int DH = 128;
-constexpr int kWavesB = 4;
-constexpr int kThreadsB = 64 * kWavesB;
-constexpr int BLK = 32 * kWavesB;                        // keys (dk, dv) or queries (dq) per workgroup
-constexpr int TB = 64;                                   // streamed rows per tile
-constexpr int kLoads = TB * DH * 2 / 16 / kThreadsB;     // 16-byte loads per thread per tile
+constexpr int TB = 64;                 // streamed rows per tile
+// dq: 4 waves (128 queries) per workgroup, two workgroups per CU.
+constexpr int kThreadsQ = 256;
+constexpr int BLKQ = kThreadsQ / 2;
+// dk, dv: 8 waves (256 keys) per workgroup, two waves per SIMD sharing each
+// streamed tile.
+constexpr int kThreadsKV = 512;
+constexpr int BLKKV = kThreadsKV / 2;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -52,33 +57,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // physical chunk c ^ (r & 7).
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 
-// Fragment whose 32 rows are tile rows: lane (l32, g) holds row r, d = 16 ks + 8 g .. +7.
-__device__ __forceinline__ bf16x8 row_frag(const uint16_t* t, int r, int ks, int g) {
-  return *reinterpret_cast<const bf16x8*>(t + r * DH + swz(r, 2 * ks + g) * 8);
-}
+// Fragment reads with per-lane bases and compile-time offsets (the swizzle
+// distributes over the lane bits, so every address is one of a few per-lane
+// bases plus a constant, which the LDS instructions take as an immediate).
+//
+// Row fragment: lane (l32, g) reads tile row rb + l32 (rb a multiple of 8),
+// d = 16 ks + 8 g .. +7, i.e. logical chunk 2 ks + g; with ks = 4 a + j the
+// physical chunk is 8 a + ((2 j + g) ^ (l32 & 7)).
+struct RowFrag {
+  int off[4];
+  __device__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) off[j] = l32 * DH + 8 * ((2 * j + g) ^ (l32 & 7));
+  }
+  __device__ __forceinline__ bf16x8 read(const uint16_t* t, int rb, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(t + off[ks & 3] + 64 * (ks >> 2) + rb * DH);
+  }
+};
 
-// Fragment whose 32 rows are d = 32 db + l32 and whose 8 k values are tile
-// rows b0 + 4g + {0..3} and b0 + 4g + 8 + {0..3} (transposing reads: in each
-// 16-lane group, lane i supplies row b0 + 4g + (i >> 2), columns
-// 32 db + 16 ((lane >> 4) & 1) + 4 (i & 3) .. +3, and receives column
-// 32 db + l32 of the four rows).
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* t, int b0, int db, int lane) {
-  const int i = lane & 15, g = lane >> 5;
-  const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-  const int r0 = b0 + 4 * g + (i >> 2), r1 = r0 + 8;
-  const lds_u16* p0 = (const lds_u16*)t + r0 * DH + swz(r0, col >> 3) * 8 + (col & 7);
-  const lds_u16* p1 = (const lds_u16*)t + r1 * DH + swz(r1, col >> 3) * 8 + (col & 7);
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
+// Transposed fragment: 32 rows d = 32 db + l32, 8 k values = tile rows
+// b0 + 4g + {0..3} and b0 + 4g + 8 + {0..3} (b0 a multiple of 16), two
+// ds_read_b64_tr_b16.  In each 16-lane group (t = (lane >> 4) & 1) lane i
+// supplies row b0 + y, y = 4 g + (i >> 2), columns 32 db + 16 t + 4 (i & 3)
+// .. +3 and receives column 32 db + l32 of the four rows.  The column's
+// chunk 4 db + x (x = 2 t + ((i & 3) >> 1)) sits at 4 (db ^ g) + (x ^ (y & 3)),
+// i.e. 32 db + 32 g (db even) or 32 db - 32 g (db odd) elements plus a lane part.
+struct TrFrag {
+  int off[2];
+  __device__ void init(int lane) {
+    const int i = lane & 15, t = (lane >> 4) & 1, g = lane >> 5;
+    const int y = 4 * g + (i >> 2), x = 2 * t + ((i & 3) >> 1);
+    const int base = y * DH + 8 * (x ^ (y & 3)) + 4 * (i & 1);
+    off[0] = base + 32 * g;
+    off[1] = base - 32 * g;
+  }
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int b0, int db) const {
+    const lds_u16* p = (const lds_u16*)tile + off[db & 1] + 32 * db + b0 * DH;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * DH));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
 
 // Accumulator element e of a 32x32 block lies in row 8 (e / 4) + 4 g + e % 4.
 __device__ __forceinline__ int acc_row(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
 
-// Global -> LDS tile loader: slot s = threads * i + tid is tile row s / 16,
-// physical chunk s % 16 (the swizzle applied on the global side).
+// Global -> LDS tile loader for a workgroup of THREADS threads: slot
+// s = THREADS * i + tid is tile row s / 16, physical chunk s % 16 (the
+// swizzle applied on the global side).
+template <int THREADS>
 struct TileLoader {
+  static constexpr int kLoads = TB * DH * 2 / 16 / THREADS;   // 16-byte loads per thread
   __amdgpu_buffer_rsrc_t rs;
   uint32_t off[kLoads];
   uint32_t tstep;
@@ -87,7 +117,7 @@ struct TileLoader {
     const int srow = tid >> 4, pch = tid & 15;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int row = (kThreadsB / 16) * i + srow;
+      const int row = (THREADS / 16) * i + srow;
       off[i] = (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)swz(row, pch) * 16u;
     }
     tstep = (uint32_t)TB * (uint32_t)ld * 2u;
@@ -95,7 +125,7 @@ struct TileLoader {
   __device__ void issue(uint16_t* dst, int tile, int wave) const {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + (kThreadsB * i + 64 * wave) * 8, 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + (THREADS * i + 64 * wave) * 8, 16,
                                                off[i], (int)(tile * tstep), 0, 0);
   }
 };
@@ -137,7 +167,7 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16& acc, in
   }
 }
 
-__global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
     int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -148,36 +178,45 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ds0[TB * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Ds1[TB * DH];
   __shared__ float Ls0[TB], Ls1[TB], Es0[TB], Es1[TB];   // lse * log2(e), delta
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[BLKKV * DH];   // this block's V rows
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
-  const int kb0 = seg0 + (int)blockIdx.x * BLK;
+  const int kb0 = seg0 + (int)blockIdx.x * BLKKV;
   if (kb0 >= seg1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int key = kb0 + 32 * wave + l32;
+  RowFrag rf;
+  TrFrag tf;
+  rf.init(lane);
+  tf.init(lane);
 
-  // K and V^T operands of this wave's 32 keys: lane (key l32, half g) holds
-  // d = 16 ks + 8 g .. +7.
-  bf16x8 kf[DH / 16], vf[DH / 16];
+  // K^T operand of this wave's 32 keys in registers: lane (key l32, half g)
+  // holds d = 16 ks + 8 g .. +7.  V's rows of the whole block wait in LDS
+  // (the same operand read per tile), which keeps a wave within 256
+  // registers, so two waves share each SIMD.
+  bf16x8 kf[DH / 16];
   {
     const bool live = key < seg1;
     const uint16_t* kp = k + (int64_t)key * ld_k + h * DH + 8 * g;
-    const uint16_t* vp = v + (int64_t)key * ld_v + h * DH + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
       const uint4 a = live ? *reinterpret_cast<const uint4*>(kp + 16 * ks) : make_uint4(0, 0, 0, 0);
-      const uint4 b = live ? *reinterpret_cast<const uint4*>(vp + 16 * ks) : make_uint4(0, 0, 0, 0);
       kf[ks] = __builtin_bit_cast(bf16x8, a);
-      vf[ks] = __builtin_bit_cast(bf16x8, b);
     }
+    TileLoader<kThreadsKV> lvb;
+    lvb.init(v + (int64_t)kb0 * ld_v + h * DH, ld_v, (uint32_t)(seg1 - kb0), tid);
+#pragma unroll
+    for (int j = 0; j < BLKKV / TB; ++j) lvb.issue(Vb + j * TB * DH, j, wave);
   }
+  const int vrb = 32 * wave;
 
   // Query tiles: causal attention reaches this block's keys only from queries >= kb0.
   const int qt0 = causal ? (kb0 - seg0) / TB : 0;
   const int nqt = (seg1 - seg0 + TB - 1) / TB;
   const uint32_t seg_rows = (uint32_t)(seg1 - seg0);
-  TileLoader lq, ld;
+  TileLoader<kThreadsKV> lq, ld;
   lq.init(q + (int64_t)seg0 * ld_q + h * DH, ld_q, seg_rows, tid);
   ld.init(dout + (int64_t)seg0 * ld_do + h * DH, ld_do, seg_rows, tid);
   const float* lse_h = lse + (int64_t)h * n;
@@ -212,37 +251,40 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(
       nxt = fetch_ld(t + 1);
     }
     const int qbase = seg0 + t * TB;
-    bf16x8 pf[4], sf[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 sacc = zero16, pacc = zero16;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qs, 32 * qb + l32, ks, g), kf[ks],
-                                                       sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ds, 32 * qb + l32, ks, g), vf[ks],
-                                                       pacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Qs, 32 * qb, ks), kf[ks], sacc, 0,
+                                                       0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Ds, 32 * qb, ks),
+                                                       rf.read(Vb, vrb, ks), pacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const bool diag = causal && qbase + 32 * qb < key;   // some query of the block precedes this key
+      bf16x8 pf[2], sf[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 32 * qb + acc_row(e, g);
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -Ls[r]));
         if (diag && qbase + r < key) p = 0.0f;
         const float ds = p * (pacc[e] - Es[r]);
-        pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
-        sf[2 * qb + (e >> 3)][e & 7] = (__bf16)ds;
+        pf[e >> 3][e & 7] = (__bf16)p;
+        sf[e >> 3][e & 7] = (__bf16)ds;
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int b0 = 16 * s;   // = 32 qb + 16 u for s = 2 qb + u
+      for (int u = 0; u < 2; ++u) {
+        const int b0 = 32 * qb + 16 * u;
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Ds, b0, db, lane), pf[s], dva[db],
-                                                          0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Qs, b0, db, lane), sf[s], dka[db],
-                                                          0, 0, 0);
+        for (int db = 0; db < DH / 32; ++db) {
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Ds, b0, db), pf[u], dva[db],
+                                                            0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Qs, b0, db), sf[u], dka[db],
+                                                            0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if (t + 1 < nqt) put_ld(Ln, En, nxt);
@@ -273,7 +315,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(
   }
 }
 
-__global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreadsQ, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
     int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -286,12 +328,16 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dq_kernel(
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
-  const int q0 = seg0 + (int)blockIdx.x * BLK;
+  const int q0 = seg0 + (int)blockIdx.x * BLKQ;
   if (q0 >= seg1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int qrow = q0 + 32 * wave + l32;
   const bool live = qrow < seg1;
+  RowFrag rf;
+  TrFrag tf;
+  rf.init(lane);
+  tf.init(lane);
 
   // Q^T and dO^T operands (B of S^T = K Q^T and dP^T = V dO^T): lane (query
   // l32, half g) holds d = 16 ks + 8 g .. +7.
@@ -310,10 +356,10 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dq_kernel(
   const float lse2 = live ? lse[(int64_t)h * n + qrow] * 1.4426950408889634f : INFINITY;
   const float dlt = live ? delta[(int64_t)h * n + qrow] : 0.0f;
 
-  const int kend = causal ? min(seg1, q0 + BLK) : seg1;
+  const int kend = causal ? min(seg1, q0 + BLKQ) : seg1;
   const int nkt = (kend - seg0 + TB - 1) / TB;
   const uint32_t seg_rows = (uint32_t)(seg1 - seg0);
-  TileLoader lk, lv;
+  TileLoader<kThreadsQ> lk, lv;
   lk.init(k + (int64_t)seg0 * ld_k + h * DH, ld_k, seg_rows, tid);
   lv.init(v + (int64_t)seg0 * ld_v + h * DH, ld_v, seg_rows, tid);
 
@@ -337,10 +383,10 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dq_kernel(
       f32x16 sacc = zero16, pacc = zero16;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, 32 * b + l32, ks, g), qf[ks],
-                                                       sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Vs, 32 * b + l32, ks, g), df[ks],
-                                                       pacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Ks, 32 * b, ks), qf[ks], sacc, 0,
+                                                       0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Vs, 32 * b, ks), df[ks], pacc, 0,
+                                                       0, 0);
       }
       const int kb = kbase + 32 * b;
       const bool edge = kb + 32 > seg1 || (causal && kb + 31 > q0 + 32 * wave);
@@ -358,8 +404,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dq_kernel(
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db)
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Ks, 16 * s, db, lane), sf[s],
-                                                          dqa[db], 0, 0, 0);
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Ks, 16 * s, db), sf[s], dqa[db],
+                                                          0, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -399,14 +445,15 @@ hipError_t launch_attn_bwd(const void* q, int64_t ld_q, const void* k, int64_t l
   attn_delta_kernel<<<dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s>>>(
       static_cast<const uint16_t*>(o), ld_o, static_cast<const uint16_t*>(dout), ld_do, delta,
       n_tokens, n_heads);
-  const dim3 grid((max_seqlen + BLK - 1) / BLK, n_seqs, n_heads);
   const float sl2 = scale * 1.4426950408889634f;
-  attn_bwd_dkdv_kernel<<<grid, dim3(kThreadsB), 0, s>>>(
+  const dim3 grid_kv((max_seqlen + BLKKV - 1) / BLKKV, n_seqs, n_heads);
+  attn_bwd_dkdv_kernel<<<grid_kv, dim3(kThreadsKV), 0, s>>>(
       static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
       static_cast<const uint16_t*>(v), ld_v, static_cast<const uint16_t*>(dout), ld_do, lse, delta,
       static_cast<uint16_t*>(dk), ld_dk, static_cast<uint16_t*>(dv), ld_dv, cu, n_tokens, scale,
       sl2, causal);
-  attn_bwd_dq_kernel<<<grid, dim3(kThreadsB), 0, s>>>(
+  const dim3 grid_q((max_seqlen + BLKQ - 1) / BLKQ, n_seqs, n_heads);
+  attn_bwd_dq_kernel<<<grid_q, dim3(kThreadsQ), 0, s>>>(
       static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
       static_cast<const uint16_t*>(v), ld_v, static_cast<const uint16_t*>(dout), ld_do, lse, delta,
       static_cast<uint16_t*>(dq), ld_dq, cu, n_tokens, scale, sl2, causal);
