@@ -54,8 +54,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // LDS tiles are [row][d] with 256-byte rows; 16-byte chunk c of row r sits at
-// physical chunk c ^ (r & 7).
-__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+// physical chunk c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1).  The tiles are
+// read both as rows (eight consecutive rows, one chunk each: f takes eight
+// distinct values) and transposed (four consecutive rows, two adjacent
+// chunks each: f >> 1 takes four distinct values), so with 4-byte banks
+// either read of 128 bytes per cycle hits 32 distinct banks.
+__device__ __forceinline__ int swz_f(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+__device__ __forceinline__ int swz(int row, int c) { return c ^ swz_f(row); }
 
 // Fragment reads with per-lane bases and compile-time offsets (the swizzle
 // distributes over the lane bits, so every address is one of a few per-lane
@@ -63,13 +68,13 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 //
 // Row fragment: lane (l32, g) reads tile row rb + l32 (rb a multiple of 8),
 // d = 16 ks + 8 g .. +7, i.e. logical chunk 2 ks + g; with ks = 4 a + j the
-// physical chunk is 8 a + ((2 j + g) ^ (l32 & 7)).
+// physical chunk is 8 a + ((2 j + g) ^ f(l32)).
 struct RowFrag {
   int off[4];
   __device__ void init(int lane) {
     const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) off[j] = l32 * DH + 8 * ((2 * j + g) ^ (l32 & 7));
+    for (int j = 0; j < 4; ++j) off[j] = l32 * DH + 8 * ((2 * j + g) ^ swz_f(l32));
   }
   __device__ __forceinline__ bf16x8 read(const uint16_t* t, int rb, int ks) const {
     return *reinterpret_cast<const bf16x8*>(t + off[ks & 3] + 64 * (ks >> 2) + rb * DH);
@@ -81,16 +86,17 @@ struct RowFrag {
 // ds_read_b64_tr_b16.  In each 16-lane group (t = (lane >> 4) & 1) lane i
 // supplies row b0 + y, y = 4 g + (i >> 2), columns 32 db + 16 t + 4 (i & 3)
 // .. +3 and receives column 32 db + l32 of the four rows.  The column's
-// chunk 4 db + x (x = 2 t + ((i & 3) >> 1)) sits at 4 (db ^ g) + (x ^ (y & 3)),
-// i.e. 32 db + 32 g (db even) or 32 db - 32 g (db odd) elements plus a lane part.
+// chunk 4 db + x (x = 2 t + ((i & 3) >> 1)) sits at 4 (db ^ (i >> 3)) +
+// (x ^ (f(y) & 3)) with f(y) = 2 (i >> 2) + g: 32 db + 32 (i >> 3) elements
+// (db even) or 32 db - 32 (i >> 3) (db odd), plus a lane part.
 struct TrFrag {
   int off[2];
   __device__ void init(int lane) {
     const int i = lane & 15, t = (lane >> 4) & 1, g = lane >> 5;
     const int y = 4 * g + (i >> 2), x = 2 * t + ((i & 3) >> 1);
-    const int base = y * DH + 8 * (x ^ (y & 3)) + 4 * (i & 1);
-    off[0] = base + 32 * g;
-    off[1] = base - 32 * g;
+    const int base = y * DH + 8 * (x ^ (swz_f(y) & 3)) + 4 * (i & 1);
+    off[0] = base + 32 * (i >> 3);
+    off[1] = base - 32 * (i >> 3);
   }
   __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int b0, int db) const {
     const lds_u16* p = (const lds_u16*)tile + off[db & 1] + 32 * db + b0 * DH;
