@@ -43,7 +43,8 @@ from .denoise import (VIDEO_LATENT_CHANNELS, clean_estimate, denoise_loop, denoi
                       euler_step, standard_velocity, timestep_from_sigma)
 from .nft import implicit_policies, nft_loss
 from .backward import (adaln_backward, attention_backward, attention_backward_rows,
-                       attention_lse, block_backward, rope3d_backward)
+                       attention_lse, block_backward, ffn_backward, gelu_tanh_grad,
+                       rope3d_backward)
 from .fp8 import (E4M3_MAX, adaln_modulate_fp8, block_forward_fp8, dequantize_rows, e4m3_decode,
                   e4m3_encode, e4m3_encode_bruteforce, e4m3_table, ffn_forward_fp8, linear_fp8,
                   quantize_rows, row_scales)
@@ -60,4 +61,5 @@ __all__ = [
     "row_scales", "quantize_rows", "dequantize_rows", "linear_fp8", "adaln_modulate_fp8",
     "block_forward_fp8", "ffn_forward_fp8", "attention_backward", "rope3d_backward",
     "adaln_backward", "block_backward", "attention_lse", "attention_backward_rows",
+    "ffn_backward", "gelu_tanh_grad",
 ]

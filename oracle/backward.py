@@ -16,7 +16,9 @@ backward pass.  It is the chain rule through the forward definitions of
     y   = xhat (1 + scale[m]) + shift[m],   xhat = (x - mean) / sqrt(var + eps)
 
 Given the upstream gradient g = dL/d(out), the functions return dL/d(every
-input): x, the three table rows of every modality, W_qkv, b_qkv, W_o, b_o.
+input): x, the three table rows of every modality, W_qkv, b_qkv, W_o, b_o;
+``ffn_backward`` does the same for the feed-forward half (W1, b1, W2, b2 and
+the MLP table rows), through the tanh-form GELU of oracle.block.gelu_tanh.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-from .block import (_f64, _probs, adaln_modulate, attention, qkv_project, rope3d,
+from .block import (_f64, _probs, adaln_modulate, attention, gelu_tanh, qkv_project, rope3d,
                     rope_frequencies)
 
 
@@ -201,3 +203,53 @@ def block_backward(x, modality, pos, cu_seqlens, table, w_qkv, w_o, dout, *,
     return dict(dx=dout + dx_ln, dtable=dtable, dw_qkv=dw_qkv, db_qkv=db_qkv, dw_o=dw_o,
                 db_o=db_o, dz=dz, do=do, dq_rot=dq_rot, dk_rot=dk_rot, dv=dv, dqkv=dqkv, dy=dy,
                 o=o, q_rot=q_rot, k_rot=k_rot, v=v, y=y, z=z)
+
+
+def gelu_tanh_grad(z) -> np.ndarray:
+    """d/dz of oracle.block.gelu_tanh: with u = c (z + 0.044715 z^3), c = sqrt(2/pi),
+    0.5 (1 + tanh u) + 0.5 z (1 - tanh^2 u) c (1 + 3 * 0.044715 z^2)."""
+    z = _f64(z)
+    c = np.sqrt(2.0 / np.pi)
+    t = np.tanh(c * (z + 0.044715 * z ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * z * z)
+
+
+def ffn_backward(x, modality, table_mlp, w1, w2, dout, b1=None, b2=None,
+                 eps: float = 1e-6) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dout * out) for the feed-forward half (oracle.block.ffn_forward):
+
+        out = x + gate[m] * z,  z = h W2^T + b2,  h = gelu_tanh(a),  a = y W1^T + b1,
+        y = AdaLN(x) with the MLP table rows.
+
+    Returns dx, dtable [3][3][D], dw1 [F][D], db1 [F], dw2 [D][F], db2 [D] and the
+    intermediate gradients dz, dh, da, dy.
+    """
+    x, dout = _f64(x), _f64(dout)
+    d = x.shape[1]
+    mod = np.asarray(modality, dtype=np.int64)
+    tab = _f64(table_mlp)
+    W1, W2 = _f64(w1), _f64(w2)
+    y = adaln_modulate(x, mod, tab, eps)
+    a = y @ W1.T
+    if b1 is not None:
+        a = a + _f64(b1)
+    h = gelu_tanh(a)
+    z = h @ W2.T
+    if b2 is not None:
+        z = z + _f64(b2)
+    dgate = np.zeros((3, d))
+    for m in range(3):
+        sel = mod == m
+        dgate[m] = (dout[sel] * z[sel]).sum(axis=0)
+    dz = tab[mod, 2, :] * dout
+    dw2 = dz.T @ h
+    db2 = dz.sum(axis=0)
+    dh = dz @ W2
+    da = dh * gelu_tanh_grad(a)
+    dw1 = da.T @ y
+    db1 = da.sum(axis=0)
+    dy = da @ W1
+    dx_ln, dshift, dscale = adaln_backward(x, mod, tab, dy, eps)
+    dtable = np.stack([dshift, dscale, dgate], axis=1)
+    return dict(dx=dout + dx_ln, dtable=dtable, dw1=dw1, db1=db1, dw2=dw2, db2=db2, dz=dz,
+                dh=dh, da=da, dy=dy)

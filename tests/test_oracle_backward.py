@@ -179,3 +179,61 @@ def test_attention_gradient_column_sums():
         for a, b in ((0, 9), (9, 21)):
             np.testing.assert_allclose(dk[a:b].sum(0), 0.0, atol=1e-12)
             np.testing.assert_allclose(dv[a:b].sum(0), do[a:b].sum(0), rtol=1e-12, atol=1e-12)
+
+
+def test_gelu_grad_matches_torch_autograd_and_central_differences():
+    z = np.linspace(-9.0, 9.0, 1201)
+    tz = torch.tensor(z, requires_grad=True)
+    F.gelu(tz, approximate="tanh").sum().backward()
+    np.testing.assert_allclose(oracle.gelu_tanh_grad(z), tz.grad.numpy(), rtol=1e-12, atol=1e-14)
+    e = 1e-6
+    fd = (oracle.gelu_tanh(z + e) - oracle.gelu_tanh(z - e)) / (2 * e)
+    np.testing.assert_allclose(oracle.gelu_tanh_grad(z), fd, rtol=1e-7, atol=1e-9)
+    assert oracle.gelu_tanh_grad(0.0) == 0.5          # GELU'(0) = 1/2
+
+
+def _ffn_setup(n=13, d=16, f=40, seed=90):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((n, d)) * 1.3 - 0.2
+    table = rng.standard_normal((3, 3, d)) * 0.3
+    w1 = rng.standard_normal((f, d)) * 0.4
+    w2 = rng.standard_normal((d, f)) * 0.3
+    b1, b2 = rng.standard_normal(f) * 0.1, rng.standard_normal(d) * 0.1
+    mod = rng.integers(0, 3, n)
+    dout = rng.standard_normal((n, d))
+    return x, table, w1, w2, b1, b2, mod, dout
+
+
+def test_ffn_backward_directional_derivatives():
+    x, table, w1, w2, b1, b2, mod, dout = _ffn_setup()
+    g = oracle.ffn_backward(x, mod, table, w1, w2, dout, b1, b2)
+    args = dict(x=x, table_mlp=table, w1=w1, w2=w2, b1=b1, b2=b2)
+    grads = dict(x=g["dx"], table_mlp=g["dtable"], w1=g["dw1"], w2=g["dw2"], b1=g["db1"],
+                 b2=g["db2"])
+
+    def obj(**kw):
+        return float(np.sum(dout * oracle.ffn_forward(modality=mod, **kw)))
+
+    rng = np.random.Generator(np.random.PCG64(91))
+    eps = 1e-5
+    for name, val in args.items():
+        delta = rng.standard_normal(val.shape)
+        fd = (obj(**dict(args, **{name: val + eps * delta}))
+              - obj(**dict(args, **{name: val - eps * delta}))) / (2 * eps)
+        an = float(np.sum(grads[name] * delta))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_ffn_backward_matches_torch_autograd():
+    x, table, w1, w2, b1, b2, mod, dout = _ffn_setup(seed=92)
+    g = oracle.ffn_backward(x, mod, table, w1, w2, dout, b1, b2)
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in
+         dict(x=x, table=table, w1=w1, w2=w2, b1=b1, b2=b2).items()}
+    m = torch.tensor(mod)
+    y = F.layer_norm(t["x"], (x.shape[1],), eps=1e-6) * (1 + t["table"][m, 1]) + t["table"][m, 0]
+    h = F.gelu(F.linear(y, t["w1"], t["b1"]), approximate="tanh")
+    out = t["x"] + t["table"][m, 2] * F.linear(h, t["w2"], t["b2"])
+    out.backward(torch.tensor(dout))
+    for key, tk in (("dx", "x"), ("dtable", "table"), ("dw1", "w1"), ("dw2", "w2"),
+                    ("db1", "b1"), ("db2", "b2")):
+        np.testing.assert_allclose(g[key], t[tk].grad.numpy(), rtol=1e-10, atol=1e-12)
