@@ -17,8 +17,9 @@ DiffusionNFT loss and its gradient (one sample per request); ``fp8`` times the
 block's four projections in FP8 (e4m3 codes, per-row scales) against the
 e4m3 MFMA peak, the row quantization and the FP8-output AdaLN against HBM,
 and the two halves of the block with FP8 projections (``block_fp8``,
-``ffn_fp8``, ms per call).  ``backward`` times the attention backward and the
-whole backward pass of the attention half (which recomputes its forward).
+``ffn_fp8``, ms per call).  ``backward`` times the attention backward, the
+whole backward pass of the attention half and that of the feed-forward half
+(each recomputes its forward).
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
 workload on the host cores.
 """
@@ -601,6 +602,26 @@ def main() -> int:
             e1.record(stream)
             torch.cuda.synchronize()
             tb[name] = e0.elapsed_time(e1) / reps
+        # the feed-forward half's backward (d_ff = 4 d_model)
+        fi_b = synth.ffn_inputs(wl)
+        fdesc_b = jav.ffn_desc(jav.DIT_BF16, d, wl.d_ff, wl.eps)
+        fws_b = torch.empty(jav.ffn_backward_workspace_bytes(fdesc_b, n), dtype=torch.uint8,
+                            device=dev)
+        w1_b, w2_b = bf(fi_b.w1), bf(fi_b.w2)
+        t2_b = torch.from_numpy(fi_b.table).to(dev)
+        fn_f = (lambda: jav.ffn_backward(fdesc_b, x, dout, mod, t2_b, w1_b, w2_b, dx=dx_b,
+                                         workspace=fws_b, stream=stream))
+        fn_f()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(2):
+            fn_f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tb["ffn_bwd"] = e0.elapsed_time(e1) / 2
+        del fws_b, w1_b, w2_b, t2_b
         a_f, q_f, o_f = block_flops(n, d, lay["cu_seqlens"].tolist(), args.causal)
         attn_bwd_f = 2.5 * a_f
         blk_bwd_f = (a_f + q_f + o_f) + o_f + attn_bwd_f + 2 * o_f + 2 * q_f
@@ -613,6 +634,10 @@ def main() -> int:
             "block_backward_tflops": round(blk_bwd_f / (tb["block_bwd"] * 1e-3) / 1e12, 1),
             "block_backward_frac_of_bf16_peak": round(
                 blk_bwd_f / (tb["block_bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            # forward again (a, z) + dh, dW2, dy, dW1: six products of 2 N D d_ff
+            "ffn_backward_ms": round(tb["ffn_bwd"], 3),
+            "ffn_backward_tflops": round(12.0 * n * d * wl.d_ff / (tb["ffn_bwd"] * 1e-3) / 1e12,
+                                         1),
         }
         del dout, q_r, k_r, v_r, o_r, lse_r, dq_r, dk_r, dv_r, aws, bws, dx_b
         print(f"# backward: {bwd_rec}", file=sys.stderr, flush=True)

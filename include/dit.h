@@ -534,6 +534,27 @@ dit_status dit_block_backward(const dit_block_desc* d, const void* x, const void
                               float* db_o, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Backward pass of the feed-forward half (dit_ffn_forward): the gradients of
+ * sum(dout * out) through the gated residual, ff.net.2, the tanh-form GELU,
+ * ff.net.0.proj and the AdaLN with the MLP table rows; the forward is
+ * recomputed inside the call.  bf16; d_model and d_ff multiples of 64. */
+
+/* Bytes of scratch dit_ffn_backward needs: about 5 bf16 [N][d_model] and 5
+ * [N][d_ff] planes (N rounded up to 64), d_ff * d_model bf16 and small
+ * buffers.  0 for a bad descriptor (also a dtype other than DIT_BF16). */
+size_t dit_ffn_backward_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens);
+
+/* Inputs as dit_ffn_forward plus dout [n_tokens][d_model] bf16.  Outputs
+ * (device): dx bf16 (may be dout, must not overlap x); dtable float32
+ * [3][3][d_model] (the MLP shift, scale and gate rows); dw1 [d_ff][d_model]
+ * and dw2 [d_model][d_ff] bf16; db1 [d_ff], db2 [d_model] float32 or NULL.
+ * Deterministic.  Errors as dit_block_backward. */
+dit_status dit_ffn_backward(const dit_ffn_desc* d, const void* x, const void* dout,
+                            const uint8_t* modality, int64_t n_tokens, const float* ada_table,
+                            const void* w1, const void* b1, const void* w2, const void* b2,
+                            void* dx, float* dtable, void* dw1, float* db1, void* dw2,
+                            float* db2, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* FP8 block halves                                                           */
 /* ------------------------------------------------------------------------ */

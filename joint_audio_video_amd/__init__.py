@@ -37,6 +37,7 @@ EXPORTED = (
     "dit_block_forward_fp8", "dit_ffn_fp8_workspace_bytes", "dit_ffn_forward_fp8",
     "attn_packed_lse", "dit_attn_backward_workspace_bytes", "attn_packed_backward",
     "dit_block_backward_workspace_bytes", "dit_block_backward",
+    "dit_ffn_backward_workspace_bytes", "dit_ffn_backward",
 )
 
 
@@ -126,6 +127,9 @@ def _load() -> ctypes.CDLL:
         "dit_block_backward_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
         "dit_block_backward": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32, I32,
                                               I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dit_ffn_backward_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
+        "dit_ffn_backward": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P, P,
+                                            P, P, P, P, P, P, P, SZ, P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -662,3 +666,33 @@ def block_backward(desc: BlockDesc, x, dout, modality, pos, cu_seqlens, max_seql
         dtable.data_ptr(), dw_qkv.data_ptr(), _ptr(db_qkv), dw_o.data_ptr(), _ptr(db_o),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return dict(dx=dx, dtable=dtable, dw_qkv=dw_qkv, dw_o=dw_o, db_qkv=db_qkv, db_o=db_o)
+
+
+def ffn_backward_workspace_bytes(desc: FfnDesc, n_tokens: int) -> int:
+    return int(_lib.dit_ffn_backward_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def ffn_backward(desc: FfnDesc, x, dout, modality, table, w1, w2, b1=None, b2=None,
+                 bias_grads: bool = True, dx=None, workspace=None, n_tokens=None,
+                 stream=None) -> dict:
+    """Gradients of sum(dout * out) of the feed-forward half (libdit dit_ffn_backward):
+    dict(dx, dtable [3][3][D] float32, dw1, dw2, db1, db2 (float32 or None))."""
+    torch = _torch()
+    n = x.shape[0] if n_tokens is None else int(n_tokens)
+    d, f = x.shape[1], w1.shape[0]
+    dev = x.device
+    dx = torch.empty_like(x) if dx is None else dx
+    dtable = torch.empty((3, 3, d), dtype=torch.float32, device=dev)
+    dw1 = torch.empty((f, d), dtype=x.dtype, device=dev)
+    dw2 = torch.empty((d, f), dtype=x.dtype, device=dev)
+    db1 = torch.empty(f, dtype=torch.float32, device=dev) if bias_grads else None
+    db2 = torch.empty(d, dtype=torch.float32, device=dev) if bias_grads else None
+    if workspace is None:
+        workspace = torch.empty(max(ffn_backward_workspace_bytes(desc, n), 1), dtype=torch.uint8,
+                                device=dev)
+    _check(_lib.dit_ffn_backward(
+        ctypes.byref(desc), x.data_ptr(), dout.data_ptr(), modality.data_ptr(), n,
+        table.data_ptr(), w1.data_ptr(), _ptr(b1), w2.data_ptr(), _ptr(b2), dx.data_ptr(),
+        dtable.data_ptr(), dw1.data_ptr(), _ptr(db1), dw2.data_ptr(), _ptr(db2),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dict(dx=dx, dtable=dtable, dw1=dw1, dw2=dw2, db1=db1, db2=db2)

@@ -1126,6 +1126,145 @@ extern "C" dit_status dit_block_backward(
 }
 
 // ---------------------------------------------------------------------------
+// Backward pass of the feed-forward half.
+//
+// Workspace (Np = n_tokens rounded up to 64; PD = round256(D Np 2), PF =
+// round256(F Np 2)): Y [N][D] | A (pre-activation) [N][F] | H = gelu(A) |
+// ZD (z, then dy) | DZ | DH (dh, then da in place) | TS (dz^T, then y^T)
+// [D][Np] | TB (h^T, then da^T) [F][Np] | WT (W2^T, then W1^T) | STATS |
+// column-sum partials.
+namespace {
+struct FfnBwdLayout {
+  size_t pd, pf, y, a, h, zd, dz, dh, ts, tb, wt, stats, part, total;
+};
+FfnBwdLayout ffn_bwd_layout(int64_t n, int32_t d, int32_t f) {
+  FfnBwdLayout L{};
+  const size_t np = (size_t)((n + 63) / 64 * 64);
+  L.pd = round256((size_t)d * np * 2);
+  L.pf = round256((size_t)f * np * 2);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round256(bytes);
+    return at;
+  };
+  L.y = take(L.pd);
+  L.a = take(L.pf);
+  L.h = take(L.pf);
+  L.zd = take(L.pd);
+  L.dz = take(L.pd);
+  L.dh = take(L.pf);
+  L.ts = take(L.pd);
+  L.tb = take(L.pf);
+  L.wt = take((size_t)f * d * 2);
+  L.stats = take((size_t)n * 8);
+  L.part = take(std::max(colsum_partial_bytes(n, f, 1), colsum_partial_bytes(n, d, 3)));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+extern "C" size_t dit_ffn_backward_workspace_bytes(const dit_ffn_desc* d, int64_t n_tokens) {
+  if (!d || d->dtype != DIT_BF16 || d->d_model < 1 || d->d_ff < 1 || n_tokens < 0) return 0;
+  return ffn_bwd_layout(n_tokens, d->d_model, d->d_ff).total;
+}
+
+extern "C" dit_status dit_ffn_backward(const dit_ffn_desc* d, const void* x, const void* dout,
+                                       const uint8_t* modality, int64_t n_tokens,
+                                       const float* ada_table, const void* w1, const void* b1,
+                                       const void* w2, const void* b2, void* dx, float* dtable,
+                                       void* dw1, float* db1, void* dw2, float* db2,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "dit_ffn_backward";
+  if (!d) return fail(DIT_EINVAL, "%s: null descriptor", who);
+  if (d->dtype != DIT_BF16)
+    return fail(DIT_EUNSUPPORTED, "%s: bf16 only (dtype %d)", who, (int)d->dtype);
+  const int32_t D = d->d_model, F = d->d_ff;
+  if (D < 1 || F < 1) return fail(DIT_EINVAL, "%s: d_model/d_ff < 1", who);
+  if (!x || !dout || !modality || !ada_table || !w1 || !w2 || !dx || !dtable || !dw1 || !dw2)
+    return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (D % 64 != 0 || F % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: d_model %d and d_ff %d must be multiples of 64", who, D,
+                F);
+  const FfnBwdLayout L = ffn_bwd_layout(n_tokens, D, F);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes,
+                L.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIT_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", who);
+  char* ws = static_cast<char*>(workspace);
+  char *Y = ws + L.y, *A = ws + L.a, *Hh = ws + L.h, *ZD = ws + L.zd, *DZ = ws + L.dz;
+  char *DH = ws + L.dh, *TS = ws + L.ts, *TB = ws + L.tb, *WT = ws + L.wt;
+  float* STATS = reinterpret_cast<float*>(ws + L.stats);
+  float* PART = reinterpret_cast<float*>(ws + L.part);
+  const int64_t np = (n_tokens + 63) / 64 * 64;
+  if (dit_status st = adaln_check(DIT_BF16, x, D, modality, ada_table, Y, D, n_tokens, D,
+                                  d->ln_eps))
+    return st;
+  if (!aligned16(dout) || !aligned16(dx) || !aligned16(w1) || !aligned16(w2) ||
+      !aligned16(dw1) || !aligned16(dw2) || !aligned16(dtable) || (b1 && !aligned16(b1)) ||
+      (b2 && !aligned16(b2)))
+    return fail(DIT_EUNSUPPORTED, "%s: pointers must be 16-byte aligned", who);
+  if (spans_overlap(dx, D, x, D, n_tokens, D, 2))
+    return fail(DIT_EINVAL, "%s: dx overlaps x", who);
+  if (n_tokens == 0) return DIT_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+#define DIT_FBWD(call, what)                                         \
+  e = (call);                                                        \
+  if (e != hipSuccess) return hip_fail(e, "dit_ffn_backward: " what)
+  GemmEpilogue plain{0, nullptr, nullptr, 0, nullptr, nullptr};
+  // forward stages, recomputed
+  DIT_FBWD(launch_adaln(1, x, D, modality, ada_table, Y, D, n_tokens, D, d->ln_eps, s), "adaln");
+  GemmEpilogue ep_b1{0, b1, nullptr, 0, nullptr, nullptr};
+  DIT_FBWD(launch_gemm(1, Y, D, w1, A, F, n_tokens, F, D, ep_b1, s), "pre-activation");
+  DIT_FBWD(launch_gelu(0, A, F, Hh, F, n_tokens, F, s), "gelu");
+  GemmEpilogue ep_b2{0, b2, nullptr, 0, nullptr, nullptr};
+  DIT_FBWD(launch_gemm(1, Hh, F, w2, ZD, D, n_tokens, D, F, ep_b2, s), "z");
+  // out = x + gate * z: dz, the gate rows, db2
+  DIT_FBWD(launch_gate_scale(dout, D, modality, ada_table, DZ, D, n_tokens, D, s), "gate");
+  DIT_FBWD(launch_colsum(1, dout, D, ZD, D, nullptr, modality, n_tokens, D, PART, dtable + 2 * D,
+                         3 * D, s),
+           "gate rows");
+  if (db2)
+    DIT_FBWD(launch_colsum(0, DZ, D, nullptr, 0, nullptr, nullptr, n_tokens, D, PART, db2, 0, s),
+             "db2");
+  // z = h W2^T + b2: dh = dz W2, dW2 = dz^T h
+  DIT_FBWD(launch_transpose(w2, F, D, F, WT, D, s), "W2^T");
+  DIT_FBWD(launch_gemm(1, DZ, D, WT, DH, F, n_tokens, F, D, plain, s), "dh");
+  DIT_FBWD(launch_transpose(DZ, D, n_tokens, D, TS, np, s), "dz^T");
+  DIT_FBWD(launch_transpose(Hh, F, n_tokens, F, TB, np, s), "h^T");
+  DIT_FBWD(launch_gemm(1, TS, np, TB, dw2, F, D, F, (int)np, plain, s), "dW2");
+  // h = gelu(a): da = dh * gelu'(a), in place
+  DIT_FBWD(launch_gelu(1, A, F, DH, F, n_tokens, F, s), "gelu backward");
+  if (db1)
+    DIT_FBWD(launch_colsum(0, DH, F, nullptr, 0, nullptr, nullptr, n_tokens, F, PART, db1, 0, s),
+             "db1");
+  // a = y W1^T + b1: dy = da W1, dW1 = da^T y
+  char* DY = ZD;
+  DIT_FBWD(launch_transpose(w1, D, F, D, WT, F, s), "W1^T");
+  DIT_FBWD(launch_gemm(1, DH, F, WT, DY, D, n_tokens, D, F, plain, s), "dy");
+  DIT_FBWD(launch_transpose(DH, F, n_tokens, F, TB, np, s), "da^T");
+  DIT_FBWD(launch_transpose(Y, D, n_tokens, D, TS, np, s), "y^T");
+  DIT_FBWD(launch_gemm(1, TB, np, TS, dw1, D, F, D, (int)np, plain, s), "dW1");
+  // AdaLN: dx, then the shift and scale rows
+  DIT_FBWD(launch_adaln_bwd(x, D, DY, D, dout, D, modality, ada_table, dx, D, STATS, n_tokens, D,
+                            d->ln_eps, s),
+           "adaln backward");
+  DIT_FBWD(launch_colsum(0, DY, D, nullptr, 0, nullptr, modality, n_tokens, D, PART, dtable,
+                         3 * D, s),
+           "shift rows");
+  DIT_FBWD(launch_colsum(2, DY, D, x, D, STATS, modality, n_tokens, D, PART, dtable + D, 3 * D,
+                         s),
+           "scale rows");
+#undef DIT_FBWD
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------------------
 
 extern "C" dit_status dit_profile_enable(int32_t max_calls) {
   clear_error();

@@ -64,6 +64,18 @@ __device__ __forceinline__ float half_swap_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// tanh-form GELU: 0.5 z (1 + tanh u) with u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated as z / (1 + exp(-2u)) (the same function; one exp and one
+// reciprocal).  Large |z| saturate to z and -0.
+__device__ __forceinline__ float gelu_tanh_fast(float z) {
+  const float u2 = 1.5957691216057308f * fmaf(0.044715f * z, z * z, z);   // 2u
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-u2));
+}
+__device__ __forceinline__ float gelu_tanh_exact(float z) {
+  const float u2 = 1.5957691216057308f * fmaf(0.044715f * z, z * z, z);
+  return z / (1.0f + expf(-u2));
+}
+
 // Four e4m3 codes of four float32 values in one word (value j in byte j):
 // nearest, ties to the even code (v_cvt_pk_fp8_f32, which rounds exactly so
 // for |v| <= 464: checked against the float64 oracle on every code, every
@@ -171,6 +183,9 @@ hipError_t launch_transpose(const void* src, int64_t ld_src, int64_t rows, int c
 // out = table[mod][GATE] * g (row-wise), d a multiple of 8.
 hipError_t launch_gate_scale(const void* g, int64_t ld_g, const uint8_t* mod, const float* table,
                              void* out, int64_t ld_out, int64_t n, int d, hipStream_t s);
+// io = gelu(a), or (backward) io = io * gelu'(a); [n][f] bf16, f a multiple of 8.
+hipError_t launch_gelu(int backward, const void* a, int64_t lda, void* io, int64_t ld_io,
+                       int64_t n, int f, hipStream_t s);
 // Column sums over n rows (deterministic): mode 0 sums a, 1 a * b, 2
 // a * (b - mean) * rstd with stats float2 [n] (mean, rstd); per modality into
 // out[m * out_gstride + j] (m = 0..2) when mod is given, else into out[j].

@@ -51,18 +51,6 @@ struct EpiArgs {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-// tanh-form GELU: 0.5 z (1 + tanh u) with u = sqrt(2/pi) (z + 0.044715 z^3),
-// evaluated as z / (1 + exp(-2u)) (the same function; one exp and one
-// reciprocal).  Large |z| saturate to z and -0.
-__device__ __forceinline__ float gelu_tanh_fast(float z) {
-  const float u2 = 1.5957691216057308f * fmaf(0.044715f * z, z * z, z);   // 2u
-  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-u2));
-}
-__device__ __forceinline__ float gelu_tanh_exact(float z) {
-  const float u2 = 1.5957691216057308f * fmaf(0.044715f * z, z * z, z);
-  return z / (1.0f + expf(-u2));
-}
-
 // Tile of this workgroup: groups of kGroupM M-tiles, walked column by column.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int pid = blockIdx.x;

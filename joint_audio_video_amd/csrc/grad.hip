@@ -81,6 +81,38 @@ __global__ __launch_bounds__(256) void gate_scale_kernel(const uint16_t* __restr
   *reinterpret_cast<uint4*>(out + row * ld_out + c) = pack8(f);
 }
 
+// io = gelu(a) (BWD false), or io = io * gelu'(a) (BWD true), elementwise over
+// [n][f] bf16; gelu is the tanh form z sigma(2u), 2u = 2 sqrt(2/pi) (z +
+// 0.044715 z^3), as the GEMM's GELU epilogue, and its derivative
+// sigma(2u) + z sigma(2u) (1 - sigma(2u)) 2 sqrt(2/pi) (1 + 3 * 0.044715 z^2).
+template <bool BWD>
+__global__ __launch_bounds__(256) void gelu_kernel(const uint16_t* __restrict__ a, int64_t lda,
+                                                   uint16_t* io, int64_t ld_io, int64_t n,
+                                                   int f) {
+  const int vpr = f / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n * vpr) return;
+  const int64_t row = idx / vpr;
+  const int c = (int)(idx - row * vpr) * 8;
+  float z[8], g[8];
+  unpack8(*reinterpret_cast<const uint4*>(a + row * lda + c), z);
+  uint4* out = reinterpret_cast<uint4*>(io + row * ld_io + c);
+  if constexpr (BWD) unpack8(*out, g);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (BWD) {
+      const float zz = z[e];
+      const float s = __builtin_amdgcn_rcpf(
+          1.0f + __expf(-1.5957691216057308f * fmaf(0.044715f * zz, zz * zz, zz)));
+      const float dsu = 1.5957691216057308f * fmaf(0.134145f * zz, zz, 1.0f);
+      g[e] *= fmaf(zz * s * (1.0f - s), dsu, s);
+    } else {
+      g[e] = gelu_tanh_fast(z[e]);
+    }
+  }
+  *out = pack8(g);
+}
+
 constexpr int kColBlock = 512;   // columns per workgroup (8 per lane)
 
 // Partial column sums over rows [chunk * rows_per_chunk, +rows_per_chunk):
@@ -182,6 +214,21 @@ hipError_t launch_gate_scale(const void* g, int64_t ld_g, const uint8_t* mod, co
   gate_scale_kernel<<<dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s>>>(
       static_cast<const uint16_t*>(g), ld_g, mod, table, static_cast<uint16_t*>(out), ld_out, n,
       d);
+  return hipGetLastError();
+}
+
+hipError_t launch_gelu(int backward, const void* a, int64_t lda, void* io, int64_t ld_io,
+                       int64_t n, int f, hipStream_t s) {
+  if (f % 8 != 0) return hipErrorInvalidValue;
+  const int64_t work = n * (f / 8);
+  if (work == 0) return hipSuccess;
+  const dim3 grid((unsigned)((work + 255) / 256)), block(256);
+  const uint16_t* ap = static_cast<const uint16_t*>(a);
+  uint16_t* op = static_cast<uint16_t*>(io);
+  if (backward)
+    gelu_kernel<true><<<grid, block, 0, s>>>(ap, lda, op, ld_io, n, f);
+  else
+    gelu_kernel<false><<<grid, block, 0, s>>>(ap, lda, op, ld_io, n, f);
   return hipGetLastError();
 }
 

@@ -237,3 +237,73 @@ def test_block_backward_full_shape(jav):
     r = rel_l2(host(a["db_o"]), want)
     print(f"  full.db_o: rel_l2={r:.2e}", flush=True)
     assert r <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# The feed-forward half's backward
+# ---------------------------------------------------------------------------
+
+def _ffn_backward(jav, name, n=None, with_bias=False, inplace=False):
+    import torch
+    wl = synth.WORKLOADS[name]
+    f = synth.ffn_inputs(wl, with_bias=with_bias)
+    x = synth.normal_array((wl.n_tokens, wl.d_model), seed=500 + wl.seed, dtype="bf16")
+    if n is not None:
+        x = x[:n]
+    n, d = x.shape
+    mod, _, _, (mod_d, _, _, _) = _layout(jav, name, n, [0, n])
+    dout = synth.normal_array((n, d), seed=1700 + n, dtype="bf16")
+    desc = jav.ffn_desc(jav.DIT_BF16, d, wl.d_ff, wl.eps)
+    print(f"ffn backward {name} n={n} bias={with_bias} inplace={inplace}", flush=True)
+    dout_d = dev(dout, "bf16")
+    args = (desc, dev(x, "bf16"), dout_d, mod_d, dev(f.table, "f32"), dev(f.w1, "bf16"),
+            dev(f.w2, "bf16"))
+    kw = dict(b1=dev(f.b1, "bf16") if with_bias else None,
+              b2=dev(f.b2, "bf16") if with_bias else None)
+    again = jav.ffn_backward(*args, **kw)
+    got = jav.ffn_backward(*args, dx=dout_d if inplace else None, **kw)
+    _sync()
+    for key in ("dx", "dtable", "dw1", "dw2", "db1", "db2"):
+        assert torch.equal(got[key], again[key]), key
+    ref = oracle.ffn_backward(x, mod, f.table, f.w1, f.w2, dout, f.b1 if with_bias else None,
+                              f.b2 if with_bias else None, wl.eps)
+    for key in ("dx", "dw1", "dw2", "db1", "db2"):
+        check_grad(host(got[key]), ref[key], f"ffn.{name}.{key}")
+    present = np.unique(mod)
+    for r, row in enumerate(("shift", "scale", "gate")):
+        check_grad(host(got["dtable"])[present, r], ref["dtable"][present, r],
+                   f"ffn.{name}.dtable.{row}")
+
+
+def test_ffn_backward_small(jav):
+    _ffn_backward(jav, "small")
+
+
+def test_ffn_backward_ragged_bias_inplace(jav):
+    _ffn_backward(jav, "small", n=1000, with_bias=True, inplace=True)
+
+
+def test_ffn_backward_full_shape(jav):
+    """58,758 tokens, d_ff 20,480: finite, deterministic, and db2 against the sum of
+    gate * dout from the inputs alone."""
+    import torch
+    wl = synth.WORKLOADS["full"]
+    f = synth.ffn_inputs(wl)
+    n, d = wl.n_tokens, wl.d_model
+    mod, _, _, (mod_d, _, _, _) = _layout(jav, "full", n, [0, n])
+    x = synth.normal_array((n, d), seed=1800, dtype="bf16")
+    dout = synth.normal_array((n, d), seed=1801, dtype="bf16")
+    desc = jav.ffn_desc(jav.DIT_BF16, d, wl.d_ff, wl.eps)
+    print(f"ffn backward full n={n}", flush=True)
+    args = (desc, dev(x, "bf16"), dev(dout, "bf16"), mod_d, dev(f.table, "f32"),
+            dev(f.w1, "bf16"), dev(f.w2, "bf16"))
+    a = jav.ffn_backward(*args)
+    b = jav.ffn_backward(*args)
+    _sync()
+    for key in ("dx", "dtable", "dw1", "dw2", "db1", "db2"):
+        assert torch.isfinite(a[key].float()).all(), key
+        assert torch.equal(a[key], b[key]), key
+    want = (f.table[mod, 2, :].astype(np.float64) * dout.astype(np.float64)).sum(0)
+    r = rel_l2(host(a["db2"]), want)
+    print(f"  ffn.full.db2: rel_l2={r:.2e}", flush=True)
+    assert r <= 1e-2
