@@ -20,9 +20,9 @@
 //     transposed operand read from LDS by ds_read_b64_tr_b16 and P / dS as
 //     the bf16 B operand in the accumulator's own row order (the k index of
 //     a product can be permuted as long as both operands agree).
-//   * attn_bwd_dq_kernel: a workgroup owns 128 queries (q, do, lse, delta of
-//     its 32 per wave in registers; two workgroups per CU) and streams the
-//     keys in tiles of 64:
+//   * attn_bwd_dq_kernel: a workgroup owns 256 queries (q, do, lse, delta of
+//     its 32 per wave in registers; 8 waves, the two of a SIMD in ping-pong)
+//     and streams the keys in tiles of 64 (triple-buffered):
 //     S^T = k q^T and dP^T = v do^T (rows = keys), dS^T, then
 //     dq^T += k^T dS^T, as the forward kernel computes O^T.
 // All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P
@@ -37,8 +37,8 @@ namespace {
 
 constexpr int DH = 128;
 constexpr int TB = 64;                 // streamed rows per tile
-// dq: 4 waves (128 queries) per workgroup, two workgroups per CU.
-constexpr int kThreadsQ = 256;
+// dq: 8 waves (256 queries) per workgroup, two per SIMD in ping-pong.
+constexpr int kThreadsQ = 512;
 constexpr int BLKQ = kThreadsQ / 2;
 // dk, dv: 8 waves (256 keys) per workgroup, two waves per SIMD sharing each
 // streamed tile.
@@ -321,16 +321,21 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
   }
 }
 
-__global__ __launch_bounds__(kThreadsQ, 2) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
     int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int64_t ld_dq, const int32_t* __restrict__ cu, int64_t n,
     float scale, float scale_log2, int causal) {
+  // Key and value tiles, three buffers each as distinct objects (the main loop
+  // is unrolled by three, so every access names its buffer at compile time and
+  // the compiler can tell a prefetch from the reads of another buffer).
   __shared__ __attribute__((aligned(16))) uint16_t Ks0[TB * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Ks1[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[TB * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[TB * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[TB * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[TB * DH];
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
@@ -375,43 +380,71 @@ __global__ __launch_bounds__(kThreadsQ, 2) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqa[db][e] = 0.0f;
   const f32x16 zero16 = {};
+  f32x16 sacc[2], pacc[2];
+  bf16x8 sf[4];
 
-  auto step = [&](const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, int t)
-      __attribute__((always_inline)) {
-    if (t + 1 < nkt) {
-      lk.issue(Kn, t + 1, wave);
-      lv.issue(Vn, t + 1, wave);
-    }
-    const int kbase = seg0 + t * TB;
-    bf16x8 sf[4];
+  // Tile t's products S^T = K Q^T and dP^T = V dO^T (two 32-key blocks).
+  auto products = [&](const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      f32x16 sacc = zero16, pacc = zero16;
+      sacc[b] = zero16;
+      pacc[b] = zero16;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Ks, 32 * b, ks), qf[ks], sacc, 0,
-                                                       0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Vs, 32 * b, ks), df[ks], pacc, 0,
-                                                       0, 0);
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Ks, 32 * b, ks), qf[ks],
+                                                          sacc[b], 0, 0, 0);
+        pacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Vs, 32 * b, ks), df[ks],
+                                                          pacc[b], 0, 0, 0);
       }
+    }
+  };
+  // Tile t's P^T and dS^T (VALU) into the bf16 operand sf.
+  auto grads = [&](int t) __attribute__((always_inline)) {
+    const int kbase = seg0 + t * TB;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
       const int kb = kbase + 32 * b;
       const bool edge = kb + 32 > seg1 || (causal && kb + 31 > q0 + 32 * wave);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -lse2));
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, -lse2));
         if (edge) {
           const int kk = kb + acc_row(e, g);
           if (kk >= seg1 || (causal && kk > qrow)) p = 0.0f;
         }
-        sf[2 * b + (e >> 3)][e & 7] = (__bf16)(p * (pacc[e] - dlt));
+        sf[2 * b + (e >> 3)][e & 7] = (__bf16)(p * (pacc[b][e] - dlt));
       }
     }
+  };
+  // dq^T += K^T dS^T with tile t's K read transposed.
+  auto accumulate = [&](const uint16_t* Ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db)
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Ks, 16 * s, db), sf[s], dqa[db],
-                                                          0, 0, 0);
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Ks, 16 * s, db), sf[s],
+                                                          dqa[db], 0, 0, 0);
+  };
+
+  // Ping-pong between the two waves of a SIMD (w and w + 4), as in the
+  // forward kernel: in phase t every wave runs the dq product of tile t-1 and
+  // the S^T, dP^T products of tile t; the leading half computes P and dS of
+  // tile t after its MFMAs, the lagging half those of tile t-1 before them,
+  // so one wave's exponentials overlap the other's MFMAs.  Phase t reads K of
+  // tiles t-1 and t and V of tile t, and loads tile t+1 into the third buffer.
+  const bool lagging = wave >= kThreadsQ / 128;
+  auto phase = [&](const uint16_t* Kprev, const uint16_t* Kcur, const uint16_t* Vcur,
+                   uint16_t* Knext, uint16_t* Vnext, int t) __attribute__((always_inline)) {
+    if (t + 1 < nkt) {
+      lk.issue(Knext, t + 1, wave);
+      lv.issue(Vnext, t + 1, wave);
+    }
+    if (lagging && t >= 1) grads(t - 1);
+    __builtin_amdgcn_s_setprio(1);
+    if (t >= 1) accumulate(Kprev);
+    if (t < nkt) products(Kcur, Vcur);
+    __builtin_amdgcn_s_setprio(0);
+    if (!lagging && t < nkt) grads(t);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -422,9 +455,10 @@ __global__ __launch_bounds__(kThreadsQ, 2) void attn_bwd_dq_kernel(
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < nkt; t += 2) {
-    step(Ks0, Vs0, Ks1, Vs1, t);
-    if (t + 1 < nkt) step(Ks1, Vs1, Ks0, Vs0, t + 1);
+  for (int t = 0; t <= nkt; t += 3) {
+    phase(Ks2, Ks0, Vs0, Ks1, Vs1, t);
+    if (t + 1 <= nkt) phase(Ks0, Ks1, Vs1, Ks2, Vs2, t + 1);
+    if (t + 2 <= nkt) phase(Ks1, Ks2, Vs2, Ks0, Vs0, t + 2);
   }
 
   if (live) {
