@@ -9,7 +9,7 @@
 //   dv = P^T do,  dS = P * (do v^T - delta),  dq = scale dS k,  dk = scale dS^T q.
 //
 // Three launches, no atomics, deterministic:
-//   * attn_delta_kernel: delta[h][row], one thread per (row, head).
+//   * attn_delta_kernel: delta[h][row], sixteen lanes per (row, head).
 //   * attn_bwd_dkdv_kernel: a workgroup owns 256 keys of one (segment,
 //     head) (32 per wave, their K and V in registers; 8 waves, two per SIMD,
 //     share every streamed tile) and streams the
@@ -136,28 +136,31 @@ struct TileLoader {
   }
 };
 
-// delta[h][row] = sum_d do[row][h d] o[row][h d]
+// delta[h][row] = sum_d do[row][h d] o[row][h d].  Sixteen lanes share one
+// (row, head): each reads 16 bytes of o and of do, so a wave reads 1 KB of
+// contiguous row per instruction, and the group sums over shuffles.
 __global__ __launch_bounds__(256) void attn_delta_kernel(const uint16_t* __restrict__ o,
                                                          int64_t ld_o,
                                                          const uint16_t* __restrict__ dout,
                                                          int64_t ld_do, float* __restrict__ delta,
                                                          int64_t n, int n_heads) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n * n_heads) return;
-  const int64_t row = idx / n_heads;
-  const int h = (int)(idx - row * n_heads);
-  const uint4* op = reinterpret_cast<const uint4*>(o + row * ld_o + h * DH);
-  const uint4* dp = reinterpret_cast<const uint4*>(dout + row * ld_do + h * DH);
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;   // (row, head) pair
+  const int part = threadIdx.x & 15;
+  const bool live = idx < n * n_heads;
+  const int64_t row = live ? idx / n_heads : 0;
+  const int h = live ? (int)(idx - row * n_heads) : 0;
   float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < DH / 8; ++c) {
-    const uint4 a = op[c], b = dp[c];
+  if (live) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + row * ld_o + h * DH + 8 * part);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * ld_do + h * DH + 8 * part);
     s = fmaf(bf16lo(a.x), bf16lo(b.x), s); s = fmaf(bf16hi(a.x), bf16hi(b.x), s);
     s = fmaf(bf16lo(a.y), bf16lo(b.y), s); s = fmaf(bf16hi(a.y), bf16hi(b.y), s);
     s = fmaf(bf16lo(a.z), bf16lo(b.z), s); s = fmaf(bf16hi(a.z), bf16hi(b.z), s);
     s = fmaf(bf16lo(a.w), bf16lo(b.w), s); s = fmaf(bf16hi(a.w), bf16hi(b.w), s);
   }
-  delta[(int64_t)h * n + row] = s;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (live && part == 0) delta[(int64_t)h * n + row] = s;
 }
 
 // Stores a 32x32 accumulator block transposed into rows of out: lane (key or
@@ -481,8 +484,8 @@ hipError_t launch_attn_bwd(const void* q, int64_t ld_q, const void* k, int64_t l
   for (int64_t ld : {ld_q, ld_k, ld_v, ld_do})
     if ((uint64_t)max_seqlen * (uint64_t)ld * 2u > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (n_tokens == 0) return hipSuccess;
-  const int64_t pairs = n_tokens * n_heads;
-  attn_delta_kernel<<<dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s>>>(
+  const int64_t lanes = n_tokens * n_heads * 16;
+  attn_delta_kernel<<<dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s>>>(
       static_cast<const uint16_t*>(o), ld_o, static_cast<const uint16_t*>(dout), ld_do, delta,
       n_tokens, n_heads);
   const float sl2 = scale * 1.4426950408889634f;
