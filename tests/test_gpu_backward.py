@@ -307,3 +307,43 @@ def test_ffn_backward_full_shape(jav):
     r = rel_l2(host(a["db2"]), want)
     print(f"  ffn.full.db2: rel_l2={r:.2e}", flush=True)
     assert r <= 1e-2
+
+
+def test_backward_workspaces_poisoned_with_nan(jav):
+    """Workspaces filled with NaN give gradients bit-identical to a zero-filled workspace:
+    no stage reads scratch it has not written (the transposes' zero padding included)."""
+    import torch
+    wl = synth.WORKLOADS["small"]
+    n = 700                                  # not a multiple of 64: padded transposes
+    inp = synth.block_inputs(wl, n_tokens=n, with_bias=True)
+    f = synth.ffn_inputs(wl, with_bias=True)
+    d = wl.d_model
+    _, _, cu, (mod_d, pos_d, cu_d, ms) = _layout(jav, "small", n, [0, 300, n])
+    dout = dev(synth.normal_array((n, d), seed=1900, dtype="bf16"), "bf16")
+    x = dev(inp.x, "bf16")
+    desc = jav.block_desc(jav.DIT_BF16, d, wl.n_heads, wl.head_dim, wl.sections, wl.theta, wl.eps)
+    fdesc = jav.ffn_desc(jav.DIT_BF16, d, wl.d_ff, wl.eps)
+    print(f"backward poison n={n}", flush=True)
+    outs = []
+    for fill in (0.0, float("nan")):
+        bws = torch.empty(jav.block_backward_workspace_bytes(desc, n), dtype=torch.uint8,
+                          device="cuda")
+        fws = torch.empty(jav.ffn_backward_workspace_bytes(fdesc, n), dtype=torch.uint8,
+                          device="cuda")
+        for w in (bws, fws):                 # sizes are multiples of 256 bytes
+            w.view(torch.float32).fill_(fill)
+        a = jav.block_backward(desc, x, dout, mod_d, pos_d, cu_d, ms, dev(inp.table, "f32"),
+                               dev(inp.w_qkv, "bf16"), dev(inp.w_o, "bf16"),
+                               b_qkv=dev(inp.b_qkv, "bf16"), b_o=dev(inp.b_o, "bf16"),
+                               workspace=bws)
+        b = jav.ffn_backward(fdesc, x, dout, mod_d, dev(f.table, "f32"), dev(f.w1, "bf16"),
+                             dev(f.w2, "bf16"), b1=dev(f.b1, "bf16"), b2=dev(f.b2, "bf16"),
+                             workspace=fws)
+        _sync()
+        outs.append((a, b))
+    for key in ("dx", "dtable", "dw_qkv", "dw_o", "db_qkv", "db_o"):
+        assert torch.isfinite(outs[1][0][key].float()).all(), key
+        assert torch.equal(outs[0][0][key], outs[1][0][key]), key
+    for key in ("dx", "dtable", "dw1", "dw2", "db1", "db2"):
+        assert torch.isfinite(outs[1][1][key].float()).all(), key
+        assert torch.equal(outs[0][1][key], outs[1][1][key]), key
