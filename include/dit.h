@@ -50,7 +50,11 @@
  * Device-array contents are a contract and are not checked on the hot path:
  *   cu_seqlens[0] == 0, non-decreasing, cu_seqlens[n_seqs] == n_tokens, every
  *   segment no longer than max_seqlen, every modality id < 3, positions >= 0.
- *   dit_pack_layout() produces such arrays.
+ *   dit_pack_layout() produces such arrays.  With DIT_VALIDATE=1 in the
+ *   environment, the entry points that take cu_seqlens or modality ids
+ *   (attention, AdaLN, the block and feed-forward halves, their FP8 and
+ *   backward forms) first copy those arrays to the host on the call's stream,
+ *   synchronously, and return DIT_EINVAL if they break the contract.
  */
 #ifndef DIT_H
 #define DIT_H

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -63,6 +64,49 @@ dit_status check_stream_rows(int64_t n_tokens) {
   return DIT_OK;
 }
 
+// DIT_VALIDATE=1 in the environment: before enqueuing, copy the device arrays
+// the kernels take on trust (cu_seqlens, modality ids) to the host on the
+// call's stream, synchronously, and check them.  Off by default: the checks
+// stall the stream.
+bool validate_on() {
+  const char* v = std::getenv("DIT_VALIDATE");
+  return v != nullptr && v[0] == '1';
+}
+
+dit_status validate_segments(const char* who, const int32_t* cu, int32_t n_seqs,
+                             int32_t max_seqlen, int64_t n_tokens, void* stream) {
+  std::vector<int32_t> h((size_t)n_seqs + 1);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  if (h[0] != 0) return fail(DIT_EINVAL, "%s: cu_seqlens[0] = %d, not 0", who, h[0]);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (h[i + 1] < h[i])
+      return fail(DIT_EINVAL, "%s: cu_seqlens decreases at %d (%d -> %d)", who, i, h[i], h[i + 1]);
+    if (h[i + 1] - h[i] > max_seqlen)
+      return fail(DIT_EINVAL, "%s: segment %d has %d tokens, max_seqlen is %d", who, i,
+                  h[i + 1] - h[i], max_seqlen);
+  }
+  if (h[n_seqs] != n_tokens)
+    return fail(DIT_EINVAL, "%s: cu_seqlens ends at %d, n_tokens is %lld", who, h[n_seqs],
+                (long long)n_tokens);
+  return DIT_OK;
+}
+
+dit_status validate_modality(const char* who, const uint8_t* mod, int64_t n, void* stream) {
+  std::vector<uint8_t> h((size_t)n);
+  hipError_t e = hipMemcpyAsync(h.data(), mod, h.size(), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  for (int64_t i = 0; i < n; ++i)
+    if (h[(size_t)i] >= DIT_NUM_MOD)
+      return fail(DIT_EINVAL, "%s: modality[%lld] = %d, not below 3", who, (long long)i,
+                  (int)h[(size_t)i]);
+  return DIT_OK;
+}
+
 // Rope frequencies theta^(-2j/s_a) for every pair of a head, in double.
 void rope_freqs(const int32_t* sec, double theta, int head_dim, double* out) {
   int p = 0;
@@ -109,6 +153,10 @@ extern "C" dit_status adaln_modulate(dit_dtype dt, const void* x, int64_t ld_x,
   if (dit_status st = adaln_check(dt, x, ld_x, modality, table, y, ld_y, n_tokens, d_model, eps))
     return st;
   if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_modality("adaln_modulate", modality, n_tokens, stream))
+      return st;
+  }
   hipError_t e = launch_adaln(dt == DIT_BF16, x, ld_x, modality, table, y, ld_y, n_tokens,
                               d_model, eps, (hipStream_t)stream);
   return e == hipSuccess ? DIT_OK : hip_fail(e, "adaln_modulate launch");
@@ -145,6 +193,10 @@ extern "C" dit_status adaln_modulate_fp8(dit_dtype dt, const void* x, int64_t ld
                                       d_model, eps))
     return st;
   if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_modality("adaln_modulate_fp8", modality, n_tokens, stream))
+      return st;
+  }
   hipError_t e = launch_adaln_fp8(dt == DIT_BF16, x, ld_x, modality, table, q, ld_q, scales,
                                   n_tokens, d_model, eps, (hipStream_t)stream);
   return e == hipSuccess ? DIT_OK : hip_fail(e, "adaln_modulate_fp8 launch");
@@ -285,6 +337,11 @@ extern "C" dit_status attn_packed(dit_dtype dt, const void* q, int64_t ld_q, con
                                  max_seqlen, n_tokens, n_heads, head_dim, softmax_scale))
     return st;
   if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_segments("attn_packed", cu_seqlens, n_seqs, max_seqlen,
+                                          n_tokens, stream))
+      return st;
+  }
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   hipError_t e = launch_attn(dt == DIT_BF16, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens,
                              n_seqs, max_seqlen, n_tokens, n_heads, head_dim, scale,
@@ -305,6 +362,11 @@ extern "C" dit_status attn_packed_lse(dit_dtype dt, const void* q, int64_t ld_q,
   if (!lse) return fail(DIT_EINVAL, "attn_packed_lse: null lse");
   if (dt != DIT_BF16) return fail(DIT_EUNSUPPORTED, "attn_packed_lse: bf16 only");
   if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_segments("attn_packed_lse", cu_seqlens, n_seqs, max_seqlen,
+                                          n_tokens, stream))
+      return st;
+  }
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   hipError_t e = launch_attn(1, q, ld_q, k, ld_k, v, ld_v, o, ld_o, cu_seqlens, n_seqs,
                              max_seqlen, n_tokens, n_heads, head_dim, scale, causal != 0, lse,
@@ -345,6 +407,11 @@ extern "C" dit_status attn_packed_backward(
   if (!workspace || workspace_bytes < need)
     return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
   if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_segments("attn_packed_backward", cu_seqlens, n_seqs, max_seqlen,
+                                          n_tokens, stream))
+      return st;
+  }
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   hipError_t e = launch_attn_bwd(q, ld_q, k, ld_k, v, ld_v, o, ld_o, dout, ld_do, lse, dq, ld_dq,
                                  dk, ld_dk, dv, ld_dv, cu_seqlens, n_seqs, max_seqlen, n_tokens,
@@ -686,6 +753,10 @@ extern "C" dit_status dit_ffn_forward(const dit_ffn_desc* d, const void* x, void
     return fail(DIT_EUNSUPPORTED, "dit_ffn_forward: pointers must be 16-byte aligned");
   if (n_tokens == 0) return DIT_OK;
 
+  if (validate_on()) {
+    if (dit_status st = validate_modality("dit_ffn_forward", modality, n_tokens, stream))
+      return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_adaln(dt == DIT_BF16, x, D, modality, ada_table, y, D, n_tokens, D,
                               d->ln_eps, s);
@@ -743,6 +814,10 @@ extern "C" dit_status dit_ffn_forward_fp8(const dit_ffn_desc* d, const void* x, 
   if (!aligned16(out)) return fail(DIT_EUNSUPPORTED, "%s: out must be 16-byte aligned", who);
   if (n_tokens == 0) return DIT_OK;
 
+  if (validate_on()) {
+    if (dit_status st = validate_modality("dit_ffn_forward_fp8", modality, n_tokens, stream))
+      return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_adaln_fp8(1, x, D, modality, ada_table, codes, D, scales, n_tokens, D,
                                   d->ln_eps, s);
@@ -826,6 +901,13 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
     return fail(DIT_EUNSUPPORTED, "dit_block_forward: x/out must be 16-byte aligned");
   if (n_tokens == 0) return DIT_OK;
 
+  if (validate_on()) {
+    if (dit_status st = validate_segments("dit_block_forward", cu_seqlens, n_seqs, max_seqlen,
+                                          n_tokens, stream))
+      return st;
+    if (dit_status st = validate_modality("dit_block_forward", modality, n_tokens, stream))
+      return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
   auto mark = [&](int i) {
@@ -920,6 +1002,13 @@ extern "C" dit_status dit_block_forward_fp8(
   if (!aligned16(out)) return fail(DIT_EUNSUPPORTED, "%s: out must be 16-byte aligned", who);
   if (n_tokens == 0) return DIT_OK;
 
+  if (validate_on()) {
+    if (dit_status st = validate_segments("dit_block_forward_fp8", cu_seqlens, n_seqs, max_seqlen,
+                                          n_tokens, stream))
+      return st;
+    if (dit_status st = validate_modality("dit_block_forward_fp8", modality, n_tokens, stream))
+      return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
   auto mark = [&](int i) {
@@ -1055,6 +1144,13 @@ extern "C" dit_status dit_block_backward(
     return fail(DIT_EINVAL, "%s: dx overlaps x", who);
   if (n_tokens == 0) return DIT_OK;
 
+  if (validate_on()) {
+    if (dit_status st = validate_segments("dit_block_backward", cu_seqlens, n_seqs, max_seqlen,
+                                          n_tokens, stream))
+      return st;
+    if (dit_status st = validate_modality("dit_block_backward", modality, n_tokens, stream))
+      return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
   double freq[64], nfreq[64];
@@ -1211,6 +1307,10 @@ extern "C" dit_status dit_ffn_backward(const dit_ffn_desc* d, const void* x, con
     return fail(DIT_EINVAL, "%s: dx overlaps x", who);
   if (n_tokens == 0) return DIT_OK;
 
+  if (validate_on()) {
+    if (dit_status st = validate_modality("dit_ffn_backward", modality, n_tokens, stream))
+      return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
 #define DIT_FBWD(call, what)                                         \

@@ -426,3 +426,40 @@ def test_block_poison_tail_and_determinism(jav):
     assert torch.equal(outp[:n].view(torch.int16), out_ref.view(torch.int16))
     assert torch.isnan(outp[n:].float()).all()
     assert torch.equal(out_rep.view(torch.int16), out_ref.view(torch.int16))
+
+
+def test_validate_env_rejects_broken_device_arrays(jav):
+    """DIT_VALIDATE=1: broken cu_seqlens or modality ids come back as DIT_EINVAL before any
+    launch; valid arrays pass.  (The broken cases here are memory-safe even unchecked: the
+    buffers cover every row a kernel could touch and the table is the front of a larger
+    allocation.)"""
+    import os
+    import torch
+    n, H = 512, 2
+    q = torch.zeros((n, H * 128), dtype=torch.bfloat16, device="cuda")
+    tab_big = torch.zeros((2, 3, 3, H * 128), dtype=torch.float32, device="cuda")
+    cases = [([0, 300, 200, 400], 300, "decreases"), ([0, 200, 480], 280, "ends at"),
+             ([0, 100, 400], 200, "max_seqlen"), ([5, 400], 395, "not 0")]
+    old = os.environ.get("DIT_VALIDATE")
+    os.environ["DIT_VALIDATE"] = "1"
+    try:
+        for cu, ms, msg in cases:
+            cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+            with pytest.raises(jav.DitError) as ei:
+                jav.attn_packed(q, q, q, cu_d, ms, H, 128, n_tokens=400)
+            assert ei.value.status == jav.DIT_EINVAL and msg in str(ei.value), (cu, str(ei.value))
+        jav.attn_packed(q, q, q, torch.tensor([0, 150, 400], dtype=torch.int32, device="cuda"),
+                        250, H, 128, n_tokens=400)
+        mod = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        mod[77] = 3
+        with pytest.raises(jav.DitError) as ei:
+            jav.adaln_modulate(q, mod, tab_big[0], n_tokens=400)
+        assert "modality[77] = 3" in str(ei.value)
+        mod[77] = 2
+        jav.adaln_modulate(q, mod, tab_big[0], n_tokens=400)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("DIT_VALIDATE", None)
+        else:
+            os.environ["DIT_VALIDATE"] = old
