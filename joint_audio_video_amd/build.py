@@ -4,6 +4,10 @@ Usage: python joint_audio_video_amd/build.py   (or __graft_entry__.build()); run
 as a file, not with -m: the package's __init__ loads the built library and
 refuses to import without it.
 
+python joint_audio_video_amd/build.py --resources prints, instead of building,
+a markdown table of every device kernel's registers, scratch, LDS and
+occupancy as the compiler reports them for gfx950.
+
 Every source under csrc/ is compiled to an object in _build/ and linked into
 joint_audio_video_amd/libdit.so.  The build always recompiles (it is the
 "does it build" check), in parallel.
@@ -66,6 +70,51 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def _demangle(name: str) -> str:
+    tool = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    out = name
+    if tool:
+        r = subprocess.run([tool, name], capture_output=True, text=True)
+        if r.returncode == 0 and r.stdout.strip():
+            out = r.stdout.strip()
+    return out.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def resources() -> str:
+    """Markdown table of the compiler's kernel-resource-usage remarks for every .hip source."""
+    import re
+    keys = ("VGPRs", "AGPRs", "ScratchSize [bytes/lane]", "Occupancy [waves/SIMD]",
+            "LDS Size [bytes/block]")
+    rows = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        cmd = [HIPCC, *COMMON_FLAGS, "-x", "hip", "--cuda-device-only", "-c",
+               os.path.join(CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark:\s+Function Name: (\S+)", line)
+            if m:
+                cur = {"name": _demangle(m.group(1)), "src": src}
+                rows.append(cur)
+                continue
+            for k in keys:
+                m = re.search(r"remark:\s+" + re.escape(k) + r": (\d+)", line)
+                if m and cur is not None:
+                    cur[k] = m.group(1)
+    out = ["| source | kernel | VGPRs | AGPRs | scratch B/lane | LDS B/workgroup | waves/SIMD |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['src']} | {r['name']} | {r.get('VGPRs', '')} | {r.get('AGPRs', '')} | "
+                   f"{r.get('ScratchSize [bytes/lane]', '')} | {r.get('LDS Size [bytes/block]', '')} | "
+                   f"{r.get('Occupancy [waves/SIMD]', '')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--resources" in sys.argv[1:]:
+        print(resources())
+    else:
+        build(verbose=True)
     sys.exit(0)
