@@ -14,7 +14,11 @@
 // AGPR half of the register file).  A and B tiles are staged through LDS
 // (double-buffered, 128 KB) by buffer loads that write straight into LDS,
 // with an XOR swizzle of the 16-byte chunk index so the rows an MFMA fragment
-// read touches spread over the banks.  Both operands are K-contiguous
+// read touches spread over the banks.  The LDS has 64 four-byte banks, so a
+// 16-byte read is served 16 lanes at a time; a tile row is 128 bytes, so
+// those 16 rows must land on 16 distinct 16-byte slots of a 256-byte sweep,
+// which chunk ^ ((row>>1) & 7) gives (row pairs share a chunk pattern and
+// differ by the 128-byte half).  Both operands are K-contiguous
 // ([rows][K]), so every fragment is one 16-byte LDS read.
 // With one wave per SIMD nothing else hides latency, so each k-step is laid
 // out by hand as 16 fenced groups of four independent MFMAs; the fragment
@@ -49,7 +53,7 @@ struct EpiArgs {
   int64_t plane_stride;     // elements between planes
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // Tile of this workgroup: groups of kGroupM M-tiles, walked column by column.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -90,12 +94,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   // Global -> LDS with buffer_load_dwordx4 ... lds: lane slot s = 256*i + tid
   // of a tile lands at LDS element 8*s, i.e. row s/8, physical chunk s%8.
   // The swizzle is applied on the global side: that slot holds logical chunk
-  // (s%8) ^ (row & 7).  For this thread the row is 32*i + tid/8 and the
-  // logical chunk (tid&7) ^ ((tid>>3)&7) for every i.  Rows past M (N) are
+  // (s%8) ^ ((row>>1) & 7).  For this thread the row is 32*i + tid/8 and the
+  // logical chunk (tid&7) ^ ((tid>>4)&7) for every i.  Rows past M (N) are
   // clamped to the last valid row: their results are never stored.  Offsets
   // are bytes from the tile's first row; the k offset is a scalar.
   const int lrow = tid >> 3;
-  const int lchunk = (tid & 7) ^ ((tid >> 3) & 7);
+  const int lchunk = (tid & 7) ^ ((tid >> 4) & 7);
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A + (int64_t)m0 * lda), 0, (int)((uint32_t)rows_a * (uint32_t)lda * 2u),
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
 
   // Global -> LDS exactly as the bf16 kernel, with 128-byte rows of codes.
   const int lrow = tid >> 3;
-  const int lchunk = (tid & 7) ^ ((tid >> 3) & 7);
+  const int lchunk = (tid & 7) ^ ((tid >> 4) & 7);
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(A + (int64_t)m0 * lda), 0, (int)((uint32_t)rows_a * (uint32_t)lda),
