@@ -94,11 +94,16 @@ constexpr int kAttnThreads = 64 * kWaves;
 constexpr int QBLK = 32 * kWaves;                  // queries per workgroup
 constexpr int kTileLoads = KB * DH * 2 / 16 / kAttnThreads;   // 16-byte loads per thread per tile
 
-// LDS tiles, row-major [key][d] (256 B per key row), 16-byte chunks XOR-swizzled:
-// K: chunk ^ (row & 7), so the 32 rows of an S^T fragment read spread over banks;
-// V: chunk ^ 2*(row & 3), so the four rows of a transposed read do.
-__device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 7); }
-__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (2 * (row & 3)); }
+// LDS tiles, row-major [key][d] (256 B per key row), 16-byte chunks XOR-swizzled.
+// The LDS has 64 four-byte banks (256 B per sweep), so one key row covers every
+// bank once and rows that a read serves together must sit in different chunks.
+// K: chunk ^ (row & 15): a 16-byte fragment read is served 16 lanes (16
+//    consecutive rows) at a time, which then touch 16 distinct chunks;
+// V: chunk ^ 4*(row & 3): a transposed 8-byte read is served 32 lanes at a time,
+//    four rows of 64 contiguous bytes each, which then touch four distinct
+//    64-byte quarters of the sweep.
+__device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (4 * (row & 3)); }
 
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
@@ -182,22 +187,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   // The XOR swizzles distribute over these lane bits, so every fragment
   // address is one of a few per-lane bases plus a compile-time offset.
   // V: logical chunk 4db + x (x = 2t1 + q1) of row 4g + kk + ... lands at
-  // physical chunk 4(db ^ zhi) + zlo with z = x ^ 2kk; db even/odd share a base.
-  int v_lane_off[2];
-  {
-    const int z = (2 * t1 + (qq >> 1)) ^ (2 * kk);
-    const int zlo = z & 3, zhi = z >> 2;
-    const int rowpart = (4 * g + kk) * DH + zlo * 8 + (qq & 1) * 4;
-    v_lane_off[0] = rowpart + 32 * zhi;          // d-blocks 0 and 2 (+64)
-    v_lane_off[1] = rowpart + 32 * (1 - zhi);    // d-blocks 1 and 3 (+64)
-  }
-  // K: chunk (2ks + g) ^ (row & 7) of row l32 = 2((ks & 4) | ((ks & 3) ^ v)) + w1
-  // with w = g ^ (l32 & 7), v = w >> 1.
-  int k_lane_off[4];
-  {
-    const int w = g ^ (l32 & 7);
+  // physical chunk 4(db ^ kk) + x.
+  int v_lane_off[DH / 32];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k_lane_off[j] = l32 * DH + 16 * (j ^ (w >> 1)) + 8 * (w & 1);
+  for (int db = 0; db < DH / 32; ++db)
+    v_lane_off[db] = (4 * g + kk) * DH + 32 * (db ^ kk) + 16 * t1 + 4 * qq;
+  // K: chunk (2ks + g) ^ (l32 & 15) of row l32 = 2(ks ^ (w >> 1)) + (w & 1)
+  // with w = g ^ (l32 & 15).
+  int k_lane_off[DH / 16];
+  {
+    const int w = g ^ (l32 & 15);
+#pragma unroll
+    for (int j = 0; j < DH / 16; ++j) k_lane_off[j] = l32 * DH + 16 * (j ^ (w >> 1)) + 8 * (w & 1);
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -220,11 +221,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   bf16x8 pf[2 * NKB];
 
   // S^T[key][query] of one tile: two 32-key blocks whose MFMA chains
-  // alternate.  Fragment (b, ks) sits at element k_lane_off[ks & 3] +
-  // 16*(ks & 4) + 4096*b (the swizzle only permutes ks within groups of four).
+  // alternate.  Fragment (b, ks) sits at element k_lane_off[ks] + 4096*b.
   auto compute_s = [&](const uint16_t* ks_t) __attribute__((always_inline)) {
     auto kfrag = [&](int b, int ks) {
-      return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ks & 3] + 16 * (ks & 4) + 4096 * b);
+      return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ks] + 4096 * b);
     };
     bf16x8 kf[DH / 16][NKB];
 #pragma unroll
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     auto vread = [&](int i) __attribute__((always_inline)) {
       const int s = i >> 2, db = i & 3;
       const int rows = 32 * (s >> 1) + 16 * (s & 1);
-      const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db & 1] + 64 * (db >> 1) + rows * DH;
+      const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db] + rows * DH;
       const v4i16 lo = lds_read_tr16(p);
       const v4i16 hi = lds_read_tr16(p + 8 * DH);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
