@@ -45,7 +45,8 @@ from .nft import implicit_policies, nft_loss
 from .backward import (adaln_backward, attention_backward, attention_backward_rows,
                        attention_lse, block_backward, ffn_backward, gelu_tanh_grad,
                        rope3d_backward)
-from .fp8 import (E4M3_MAX, adaln_modulate_fp8, block_forward_fp8, dequantize_rows, e4m3_decode,
+from .fp8 import (E4M3_MAX, adaln_modulate_fp8, attention_fp8, attention_fp8_operands,
+                  dequantize_attention_operands, quantize_tensor, block_forward_fp8, dequantize_rows, e4m3_decode,
                   e4m3_encode, e4m3_encode_bruteforce, e4m3_table, ffn_forward_fp8, linear_fp8,
                   quantize_rows, row_scales)
 
@@ -58,7 +59,8 @@ __all__ = [
     "VIDEO_LATENT_CHANNELS", "timestep_from_sigma", "standard_velocity", "clean_estimate",
     "euler_step", "denoise_step", "denoise_loop", "implicit_policies", "nft_loss",
     "E4M3_MAX", "e4m3_decode", "e4m3_table", "e4m3_encode", "e4m3_encode_bruteforce",
-    "row_scales", "quantize_rows", "dequantize_rows", "linear_fp8", "adaln_modulate_fp8",
+    "row_scales", "quantize_rows", "quantize_tensor", "attention_fp8_operands",
+    "dequantize_attention_operands", "attention_fp8", "dequantize_rows", "linear_fp8", "adaln_modulate_fp8",
     "block_forward_fp8", "ffn_forward_fp8", "attention_backward", "rope3d_backward",
     "adaln_backward", "block_backward", "attention_lse", "attention_backward_rows",
     "ffn_backward", "gelu_tanh_grad",

@@ -25,6 +25,17 @@ layers in FP8; the pages give no scaling recipe.  Readings:
   output, the attention output, the activated hidden state) is quantized per
   row from its float32 value; rotary embedding, attention, the activation
   and the gated residual stay in the plain oracle's float64 arithmetic.
+* FP8 attention (the softmax products in FP8): q is quantized per (token,
+  head) row as above; k and v with one scale per head, amax / 448 over every
+  packed token of that head (one scale factors out of both products: out of
+  s = q k^T for k, out of o = P v for v, whose sum runs over keys).  The
+  scores and o = softmax(s) v are then evaluated here in float64 from the
+  dequantized operands with exact probabilities; the GPU also rounds the
+  probabilities to e4m3 (2^8 times their value relative to a running row
+  maximum, so at most 448), which this function does not model: it moves
+  each o element by at most 2^-4 sum_k P_k |v_k| / sum_k P_k (relative
+  half-step of a normal e4m3 value) plus 2^-18 max_k |v_k| per key for
+  probabilities in the subnormal range.
 """
 from __future__ import annotations
 
@@ -182,3 +193,58 @@ def ffn_forward_fp8(x, modality, table_mlp, w1_codes, w1_scales, w2_codes, w2_sc
     out = out_proj_gated(dequantize_rows(hc, hs), dequantize_rows(w2_codes, w2_scales), x,
                          modality, table_mlp, b2, rows=rows)
     return dict(y_codes=yc, y_scales=ys, h=h, h_codes=hc, h_scales=hs, out=out)
+
+
+# ---------------------------------------------------------------------------
+# FP8 attention
+# ---------------------------------------------------------------------------
+
+def quantize_tensor(x):
+    """One float32 scale for the whole array (amax / 448, 1 for an all-zero
+    array) and the e4m3 codes of every value: the per-row recipe applied to
+    the array as one row."""
+    x32 = np.asarray(x, dtype=np.float32)
+    codes, s = quantize_rows(x32.reshape(1, -1))
+    return codes.reshape(x32.shape), np.float32(s[0])
+
+
+def attention_fp8_operands(q, k, v, n_heads: int, head_dim: int) -> Dict[str, np.ndarray]:
+    """Codes and scales of the FP8 attention operands (q, k, v: [N][H*Dh]):
+    q_codes [N][H*Dh] with q_scales [N][H] (one per token and head), k_codes /
+    v_codes [N][H*Dh] with k_scales / v_scales [H] (one per head)."""
+    q = np.asarray(q, dtype=np.float32)
+    n = q.shape[0]
+    qc, qs = quantize_rows(q.reshape(n * n_heads, head_dim))
+    out = dict(q_codes=qc.reshape(n, n_heads * head_dim), q_scales=qs.reshape(n, n_heads))
+    for name, t in (("k", k), ("v", v)):
+        t = np.asarray(t, dtype=np.float32)
+        codes = np.empty(t.shape, dtype=np.uint8)
+        scales = np.empty(n_heads, dtype=np.float32)
+        for h in range(n_heads):
+            cols = slice(h * head_dim, (h + 1) * head_dim)
+            codes[:, cols], scales[h] = quantize_tensor(t[:, cols])
+        out[name + "_codes"], out[name + "_scales"] = codes, scales
+    return out
+
+
+def dequantize_attention_operands(ops: Dict[str, np.ndarray], n_heads: int, head_dim: int):
+    """float64 q, k, v [N][H*Dh] from attention_fp8_operands' codes and scales."""
+    tab = e4m3_table()
+    qs = np.repeat(np.asarray(ops["q_scales"], np.float64), head_dim, axis=1)
+    q = tab[ops["q_codes"]] * qs
+    k = tab[ops["k_codes"]] * np.repeat(np.asarray(ops["k_scales"], np.float64), head_dim)[None, :]
+    v = tab[ops["v_codes"]] * np.repeat(np.asarray(ops["v_scales"], np.float64), head_dim)[None, :]
+    return q, k, v
+
+
+def attention_fp8(q, k, v, cu_seqlens, n_heads: int, head_dim: int, causal: bool = False,
+                  scale: Optional[float] = None, rows=None) -> Dict[str, np.ndarray]:
+    """Softmax attention (oracle.block.attention) of the dequantized FP8
+    operands with exact probabilities.  Returns the operands' codes and
+    scales, o (float64 [rows][H*Dh]) and o_abs, the same attention of |v|
+    (sum_k P_k |v_k| / sum_k P_k, the weight of the probability-rounding bound)."""
+    ops = attention_fp8_operands(q, k, v, n_heads, head_dim)
+    qd, kd, vd = dequantize_attention_operands(ops, n_heads, head_dim)
+    o = attention(qd, kd, vd, cu_seqlens, n_heads, head_dim, causal, scale, rows)
+    o_abs = attention(qd, kd, np.abs(vd), cu_seqlens, n_heads, head_dim, causal, scale, rows)
+    return dict(o=o, o_abs=o_abs, **ops)

@@ -236,3 +236,119 @@ def test_fp8_block_tiny_workload_is_close_to_the_unquantized_block():
     assert 5e-3 < rel < 8e-2
     assert np.abs(f8["out"] - ref["out"]).max() <= 3e-2
     assert np.linalg.norm(f8["out"] - ref["out"]) <= 1e-2 * np.linalg.norm(ref["out"])
+
+
+# ---------------------------------------------------------------------------
+# FP8 attention: q per (token, head) row, k and v per head, exact probabilities
+# ---------------------------------------------------------------------------
+
+def _grid_rows(rng, n_rows, width, exps):
+    """Rows of e4m3 grid values times 2^e (e per row), each row holding one
+    +-448 * 2^e element: the row's amax / 448 is exactly 2^e, so per-row
+    quantization reproduces the row bit for bit."""
+    tab = oracle.e4m3_table()
+    fin = tab[np.isfinite(tab)]
+    vals = rng.choice(fin[np.abs(fin) <= 64.0], size=(n_rows, width))
+    vals[np.arange(n_rows), rng.integers(0, width, n_rows)] = 448.0 * rng.choice([-1.0, 1.0], n_rows)
+    return vals * (2.0 ** np.asarray(exps, np.float64))[:, None]
+
+
+def test_quantize_tensor_scale_codes_and_zero():
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = (rng.standard_normal((37, 19)) * 3.0).astype(np.float32)
+    codes, s = oracle.quantize_tensor(x)
+    amax = np.float32(np.max(np.abs(x)))
+    assert s == np.float32(amax / np.float32(448.0))
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert codes[i] in (0x7E, 0xFE)                     # the amax lands on +-448
+    dec = oracle.e4m3_table()[codes] * np.float64(s)
+    err = np.abs(dec - x)
+    normal = np.abs(x) / s >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0 ** -10 * s * (1 + 1e-6))
+    zc, zs = oracle.quantize_tensor(np.zeros((4, 4)))
+    assert zs == np.float32(1.0) and not zc.any()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_of_grid_operands_is_the_plain_attention(causal):
+    """Operands on the e4m3 grid with q's power-of-two scale varying per
+    (token, head) row and k's, v's per head: quantization is lossless, so the
+    FP8 attention equals the plain one.  Quantizing q per head, or k or v per
+    row, would put non-power-of-two scales on these rows and fail."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    n, hh, dh = 40, 2, 16
+    cu = [0, 17, 40]
+    q = _grid_rows(rng, n * hh, dh, rng.integers(-9, -4, n * hh)).reshape(n, hh * dh)
+    k = np.empty((n, hh * dh))
+    v = np.empty((n, hh * dh))
+    for h in range(hh):
+        cols = slice(h * dh, (h + 1) * dh)
+        for t, e in ((k, -7 + h), (v, -6 - h)):
+            blk = _grid_rows(rng, n, dh, np.full(n, e))
+            blk[np.abs(blk) == 448.0 * 2.0 ** e] = 64.0 * 2.0 ** e   # one 448 per head only
+            blk[rng.integers(0, n), rng.integers(0, dh)] = -448.0 * 2.0 ** e
+            t[:, cols] = blk
+    r = oracle.attention_fp8(q, k, v, cu, hh, dh, causal=causal)
+    qd, kd, vd = oracle.dequantize_attention_operands(r, hh, dh)
+    np.testing.assert_array_equal(qd, q)
+    np.testing.assert_array_equal(kd, k)
+    np.testing.assert_array_equal(vd, v)
+    ref = oracle.attention(q, k, v, cu, hh, dh, causal=causal)
+    np.testing.assert_allclose(r["o"], ref, rtol=1e-12, atol=1e-15)
+    assert np.array_equal(r["k_scales"], np.float32([2.0 ** -7, 2.0 ** -6]))
+    assert np.array_equal(r["v_scales"], np.float32([2.0 ** -6, 2.0 ** -7]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_with_zero_queries_averages_the_values(causal):
+    """q = 0 gives every key the same weight: o is the mean of the dequantized
+    v over the query's keys (its segment, or the segment's prefix when
+    causal), and o_abs the mean of |v|."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    n, hh, dh = 30, 2, 8
+    cu = [0, 7, 30]
+    q = np.zeros((n, hh * dh))
+    k = rng.standard_normal((n, hh * dh))
+    v = rng.standard_normal((n, hh * dh)) * 2.0
+    r = oracle.attention_fp8(q, k, v, cu, hh, dh, causal=causal)
+    _, _, vd = oracle.dequantize_attention_operands(r, hh, dh)
+    for s in range(len(cu) - 1):
+        for i in range(cu[s], cu[s + 1]):
+            keys = slice(cu[s], i + 1 if causal else cu[s + 1])
+            np.testing.assert_allclose(r["o"][i], vd[keys].mean(axis=0), rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(r["o_abs"][i], np.abs(vd[keys]).mean(axis=0), rtol=1e-12)
+    assert np.all(r["q_scales"] == 1.0) and not r["q_codes"].any()
+
+
+def test_fp8_attention_per_head_scaling():
+    """Scaling one head's v by 8 scales that head's o by exactly 8 (its codes
+    are unchanged, its scale is 8 times larger) and leaves the other heads
+    bit for bit; o_abs bounds |o| (triangle inequality)."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    n, hh, dh = 26, 3, 8
+    cu = [0, 11, 26]
+    q = rng.standard_normal((n, hh * dh))
+    k = rng.standard_normal((n, hh * dh))
+    v = rng.standard_normal((n, hh * dh))
+    a = oracle.attention_fp8(q, k, v, cu, hh, dh)
+    v2 = v.copy()
+    v2[:, dh:2 * dh] *= 8.0
+    b = oracle.attention_fp8(q, k, v2, cu, hh, dh)
+    np.testing.assert_array_equal(a["v_codes"], b["v_codes"])
+    assert b["v_scales"][1] == 8 * a["v_scales"][1]
+    np.testing.assert_allclose(b["o"][:, dh:2 * dh], 8 * a["o"][:, dh:2 * dh], rtol=1e-12)
+    np.testing.assert_array_equal(b["o"][:, :dh], a["o"][:, :dh])
+    np.testing.assert_array_equal(b["o"][:, 2 * dh:], a["o"][:, 2 * dh:])
+    assert np.all(np.abs(a["o"]) <= a["o_abs"] * (1 + 1e-12))
+
+
+def test_fp8_attention_rows_subset_matches_every_row():
+    rng = np.random.Generator(np.random.PCG64(14))
+    n, hh, dh = 33, 2, 8
+    cu = [0, 20, 33]
+    q, k, v = (rng.standard_normal((n, hh * dh)) for _ in range(3))
+    full = oracle.attention_fp8(q, k, v, cu, hh, dh, causal=True)
+    rows = [0, 5, 19, 20, 32]
+    part = oracle.attention_fp8(q, k, v, cu, hh, dh, causal=True, rows=rows)
+    np.testing.assert_array_equal(part["o"], full["o"][rows])
