@@ -378,6 +378,69 @@ dit_status linear_fp8(const uint8_t* a, int64_t ld_a, const float* a_scales, con
                       void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* FP8 attention                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* The attention of attn_packed ([vLLM-Omni] section 3: softmax inside each
+ * cu_seqlens segment, full or causal) with both products in FP8 (section 5:
+ * the active layers in FP8; no recipe on the pages).  Here: q is quantized
+ * per (token, head) row, k and v with one scale per head (amax / 448 over all
+ * n_tokens rows of that head), codes and scales as quantize_rows_fp8.  Scores
+ * and the softmax are float32; the probabilities enter the second product as
+ * e4m3 codes of 2^8 times their value relative to the row's running maximum
+ * (at most 2^8.75), o is float32 until its bf16 store.  Against attention of
+ * the dequantized operands with exact probabilities, an o element moves by at
+ * most 2^-4 sum_k P_k |v_k| / sum_k P_k (plus 2^-18 max_k |v_k| per key for
+ * probabilities below 2^-14 and the bf16 rounding of o).  bf16 inputs and
+ * output, head_dim 128 only.  NaN inputs give unspecified results. */
+
+/* Bytes of the operand workspace for n_tokens, n_seqs segments and n_heads:
+ * q and k codes (n_tokens x n_heads x 128 bytes each), v codes transposed
+ * (n_heads x 128 rows of ld_vt = roundup64(n_tokens) + 128 n_seqs bytes),
+ * n_heads x n_tokens q scales, per-head k and v scales and 2 x n_heads words
+ * of scratch, each part rounded up to 256.  0 for bad sizes or a head_dim
+ * other than 128. */
+size_t dit_attn_fp8_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads,
+                                    int32_t head_dim);
+
+/* Byte offsets in that workspace, out[9] = {q8, k8, vt, sq, sk, sv, amax, ld8,
+ * ld_vt}: q8 / k8 e4m3 codes [n_tokens][ld8 = n_heads * 128] ([token][head][d]),
+ * vt e4m3 codes [n_heads * 128][ld_vt] (row h * 128 + d; segment s's key r at
+ * column roundup64(cu_seqlens[s]) + 128 s + r, zero codes up to the segment's
+ * next multiple of 64), sq float32 [n_heads][n_tokens], sk and sv float32
+ * [n_heads].  Errors: DIT_EINVAL for a null out or bad sizes,
+ * DIT_EUNSUPPORTED for head_dim != 128. */
+dit_status dit_attn_fp8_layout(int64_t n_tokens, int32_t n_seqs, int32_t n_heads,
+                               int32_t head_dim, int64_t* out);
+
+/* attn_fp8_prepare: q, k, v bf16 [n_tokens][ld] (device; the first
+ * n_heads * head_dim columns, [head][d]) -> the operands in workspace (device,
+ * caller-owned, dit_attn_fp8_workspace_bytes), enqueued on stream.
+ * cu_seqlens int32 [n_seqs + 1] (device), as attn_packed.  Errors: DIT_EINVAL
+ * for a null pointer, n_seqs / n_heads < 1, an ld below n_heads * head_dim,
+ * max_seqlen < 1 or above n_tokens; DIT_EUNSUPPORTED for head_dim != 128,
+ * more than 65535 segments or heads, n_tokens * n_heads above 2^27, a
+ * segment's k codes spanning 2 GiB, or a pointer / ld off the 16-byte rule;
+ * DIT_EWORKSPACE for a missing or short workspace; DIT_EHIP on a launch
+ * failure. */
+dit_status attn_fp8_prepare(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                            const void* v, int64_t ld_v, const int32_t* cu_seqlens,
+                            int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
+                            int32_t n_heads, int32_t head_dim, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* attn_packed_fp8: o bf16 [n_tokens][ld_o] (device) from the operands that
+ * attn_fp8_prepare wrote for the same cu_seqlens, sizes and n_heads.
+ * softmax_scale 0 means 1/sqrt(head_dim); causal as attn_packed.  Rows outside
+ * every segment are not written.  Errors: those of attn_fp8_prepare (prefix
+ * attn_packed_fp8), plus DIT_EINVAL for a null o, ld_o below
+ * n_heads * head_dim or softmax_scale < 0. */
+dit_status attn_packed_fp8(const void* workspace, size_t workspace_bytes, void* o, int64_t ld_o,
+                           const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                           int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                           float softmax_scale, int32_t causal, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* The denoising step around the block                                        */
 /* ------------------------------------------------------------------------ */
 

@@ -38,6 +38,7 @@ EXPORTED = (
     "attn_packed_lse", "dit_attn_backward_workspace_bytes", "attn_packed_backward",
     "dit_block_backward_workspace_bytes", "dit_block_backward",
     "dit_ffn_backward_workspace_bytes", "dit_ffn_backward",
+    "dit_attn_fp8_workspace_bytes", "dit_attn_fp8_layout", "attn_fp8_prepare", "attn_packed_fp8",
 )
 
 
@@ -130,6 +131,12 @@ def _load() -> ctypes.CDLL:
         "dit_ffn_backward_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
         "dit_ffn_backward": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P, P,
                                             P, P, P, P, P, P, P, SZ, P]),
+        "dit_attn_fp8_workspace_bytes": (SZ, [I64, I32, I32, I32]),
+        "dit_attn_fp8_layout": (ctypes.c_int, [I64, I32, I32, I32, ctypes.POINTER(I64)]),
+        "attn_fp8_prepare": (ctypes.c_int, [P, I64, P, I64, P, I64, P, I32, I32, I64, I32, I32, P,
+                                            SZ, P]),
+        "attn_packed_fp8": (ctypes.c_int, [P, SZ, P, I64, P, I32, I32, I64, I32, I32, F32, I32,
+                                           P]),
         "dit_profile_enable": (ctypes.c_int, [I32]),
         "dit_profile_read": (ctypes.c_int, [ctypes.POINTER(F32), ctypes.POINTER(I32)]),
     }
@@ -301,6 +308,57 @@ def attn_packed_lse(q, k, v, cu_seqlens, max_seqlen: int, n_heads: int, head_dim
                                 int(max_seqlen), n, n_heads, head_dim, float(softmax_scale),
                                 int(bool(causal)), _stream(stream)))
     return out, lse
+
+
+def attn_fp8_workspace_bytes(n_tokens: int, n_seqs: int, n_heads: int, head_dim: int = 128) -> int:
+    return int(_lib.dit_attn_fp8_workspace_bytes(int(n_tokens), int(n_seqs), int(n_heads),
+                                                 int(head_dim)))
+
+
+def attn_fp8_layout(n_tokens: int, n_seqs: int, n_heads: int, head_dim: int = 128) -> dict:
+    """Byte offsets of the FP8 attention operands in the workspace
+    (libdit dit_attn_fp8_layout): q8, k8, vt, sq, sk, sv, amax, and the row
+    strides ld8 (bytes per token of q8 / k8) and ld_vt (bytes per d row of vt)."""
+    out = (ctypes.c_int64 * 9)()
+    _check(_lib.dit_attn_fp8_layout(int(n_tokens), int(n_seqs), int(n_heads), int(head_dim), out))
+    keys = ("q8", "k8", "vt", "sq", "sk", "sv", "amax", "ld8", "ld_vt")
+    return {k: int(v) for k, v in zip(keys, out)}
+
+
+def attn_fp8_prepare(q, k, v, cu_seqlens, max_seqlen: int, n_heads: int, head_dim: int = 128,
+                     workspace=None, n_tokens=None, stream=None):
+    """FP8 operands of attn_packed_fp8 from bf16 q, k, v rows
+    (libdit attn_fp8_prepare); returns the workspace (uint8, device)."""
+    torch = _torch()
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    n_seqs = cu_seqlens.numel() - 1
+    if workspace is None:
+        workspace = torch.empty(max(attn_fp8_workspace_bytes(n, n_seqs, n_heads, head_dim), 1),
+                                dtype=torch.uint8, device=q.device)
+    pq, ldq = _rows(q)
+    pk, ldk = _rows(k)
+    pv, ldv = _rows(v)
+    _check(_lib.attn_fp8_prepare(pq, ldq, pk, ldk, pv, ldv, cu_seqlens.data_ptr(), n_seqs,
+                                 int(max_seqlen), n, n_heads, head_dim, workspace.data_ptr(),
+                                 workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def attn_packed_fp8(workspace, cu_seqlens, max_seqlen: int, n_tokens: int, n_heads: int,
+                    head_dim: int = 128, softmax_scale: float = 0.0, causal: bool = False,
+                    out=None, stream=None):
+    """bf16 o [n_tokens][n_heads*head_dim] of the FP8 attention over operands
+    that attn_fp8_prepare wrote (libdit attn_packed_fp8)."""
+    torch = _torch()
+    n = int(n_tokens)
+    if out is None:
+        out = torch.empty((n, n_heads * head_dim), dtype=torch.bfloat16, device=workspace.device)
+    po, ldo = _rows(out)
+    _check(_lib.attn_packed_fp8(workspace.data_ptr(), workspace.numel(), po, ldo,
+                                cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), n,
+                                n_heads, head_dim, float(softmax_scale), int(bool(causal)),
+                                _stream(stream)))
+    return out
 
 
 def attn_backward_workspace_bytes(n_tokens: int, n_heads: int) -> int:

@@ -39,7 +39,7 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["abi.cpp", "layout.cpp", "adaln.hip", "rope.hip", "gemm.hip", "attn.hip",
-           "attn_bwd.hip", "grad.hip", "denoise.hip", "nft.hip"]
+           "attn_fp8.hip", "attn_bwd.hip", "grad.hip", "denoise.hip", "nft.hip"]
 
 
 def _compile(src: str) -> str:

@@ -421,6 +421,148 @@ extern "C" dit_status attn_packed_backward(
 }
 
 // ---------------------------------------------------------------------------
+// FP8 attention: operand preparation and the attention itself.
+
+namespace {
+struct Fp8AttnLayout {
+  size_t q8, k8, vt, sq, sk, sv, amax, total;
+  int64_t ld8, ld_vt;
+};
+Fp8AttnLayout fp8_attn_layout(int64_t n, int32_t n_seqs, int32_t h) {
+  Fp8AttnLayout L{};
+  L.ld8 = (int64_t)h * 128;
+  L.ld_vt = (n + 63) / 64 * 64 + 128 * (int64_t)n_seqs;
+  size_t off = 0;
+  L.q8 = off;   off += round256((size_t)n * (size_t)L.ld8);
+  L.k8 = off;   off += round256((size_t)n * (size_t)L.ld8);
+  L.vt = off;   off += round256((size_t)h * 128 * (size_t)L.ld_vt);
+  L.sq = off;   off += round256((size_t)h * (size_t)n * 4);
+  L.sk = off;   off += round256((size_t)h * 4);
+  L.sv = off;   off += round256((size_t)h * 4);
+  L.amax = off; off += round256((size_t)h * 8);
+  L.total = off;
+  return L;
+}
+AttnFp8Ops fp8_attn_ops(void* ws, const Fp8AttnLayout& L) {
+  char* b = static_cast<char*>(ws);
+  AttnFp8Ops o;
+  o.q8 = reinterpret_cast<uint8_t*>(b + L.q8);
+  o.k8 = reinterpret_cast<uint8_t*>(b + L.k8);
+  o.vt = reinterpret_cast<uint8_t*>(b + L.vt);
+  o.sq = reinterpret_cast<float*>(b + L.sq);
+  o.sk = reinterpret_cast<float*>(b + L.sk);
+  o.sv = reinterpret_cast<float*>(b + L.sv);
+  o.amax = reinterpret_cast<uint32_t*>(b + L.amax);
+  o.ld8 = L.ld8;
+  o.ld_vt = L.ld_vt;
+  return o;
+}
+}  // namespace
+
+extern "C" size_t dit_attn_fp8_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads,
+                                               int32_t head_dim) {
+  if (n_tokens < 0 || n_seqs < 1 || n_heads < 1 || head_dim != 128) return 0;
+  return fp8_attn_layout(n_tokens, n_seqs, n_heads).total;
+}
+
+extern "C" dit_status dit_attn_fp8_layout(int64_t n_tokens, int32_t n_seqs, int32_t n_heads,
+                                          int32_t head_dim, int64_t* out) {
+  clear_error();
+  if (!out) return fail(DIT_EINVAL, "dit_attn_fp8_layout: null out");
+  if (n_tokens < 0 || n_seqs < 1 || n_heads < 1)
+    return fail(DIT_EINVAL, "dit_attn_fp8_layout: bad sizes");
+  if (head_dim != 128) return fail(DIT_EUNSUPPORTED, "dit_attn_fp8_layout: head_dim must be 128");
+  const Fp8AttnLayout L = fp8_attn_layout(n_tokens, n_seqs, n_heads);
+  const int64_t v[9] = {(int64_t)L.q8, (int64_t)L.k8, (int64_t)L.vt, (int64_t)L.sq, (int64_t)L.sk,
+                        (int64_t)L.sv, (int64_t)L.amax, L.ld8, L.ld_vt};
+  for (int i = 0; i < 9; ++i) out[i] = v[i];
+  return DIT_OK;
+}
+
+static dit_status fp8_attn_check(const char* who, const int32_t* cu, int32_t n_seqs,
+                                 int32_t max_seqlen, int64_t n_tokens, int32_t n_heads,
+                                 int32_t head_dim, const void* workspace,
+                                 size_t workspace_bytes) {
+  if (!cu) return fail(DIT_EINVAL, "%s: null cu_seqlens", who);
+  if (n_seqs < 1) return fail(DIT_EINVAL, "%s: n_seqs < 1", who);
+  if (n_heads < 1) return fail(DIT_EINVAL, "%s: n_heads < 1", who);
+  if (head_dim != 128) return fail(DIT_EUNSUPPORTED, "%s: head_dim must be 128", who);
+  if (dit_status st = check_stream_rows(n_tokens)) return st;
+  if (n_tokens > 0 && max_seqlen < 1) return fail(DIT_EINVAL, "%s: max_seqlen < 1", who);
+  if (max_seqlen > n_tokens && n_tokens > 0)
+    return fail(DIT_EINVAL, "%s: max_seqlen %d > n_tokens", who, max_seqlen);
+  if (n_seqs > 65535 || n_heads > 65535)
+    return fail(DIT_EUNSUPPORTED, "%s: more than 65535 segments or heads", who);
+  if ((double)n_tokens * (double)n_heads * 16.0 > 2147483647.0)
+    return fail(DIT_EUNSUPPORTED, "%s: n_tokens * n_heads too large", who);
+  if ((double)max_seqlen * (double)n_heads * 128.0 >= 2147483648.0)
+    return fail(DIT_EUNSUPPORTED, "%s: a segment's K codes span 2 GiB or more", who);
+  const size_t need = fp8_attn_layout(n_tokens, n_seqs, n_heads).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(DIT_EUNSUPPORTED, "%s: workspace must be 16-byte aligned", who);
+  return DIT_OK;
+}
+
+extern "C" dit_status attn_fp8_prepare(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                                       const void* v, int64_t ld_v, const int32_t* cu_seqlens,
+                                       int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
+                                       int32_t n_heads, int32_t head_dim, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "attn_fp8_prepare";
+  if (!q || !k || !v) return fail(DIT_EINVAL, "%s: null pointer", who);
+  if (dit_status st = fp8_attn_check(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, n_heads,
+                                     head_dim, workspace, workspace_bytes))
+    return st;
+  const int64_t width = (int64_t)n_heads * head_dim;
+  if (ld_q < width || ld_k < width || ld_v < width) return fail(DIT_EINVAL, "%s: ld too small", who);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !ld_aligned(DIT_BF16, ld_q) ||
+      !ld_aligned(DIT_BF16, ld_k) || !ld_aligned(DIT_BF16, ld_v))
+    return fail(DIT_EUNSUPPORTED, "%s: pointers/ld must be 16-byte aligned", who);
+  if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_segments(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, stream))
+      return st;
+  }
+  const Fp8AttnLayout L = fp8_attn_layout(n_tokens, n_seqs, n_heads);
+  hipError_t e = launch_attn_fp8_prepare(
+      static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
+      static_cast<const uint16_t*>(v), ld_v, cu_seqlens, n_seqs, max_seqlen, n_tokens, n_heads,
+      fp8_attn_ops(workspace, L), (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_fp8_prepare launch");
+}
+
+extern "C" dit_status attn_packed_fp8(const void* workspace, size_t workspace_bytes, void* o,
+                                      int64_t ld_o, const int32_t* cu_seqlens, int32_t n_seqs,
+                                      int32_t max_seqlen, int64_t n_tokens, int32_t n_heads,
+                                      int32_t head_dim, float softmax_scale, int32_t causal,
+                                      void* stream) {
+  clear_error();
+  const char* who = "attn_packed_fp8";
+  if (!o) return fail(DIT_EINVAL, "%s: null o", who);
+  if (dit_status st = fp8_attn_check(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, n_heads,
+                                     head_dim, workspace, workspace_bytes))
+    return st;
+  if (!(softmax_scale >= 0.0f)) return fail(DIT_EINVAL, "%s: softmax_scale < 0", who);
+  if (ld_o < (int64_t)n_heads * head_dim) return fail(DIT_EINVAL, "%s: ld_o too small", who);
+  if (!aligned16(o) || !ld_aligned(DIT_BF16, ld_o))
+    return fail(DIT_EUNSUPPORTED, "%s: o/ld_o must be 16-byte aligned", who);
+  if (n_tokens == 0) return DIT_OK;
+  if (validate_on()) {
+    if (dit_status st = validate_segments(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, stream))
+      return st;
+  }
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  const Fp8AttnLayout L = fp8_attn_layout(n_tokens, n_seqs, n_heads);
+  AttnFp8Ops ops = fp8_attn_ops(const_cast<void*>(workspace), L);
+  hipError_t e = launch_attn_fp8(ops, static_cast<uint16_t*>(o), ld_o, cu_seqlens, n_seqs,
+                                 max_seqlen, n_tokens, n_heads, scale, causal != 0,
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_packed_fp8 launch");
+}
+
+// ---------------------------------------------------------------------------
 
 // C [n_tokens][width_out] = A [n_tokens][k_in] W^T: inner width k_in (a
 // multiple of the 64-deep k-step), output width a multiple of 4 (the

@@ -122,6 +122,33 @@ hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int
                        int n_heads, int head_dim, float scale, int causal, float* lse,
                        hipStream_t s);
 
+// FP8 attention operands (head_dim 128): e4m3 codes of q and k [token][head][128]
+// (ld8 bytes per token), q's per-row scales sq [head][token], the per-head
+// scales sk, sv, and v's codes transposed to vt [head][d][column] (ld_vt bytes
+// per d row; segment s starts at column roundup64(cu[s]) + 128 s).  amax:
+// [2][head] scratch.
+struct AttnFp8Ops {
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* vt;
+  float* sq;
+  float* sk;
+  float* sv;
+  uint32_t* amax;
+  int64_t ld8;
+  int64_t ld_vt;
+};
+// q, k, v bf16 [token][head][128] (row strides in elements) -> ops.
+hipError_t launch_attn_fp8_prepare(const uint16_t* q, int64_t ld_q, const uint16_t* k,
+                                   int64_t ld_k, const uint16_t* v, int64_t ld_v,
+                                   const int32_t* cu, int n_seqs, int max_seqlen,
+                                   int64_t n_tokens, int n_heads, const AttnFp8Ops& ops,
+                                   hipStream_t s);
+// o bf16 [token][head][128] from prepared operands.
+hipError_t launch_attn_fp8(const AttnFp8Ops& ops, uint16_t* o, int64_t ld_o, const int32_t* cu,
+                           int n_seqs, int max_seqlen, int64_t n_tokens, int n_heads, float scale,
+                           int causal, hipStream_t s);
+
 // Attention backward (bf16, head_dim 128): delta[h][row] = sum_d do * o, then
 // dk, dv (one pass over the queries per key block) and dq (one pass over the
 // keys per query block), recomputing P = exp(s scale - lse).  delta: float

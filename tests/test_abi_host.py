@@ -322,3 +322,42 @@ def test_fp8_block_halves_validate_before_enqueue():
     narrow = jav.ffn_desc(B, 5120, 20480 - 64)
     assert jav._lib.dit_ffn_forward_fp8(ctypes.byref(narrow), *fargs, fake, 1 << 40, None) == jav.DIT_EUNSUPPORTED
     assert jav.ffn_fp8_workspace_bytes(jav.ffn_desc(F32, 256, 1024), 10) == 0
+
+
+def test_fp8_attention_layout_and_validation():
+    """Workspace layout arithmetic of the FP8 attention operands and the
+    argument checks of attn_fp8_prepare / attn_packed_fp8 (nothing enqueued)."""
+    n, s, h = 58758, 1, 40
+    lay = jav.attn_fp8_layout(n, s, h)
+    r = lambda b: (b + 255) // 256 * 256
+    ld_vt = (n + 63) // 64 * 64 + 128 * s
+    assert lay["ld8"] == h * 128 and lay["ld_vt"] == ld_vt
+    sizes = [n * h * 128, n * h * 128, h * 128 * ld_vt, h * n * 4, h * 4, h * 4, 2 * h * 4]
+    offs = [0]
+    for b in sizes:
+        offs.append(offs[-1] + r(b))
+    assert [lay[k] for k in ("q8", "k8", "vt", "sq", "sk", "sv", "amax")] == offs[:-1]
+    assert jav.attn_fp8_workspace_bytes(n, s, h) == offs[-1]
+    assert jav.attn_fp8_workspace_bytes(n, s, h, 64) == 0
+    assert jav.attn_fp8_workspace_bytes(n, 0, h) == 0
+    with pytest.raises(jav.DitError):
+        jav.attn_fp8_layout(n, s, h, 64)
+    fake = 1 << 20
+    need = jav.attn_fp8_workspace_bytes(100, 1, 40)
+    # attn_fp8_prepare(q, ld_q, k, ld_k, v, ld_v, cu, n_seqs, max_seqlen, n, H, dh, ws, bytes, stream)
+    Q = [fake, 5120, fake, 5120, fake, 5120]
+    assert _call("attn_fp8_prepare", None, 5120, fake, 5120, fake, 5120, fake, 1, 100, 100, 40, 128, fake, need, None) == jav.DIT_EINVAL
+    assert _call("attn_fp8_prepare", *Q, fake, 1, 100, 100, 40, 64, fake, need, None) == jav.DIT_EUNSUPPORTED
+    assert _call("attn_fp8_prepare", *Q, fake, 1, 100, 100, 40, 128, fake, need - 1, None) == jav.DIT_EWORKSPACE
+    assert _call("attn_fp8_prepare", fake, 5000, fake, 5120, fake, 5120, fake, 1, 100, 100, 40, 128, fake, need, None) == jav.DIT_EINVAL
+    assert _call("attn_fp8_prepare", fake + 8, 5120, fake, 5120, fake, 5120, fake, 1, 100, 100, 40, 128, fake, need, None) == jav.DIT_EUNSUPPORTED
+    assert _call("attn_fp8_prepare", *Q, fake, 1, 101, 100, 40, 128, fake, need, None) == jav.DIT_EINVAL   # max_seqlen > n
+    assert _call("attn_fp8_prepare", *Q, fake, 0, 100, 100, 40, 128, fake, need, None) == jav.DIT_EINVAL   # n_seqs
+    assert "attn_fp8_prepare" in jav.last_error()
+    # attn_packed_fp8(ws, bytes, o, ld_o, cu, n_seqs, max_seqlen, n, H, dh, scale, causal, stream)
+    assert _call("attn_packed_fp8", fake, need, None, 5120, fake, 1, 100, 100, 40, 128, 0.0, 0, None) == jav.DIT_EINVAL
+    assert _call("attn_packed_fp8", fake, need, fake, 5120, fake, 1, 100, 100, 40, 128, -1.0, 0, None) == jav.DIT_EINVAL
+    assert _call("attn_packed_fp8", fake, need, fake, 4096, fake, 1, 100, 100, 40, 128, 0.0, 0, None) == jav.DIT_EINVAL
+    assert _call("attn_packed_fp8", fake, 10, fake, 5120, fake, 1, 100, 100, 40, 128, 0.0, 0, None) == jav.DIT_EWORKSPACE
+    assert _call("attn_packed_fp8", fake, need, fake + 2, 5120, fake, 1, 100, 100, 40, 128, 0.0, 0, None) == jav.DIT_EUNSUPPORTED
+    assert _call("attn_packed_fp8", fake, need, fake, 5120, fake, 1, 0, 0, 40, 128, 0.0, 0, None) == jav.DIT_OK
