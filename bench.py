@@ -16,8 +16,10 @@ batch large enough to stream from HBM; ``nft_loss`` does the same for the
 DiffusionNFT loss and its gradient (one sample per request); ``fp8`` times the
 block's four projections in FP8 (e4m3 codes, per-row scales) against the
 e4m3 MFMA peak, the row quantization and the FP8-output AdaLN against HBM,
-and the two halves of the block with FP8 projections (``block_fp8``,
-``ffn_fp8``, ms per call).  ``backward`` times the attention backward, the
+the two halves of the block with FP8 projections (``block_fp8``,
+``ffn_fp8``, ms per call), the FP8 attention (operand preparation and the
+attention, against the e4m3 peak) and the attention half with the attention
+in FP8 too (``block_fp8_attn``).  ``backward`` times the attention backward, the
 whole backward pass of the attention half and that of the feed-forward half
 (each recomputes its forward).
 ``cpu_baseline`` times the float64 oracle on a bounded row sample of the same
@@ -510,7 +512,11 @@ def main() -> int:
         h8 = torch.empty((n, F), dtype=torch.bfloat16, device=dev)
         out8 = torch.empty_like(x)
         table8 = torch.from_numpy(fi.table).to(dev)
-        ws_b8 = torch.empty(jav.block_fp8_workspace_bytes(desc, n), dtype=torch.uint8, device=dev)
+        ws_b8 = torch.empty(jav.block_fp8_attn_workspace_bytes(desc, n, cu.numel() - 1),
+                            dtype=torch.uint8, device=dev)
+        ws_a8 = torch.empty(jav.attn_fp8_workspace_bytes(n, cu.numel() - 1, H), dtype=torch.uint8,
+                            device=dev)
+        o8 = torch.empty_like(x)
         fdesc8 = jav.ffn_desc(jav.DIT_BF16, d, F, wl.eps)
         ws_f8 = torch.empty(jav.ffn_fp8_workspace_bytes(fdesc8, n), dtype=torch.uint8,
                             device=dev)
@@ -533,6 +539,16 @@ def main() -> int:
             "ffn_down": (5, lambda: jav.linear_fp8(hq, hs, w2q, w2s, epilogue="gated", x=x,
                                                    modality=mod, table=table, out=out8,
                                                    stream=stream)),
+            # FP8 attention on the QKV product above (q, k, v: strided column blocks)
+            "attn_fp8_prepare": (5, lambda: jav.attn_fp8_prepare(
+                qkv8[:, :d], qkv8[:, d:2 * d], qkv8[:, 2 * d:], cu, ms_len, H, Dh,
+                workspace=ws_a8, stream=stream)),
+            "attn_fp8": (3, lambda: jav.attn_packed_fp8(ws_a8, cu, ms_len, n, H, Dh,
+                                                        causal=args.causal, out=o8,
+                                                        stream=stream)),
+            "block_fp8_attn": (3, lambda: jav.block_forward_fp8(
+                desc, x, mod, pos, cu, ms_len, table, wq, wqs, wo, wos, out=out8,
+                workspace=ws_b8, stream=stream, fp8_attention=True)),
         }
         t8 = {}
         for name, (reps, fn) in ops8.items():
@@ -553,6 +569,10 @@ def main() -> int:
             tf = f / (t8[k] * 1e-3) / 1e12
             fp8_rec[f"{k}_tflops"] = round(tf, 1)
             fp8_rec[f"{k}_frac_of_fp8_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
+        af8 = block_flops(n, d, lay["cu_seqlens"].tolist(), args.causal)[0]
+        fp8_rec["attn_fp8_tflops"] = round(af8 / (t8["attn_fp8"] * 1e-3) / 1e12, 1)
+        fp8_rec["attn_fp8_frac_of_fp8_peak"] = round(af8 / (t8["attn_fp8"] * 1e-3) / 1e12
+                                                     / PEAK_FP8_TFLOPS, 4)
         qb = n * (d * 2 + d + 4)
         fp8_rec["quant_x_gbs"] = round(qb / (t8["quant_x"] * 1e-3) / 1e9, 1)
         fp8_rec["quant_x_frac_of_hbm"] = round(qb / (t8["quant_x"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
@@ -560,7 +580,7 @@ def main() -> int:
         fp8_rec["adaln_fp8_gbs"] = round(qb / (t8["adaln_fp8"] * 1e-3) / 1e9, 1)
         fp8_rec["adaln_fp8_frac_of_hbm"] = round(qb / (t8["adaln_fp8"] * 1e-3) / 1e9
                                                  / PEAK_HBM_GBS, 4)
-        del wq, wo, w1q, w2q, xq, hq, qkv8, h8, out8, ws_b8, ws_f8, table8
+        del wq, wo, w1q, w2q, xq, hq, qkv8, h8, out8, ws_b8, ws_f8, table8, ws_a8, o8
         print(f"# fp8: {fp8_rec}", file=sys.stderr, flush=True)
 
     # The backward pass of the attention half: the attention backward on its own

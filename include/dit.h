@@ -653,6 +653,27 @@ dit_status dit_block_forward_fp8(const dit_block_desc* d, const void* x, void* o
                                  const uint8_t* w_o, const float* w_o_scales, const void* b_o,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of scratch dit_block_forward_fp8_attn needs: that of
+ * dit_block_forward_fp8, then the FP8 attention operands
+ * (dit_attn_fp8_workspace_bytes for n_tokens, n_seqs and the descriptor's
+ * heads).  0 for a bad descriptor, n_seqs < 1 or head_dim != 128. */
+size_t dit_block_fp8_attn_workspace_bytes(const dit_block_desc* d, int64_t n_tokens,
+                                          int32_t n_seqs);
+
+/* dit_block_forward_fp8 with the attention in FP8 as well: its attention
+ * stage is attn_fp8_prepare + attn_packed_fp8 (operands in the workspace past
+ * the block's own planes) instead of attn_packed.  Arguments as
+ * dit_block_forward_fp8; errors those of its stages, plus DIT_EWORKSPACE. */
+dit_status dit_block_forward_fp8_attn(const dit_block_desc* d, const void* x, void* out,
+                                      const uint8_t* modality, const int32_t* pos_thw,
+                                      const int32_t* cu_seqlens, int32_t n_seqs,
+                                      int32_t max_seqlen, int64_t n_tokens,
+                                      const float* ada_table, const uint8_t* w_qkv,
+                                      const float* w_qkv_scales, const void* b_qkv,
+                                      const uint8_t* w_o, const float* w_o_scales,
+                                      const void* b_o, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* Bytes of scratch dit_ffn_forward_fp8 needs: codes [N][max(d_ff, d_model)]
  * bytes, h bf16 [N][d_ff] and N float32 row scales, each region rounded up to
  * 256 bytes.  0 for a bad descriptor (also for a dtype other than DIT_BF16). */

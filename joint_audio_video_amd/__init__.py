@@ -39,6 +39,7 @@ EXPORTED = (
     "dit_block_backward_workspace_bytes", "dit_block_backward",
     "dit_ffn_backward_workspace_bytes", "dit_ffn_backward",
     "dit_attn_fp8_workspace_bytes", "dit_attn_fp8_layout", "attn_fp8_prepare", "attn_packed_fp8",
+    "dit_block_fp8_attn_workspace_bytes", "dit_block_forward_fp8_attn",
 )
 
 
@@ -116,6 +117,10 @@ def _load() -> ctypes.CDLL:
         "dit_block_fp8_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
         "dit_block_forward_fp8": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32,
                                                  I32, I64, P, P, P, P, P, P, P, P, SZ, P]),
+        "dit_block_fp8_attn_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64, I32]),
+        "dit_block_forward_fp8_attn": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P,
+                                                      I32, I32, I64, P, P, P, P, P, P, P, P, SZ,
+                                                      P]),
         "dit_ffn_fp8_workspace_bytes": (SZ, [ctypes.POINTER(FfnDesc), I64]),
         "dit_ffn_forward_fp8": (ctypes.c_int, [ctypes.POINTER(FfnDesc), P, P, P, I64, P, P, P, P,
                                                P, P, P, P, SZ, P]),
@@ -649,18 +654,30 @@ def block_fp8_workspace_bytes(desc: BlockDesc, n_tokens: int) -> int:
     return int(_lib.dit_block_fp8_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
 
 
+def block_fp8_attn_workspace_bytes(desc: BlockDesc, n_tokens: int, n_seqs: int) -> int:
+    return int(_lib.dit_block_fp8_attn_workspace_bytes(ctypes.byref(desc), int(n_tokens),
+                                                        int(n_seqs)))
+
+
 def block_forward_fp8(desc: BlockDesc, x, modality, pos, cu_seqlens, max_seqlen: int, table,
                       w_qkv_codes, w_qkv_scales, w_o_codes, w_o_scales, b_qkv=None, b_o=None,
-                      out=None, workspace=None, n_tokens=None, stream=None):
-    """The attention half with FP8 projections (libdit dit_block_forward_fp8)."""
+                      out=None, workspace=None, n_tokens=None, stream=None,
+                      fp8_attention: bool = False):
+    """The attention half with FP8 projections (libdit dit_block_forward_fp8),
+    or with the attention in FP8 too (dit_block_forward_fp8_attn)."""
     torch = _torch()
     n = x.shape[0] if n_tokens is None else int(n_tokens)
     if out is None:
         out = torch.empty_like(x)
-    need = block_fp8_workspace_bytes(desc, n)
+    if fp8_attention:
+        need = block_fp8_attn_workspace_bytes(desc, n, cu_seqlens.numel() - 1)
+        fn = _lib.dit_block_forward_fp8_attn
+    else:
+        need = block_fp8_workspace_bytes(desc, n)
+        fn = _lib.dit_block_forward_fp8
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    _check(_lib.dit_block_forward_fp8(
+    _check(fn(
         ctypes.byref(desc), x.data_ptr(), out.data_ptr(), modality.data_ptr(), pos.data_ptr(),
         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), n, table.data_ptr(),
         w_qkv_codes.data_ptr(), w_qkv_scales.data_ptr(), _ptr(b_qkv), w_o_codes.data_ptr(),

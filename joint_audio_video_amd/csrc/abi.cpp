@@ -1092,14 +1092,23 @@ extern "C" size_t dit_block_fp8_workspace_bytes(const dit_block_desc* d, int64_t
   return 5 * round256(n * D * 2) + round256(n * 4);
 }
 
-extern "C" dit_status dit_block_forward_fp8(
-    const dit_block_desc* d, const void* x, void* out, const uint8_t* modality,
-    const int32_t* pos_thw, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
-    int64_t n_tokens, const float* ada_table, const uint8_t* w_qkv, const float* w_qkv_scales,
-    const void* b_qkv, const uint8_t* w_o, const float* w_o_scales, const void* b_o,
-    void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" size_t dit_block_fp8_attn_workspace_bytes(const dit_block_desc* d, int64_t n_tokens,
+                                                     int32_t n_seqs) {
+  const size_t base = dit_block_fp8_workspace_bytes(d, n_tokens);
+  if (base == 0 || d->n_heads < 1) return 0;
+  const size_t att = dit_attn_fp8_workspace_bytes(n_tokens, n_seqs, d->n_heads, d->head_dim);
+  return att == 0 ? 0 : base + att;
+}
+
+// The FP8 block; with fp8_attn the attention stage is attn_fp8_prepare +
+// attn_packed_fp8 on operands in the workspace past the block's own planes.
+static dit_status block_forward_fp8_impl(
+    const char* who, bool fp8_attn, const dit_block_desc* d, const void* x, void* out,
+    const uint8_t* modality, const int32_t* pos_thw, const int32_t* cu_seqlens, int32_t n_seqs,
+    int32_t max_seqlen, int64_t n_tokens, const float* ada_table, const uint8_t* w_qkv,
+    const float* w_qkv_scales, const void* b_qkv, const uint8_t* w_o, const float* w_o_scales,
+    const void* b_o, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  const char* who = "dit_block_forward_fp8";
   if (!d) return fail(DIT_EINVAL, "%s: null descriptor", who);
   if (d->dtype != DIT_BF16)
     return fail(DIT_EUNSUPPORTED, "%s: bf16 activations only (dtype %d)", who, (int)d->dtype);
@@ -1109,11 +1118,17 @@ extern "C" dit_status dit_block_forward_fp8(
   if (!x || !out || !modality || !pos_thw || !cu_seqlens || !ada_table)
     return fail(DIT_EINVAL, "%s: null pointer", who);
   if (dit_status st = check_stream_rows(n_tokens)) return st;
-  const size_t need = dit_block_fp8_workspace_bytes(d, n_tokens);
+  const size_t base_need = dit_block_fp8_workspace_bytes(d, n_tokens);
+  const size_t need = fp8_attn ? dit_block_fp8_attn_workspace_bytes(d, n_tokens, n_seqs) : base_need;
+  if (fp8_attn && need == 0)
+    return fail(n_seqs < 1 ? DIT_EINVAL : DIT_EUNSUPPORTED, "%s: n_seqs %d / head_dim %d", who,
+                n_seqs, Dh);
   if (!workspace || workspace_bytes < need)
     return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(DIT_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", who);
+  void* attn_ws = static_cast<char*>(workspace) + base_need;
+  const size_t attn_ws_bytes = workspace_bytes - base_need;
 
   const size_t n = (size_t)n_tokens;
   const size_t plane_bytes = round256(n * D * 2);
@@ -1140,16 +1155,19 @@ extern "C" dit_status dit_block_forward_fp8(
   if (dit_status st = attn_check(DIT_BF16, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs,
                                  max_seqlen, n_tokens, H, Dh, d->softmax_scale))
     return st;
+  if (fp8_attn) {
+    if (dit_status st = fp8_attn_check(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
+                                       attn_ws, attn_ws_bytes))
+      return st;
+  }
   if (dit_status st = fp8_weight_check(who, w_o, w_o_scales, b_o, D, D)) return st;
   if (!aligned16(out)) return fail(DIT_EUNSUPPORTED, "%s: out must be 16-byte aligned", who);
   if (n_tokens == 0) return DIT_OK;
 
   if (validate_on()) {
-    if (dit_status st = validate_segments("dit_block_forward_fp8", cu_seqlens, n_seqs, max_seqlen,
-                                          n_tokens, stream))
+    if (dit_status st = validate_segments(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, stream))
       return st;
-    if (dit_status st = validate_modality("dit_block_forward_fp8", modality, n_tokens, stream))
-      return st;
+    if (dit_status st = validate_modality(who, modality, n_tokens, stream)) return st;
   }
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
@@ -1172,8 +1190,19 @@ extern "C" dit_status dit_block_forward_fp8(
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: rope launch");
   mark(3);
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
-  e = launch_attn(1, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
-                  scale, d->causal != 0, nullptr, s);
+  if (fp8_attn) {
+    const AttnFp8Ops ops = fp8_attn_ops(attn_ws, fp8_attn_layout(n_tokens, n_seqs, H));
+    e = launch_attn_fp8_prepare(static_cast<const uint16_t*>(qr), D,
+                                static_cast<const uint16_t*>(kr), D,
+                                static_cast<const uint16_t*>(static_cast<void*>(v)), D,
+                                cu_seqlens, n_seqs, max_seqlen, n_tokens, H, ops, s);
+    if (e == hipSuccess)
+      e = launch_attn_fp8(ops, reinterpret_cast<uint16_t*>(o), D, cu_seqlens, n_seqs, max_seqlen,
+                          n_tokens, H, scale, d->causal != 0, s);
+  } else {
+    e = launch_attn(1, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen, n_tokens, H, Dh,
+                    scale, d->causal != 0, nullptr, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: attention launch");
   mark(4);
   e = launch_quant_rows_fp8(1, o, D, codes, D, scales, n_tokens, D, s);
@@ -1183,6 +1212,30 @@ extern "C" dit_status dit_block_forward_fp8(
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward_fp8: out-proj launch");
   mark(5);
   return DIT_OK;
+}
+
+extern "C" dit_status dit_block_forward_fp8(
+    const dit_block_desc* d, const void* x, void* out, const uint8_t* modality,
+    const int32_t* pos_thw, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+    int64_t n_tokens, const float* ada_table, const uint8_t* w_qkv, const float* w_qkv_scales,
+    const void* b_qkv, const uint8_t* w_o, const float* w_o_scales, const void* b_o,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return block_forward_fp8_impl("dit_block_forward_fp8", false, d, x, out, modality, pos_thw,
+                                cu_seqlens, n_seqs, max_seqlen, n_tokens, ada_table, w_qkv,
+                                w_qkv_scales, b_qkv, w_o, w_o_scales, b_o, workspace,
+                                workspace_bytes, stream);
+}
+
+extern "C" dit_status dit_block_forward_fp8_attn(
+    const dit_block_desc* d, const void* x, void* out, const uint8_t* modality,
+    const int32_t* pos_thw, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+    int64_t n_tokens, const float* ada_table, const uint8_t* w_qkv, const float* w_qkv_scales,
+    const void* b_qkv, const uint8_t* w_o, const float* w_o_scales, const void* b_o,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return block_forward_fp8_impl("dit_block_forward_fp8_attn", true, d, x, out, modality, pos_thw,
+                                cu_seqlens, n_seqs, max_seqlen, n_tokens, ada_table, w_qkv,
+                                w_qkv_scales, b_qkv, w_o, w_o_scales, b_o, workspace,
+                                workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -154,12 +154,14 @@ def block_forward_fp8(x, modality, pos, cu_seqlens, table, wq_codes, wq_scales, 
                       wo_scales, *, n_heads: int, head_dim: int, sections: Sequence[int],
                       theta: float = 10000.0, eps: float = 1e-6, causal: bool = False,
                       scale: Optional[float] = None, b_qkv=None, b_o=None,
-                      rows=None) -> Dict[str, np.ndarray]:
+                      rows=None, fp8_attention: bool = False) -> Dict[str, np.ndarray]:
     """The attention half of the block (oracle.block.block_forward) with both
     projections in FP8: the AdaLN output and the attention output are
     quantized per row, W_qkv [3D][D] and W_o [D][D] are given as per-row codes
-    and scales.  Returns y_codes, y_scales, q, k, v, o, o_codes, o_scales and
-    out (float64); with ``rows``, o, its codes and out hold those rows only.
+    and scales.  With ``fp8_attention`` the attention is attention_fp8 of the
+    rotated q, k and v.  Returns y_codes, y_scales, q, k, v, o, o_codes,
+    o_scales and out (float64); with ``rows``, o, its codes and out hold those
+    rows only.
     """
     x = np.asarray(x)
     n, d = x.shape
@@ -175,7 +177,10 @@ def block_forward_fp8(x, modality, pos, cu_seqlens, table, wq_codes, wq_scales, 
     q[idx] = qkv_project(y[idx], w[:d], bias[0])
     q_rot = np.zeros((n, d))
     q_rot[idx] = rope3d(q[idx], np.asarray(pos)[idx], n_heads, head_dim, sections, theta)
-    o = attention(q_rot, k_rot, v, cu_seqlens, n_heads, head_dim, causal, scale, rows)
+    if fp8_attention:
+        o = attention_fp8(q_rot, k_rot, v, cu_seqlens, n_heads, head_dim, causal, scale, rows)["o"]
+    else:
+        o = attention(q_rot, k_rot, v, cu_seqlens, n_heads, head_dim, causal, scale, rows)
     oc, os_ = quantize_rows(o)
     out = out_proj_gated(dequantize_rows(oc, os_), dequantize_rows(wo_codes, wo_scales), x,
                          modality, table, b_o, rows)
