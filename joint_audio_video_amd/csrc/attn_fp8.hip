@@ -23,7 +23,9 @@
 //     gaps between segments never overlap), its last tile zero-padded.
 //
 // attn_fp8_kernel: the bf16 kernel's organisation with FP8 operands.  A
-// workgroup owns 256 queries of one (segment, head), 8 waves of 32; Q codes
+// workgroup owns 384 queries of one (segment, head), 12 waves of 32 (three
+// per SIMD: the FP8 products leave the matrix pipe idle more often, so more
+// waves hide the latency; 168 registers each); Q codes
 // stay in registers, K tiles [64 keys][128 B] and V^T tiles [128 d][64 B]
 // are double-buffered in LDS (32 KB), filled by buffer loads that write
 // straight into LDS.  Per 64-key tile a wave issues 8
@@ -31,8 +33,9 @@
 // 64-deep d steps; O^T += V^T P^T: four d blocks x one 64-key step).  The
 // probabilities leave the S^T accumulators as four e4m3 words per key block
 // per lane; one v_permlane32_swap per word pair hands each lane half the 32
-// consecutive keys the B operand of the second product expects.  The two
-// waves of a SIMD run half a phase apart (ping-pong), as in the bf16 kernel.
+// consecutive keys the B operand of the second product expects.  Waves 4-7
+// (the middle wave of each SIMD) run half a phase behind the others
+// (ping-pong), as in the bf16 kernel.
 #include <cmath>
 
 #include "common.h"
@@ -42,7 +45,13 @@ namespace {
 
 constexpr int DH = 128;
 constexpr int KB = 64;                    // keys per tile
-constexpr int kWaves = 8;
+// Waves per workgroup: 12 (three per SIMD; measured 2-9% faster than 8, two
+// per SIMD, across one segment, four segments and causal).
+#ifndef DIT_ATTN_FP8_WAVES
+#define DIT_ATTN_FP8_WAVES 12
+#endif
+constexpr int kWaves = DIT_ATTN_FP8_WAVES;
+static_assert(kWaves == 8 || kWaves == 12, "8 or 12 waves per workgroup");
 constexpr int kThreads = 64 * kWaves;
 constexpr int QBLK = 32 * kWaves;         // queries per workgroup
 // A tile may exceed the running maximum by this much (log2 units) before the
@@ -196,7 +205,7 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restric
 
 // ---- attention ----
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(
+__global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, int64_t ld_q8, const float* __restrict__ sq, int64_t ld_sq,
     const uint8_t* __restrict__ k8, int64_t ld_k8, const float* __restrict__ sk,
     const uint8_t* __restrict__ vt, int64_t ld_vt, const float* __restrict__ sv,
@@ -241,9 +250,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(
   const int kend = causal ? min(seg1, q0 + QBLK) : seg1;
   const int nkt = (kend - seg0 + KB - 1) / KB;
 
-  // Global -> LDS, 16 bytes per lane: slot tid of a K tile is key row tid/8,
-  // physical chunk tid%8 holding logical chunk (tid%8) ^ ((row >> 1) & 7); of
-  // a V^T tile d row tid/4, physical chunk tid%4 holding (tid%4) ^ ((d >> 2) & 3).
+  // Global -> LDS, 16 bytes per lane, 1 KB (64 slots) per wave and load: slot
+  // s of a K tile is key row s/8, physical chunk s%8 holding logical chunk
+  // (s%8) ^ ((row >> 1) & 7); of a V^T tile d row s/4, physical chunk s%4
+  // holding (s%4) ^ ((d >> 2) & 3).  With 8 waves wave w loads K and V slots
+  // 64w..64w+63; with 12, waves 0-7 load K and waves 8-11 two kilobytes of V.
   // With 64 four-byte banks a fragment read (16 consecutive rows per cycle)
   // then touches 16 distinct 16-byte slots.  K rows past the segment end lie
   // outside the buffer range and arrive as zeros; V^T columns past it are
@@ -254,16 +265,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(
   const int col0 = vt_col0(seg0, seq);
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc(vt + (int64_t)h * DH * ld_vt + col0, (uint32_t)(DH * ld_vt - col0));
-  const int krow = tid >> 3, vrow = tid >> 2;
-  const uint32_t koff = (uint32_t)krow * (uint32_t)ld_k8 + (uint32_t)(((tid & 7) ^ ((krow >> 1) & 7)) * 16);
-  const uint32_t voff = (uint32_t)vrow * (uint32_t)ld_vt + (uint32_t)(((tid & 3) ^ ((vrow >> 2) & 3)) * 16);
+  constexpr int kVLoads = kWaves == 8 ? 1 : 2;         // V loads per V-loading wave
+  const bool k_loader = wave < 8;
+  const bool v_loader = kWaves == 8 || wave >= 8;
+  const int kslot = 64 * wave + lane;                   // K: waves 0-7
+  const int vbase = kWaves == 8 ? 64 * wave : 128 * (wave - 8);
+  const int krow = kslot >> 3;
+  const uint32_t koff = (uint32_t)krow * (uint32_t)ld_k8 + (uint32_t)(((kslot & 7) ^ ((krow >> 1) & 7)) * 16);
+  uint32_t voff[kVLoads];
+#pragma unroll
+  for (int i = 0; i < kVLoads; ++i) {
+    const int vslot = vbase + 64 * i + lane;
+    const int vrow = vslot >> 2;
+    voff[i] = (uint32_t)vrow * (uint32_t)ld_vt + (uint32_t)(((vslot & 3) ^ ((vrow >> 2) & 3)) * 16);
+  }
   const uint32_t k_tstep = (uint32_t)KB * (uint32_t)ld_k8;
   auto issue_k = [&](uint8_t* dst, int tile) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst + 64 * wave * 16, 16, koff,
-                                             (int)(tile * k_tstep), 0, 0);
+    if (k_loader)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst + 64 * wave * 16, 16, koff,
+                                               (int)(tile * k_tstep), 0, 0);
   };
   auto issue_v = [&](uint8_t* dst, int tile) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst + 64 * wave * 16, 16, voff, tile * KB, 0, 0);
+    if (v_loader) {
+#pragma unroll
+      for (int i = 0; i < kVLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst + (vbase + 64 * i) * 16, 16, voff[i],
+                                                 tile * KB, 0, 0);
+    }
   };
 
   // Fragment byte offsets.  K (A of S^T): lane (key 32 b + l32, half g) reads
@@ -301,19 +329,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(
 
   // S^T[key][query] of one tile: element e of block b is key
   // 32 b + 8 (e / 4) + 4 g + e % 4 of the tile, column query l32.
+  // With three waves per SIMD the fragments of one d step (both key blocks)
+  // are in flight at a time; the second step's reads follow the first step's
+  // MFMAs.
   auto compute_s = [&](const uint8_t* ks_t) __attribute__((always_inline)) {
-    v8i32 kf[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) kf[b][ks] = kfrag(ks_t, b, ks);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    if constexpr (kWaves == 8) {
+      v8i32 kf[2][2];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        sacc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            kf[b][ks], qf[ks], ks == 0 ? zero16 : sacc[b], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kf[b][ks] = kfrag(ks_t, b, ks);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          sacc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              kf[b][ks], qf[ks], ks == 0 ? zero16 : sacc[b], 0, 0, 0, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v8i32 kf[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) kf[b] = kfrag(ks_t, b, ks);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          sacc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              kf[b], qf[ks], ks == 0 ? zero16 : sacc[b], 0, 0, 0, 0, 0, 0);
+      }
+    }
   };
 
   // Online softmax of tile j into the e4m3 operand pf (keys 32 g .. +31 of
@@ -376,14 +421,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(
 
   // O^T[d][query] += V^T P^T: one 64-key step per d block.
   auto pv = [&](const uint8_t* vs_t) __attribute__((always_inline)) {
-    v8i32 vf[DH / 32];
+    constexpr int kAhead = kWaves == 8 ? DH / 32 : 2;     // fragments in flight
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db) vf[db] = vfrag(vs_t, db);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int d0 = 0; d0 < DH / 32; d0 += kAhead) {
+      v8i32 vf[kAhead];
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pf, oacc[db], 0, 0, 0, 0,
-                                                                 0, 0);
+      for (int i = 0; i < kAhead; ++i) vf[i] = vfrag(vs_t, d0 + i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i)
+        oacc[d0 + i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[i], pf, oacc[d0 + i], 0,
+                                                                       0, 0, 0, 0, 0);
+    }
   };
 
   // Ping-pong as in the bf16 kernel: phase t runs PV of tile t-1 and S^T of
@@ -391,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(
   // its products, the lagging half that of tile t-1 before them.  Phase t
   // reads K(t) and V(t-1) and loads K(t+1) and V(t); its closing barrier
   // frees both buffers.
-  const bool lagging = wave >= kWaves / 2;
+  const bool lagging = ((wave >> 2) & 1) != 0;   // waves 4-7: the second of their SIMD
   auto phase = [&](const uint8_t* kcur, const uint8_t* vprev, uint8_t* knext, uint8_t* vnext,
                    int t) __attribute__((always_inline)) {
     if (t + 1 < nkt) issue_k(knext, t + 1);
