@@ -25,10 +25,19 @@
 // reads of the next sub-step and the next tile's global loads ride in the
 // groups' shadows (the loads in the first half, so they land before the
 // step's closing barrier).
-// Tile order: workgroups in launch order walk groups of kGroupM M-tiles
-// column by column.  The hardware deals consecutive workgroups to the 8 XCDs
-// round-robin, so each XCD sees one A panel of the group (kept in its L2)
-// against every other B panel.
+// Tile order.  The hardware deals consecutive workgroups to the 8 XCDs (one
+// L2 each) round-robin, and an XCD runs about 32 of them at once (one per CU).
+//   bf16: workgroups in launch order walk groups of 4 M-tiles column by
+//   column, so each XCD sees one A panel of the group (kept in its L2) against
+//   every other B panel: 33 panel k-slices per k-step for 32 workgroups.
+//   FP8: workgroup pid = 8 j + x becomes the j-th tile of XCD x's contiguous
+//   share of a linear order in which 32 consecutive tiles form a block of
+//   4 M-tiles by 8 N-tiles, so the 32 workgroups an XCD runs together read 4 A
+//   and 8 B panels (12 slices); the last T mod 8 workgroups keep their index.
+// Measured on one box: the blocked order cuts the QKV product's L2 fills from
+// 40 to 16 GB and makes the FP8 QKV, out and up products 4-5% faster (the
+// down product 2% slower), but the bf16 products 0-2% slower, so each keeps
+// the order that is faster for it.
 //
 // float32 path: a plain LDS-tiled VALU kernel (the tiny float32 workload only
 // needs to be exact, not fast).
@@ -39,7 +48,7 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kGroupM = 4;
+constexpr int kXcds = 8;
 
 struct EpiArgs {
   int kind;
@@ -55,16 +64,32 @@ struct EpiArgs {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// Tile of this workgroup: groups of kGroupM M-tiles, walked column by column.
+// Tile of this workgroup: a bijection from workgroup ids onto the
+// tiles_m x tiles_n tiles (both orders checked exhaustively on the host for
+// the workloads' shapes and 3,000 random ones).
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int pid = blockIdx.x;
-  const int group_span = kGroupM * tiles_n;
+  const int group_span = 4 * tiles_n;
   const int group = pid / group_span;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int first_m = group * 4;
+  const int gsize = min(tiles_m - first_m, 4);
   const int in_group = pid - group * group_span;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+// The XCD-blocked order: linear index L in groups of 4 M-tiles, each walked in
+// chunks of 8 N-tiles, M fastest inside a chunk.
+__device__ __forceinline__ void tile_coords_xcd(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int pid = blockIdx.x;
+  const int per_xcd = (tiles_m * tiles_n) / kXcds;
+  const int L = pid < kXcds * per_xcd ? (pid % kXcds) * per_xcd + pid / kXcds : pid;
+  const int group = L / (4 * tiles_n);
+  const int idx = L - group * 4 * tiles_n;
+  const int gsize = min(4, tiles_m - 4 * group);
+  const int chunk = idx / (gsize * 8);
+  const int r = idx - chunk * gsize * 8;
+  tm = 4 * group + r % gsize;
+  tn = 8 * chunk + r / gsize;
 }
 
 template <int KIND>
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
