@@ -183,3 +183,32 @@ def test_fp8_attention_full_shape(jav, variant):
     rows = sample_rows(cu, n, extra_every=1499, edge=3, limit=96)
     _run(jav, q, k, v, cu, H, variant == "varlen_causal", rows=rows, heads=(0, 17, 39),
          label=variant)
+
+
+def test_fp8_attention_poisoned_workspace_and_tail(jav):
+    """Operands prepared into a workspace filled with 0xFF bytes (NaN codes,
+    NaN floats) give bit for bit the output of a zero-filled workspace: no
+    byte the preparation does not write (gaps between segments' v columns,
+    padding) is read.  Output rows at and past n_tokens keep their NaN, rows
+    before them are finite."""
+    import torch
+    cu = _cu([5, 70, 1, 130])
+    n, H = cu[-1], 2
+    q = synth.normal_array((n, H * 128), seed=650, dtype="bf16")
+    k = synth.normal_array((n, H * 128), seed=651, dtype="bf16")
+    v = synth.normal_array((n, H * 128), seed=652, dtype="bf16")
+    cu_d = dev_int(np.array(cu, np.int32), torch.int32)
+    need = jav.attn_fp8_workspace_bytes(n, len(cu) - 1, H)
+    outs = []
+    for fill in (0x00, 0xFF):
+        print(f"fp8 attn poison fill=0x{fill:02X} N={n}", flush=True)
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        jav.attn_fp8_prepare(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), cu_d, 130, H,
+                             workspace=ws)
+        o = torch.full((n + 40, H * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        jav.attn_packed_fp8(ws, cu_d, 130, n, H, out=o)
+        _sync()
+        outs.append(o)
+    assert torch.isfinite(outs[1][:n].float()).all()
+    assert torch.isnan(outs[1][n:].float()).all()
+    assert torch.equal(outs[0][:n].view(torch.int16), outs[1][:n].view(torch.int16))
