@@ -212,3 +212,40 @@ def test_fp8_attention_poisoned_workspace_and_tail(jav):
     assert torch.isfinite(outs[1][:n].float()).all()
     assert torch.isnan(outs[1][n:].float()).all()
     assert torch.equal(outs[0][:n].view(torch.int16), outs[1][:n].view(torch.int16))
+
+
+def test_fp8_attention_validate_env_rejects_broken_cu_seqlens(jav):
+    """DIT_VALIDATE=1: attn_fp8_prepare and attn_packed_fp8 return DIT_EINVAL for
+    a broken cu_seqlens before any launch; a valid one passes.  (Memory-safe
+    even unchecked: 512-row inputs and output, a workspace sized for 400
+    tokens, every segment inside it.)"""
+    import os
+    import torch
+    n, H = 512, 2
+    q = torch.zeros((n, H * 128), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros_like(q)
+    cases = [([0, 300, 200, 400], 300, "decreases"), ([0, 200, 480], 280, "ends at"),
+             ([0, 100, 400], 200, "max_seqlen"), ([5, 400], 395, "not 0")]
+    old = os.environ.get("DIT_VALIDATE")
+    os.environ["DIT_VALIDATE"] = "1"
+    try:
+        for cu, ms, msg in cases:
+            cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+            ws = torch.zeros(jav.attn_fp8_workspace_bytes(400, len(cu) - 1, H),
+                             dtype=torch.uint8, device="cuda")
+            with pytest.raises(jav.DitError) as ei:
+                jav.attn_fp8_prepare(q, q, q, cu_d, ms, H, workspace=ws, n_tokens=400)
+            assert ei.value.status == jav.DIT_EINVAL and msg in str(ei.value), (cu, str(ei.value))
+            with pytest.raises(jav.DitError) as ei:
+                jav.attn_packed_fp8(ws, cu_d, ms, 400, H, out=o)
+            assert ei.value.status == jav.DIT_EINVAL and msg in str(ei.value), (cu, str(ei.value))
+        cu_d = torch.tensor([0, 150, 400], dtype=torch.int32, device="cuda")
+        ws = jav.attn_fp8_prepare(q, q, q, cu_d, 250, H, n_tokens=400)
+        jav.attn_packed_fp8(ws, cu_d, 250, 400, H, out=o)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o[:400].float()).all()
+    finally:
+        if old is None:
+            os.environ.pop("DIT_VALIDATE", None)
+        else:
+            os.environ["DIT_VALIDATE"] = old
