@@ -447,8 +447,12 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
     if (t < nkt) issue_v(vnext, t);
     if (lagging && t >= 1) softmax(t - 1);
     __builtin_amdgcn_s_setprio(1);
+    // The leading waves issue S^T(t) before PV(t-1), so their softmax of tile
+    // t starts while their own PV products still run (measured 3% faster);
+    // the lagging waves need P(t-1) first and keep the bf16 kernel's order.
+    if (!lagging && t < nkt) compute_s(kcur);
     if (t >= 1) pv(vprev);
-    if (t < nkt) compute_s(kcur);
+    if (lagging && t < nkt) compute_s(kcur);
     __builtin_amdgcn_s_setprio(0);
     if (!lagging && t < nkt) softmax(t);
     __builtin_amdgcn_s_waitcnt(0);
