@@ -352,3 +352,46 @@ def test_fp8_attention_rows_subset_matches_every_row():
     rows = [0, 5, 19, 20, 32]
     part = oracle.attention_fp8(q, k, v, cu, hh, dh, causal=True, rows=rows)
     np.testing.assert_array_equal(part["o"], full["o"][rows])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_block_with_fp8_attention_and_zero_queries_averages_v(causal):
+    """With W_q = 0 (no bias) every key gets the same weight, so the FP8
+    attention half's o is, per head, the mean of v's per-head dequantized codes
+    over the query's keys (its segment, or the segment's prefix when causal):
+    checks that the half hands its own v, the segments and the per-head scale
+    (over all tokens) to the attention."""
+    x, table, mod, pos, wq, wo, _, _ = _lossless_block(81, d=16, h=2, n=14, with_bias=False)
+    codes, scales = wq
+    codes = codes.copy()
+    codes[:16] = 0
+    kw = dict(n_heads=2, head_dim=8, sections=(2, 2, 4), theta=100.0)
+    cu = [0, 6, 14]
+    f8 = oracle.block_forward_fp8(x, mod, pos, cu, table, codes, scales, *wo, causal=causal,
+                                  fp8_attention=True, **kw)
+    assert not f8["q"].any()
+    tab = oracle.e4m3_table()
+    vd = np.empty_like(f8["v"])
+    for h in range(2):
+        cols = slice(8 * h, 8 * h + 8)
+        c, s = oracle.quantize_tensor(f8["v"][:, cols])
+        vd[:, cols] = tab[c] * np.float64(s)
+    for a, b in zip(cu, cu[1:]):
+        for i in range(a, b):
+            keys = slice(a, i + 1 if causal else b)
+            np.testing.assert_allclose(f8["o"][i], vd[keys].mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_block_with_fp8_attention_and_zero_values():
+    """W_v = 0 (no qkv bias): v = 0, so the FP8 attention gives o = 0 exactly and
+    the half returns x + gate[m] * b_o."""
+    x, table, mod, pos, wq, wo, _, b_o = _lossless_block(82, d=16, h=2, n=12, with_bias=True)
+    codes, scales = wq
+    codes = codes.copy()
+    codes[32:] = 0
+    kw = dict(n_heads=2, head_dim=8, sections=(2, 2, 4), theta=100.0)
+    f8 = oracle.block_forward_fp8(x, mod, pos, [0, 5, 12], table, codes, scales, *wo, b_o=b_o,
+                                  fp8_attention=True, **kw)
+    assert not f8["v"].any() and not f8["o"].any()
+    np.testing.assert_allclose(f8["out"], x + table[mod, 2, :] * b_o[None, :], rtol=1e-12,
+                               atol=1e-14)
