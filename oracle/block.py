@@ -92,7 +92,10 @@ def rope3d(x, pos, n_heads: int, head_dim: int, sections: Sequence[int],
     complex number u + i w multiplied by exp(i pos_a omega_j) with
     omega_j = theta^(-2j / s_a) (RoFormer's rotary embedding, one 1-D RoPE
     per axis).  Audio and text rows have h = w = 0, so only their time
-    section turns.
+    section turns.  The pairing convention is parity unpinned by the pages:
+    the tests pin the frequencies, the rotation and its relative-offset
+    invariant, which hold for any pairing, so which dimensions pair up rests
+    on this reading alone.
 
     x: [N][n_heads*head_dim]; pos: [N][3] ints.  Returns float64 [rows][H*Dh].
     """
