@@ -186,37 +186,207 @@ def nft_bytes(keep, channels, v_elt=2):
     return int(keep.size * (1 + 4 * c) + int((keep != 0).sum()) * (2 * v_elt * c + 4 * c))
 
 
-def cpu_baseline(wl, inp, lay, rows_n: int):
-    """Oracle (float64 NumPy) on a bounded sample: every stage for `rows_n` query rows,
-    attention of those rows against all keys of their segment (synthetic k, v)."""
+def _cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _attn_head_task(task):
+    """One (segment, head) of the oracle's attention for the sampled query rows,
+    in a worker process with one BLAS thread.  The segment's keys and values are
+    seeded N(0, 1) bf16 values generated here (they cost the same arithmetic as
+    the block's own and need no transfer)."""
     import oracle
     import synth
-    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
-    rng_rows = np.random.Generator(np.random.PCG64(7)).choice(n, size=rows_n, replace=False)
-    rows = np.sort(rng_rows)
-    k_h = synth.normal_array((n, d), seed=901, dtype="bf16")
-    v_h = synth.normal_array((n, d), seed=902, dtype="bf16")
+    seg_len, rows_rel, q_rows, seed = task
+    k = synth.normal_array((seg_len, q_rows.shape[1]), seed=seed, dtype="bf16")
+    v = synth.normal_array((seg_len, q_rows.shape[1]), seed=seed + 1, dtype="bf16")
+    q = np.zeros((seg_len, q_rows.shape[1]))
+    q[rows_rel] = q_rows
     t0 = time.perf_counter()
-    y = oracle.adaln_modulate(inp.x, lay["modality"], inp.table, wl.eps, rows=rows)
-    qkv = oracle.qkv_project(y, inp.w_qkv)
-    q = np.zeros((n, d))
-    q[rows] = oracle.rope3d(qkv[:, :d], np.asarray(lay["pos"])[rows], H, Dh, wl.sections, wl.theta)
-    _ = oracle.rope3d(qkv[:, d:2 * d], np.asarray(lay["pos"])[rows], H, Dh, wl.sections, wl.theta)
-    o = oracle.attention(q, k_h, v_h, lay["cu_seqlens"], H, Dh, rows=rows)
-    _ = oracle.out_proj_gated(o, inp.w_o, inp.x, lay["modality"], inp.table, rows=rows)
-    dt = time.perf_counter() - t0
-    seg_len = {}
-    cu = lay["cu_seqlens"]
+    o = oracle.attention(q, k, v, [0, seg_len], 1, q_rows.shape[1], rows=rows_rel)
+    return time.perf_counter() - t0, o
+
+
+def cpu_baseline(wl, inp, lay, rows_n: int, workers: int):
+    """Oracle (float64 NumPy) on a bounded sample of the block: `rows_n` random
+    query rows through AdaLN, the fused QKV projection (all 3 D columns) and the
+    3D RoPE with BLAS on every core; their attention against all keys of their
+    segment as a process pool over (segment, head), one BLAS thread per worker;
+    then to_out.0 with the gated residual.  Keys and values are synthetic (see
+    _attn_head_task).  The rate is the sample's algorithmic FLOPs over its wall
+    time; the full block's oracle time is that rate applied to the block's FLOPs
+    (extrapolated, not run)."""
+    import multiprocessing as mp
+
+    import oracle
+    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
+    rows = np.sort(np.random.Generator(np.random.PCG64(7)).choice(n, size=rows_n, replace=False))
+    cu = [int(c) for c in lay["cu_seqlens"]]
+    # one BLAS thread in the workers: set before they start (spawned: they
+    # import NumPy afresh and read these)
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                             "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    ctx = mp.get_context("spawn")
+    pool = ctx.Pool(workers)
+    for k, v in saved.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+    try:
+        # warm the workers (each imports NumPy and the oracle); a worker that cannot
+        # start makes the pool respawn it forever, so every wait has a limit
+        pool.map_async(_attn_head_task,
+                       [(64, np.arange(1), np.zeros((1, Dh)), 1)] * workers).get(timeout=300)
+        t0 = time.perf_counter()
+        y = oracle.adaln_modulate(inp.x, lay["modality"], inp.table, wl.eps, rows=rows)
+        qkv = oracle.qkv_project(y, inp.w_qkv)
+        pos = np.asarray(lay["pos"])[rows]
+        q_rot = oracle.rope3d(qkv[:, :d], pos, H, Dh, wl.sections, wl.theta)
+        _ = oracle.rope3d(qkv[:, d:2 * d], pos, H, Dh, wl.sections, wl.theta)
+        t_rows = time.perf_counter() - t0
+        tasks, where = [], []
+        for si, (a, b) in enumerate(zip(cu, cu[1:])):
+            sel = np.nonzero((rows >= a) & (rows < b))[0]
+            if sel.size == 0:
+                continue
+            for h in range(H):
+                tasks.append((b - a, rows[sel] - a,
+                              q_rot[sel, h * Dh:(h + 1) * Dh], 1000 + 2 * (si * H + h)))
+                where.append((sel, h))
+        t1 = time.perf_counter()
+        res = pool.map_async(_attn_head_task, tasks, chunksize=1).get(timeout=900)
+        t_attn = time.perf_counter() - t1
+        o = np.zeros((rows.size, d))
+        for (sel, h), (_, oh) in zip(where, res):
+            o[sel, h * Dh:(h + 1) * Dh] = oh
+        t2 = time.perf_counter()
+        _ = oracle.out_proj_gated(o, inp.w_o, inp.x, lay["modality"], inp.table, rows=rows)
+        t_out = time.perf_counter() - t2
+    finally:
+        pool.terminate()
+        pool.join()
+    dt = t_rows + t_attn + t_out
+    flops = 0.0
     for a, b in zip(cu, cu[1:]):
-        for r in rows[(rows >= a) & (rows < b)]:
-            seg_len[int(r)] = b - a
-    flops = sum(4.0 * d * L + 8.0 * d * d for L in seg_len.values())
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s",
-                cores=len(os.sched_getaffinity(0)), kind="oracle",
-                sample=(f"{rows_n} random query rows of the full 58,758-token block through "
-                        f"every stage (attention against all keys of their segment), "
-                        f"float64 NumPy; {dt:.1f} s"),
+        cnt = int(((rows >= a) & (rows < b)).sum())
+        flops += cnt * (4.0 * d * (b - a) + 8.0 * d * d)
+    rate = flops / dt
+    a_f, q_f, o_f = block_flops(n, d, cu)
+    return dict(value=rate / 1e12, unit="TFLOP/s", cores=len(os.sched_getaffinity(0)),
+                kind="oracle",
+                sample=(f"{rows_n} random query rows of the {n:,}-token block: AdaLN, fused QKV "
+                        f"and RoPE with BLAS on every core ({t_rows:.1f} s), their attention "
+                        f"against all {n:,} keys (synthetic seeded k, v) as {len(tasks)} "
+                        f"(segment, head) tasks on {workers} one-thread processes "
+                        f"({t_attn:.1f} s wall, {sum(r[0] for r in res):.1f} s in tasks), "
+                        f"to_out.0 + gated residual ({t_out:.1f} s); float64 NumPy"),
+                cpu_model=_cpu_model(), workers=workers,
+                oracle_block_ms_extrapolated=round((a_f + q_f + o_f) / rate * 1e3, 1),
                 seconds=dt)
+
+
+CONFIG_RUNS = (("tiny_f32", "tiny", False), ("small", "small", False), ("medium", "medium", False),
+               ("varlen_bidirectional", "varlen", False), ("varlen_causal", "varlen", True))
+
+
+def _timed(torch, fn, reps, stream):
+    fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_workload(jav, torch, name, causal, stream, reps=10):
+    """dit_block_forward on one workload (seeded inputs resident in HBM): block ms
+    and the in-block stage ms from the library's events, the attention's and the
+    projections' TFLOP/s, and the standalone AdaLN and RoPE kernels' GB/s on the
+    workload's shapes (the block rotates q and k inside its QKV stage)."""
+    import synth
+    wl = synth.WORKLOADS[name]
+    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
+    inp = synth.block_inputs(wl)
+    lay = jav.pack_layout([r.grid for r in wl.requests])
+    bf = wl.dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(tdt).cuda()
+
+    x, w_qkv, w_o = t(inp.x), t(inp.w_qkv), t(inp.w_o)
+    table = torch.from_numpy(inp.table).cuda()
+    mod = torch.from_numpy(lay["modality"]).cuda()
+    pos = torch.from_numpy(lay["pos"]).cuda()
+    cu = torch.from_numpy(lay["cu_seqlens"]).cuda()
+    desc = jav.block_desc(jav.DIT_BF16 if bf else jav.DIT_F32, d, H, Dh, wl.sections, wl.theta,
+                          wl.eps, causal=causal)
+    ws = torch.empty(jav.block_workspace_bytes(desc, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+
+    def blk():
+        jav.block_forward(desc, x, mod, pos, cu, lay["max_seqlen"], table, w_qkv, w_o, out=out,
+                          workspace=ws, stream=stream)
+
+    blk()
+    torch.cuda.synchronize()
+    jav.profile_enable(reps)
+    block_ms = _timed(torch, blk, reps, stream)
+    st_sum, calls = jav.profile_read()
+    jav.profile_enable(0)
+    st = {k: v / max(calls, 1) for k, v in zip(jav.STAGES, st_sum)}
+    y = torch.empty_like(x)
+    qk = torch.zeros((2, n, d), dtype=tdt, device="cuda")
+    iso_adaln = _timed(torch, lambda: jav.adaln_modulate(x, mod, table, wl.eps, out=y,
+                                                         stream=stream), 20, stream)
+    iso_rope = _timed(torch, lambda: jav.rope3d_apply(qk[0], qk[1], pos, H, Dh, wl.sections,
+                                                      wl.theta, stream=stream), 20, stream)
+    a_f, q_f, o_f = block_flops(n, d, lay["cu_seqlens"].tolist(), causal)
+    ab, rb = elementwise_bytes(n, d, 2 if bf else 4)
+    rec = {
+        "n_tokens": n, "d_model": d, "n_heads": H, "dtype": wl.dtype,
+        "segments": int(cu.numel() - 1), "causal": causal,
+        "block_ms": round(block_ms, 4),
+        "block_tflops": round((a_f + q_f + o_f) / (block_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in st.items()},
+        "attention_ms": round(st["attn"], 4),
+        "attention_tflops": round(a_f / (st["attn"] * 1e-3) / 1e12, 2),
+        "qkv_rope_tflops": round(q_f / (st["qkv"] * 1e-3) / 1e12, 2),
+        "out_proj_tflops": round(o_f / (st["out"] * 1e-3) / 1e12, 2),
+        "adaln_isolated_gbs": round(ab / (iso_adaln * 1e-3) / 1e9, 1),
+        "rope_isolated_gbs": round(rb / (iso_rope * 1e-3) / 1e9, 1),
+    }
+    if bf:
+        rec["attention_frac_of_bf16_peak"] = round(a_f / (st["attn"] * 1e-3) / 1e12
+                                                   / PEAK_BF16_TFLOPS, 4)
+        rec["block_frac_of_bf16_peak"] = round((a_f + q_f + o_f) / (block_ms * 1e-3) / 1e12
+                                               / PEAK_BF16_TFLOPS, 4)
+        rec["adaln_isolated_frac_of_hbm"] = round(ab / (iso_adaln * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        rec["rope_isolated_frac_of_hbm"] = round(rb / (iso_rope * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    del x, w_qkv, w_o, ws, out, y, qk
+    return rec
 
 
 def main() -> int:
@@ -238,6 +408,9 @@ def main() -> int:
                     help="skip timing the FP8 projections")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward pass of the attention half")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the block on the other workloads (tiny float32, small, medium, "
+                         "the 4-request pack bidirectional and causal)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("KIND", "DIR"),
@@ -662,6 +835,15 @@ def main() -> int:
         del dout, q_r, k_r, v_r, o_r, lse_r, dq_r, dk_r, dv_r, aws, bws, dx_b
         print(f"# backward: {bwd_rec}", file=sys.stderr, flush=True)
 
+    cfg_rec = None
+    if not args.no_configs:
+        print("# other workloads ...", file=sys.stderr, flush=True)
+        cfg_rec = {}
+        for label, name, causal in CONFIG_RUNS:
+            cfg_rec[label] = measure_workload(jav, torch, name, causal, stream)
+            print(f"# {label}: {cfg_rec[label]}", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+
     cu_list = lay["cu_seqlens"].tolist()
     attn_f, qkv_f, out_f = block_flops(n, d, cu_list, args.causal)
     blk_f = attn_f + qkv_f + out_f
@@ -695,10 +877,13 @@ def main() -> int:
         "attention_tflops": round(attn_tflops, 2),
         "attention_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        # the qkv stage is the rotation table's kernel plus the QKV GEMM, which
+        # rotates q and k in its epilogue: RoPE has no stage of its own in the block
         "qkv_tflops": round(qkv_f / (stage_ms["qkv"] * 1e-3) / 1e12, 2),
+        "rope_in_qkv_epilogue": True,
         "out_proj_tflops": round(out_f / (stage_ms["out"] * 1e-3) / 1e12, 2),
         "adaln_gbs": round(adaln_b / (stage_ms["adaln"] * 1e-3) / 1e9, 1),
-        "rope_gbs": round(rope_b / (stage_ms["rope"] * 1e-3) / 1e9, 1),
+        "adaln_frac_of_hbm": round(adaln_b / (stage_ms["adaln"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "isolated_ms": {k: round(v, 4) for k, v in iso_ms.items()},
         "isolated": {
             "attention_tflops": round(attn_f / (iso_ms["attn"] * 1e-3) / 1e12, 2),
@@ -722,6 +907,8 @@ def main() -> int:
             "traffic": recorded_traffic() if (wl.name == "full" and not args.causal) else None,
         },
     }
+    if cfg_rec is not None:
+        rec["workloads"] = cfg_rec
     if ffn_rec is not None:
         rec["ffn_half"] = ffn_rec
     if den_rec is not None:
@@ -736,9 +923,11 @@ def main() -> int:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle
         olay = oracle.pack_layout([r.grid for r in wl.requests])
-        cb = cpu_baseline(wl, inp, olay, args.cpu_rows)
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        cb = cpu_baseline(wl, inp, olay, args.cpu_rows, workers)
         cb.pop("seconds")
         cb["value"] = round(cb["value"], 6)
+        cb["gpu_block_ms"] = rec["block_ms"]
         rec["cpu_baseline"] = cb
     print(json.dumps(rec), flush=True)
     return 0

@@ -137,6 +137,17 @@ dit_status dit_pack_layout(const dit_grid* reqs, int32_t n_reqs,
                            int64_t capacity_tokens, int64_t* n_tokens,
                            int32_t* max_seqlen);
 
+/* Size of the pack dit_pack_layout would build, without building it: the
+ * total token count (the capacity its host buffers need) and the longest
+ * request.  One request holds t*h*w video + 2*audio_per_ch audio + text_len
+ * text tokens ([H3-NFT] section "MiniMax H3 and Why Joint Audio-Video
+ * Generation Complicates RL Training": stereo audio, one token stream per
+ * channel; [vLLM-Omni] section 1 table: the three modalities of a request).
+ * Host-only.  DIT_EINVAL for null pointers, n_reqs < 1, a negative grid entry
+ * or a total above INT32_MAX; nothing is written on failure. */
+dit_status dit_pack_count(const dit_grid* reqs, int32_t n_reqs, int64_t* n_tokens,
+                          int32_t* max_seqlen);
+
 /* ------------------------------------------------------------------------ */
 /* Device stages (asynchronous on `stream`; all pointers device memory)      */
 /* ------------------------------------------------------------------------ */
@@ -544,17 +555,22 @@ typedef struct {
   int32_t causal;             /* 0: bidirectional inside each segment */
 } dit_block_desc;
 
-/* Bytes of scratch dit_block_forward needs: five [N][D] planes y, q, k, v, o
- * (q, k, v are the fused projection's output split by column), each rounded
- * up to 256 bytes.  0 for a bad descriptor. */
+/* Bytes of scratch dit_block_forward needs: five [N][D] planes y, q', k', v,
+ * o (q', k', v are the fused projection's output split by column, q and k
+ * rotated), each rounded up to 256 bytes, then a float [N][head_dim] table of
+ * the rotation's (cos, sin) pairs.  0 for a bad descriptor. */
 size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
 
 /* x, out: [n_tokens][d_model] contiguous (out may equal x); modality, pos_thw,
  * cu_seqlens as above (device); ada_table f32 [3][3][d_model]; w_qkv
  * [3D][D]; w_o [D][D]; biases nullable; workspace: device, at least
- * dit_block_workspace_bytes() bytes, 256-byte aligned.  Enqueues adaln_modulate
- * -> qkv_project -> rope3d_apply -> attn_packed -> out_proj_gated on stream.
- * Errors: those of the stages, plus DIT_EWORKSPACE. */
+ * dit_block_workspace_bytes() bytes, 256-byte aligned.  Enqueues the stages
+ * of adaln_modulate -> qkv_project -> rope3d_apply -> attn_packed ->
+ * out_proj_gated on stream; in bf16 the rotation of q and k is applied by the
+ * QKV projection as it stores them (the same rotation, one bf16 rounding of
+ * q' and k' instead of two).  On completion the workspace holds the block's
+ * intermediates (dit_block_intermediates).  Errors: those of the stages, plus
+ * DIT_EWORKSPACE. */
 dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
                              const uint8_t* modality, const int32_t* pos_thw,
                              const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
@@ -562,6 +578,16 @@ dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
                              const void* w_qkv, const void* b_qkv,
                              const void* w_o, const void* b_o,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Where dit_block_forward leaves its intermediates in the workspace: byte
+ * offsets[0..4] of y (the AdaLN output), q' (the rotated queries), k' (the
+ * rotated keys), v and o (the attention output before to_out.0), each
+ * [n_tokens][d_model] of the block's dtype with leading dimension d_model,
+ * valid once the call has completed on its stream and until the workspace is
+ * reused.  Host-only.  DIT_EINVAL for a null pointer, a bad descriptor or
+ * n_tokens < 0. */
+dit_status dit_block_intermediates(const dit_block_desc* d, int64_t n_tokens,
+                                   int64_t offsets[5]);
 
 /* ------------------------------------------------------------------------ */
 /* Backward pass of the attention half                                        */

@@ -29,6 +29,7 @@ _STATUS_NAMES = {1: "DIT_EINVAL", 2: "DIT_EUNSUPPORTED", 3: "DIT_EWORKSPACE", 4:
 
 EXPORTED = (
     "dit_abi_version", "dit_last_error", "dit_grid_from_media", "dit_pack_layout",
+    "dit_pack_count", "dit_block_intermediates",
     "adaln_modulate", "rope3d_apply", "attn_packed", "qkv_project", "out_proj_gated",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_profile_enable", "dit_profile_read",
     "ffn_up_gelu", "ffn_down_gated", "dit_ffn_workspace_bytes", "dit_ffn_forward",
@@ -85,6 +86,8 @@ def _load() -> ctypes.CDLL:
         "dit_grid_from_media": (ctypes.c_int, [ctypes.POINTER(_Media), ctypes.POINTER(_Grid)]),
         "dit_pack_layout": (ctypes.c_int, [ctypes.POINTER(_Grid), I32, P, P, P, I64,
                                            ctypes.POINTER(I64), ctypes.POINTER(I32)]),
+        "dit_pack_count": (ctypes.c_int, [ctypes.POINTER(_Grid), I32, ctypes.POINTER(I64),
+                                          ctypes.POINTER(I32)]),
         "adaln_modulate": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, F32, P]),
         "rope3d_apply": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, I32, I32,
                                         ctypes.POINTER(I32), F32, P]),
@@ -96,6 +99,8 @@ def _load() -> ctypes.CDLL:
         "out_proj_gated": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, P, P, P, I64, I64,
                                           I32, P]),
         "dit_block_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
+        "dit_block_intermediates": (ctypes.c_int, [ctypes.POINTER(BlockDesc), I64,
+                                                   ctypes.POINTER(I64)]),
         "dit_block_forward": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32, I32,
                                              I64, P, P, P, P, P, P, SZ, P]),
         "ffn_up_gelu": (ctypes.c_int, [ctypes.c_int, P, I64, P, P, P, I64, I64, I32, I32, P]),
@@ -180,13 +185,22 @@ def grid_from_media(frames: int, height_px: int, width_px: int, audio_samples_pe
     return (g.t, g.h, g.w, g.audio_per_ch, g.text_len)
 
 
+def pack_count(grids: Sequence[Sequence[int]]) -> Tuple[int, int]:
+    """(n_tokens, max_seqlen) of the pack of these request grids (libdit dit_pack_count)."""
+    n = len(grids)
+    arr = (_Grid * max(n, 1))(*[_Grid(*map(int, g)) for g in grids])
+    nt = ctypes.c_int64(0)
+    ms = ctypes.c_int32(0)
+    _check(_lib.dit_pack_count(arr, n, ctypes.byref(nt), ctypes.byref(ms)))
+    return nt.value, ms.value
+
+
 def pack_layout(grids: Sequence[Sequence[int]], capacity: Optional[int] = None) -> dict:
     """Returns dict(modality uint8[N], pos int32[N][3], cu_seqlens int32[R+1], max_seqlen, n_tokens)."""
     n = len(grids)
     arr = (_Grid * max(n, 1))(*[_Grid(*map(int, g)) for g in grids])
     if capacity is None:
-        capacity = sum(max(0, g[0] * g[1] * g[2]) + 2 * max(0, g[3]) + max(0, g[4])
-                       for g in grids)
+        capacity = pack_count(grids)[0]
     cap = max(int(capacity), 1)
     mod = np.zeros(cap, dtype=np.uint8)
     pos = np.zeros((cap, 3), dtype=np.int32)
@@ -436,6 +450,27 @@ def block_desc(dtype_code: int, d_model: int, n_heads: int, head_dim: int,
 
 def block_workspace_bytes(desc: BlockDesc, n_tokens: int) -> int:
     return int(_lib.dit_block_workspace_bytes(ctypes.byref(desc), int(n_tokens)))
+
+
+def block_intermediates(desc: BlockDesc, n_tokens: int) -> dict:
+    """Byte offsets of y, q', k', v and o in dit_block_forward's workspace
+    (libdit dit_block_intermediates)."""
+    out = (ctypes.c_int64 * 5)()
+    _check(_lib.dit_block_intermediates(ctypes.byref(desc), int(n_tokens), out))
+    return dict(zip(("y", "q_rot", "k_rot", "v", "o"), (int(v) for v in out)))
+
+
+def block_planes(desc: BlockDesc, workspace, n_tokens: int) -> dict:
+    """Views of the intermediates dit_block_forward left in `workspace`: y, q_rot,
+    k_rot, v, o as [n_tokens][d_model] tensors of the block's dtype."""
+    torch = _torch()
+    dt = torch.bfloat16 if desc.dtype == DIT_BF16 else torch.float32
+    es = 2 if desc.dtype == DIT_BF16 else 4
+    nbytes = int(n_tokens) * desc.d_model * es
+    views = {}
+    for name, off in block_intermediates(desc, n_tokens).items():
+        views[name] = workspace[off:off + nbytes].view(dt).view(int(n_tokens), desc.d_model)
+    return views
 
 
 def block_forward(desc: BlockDesc, x, modality, pos, cu_seqlens, max_seqlen: int, table, w_qkv,

@@ -978,13 +978,42 @@ extern "C" dit_status dit_ffn_forward_fp8(const dit_ffn_desc* d, const void* x, 
 
 // ---------------------------------------------------------------------------
 
-// Block workspace: five [N][D] planes, y | q | k | v | o, each rounded up to
-// 256 bytes.  q, k and v are separate planes (not one [N][3D] array): the
-// in-place RoPE pass and the attention K/V loads then stream contiguous rows.
+// Block workspace: five [N][D] planes, y | q' | k' | v | o, each rounded up to
+// 256 bytes, then the rotation table [N][head_dim] float ((cos, sin) per
+// token and pair).  q, k and v are separate planes (not one [N][3D] array), so
+// the attention's K/V loads stream contiguous rows.  bf16: the QKV GEMM
+// rotates q and k in its epilogue (kind 3) with the table, built first by a
+// small kernel, and stores q', k', v straight into planes 1-3.  float32: the
+// GEMM stores q, k, v and RoPE then turns planes 1 and 2 in place.
+namespace {
+struct BlockLayout {
+  size_t plane, table, total;
+};
+BlockLayout block_layout(const dit_block_desc* d, int64_t n_tokens) {
+  const size_t es = elt_size(d->dtype), n = (size_t)n_tokens, D = (size_t)d->d_model;
+  const size_t dh = d->head_dim > 0 ? (size_t)d->head_dim : 0;
+  BlockLayout L;
+  L.plane = round256(n * D * es);
+  L.table = 5 * L.plane;
+  L.total = L.table + round256(n * dh * 4);
+  return L;
+}
+}  // namespace
+
 extern "C" size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens) {
   if (!d || !dtype_ok(d->dtype) || d->d_model < 1 || n_tokens < 0) return 0;
-  const size_t es = elt_size(d->dtype), n = (size_t)n_tokens, D = (size_t)d->d_model;
-  return 5 * round256(n * D * es);
+  return block_layout(d, n_tokens).total;
+}
+
+extern "C" dit_status dit_block_intermediates(const dit_block_desc* d, int64_t n_tokens,
+                                              int64_t offsets[5]) {
+  clear_error();
+  if (!d || !offsets) return fail(DIT_EINVAL, "dit_block_intermediates: null pointer");
+  if (!dtype_ok(d->dtype) || d->d_model < 1 || n_tokens < 0)
+    return fail(DIT_EINVAL, "dit_block_intermediates: bad descriptor or n_tokens");
+  const BlockLayout L = block_layout(d, n_tokens);
+  for (int i = 0; i < 5; ++i) offsets[i] = (int64_t)(i * L.plane);
+  return DIT_OK;
 }
 
 extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,
@@ -1011,14 +1040,15 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(DIT_EUNSUPPORTED, "dit_block_forward: workspace must be 256-byte aligned");
 
-  const size_t es = elt_size(dt), n = (size_t)n_tokens;
-  const size_t plane_bytes = round256(n * D * es);
+  const size_t es = elt_size(dt);
+  const BlockLayout L = block_layout(d, n_tokens);
   char* ws = static_cast<char*>(workspace);
   void* y = ws;
-  char* q = ws + plane_bytes;
-  char* k = q + plane_bytes;
-  char* v = k + plane_bytes;
-  void* o = v + plane_bytes;
+  char* q = ws + L.plane;
+  char* k = q + L.plane;
+  char* v = k + L.plane;
+  void* o = v + L.plane;
+  float* rope_tab = reinterpret_cast<float*>(ws + L.table);
 
   // Validate every stage before enqueuing any of them.
   if (dit_status st = adaln_check(dt, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps))
@@ -1028,13 +1058,7 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   if (dit_status st = rope_check(dt, q, D, k, D, pos_thw, n_tokens, H, Dh, d->rope_sections,
                                  d->rope_theta))
     return st;
-  // RoPE writes the rotated q into the y plane (dead after the QKV GEMM) and
-  // the rotated k over q's plane (each vector is read before it is
-  // overwritten): an out-of-place pass with no extra memory.  Attention then
-  // reads q' = y, k' = q's plane, v.
-  void* qr = y;
-  void* kr = q;
-  if (dit_status st = attn_check(dt, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
+  if (dit_status st = attn_check(dt, q, D, k, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
                                  n_tokens, H, Dh, d->softmax_scale))
     return st;
   if (dit_status st = proj_check("out_proj_gated", dt, o, D, w_o, out, D, n_tokens, D, D))
@@ -1055,24 +1079,35 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], s);
   };
+  double freq[64];
+  rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
+  const int s_t = d->rope_sections[0], s_h = d->rope_sections[1];
   hipError_t e;
   mark(0);
   e = launch_adaln(dt == DIT_BF16, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: adaln launch");
   mark(1);
-  // One GEMM over the fused W_qkv [3D][D], its output split into the q, k, v planes.
-  GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr, D, (int64_t)(plane_bytes / es)};
-  e = launch_gemm(dt == DIT_BF16, y, D, w_qkv, q, D, n_tokens, 3 * D, D, ep_qkv, s);
-  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: qkv launch");
-  mark(2);
-  double freq[64];
-  rope_freqs(d->rope_sections, (double)d->rope_theta, Dh, freq);
-  e = launch_rope(dt == DIT_BF16, q, D, k, D, qr, D, kr, D, pos_thw, n_tokens, H, Dh,
-                  d->rope_sections[0], d->rope_sections[1], freq, s);
-  if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope launch");
+  // One GEMM over the fused W_qkv [3D][D], its output split into the q', k', v
+  // planes; bf16 rotates q and k in the epilogue.
+  if (dt == DIT_BF16) {
+    e = launch_rope_table(pos_thw, n_tokens, Dh, s_t, s_h, freq, rope_tab, s);
+    if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope table launch");
+    GemmEpilogue ep_qkv{3, b_qkv, nullptr, 0, nullptr, nullptr, D,
+                        (int64_t)(L.plane / es), rope_tab, Dh};
+    e = launch_gemm(1, y, D, w_qkv, q, D, n_tokens, 3 * D, D, ep_qkv, s);
+    if (e != hipSuccess) return hip_fail(e, "dit_block_forward: qkv launch");
+    mark(2);
+  } else {
+    GemmEpilogue ep_qkv{0, b_qkv, nullptr, 0, nullptr, nullptr, D, (int64_t)(L.plane / es)};
+    e = launch_gemm(0, y, D, w_qkv, q, D, n_tokens, 3 * D, D, ep_qkv, s);
+    if (e != hipSuccess) return hip_fail(e, "dit_block_forward: qkv launch");
+    mark(2);
+    e = launch_rope(0, q, D, k, D, q, D, k, D, pos_thw, n_tokens, H, Dh, s_t, s_h, freq, s);
+    if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope launch");
+  }
   mark(3);
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)Dh);
-  e = launch_attn(dt == DIT_BF16, qr, D, kr, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
+  e = launch_attn(dt == DIT_BF16, q, D, k, D, v, D, o, D, cu_seqlens, n_seqs, max_seqlen,
                   n_tokens, H, Dh, scale, d->causal != 0, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "dit_block_forward: attention launch");
   mark(4);

@@ -1,7 +1,13 @@
-// Projections of the block: C = A B^T (+ bias), with three epilogues.
+// Projections of the block: C = A B^T (+ bias), with four epilogues.
 //   plain:          qkv = y W_qkv^T + b          (fused to_q | to_k | to_v)
 //   gated residual: out = x + gate[m] * (o W_o^T + b)   (to_out.0, ff.net.2)
 //   GELU:           h = gelu_tanh(y W_1^T + b)   (ff.net.0.proj)
+//   planes + RoPE:  q', k', v = rotate(y W_qkv^T + b) into three planes, the
+//                   3D rotation applied to q and k from a per-token table of
+//                   (cos, sin) pairs before the single bf16 rounding
+//                   ([H3-NFT] section "MiniMax H3 and Why Joint Audio-Video
+//                   Generation Complicates RL Training": RoPE over time,
+//                   height and width)
 // [VeRL-Omni] section 5.2 (Q, K, V packed into one matrix on the rollout
 // side); [H3-NFT] section "How VeRL-Omni's Adapter Architecture Keeps
 // H3-Specific Logic Contained" (projection names to_q, to_k, to_v, to_out.0,
@@ -58,8 +64,10 @@ struct EpiArgs {
   const uint8_t* mod;
   const float* gate;
   int64_t gate_stride;      // floats between the gate rows of two modalities
-  int plane_cols;           // kind 0: output split into planes of this many columns (0: none)
+  int plane_cols;           // kinds 0, 3: output split into planes of this many columns (0: none)
   int64_t plane_stride;     // elements between planes
+  const float* rope;        // kind 3: (cos, sin) per (row, pair), [M][rope_dh] floats
+  int rope_dh;              // kind 3: head_dim (a power of two dividing plane_cols)
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
@@ -231,18 +239,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
       // A 32-column block never straddles two planes (plane_cols is a multiple of 32).
       uint16_t* cbase = crow;
       int cshift = 0;
-      if (KIND == 0 && ep.plane_cols > 0) {
+      bool rot = false;
+      if ((KIND == 0 || KIND == 3) && ep.plane_cols > 0) {
         const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
         cbase = crow + plane * ep.plane_stride;
         cshift = plane * ep.plane_cols;
+        rot = KIND == 3 && plane < 2;
       }
+      // The block's accumulators move to VGPRs here, one 16-value block at a
+      // time (left alone the compiler copies all 256 out of the AGPRs at once
+      // and spills).
+      f32x16 blk = acc[mb][nb];
+      asm volatile("" : "+v"(blk));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
         if (col >= N) continue;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[mb][nb][4 * r + e];
+        for (int e = 0; e < 4; ++e) v[e] = blk[4 * r + e];
         if (ep.bias) {
           const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
           v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
@@ -258,6 +273,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
           v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
           v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
           v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
+        }
+        if constexpr (KIND == 3) {
+          // the lane's 4 columns are pairs p, p+1 of one head (col - cshift
+          // and rope_dh are multiples of 4); a zero angle leaves a pair's bits
+          if (rot) {
+            const float4 cs = *reinterpret_cast<const float4*>(
+                ep.rope + (int64_t)row * ep.rope_dh + ((col - cshift) & (ep.rope_dh - 1)));
+            if (cs.y != 0.0f) {
+              const float u = v[0], w = v[1];
+              v[0] = fmaf(u, cs.x, -w * cs.y);
+              v[1] = fmaf(u, cs.y, w * cs.x);
+            }
+            if (cs.w != 0.0f) {
+              const float u = v[2], w = v[3];
+              v[2] = fmaf(u, cs.z, -w * cs.w);
+              v[3] = fmaf(u, cs.w, w * cs.z);
+            }
+          }
         }
         *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -556,15 +589,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c, int64_t ldc,
                        int64_t m, int n, int k, const GemmEpilogue& ep, hipStream_t s) {
   if (k % BK != 0 || m > INT32_MAX) return hipErrorInvalidValue;
-  if (ep.plane_cols < 0 || ep.plane_cols % 32 != 0 || (ep.plane_cols > 0 && ep.kind != 0))
+  if (ep.plane_cols < 0 || ep.plane_cols % 32 != 0 ||
+      (ep.plane_cols > 0 && ep.kind != 0 && ep.kind != 3))
+    return hipErrorInvalidValue;
+  if (ep.kind == 3 && (!bf16 || !ep.rope || (ep.rope_dh != 64 && ep.rope_dh != 128) ||
+                       ep.plane_cols <= 0 || ep.plane_cols % ep.rope_dh != 0))
     return hipErrorInvalidValue;
   // gate rows of the table are 3*N floats apart (table [3][3][N], N = d_model)
   const int64_t gate_stride = 3 * (int64_t)n;
   if (bf16) {
     const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
-              ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride};
-    if (ep.kind == 1)
+              ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride, ep.rope,
+              ep.rope_dh};
+    if (ep.kind == 3)
+      gemm_bf16_kernel<3><<<dim3(tiles), dim3(kThreads), 0, s>>>(
+          static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
+          static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
+    else if (ep.kind == 1)
       gemm_bf16_kernel<1><<<dim3(tiles), dim3(kThreads), 0, s>>>(
           static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
           static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
@@ -593,10 +635,11 @@ hipError_t launch_gemm_fp8(const uint8_t* a, int64_t lda, const float* sa, const
   if (k % BK8 != 0 || m > INT32_MAX) return hipErrorInvalidValue;
   if (ep.plane_cols < 0 || ep.plane_cols % 32 != 0 || (ep.plane_cols > 0 && ep.kind != 0))
     return hipErrorInvalidValue;
+  if (ep.kind == 3) return hipErrorInvalidValue;
   const int64_t gate_stride = 3 * (int64_t)n;
   const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
-            ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride};
+            ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride, nullptr, 0};
   EpiArgs8 e8{sa, sw};
   uint16_t* cp = static_cast<uint16_t*>(c);
   if (ep.kind == 1)

@@ -52,6 +52,36 @@ extern "C" dit_status dit_grid_from_media(const dit_media* m, dit_grid* g) {
   return DIT_OK;
 }
 
+namespace {
+// Token count of the pack and its longest request; nothing is written on
+// failure.  One request holds t*h*w video + 2*audio_per_ch audio + text_len
+// text tokens.
+dit_status count_pack(const char* who, const dit_grid* reqs, int32_t n_reqs, int64_t* total_out,
+                      int32_t* longest_out) {
+  if (n_reqs < 1) return dit::fail(DIT_EINVAL, "%s: n_reqs < 1", who);
+  int64_t total = 0, longest = 0;
+  for (int32_t r = 0; r < n_reqs; ++r) {
+    const dit_grid& g = reqs[r];
+    if (g.t < 0 || g.h < 0 || g.w < 0 || g.audio_per_ch < 0 || g.text_len < 0)
+      return dit::fail(DIT_EINVAL, "%s: negative grid entry in request %d", who, r);
+    const int64_t len = (int64_t)g.t * g.h * g.w + (int64_t)kChannels * g.audio_per_ch + g.text_len;
+    total += len;
+    if (len > longest) longest = len;
+    if (total > INT32_MAX) return dit::fail(DIT_EINVAL, "%s: more than 2^31-1 tokens", who);
+  }
+  *total_out = total;
+  *longest_out = (int32_t)longest;
+  return DIT_OK;
+}
+}  // namespace
+
+extern "C" dit_status dit_pack_count(const dit_grid* reqs, int32_t n_reqs, int64_t* n_tokens,
+                                     int32_t* max_seqlen) {
+  dit::clear_error();
+  if (!reqs || !n_tokens || !max_seqlen) return dit::fail(DIT_EINVAL, "dit_pack_count: null pointer");
+  return count_pack("dit_pack_count", reqs, n_reqs, n_tokens, max_seqlen);
+}
+
 extern "C" dit_status dit_pack_layout(const dit_grid* reqs, int32_t n_reqs, uint8_t* modality,
                                       int32_t* pos_thw, int32_t* cu_seqlens,
                                       int64_t capacity_tokens, int64_t* n_tokens,
@@ -59,16 +89,10 @@ extern "C" dit_status dit_pack_layout(const dit_grid* reqs, int32_t n_reqs, uint
   dit::clear_error();
   if (!reqs || !modality || !pos_thw || !cu_seqlens || !n_tokens || !max_seqlen)
     return dit::fail(DIT_EINVAL, "dit_pack_layout: null pointer");
-  if (n_reqs < 1) return dit::fail(DIT_EINVAL, "dit_pack_layout: n_reqs < 1");
   // Size check first, so nothing is written on failure.
   int64_t total = 0;
-  for (int32_t r = 0; r < n_reqs; ++r) {
-    const dit_grid& g = reqs[r];
-    if (g.t < 0 || g.h < 0 || g.w < 0 || g.audio_per_ch < 0 || g.text_len < 0)
-      return dit::fail(DIT_EINVAL, "dit_pack_layout: negative grid entry in request %d", r);
-    total += (int64_t)g.t * g.h * g.w + (int64_t)kChannels * g.audio_per_ch + g.text_len;
-    if (total > INT32_MAX) return dit::fail(DIT_EINVAL, "dit_pack_layout: more than 2^31-1 tokens");
-  }
+  int32_t longest_len = 0;
+  if (dit_status st = count_pack("dit_pack_layout", reqs, n_reqs, &total, &longest_len)) return st;
   if (total > capacity_tokens)
     return dit::fail(DIT_EINVAL, "dit_pack_layout: %lld tokens exceed capacity %lld",
                      (long long)total, (long long)capacity_tokens);

@@ -71,3 +71,32 @@ def sample_rows(cu, n, extra_every=97, edge=8, seed=0, limit=None):
         keep |= set(rng.choice(rest, size=limit - len(keep), replace=False).tolist())
         rows = sorted(keep)
     return np.array(rows, dtype=np.int64)
+
+
+def ci_sample_rows(layout, every=97, edge=64):
+    """The CI row sample of a packed layout: the first and last `edge` rows of
+    every segment, every text row, the first and last audio frame of both
+    channels of every request (k = 0 and k = n_a - 1), every `every`-th row,
+    and two rows on each side of every change of modality.  About 800 rows of
+    the full 58,758-token pack."""
+    mod = np.asarray(layout["modality"])
+    pos = np.asarray(layout["pos"])
+    cu = [int(c) for c in layout["cu_seqlens"]]
+    n = int(mod.size)
+    rows = set(range(0, n, every))
+    for a, b in zip(cu, cu[1:]):
+        if b <= a:
+            continue
+        rows.update(range(a, min(b, a + edge)))
+        rows.update(range(max(a, b - edge), b))
+        seg_mod = mod[a:b]
+        rows.update((a + np.nonzero(seg_mod == 2)[0]).tolist())
+        aud = a + np.nonzero(seg_mod == 1)[0]
+        if aud.size:
+            t = pos[aud, 0]
+            last = int(t.max())
+            rows.update(aud[(t == 0) | (t == last)].tolist())
+    # two rows on each side of every change of modality (video/audio, audio/text)
+    for i in (np.nonzero(mod[1:] != mod[:-1])[0] + 1).tolist():
+        rows.update(r for r in range(i - 2, i + 2) if 0 <= r < n)
+    return np.array(sorted(rows), dtype=np.int64)

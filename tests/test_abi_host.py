@@ -131,8 +131,9 @@ def test_device_entry_points_validate_before_enqueue():
 def test_block_workspace_and_descriptor_checks():
     desc = jav.block_desc(jav.DIT_BF16, 5120, 40, 128, (32, 48, 48))
     n = 58758
-    want = 5 * (((n * 5120 * 2 + 255) // 256) * 256)      # y, q, k, v, o planes
-    assert jav.block_workspace_bytes(desc, n) == want
+    planes = 5 * (((n * 5120 * 2 + 255) // 256) * 256)    # y, q', k', v, o planes
+    table = ((n * 128 * 4 + 255) // 256) * 256             # (cos, sin) per token and pair
+    assert jav.block_workspace_bytes(desc, n) == planes + table
     fake = 1 << 20
     args = [fake, fake, fake, fake, fake, 1, 100, 100, fake, fake, None, fake, None]
     # workspace too small
@@ -361,3 +362,39 @@ def test_fp8_attention_layout_and_validation():
     assert _call("attn_packed_fp8", fake, 10, fake, 5120, fake, 1, 100, 100, 40, 128, 0.0, 0, None) == jav.DIT_EWORKSPACE
     assert _call("attn_packed_fp8", fake, need, fake + 2, 5120, fake, 1, 100, 100, 40, 128, 0.0, 0, None) == jav.DIT_EUNSUPPORTED
     assert _call("attn_packed_fp8", fake, need, fake, 5120, fake, 1, 0, 0, 40, 128, 0.0, 0, None) == jav.DIT_OK
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_pack_count_matches_layout(name):
+    grids = [r.grid for r in synth.WORKLOADS[name].requests]
+    lay = oracle.pack_layout(grids)
+    assert jav.pack_count(grids) == (lay["n_tokens"], max(
+        b - a for a, b in zip(lay["cu_seqlens"], lay["cu_seqlens"][1:])))
+
+
+def test_pack_count_rejects_and_edge_cases():
+    assert jav.pack_count([(0, 0, 0, 0, 0)]) == (0, 0)
+    assert jav.pack_count([(1, 2, 3, 4, 5), (0, 0, 0, 0, 7)]) == (6 + 8 + 5 + 7, 19)
+    for bad in ([], [(1, 1, -1, 0, 0)], [(1, 1, 1, 0, -2)], [(2000, 2000, 1000, 0, 0)]):
+        with pytest.raises(jav.DitError) as e:
+            jav.pack_count(bad)
+        assert e.value.status == jav.DIT_EINVAL
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_block_intermediates_fit_the_workspace(name):
+    """y, q', k', v and o: five distinct [N][D] planes, 256-byte aligned, inside
+    dit_block_workspace_bytes."""
+    wl = synth.WORKLOADS[name]
+    code = jav.DIT_BF16 if wl.dtype == "bf16" else jav.DIT_F32
+    desc = jav.block_desc(code, wl.d_model, wl.n_heads, wl.head_dim, wl.sections)
+    n, es = wl.n_tokens, 2 if wl.dtype == "bf16" else 4
+    offs = jav.block_intermediates(desc, n)
+    total = jav.block_workspace_bytes(desc, n)
+    assert list(offs) == ["y", "q_rot", "k_rot", "v", "o"]
+    spans = sorted((o, o + n * wl.d_model * es) for o in offs.values())
+    assert all(o % 256 == 0 for o, _ in spans)
+    assert all(b <= c for (_, b), (c, _) in zip(spans, spans[1:]))
+    assert spans[-1][1] <= total
+    with pytest.raises(jav.DitError):
+        jav.block_intermediates(desc, -1)

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check, dev, dev_f32, dev_int, host, sample_rows
+from gpu_util import check, ci_sample_rows, dev, dev_f32, dev_int, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -263,15 +263,31 @@ def test_attention_small(jav):
                label="small")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_medium(jav, causal):
+    """The 16,384-token pack with 24 heads, on the CI sample of its layout."""
+    wl = synth.WORKLOADS["medium"]
+    rows = ci_sample_rows(_layout("medium"))
+    _attn_case(jav, wl.n_tokens, wl.n_heads, 128, [0, wl.n_tokens], "bf16", causal, 235,
+               rows=rows, label=f"medium c={causal}")
+
+
 @pytest.mark.parametrize("variant", ["full", "modality_isolated", "varlen", "varlen_causal"])
 def test_attention_full_shape(jav, variant):
-    wl = synth.WORKLOADS["varlen" if variant.startswith("varlen") else "full"]
+    """58,758 tokens x 40 heads on the CI sample of the pack's layout (segment
+    edges, every text row, the audio ends of both channels, the modality
+    boundaries, every 97th row); the modality-isolated variant cuts segments at
+    the modality boundaries of the full pack."""
+    name = "varlen" if variant.startswith("varlen") else "full"
+    wl = synth.WORKLOADS[name]
     n, H = wl.n_tokens, wl.n_heads
     if variant == "modality_isolated":
         cu = [0, 57040, 58640, 58758]
+        lay = dict(_layout(name), cu_seqlens=cu)
     else:
         cu = list(wl.expected_cu_seqlens)
-    rows = sample_rows(cu, n, extra_every=1499, edge=3, limit=96)
+        lay = _layout(name)
+    rows = ci_sample_rows(lay)
     _attn_case(jav, n, H, 128, cu, "bf16", variant == "varlen_causal", 240, rows=rows,
                label=variant)
 
@@ -323,7 +339,8 @@ def test_gemm_odd_depths_and_ragged_tiles(jav, d, n):
 
 
 @pytest.mark.parametrize("name,bias,inplace", [("tiny", True, False), ("small", False, False),
-                                               ("small", True, True), ("full", False, True)])
+                                               ("small", True, True), ("medium", False, False),
+                                               ("full", False, True)])
 def test_out_proj_gated_parity(jav, name, bias, inplace):
     import torch
     wl = synth.WORKLOADS[name]
@@ -339,7 +356,7 @@ def test_out_proj_gated_parity(jav, name, bias, inplace):
                              dev_f32(inp.table), dev(inp.b_o, wl.dtype) if bias else None,
                              out=x if inplace else None)
     _sync()
-    rows = None if n <= 4096 else sample_rows([0, n], n, limit=700)
+    rows = None if n <= 4096 else ci_sample_rows(lay)
     ref = oracle.out_proj_gated(o_h if rows is None else o_h[rows], inp.w_o, x_h,
                                 lay["modality"], inp.table, inp.b_o if bias else None, rows=rows)
     got = host(out) if rows is None else host(out[torch.from_numpy(rows).cuda()])
@@ -353,29 +370,104 @@ def test_out_proj_gated_parity(jav, name, bias, inplace):
 # dit_block_forward
 # ---------------------------------------------------------------------------
 
-def _block(jav, name, causal=False, with_bias=False, rows=None):
-    import torch
+_REF_CACHE = {}
+
+
+def _oracle_block(name, causal, with_bias, rows):
+    """The oracle's block from the original inputs.  The bidirectional run is
+    kept for the workload (y, k, v, k' and the sampled q' do not depend on the
+    mask), and the causal form reuses its stages: attention with the causal
+    mask, then the gated output projection."""
     wl = synth.WORKLOADS[name]
     inp = synth.block_inputs(wl, with_bias=True) if with_bias else _inputs(name)
     lay = _layout(name)
+    key = (name, with_bias, None if rows is None else rows.tobytes())
+    base = _REF_CACHE.get(key)
+    if base is None:
+        _REF_CACHE.clear()
+        base = oracle.block_forward(inp.x, lay["modality"], lay["pos"], lay["cu_seqlens"],
+                                    inp.table, inp.w_qkv, inp.w_o, n_heads=wl.n_heads,
+                                    head_dim=wl.head_dim, sections=wl.sections, theta=wl.theta,
+                                    eps=wl.eps, causal=False,
+                                    b_qkv=inp.b_qkv if with_bias else None,
+                                    b_o=inp.b_o if with_bias else None, rows=rows)
+        _REF_CACHE[key] = base
+    if not causal:
+        return base
+    o = oracle.attention(base["q_rot"], base["k_rot"], base["v"], lay["cu_seqlens"], wl.n_heads,
+                         wl.head_dim, True, rows=rows)
+    out = oracle.out_proj_gated(o, inp.w_o, inp.x, lay["modality"], inp.table,
+                                inp.b_o if with_bias else None, rows=rows)
+    return dict(base, o=o, out=out)
+
+
+def _block(jav, name, causal=False, with_bias=False, rows=None):
+    """dit_block_forward against the oracle: the output and the intermediates the
+    call leaves in its workspace (q', k', v and o), on every row or on `rows`.
+    The block's output is dominated by the residual x, so the intermediates are
+    the sensitive checks (a block without RoPE or with a wrong mask still comes
+    within tolerance on `out`; see test_oracle_block.py)."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp = synth.block_inputs(wl, with_bias=True) if with_bias else _inputs(name)
     mod_d, pos_d, cu_d, ms = _dev_layout(jav, name)
+    n = wl.n_tokens
     code = jav.DIT_BF16 if wl.dtype == "bf16" else jav.DIT_F32
     desc = jav.block_desc(code, wl.d_model, wl.n_heads, wl.head_dim, wl.sections, wl.theta,
                           wl.eps, causal=causal)
-    print(f"block {name} causal={causal} bias={with_bias}", flush=True)
-    out = jav.block_forward(desc, dev(inp.x, wl.dtype), mod_d, pos_d, cu_d, ms,
-                            dev_f32(inp.table), dev(inp.w_qkv, wl.dtype), dev(inp.w_o, wl.dtype),
+    nrows = n if rows is None else len(rows)
+    print(f"block {name} causal={causal} bias={with_bias} rows={nrows}", flush=True)
+    x = dev(inp.x, wl.dtype)
+    ws = torch.empty(jav.block_workspace_bytes(desc, n), dtype=torch.uint8, device="cuda")
+    out = jav.block_forward(desc, x, mod_d, pos_d, cu_d, ms, dev_f32(inp.table),
+                            dev(inp.w_qkv, wl.dtype), dev(inp.w_o, wl.dtype),
                             b_qkv=dev(inp.b_qkv, wl.dtype) if with_bias else None,
-                            b_o=dev(inp.b_o, wl.dtype) if with_bias else None)
+                            b_o=dev(inp.b_o, wl.dtype) if with_bias else None, workspace=ws)
     _sync()
-    ref = oracle.block_forward(inp.x, lay["modality"], lay["pos"], lay["cu_seqlens"], inp.table,
-                               inp.w_qkv, inp.w_o, n_heads=wl.n_heads, head_dim=wl.head_dim,
-                               sections=wl.sections, theta=wl.theta, eps=wl.eps, causal=causal,
-                               b_qkv=inp.b_qkv if with_bias else None,
-                               b_o=inp.b_o if with_bias else None, rows=rows)
-    got = host(out) if rows is None else host(out[torch.from_numpy(rows).cuda()])
-    check(got, ref["out"], wl.dtype, f"block[{name}]")
-    return out
+    ref = _oracle_block(name, causal, with_bias, rows)
+    planes = jav.block_planes(desc, ws, n)
+    idx = None if rows is None else torch.from_numpy(rows).cuda()
+
+    def got(t):
+        return host(t) if idx is None else host(t[idx])
+
+    def at(a):
+        return a if rows is None else a[rows]
+
+    tag = f"block[{name}{' causal' if causal else ''}]"
+    check(got(planes["q_rot"]), at(ref["q_rot"]), wl.dtype, f"{tag}.q'")
+    check(got(planes["k_rot"]), at(ref["k_rot"]), wl.dtype, f"{tag}.k'")
+    check(got(planes["v"]), at(ref["v"]), wl.dtype, f"{tag}.v")
+    check(got(planes["o"]), ref["o"], wl.dtype, f"{tag}.o")
+    check(got(out), ref["out"], wl.dtype, f"{tag}.out")
+    if wl.dtype == "f32":
+        # the branch alone, out - x = gate * (o W_o^T + b), where x does not hide errors
+        check(got(out) - at(np.asarray(inp.x, np.float64)), ref["out"] - at(inp.x), "f32",
+              f"{tag}.branch")
+    return out, planes, ws, desc
+
+
+def _assert_unrotated_bits(jav, name, planes, ws, desc, with_bias=False):
+    """The rotation leaves what it must not touch bit for bit: v, and the h and w
+    sections of q and k on audio and text rows (their h = w = 0).  Reference: the
+    standalone QKV projection of the AdaLN output y the block left in its
+    workspace (the same GEMM, so the same bits before any rotation)."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    n, d, H, Dh = wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim
+    inp = synth.block_inputs(wl, with_bias=True) if with_bias else _inputs(name)
+    qkv = jav.qkv_project(planes["y"], dev(inp.w_qkv, wl.dtype),
+                          dev(inp.b_qkv, wl.dtype) if with_bias else None)
+    _sync()
+    ibits = torch.int16 if wl.dtype == "bf16" else torch.int32
+    assert torch.equal(planes["v"].view(ibits), qkv[:, 2 * d:].contiguous().view(ibits))
+    mod = np.asarray(_layout(name)["modality"])
+    at = torch.from_numpy(np.nonzero(mod != 0)[0]).cuda()
+    s_t = wl.sections[0]
+    for plane, lo in (("q_rot", 0), ("k_rot", d)):
+        a = planes[plane].view(n, H, Dh)[at][:, :, s_t:].contiguous()
+        b = qkv[:, lo:lo + d].reshape(n, H, Dh)[at][:, :, s_t:].contiguous()
+        assert torch.equal(a.view(ibits), b.view(ibits)), plane
 
 
 def test_block_tiny_f32(jav):
@@ -384,14 +476,34 @@ def test_block_tiny_f32(jav):
 
 
 def test_block_small_bf16(jav):
-    wl = synth.WORKLOADS["small"]
-    _block(jav, "small", rows=sample_rows([0, wl.n_tokens], wl.n_tokens, limit=256))
+    rows = ci_sample_rows(_layout("small"))
+    _, planes, ws, desc = _block(jav, "small", rows=rows)
+    _assert_unrotated_bits(jav, "small", planes, ws, desc)
+
+
+def test_block_small_bias_causal(jav):
+    rows = ci_sample_rows(_layout("small"))
+    _, planes, ws, desc = _block(jav, "small", causal=True, with_bias=True, rows=rows)
+    _assert_unrotated_bits(jav, "small", planes, ws, desc, with_bias=True)
+
+
+def test_block_medium_sampled(jav):
+    _block(jav, "medium", rows=ci_sample_rows(_layout("medium")))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_varlen_pack_sampled(jav, causal):
+    """The 4-request pack (14,690 / 14,690 / 14,689 / 14,689 tokens), each
+    request attending only inside its own cu_seqlens segment."""
+    _block(jav, "varlen", causal=causal, rows=ci_sample_rows(_layout("varlen")))
 
 
 def test_block_full_shape_sampled(jav):
-    wl = synth.WORKLOADS["full"]
-    rows = sample_rows([0, wl.n_tokens], wl.n_tokens, extra_every=4999, edge=2, limit=40)
-    _block(jav, "full", rows=rows)
+    """58,758 tokens on the CI sample: segment edges, every text row, the first and
+    last audio frame of both channels, the modality boundaries, every 97th row."""
+    rows = ci_sample_rows(_layout("full"))
+    _, planes, ws, desc = _block(jav, "full", rows=rows)
+    _assert_unrotated_bits(jav, "full", planes, ws, desc)
 
 
 def test_block_poison_tail_and_determinism(jav):

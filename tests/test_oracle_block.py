@@ -98,3 +98,38 @@ def test_tiny_workload_runs_and_is_finite():
                                head_dim=wl.head_dim, sections=wl.sections)
     assert res["out"].shape == (328, 256)
     assert np.isfinite(res["out"]).all()
+
+
+def test_intermediates_catch_wiring_mistakes_that_out_does_not():
+    """Why the block's GPU parity compares q', o and the other intermediates, not
+    only out: the residual x dominates out (the branch is a gate ~ N(0, 0.1)
+    times a projection of a softmax average), so a block without RoPE (every
+    position 0) or with the mask split into four segments stays within the bf16
+    tolerance on out, while q' and o move far past it.  The mistakes are planted
+    in the oracle itself, on a 640-token pack with the bf16 workloads' value
+    distributions."""
+    wl = synth.WORKLOADS["small"]
+    grid = (4, 8, 15, 40, 40)                       # 480 video + 2 x 40 audio + 40 text
+    lay = oracle.pack_layout([grid])
+    n, d, h, dh = lay["n_tokens"], 512, 4, 128
+    x = synth.normal_array((n, d), seed=61, dtype="bf16")
+    table = synth.normal_array((3, 3, d), seed=62, std=0.1)
+    w_qkv = synth.normal_array((3 * d, d), seed=63, std=0.02, dtype="bf16")
+    w_o = synth.normal_array((d, d), seed=64, std=0.02, dtype="bf16")
+
+    def run(pos, cu):
+        return oracle.block_forward(x, lay["modality"], pos, cu, table, w_qkv, w_o,
+                                    n_heads=h, head_dim=dh, sections=wl.sections)
+
+    def rel(a, b):
+        return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+    good = run(lay["pos"], lay["cu_seqlens"])
+    no_rope = run(np.zeros_like(lay["pos"]), lay["cu_seqlens"])
+    split = run(lay["pos"], [0, n // 4, n // 2, 3 * n // 4, n])
+    tol = 1e-2                                             # the bf16 rel-L2 bound
+    for bad in (no_rope, split):
+        assert rel(bad["out"], good["out"]) < tol          # out alone would pass
+    assert rel(no_rope["q_rot"], good["q_rot"]) > 5 * tol
+    assert rel(no_rope["o"], good["o"]) > 5 * tol
+    assert rel(split["o"], good["o"]) > 5 * tol
