@@ -159,9 +159,9 @@ def block_forward_fp8(x, modality, pos, cu_seqlens, table, wq_codes, wq_scales, 
     projections in FP8: the AdaLN output and the attention output are
     quantized per row, W_qkv [3D][D] and W_o [D][D] are given as per-row codes
     and scales.  With ``fp8_attention`` the attention is attention_fp8 of the
-    rotated q, k and v.  Returns y_codes, y_scales, q, k, v, o, o_codes,
-    o_scales and out (float64); with ``rows``, o, its codes and out hold those
-    rows only.
+    rotated q, k and v.  Returns y_codes, y_scales, q, k, v, q_rot, k_rot, o,
+    o_codes, o_scales and out (float64); with ``rows``, o, its codes and out
+    hold those rows only, and q, q_rot are filled only at those rows.
     """
     x = np.asarray(x)
     n, d = x.shape
@@ -184,7 +184,8 @@ def block_forward_fp8(x, modality, pos, cu_seqlens, table, wq_codes, wq_scales, 
     oc, os_ = quantize_rows(o)
     out = out_proj_gated(dequantize_rows(oc, os_), dequantize_rows(wo_codes, wo_scales), x,
                          modality, table, b_o, rows)
-    return dict(y_codes=yc, y_scales=ys, q=q, k=k, v=v, o=o, o_codes=oc, o_scales=os_, out=out)
+    return dict(y_codes=yc, y_scales=ys, q=q, k=k, v=v, q_rot=q_rot, k_rot=k_rot, o=o,
+                o_codes=oc, o_scales=os_, out=out)
 
 
 def ffn_forward_fp8(x, modality, table_mlp, w1_codes, w1_scales, w2_codes, w2_scales,

@@ -212,6 +212,65 @@ def test_block_backward_ragged_causal_bias_inplace(jav):
                     inplace=True)
 
 
+def _golden_module():
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "make_block_backward_medium.py")
+    spec = importlib.util.spec_from_file_location("_make_block_backward_medium", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_block_backward_medium_against_stored_oracle(jav):
+    """dit_block_backward at the medium workload (16,384 tokens, d_model 3072, 24
+    heads) against the float64 oracle's gradients, which
+    tests/golden/make_block_backward_medium.py stored (the oracle needs minutes
+    there).  db_qkv, db_o and every table row are compared whole; dx, dW_qkv and
+    dW_o on 16,384 sampled elements each, through every row's norm, the
+    Frobenius norm, and a two-sided Gaussian sketch A G B whose relative
+    distance estimates the whole tensor's (2e-2: the estimate of a 1e-2-scale
+    error varies by a small factor with the error's shape)."""
+    import torch
+    gm = _golden_module()
+    gold = np.load(gm.OUT)
+    wl = synth.WORKLOADS["medium"]
+    inp = synth.block_inputs(wl)
+    n, d = inp.x.shape
+    mod, _, _, (mod_d, pos_d, cu_d, ms) = _layout(jav, "medium", n, None)
+    dout = synth.normal_array((n, d), seed=1500 + n, dtype="bf16")
+    desc = jav.block_desc(jav.DIT_BF16, d, wl.n_heads, wl.head_dim, wl.sections, wl.theta,
+                          wl.eps)
+    print(f"block backward medium n={n} (stored oracle)", flush=True)
+    got = jav.block_backward(desc, dev(inp.x, "bf16"), dev(dout, "bf16"), mod_d, pos_d, cu_d, ms,
+                             dev(inp.table, "f32"), dev(inp.w_qkv, "bf16"), dev(inp.w_o, "bf16"))
+    _sync()
+    check_grad(host(got["db_qkv"]), gold["db_qkv"], "medium.db_qkv")
+    check_grad(host(got["db_o"]), gold["db_o"], "medium.db_o")
+    present = np.unique(mod)
+    for r, row in enumerate(("shift", "scale", "gate")):
+        check_grad(host(got["dtable"])[present, r], gold["dtable"][present, r],
+                   f"medium.dtable.{row}")
+    for key, seed in gm.BIG.items():
+        g = host(got[key])
+        pos = gold[f"{key}_pos"]
+        vals = g.reshape(-1)[pos]
+        ref = gold[f"{key}_val"].astype(np.float64)
+        r = rel_l2(vals, ref)
+        m = float(np.max(np.abs(vals - ref)))
+        bound = 3e-2 * max(1.0, float(gold[f"{key}_maxabs"]))
+        rn = rel_l2(np.linalg.norm(g, axis=1), gold[f"{key}_rownorm"])
+        nr = abs(float(np.linalg.norm(g)) - float(gold[f"{key}_norm"])) / float(gold[f"{key}_norm"])
+        a, b = gm.sketch_mats(g.shape[0], g.shape[1], seed)
+        sk = rel_l2(a @ g @ b, gold[f"{key}_sketch"])
+        print(f"  medium.{key}: sampled rel_l2={r:.3e} max_abs={m:.3e} (bound {bound:.2e}) "
+              f"row norms {rn:.3e} norm {nr:.3e} sketch {sk:.3e}", flush=True)
+        assert np.isfinite(g).all(), key
+        assert r <= 1e-2 and m <= bound, (key, r, m)
+        assert rn <= 1e-2 and nr <= 1e-2 and sk <= 2e-2, (key, rn, nr, sk)
+
+
 def test_block_backward_full_shape(jav):
     """58,758 tokens: finite and deterministic; db_o against the sum of gate * dout from the
     inputs alone; absent modalities get zero table rows (the full pack has all three)."""

@@ -12,6 +12,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
+import synth
 
 
 def _setup(n=14, d=16, h=2, seed=80, bias=True):
@@ -237,3 +238,27 @@ def test_ffn_backward_matches_torch_autograd():
     for key, tk in (("dx", "x"), ("dtable", "table"), ("dw1", "w1"), ("dw2", "w2"),
                     ("db1", "b1"), ("db2", "b2")):
         np.testing.assert_allclose(g[key], t[tk].grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_stored_medium_backward_belongs_to_the_current_inputs():
+    """tests/golden/block_backward_medium.npz (written by the oracle through
+    make_block_backward_medium.py) matches the medium workload's current inputs:
+    its db_o equals the closed form sum_i gate[m_i] * dout_i, its gate-row table
+    gradients are zero nowhere the modality is present, and it holds every
+    array the GPU test reads."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "block_backward_medium.npz")
+    gold = np.load(path)
+    wl = synth.WORKLOADS["medium"]
+    inp = synth.block_inputs(wl)
+    lay = oracle.pack_layout([r.grid for r in wl.requests])
+    n, d = wl.n_tokens, wl.d_model
+    dout = synth.normal_array((n, d), seed=1500 + n, dtype="bf16")
+    gate = np.asarray(inp.table, np.float64)[np.asarray(lay["modality"]), 2, :]
+    db_o = (gate * dout).sum(axis=0)
+    np.testing.assert_allclose(gold["db_o"], db_o, rtol=1e-5, atol=1e-4)
+    assert np.all(np.abs(gold["dtable"][:, 2, :]).max(axis=1) > 0)
+    for key in ("dx", "dw_qkv", "dw_o"):
+        for part in ("pos", "val", "rownorm", "norm", "maxabs", "sketch"):
+            assert f"{key}_{part}" in gold.files, (key, part)
