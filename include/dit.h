@@ -336,6 +336,28 @@ dit_status attn_packed_backward(dit_dtype dt, const void* q, int64_t ld_q, const
                                 int32_t head_dim, float softmax_scale, int32_t causal,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * attn_packed_backward with the same arguments, results and errors, minus
+ * the workspace.  Its scratch (delta, n_heads * n_tokens floats) is a fixed
+ * array in the library's device memory, one per GPU, kept until the process
+ * ends; its address is looked up on the first call with a device current, so
+ * the stream must belong to the current device.  Limit: n_heads * n_tokens <=
+ * dit_attn_backward_noalloc_max_elements() (4,194,304: 40 heads x 58,758
+ * tokens fit), otherwise DIT_EWORKSPACE.  Every call on one GPU uses that
+ * GPU's array: calls that overlap on one GPU (other streams or threads) race
+ * and must be serialised by the caller.  Allocates nothing. */
+size_t dit_attn_backward_noalloc_max_elements(void);
+dit_status attn_packed_backward_noalloc(dit_dtype dt, const void* q, int64_t ld_q, const void* k,
+                                        int64_t ld_k, const void* v, int64_t ld_v, const void* o,
+                                        int64_t ld_o, const void* dout, int64_t ld_do,
+                                        const float* lse, void* dq, int64_t ld_dq, void* dk,
+                                        int64_t ld_dk, void* dv, int64_t ld_dv,
+                                        const int32_t* cu_seqlens, int32_t n_seqs,
+                                        int32_t max_seqlen, int64_t n_tokens, int32_t n_heads,
+                                        int32_t head_dim, float softmax_scale, int32_t causal,
+                                        void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* FP8 projections                                                            */
 /* ------------------------------------------------------------------------ */

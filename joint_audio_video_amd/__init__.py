@@ -41,6 +41,7 @@ EXPORTED = (
     "dit_ffn_backward_workspace_bytes", "dit_ffn_backward",
     "dit_attn_fp8_workspace_bytes", "dit_attn_fp8_layout", "attn_fp8_prepare", "attn_packed_fp8",
     "dit_block_fp8_attn_workspace_bytes", "dit_block_forward_fp8_attn",
+    "dit_attn_backward_noalloc_max_elements", "attn_packed_backward_noalloc",
 )
 
 
@@ -135,6 +136,10 @@ def _load() -> ctypes.CDLL:
         "attn_packed_backward": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P, I64, P,
                                                 I64, P, P, I64, P, I64, P, I64, P, I32, I32, I64,
                                                 I32, I32, F32, I32, P, SZ, P]),
+        "dit_attn_backward_noalloc_max_elements": (SZ, []),
+        "attn_packed_backward_noalloc": (ctypes.c_int, [ctypes.c_int, P, I64, P, I64, P, I64, P,
+                                                        I64, P, I64, P, P, I64, P, I64, P, I64, P,
+                                                        I32, I32, I64, I32, I32, F32, I32, P]),
         "dit_block_backward_workspace_bytes": (SZ, [ctypes.POINTER(BlockDesc), I64]),
         "dit_block_backward": (ctypes.c_int, [ctypes.POINTER(BlockDesc), P, P, P, P, P, I32, I32,
                                               I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -408,6 +413,36 @@ def attn_packed_backward(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, n_h
                                      cu_seqlens.numel() - 1, int(max_seqlen), n, n_heads,
                                      head_dim, float(softmax_scale), int(bool(causal)),
                                      workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_backward_noalloc_max_elements() -> int:
+    return int(_lib.dit_attn_backward_noalloc_max_elements())
+
+
+def attn_packed_backward_noalloc(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
+                                 n_heads: int, head_dim: int, softmax_scale: float = 0.0,
+                                 causal: bool = False, dq=None, dk=None, dv=None, n_tokens=None,
+                                 stream=None):
+    """attn_packed_backward with its scratch in the library's fixed device array
+    (libdit attn_packed_backward_noalloc): no workspace argument.  dq, dk, dv
+    must be given (caller-owned) or are allocated here by torch."""
+    torch = _torch()
+    n = q.shape[0] if n_tokens is None else int(n_tokens)
+    w = n_heads * head_dim
+    dq = torch.empty((q.shape[0], w), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((q.shape[0], w), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((q.shape[0], w), dtype=q.dtype, device=q.device) if dv is None else dv
+    args = []
+    for t in (q, k, v, o, dout):
+        args += list(_rows(t))
+    args.append(lse.data_ptr())
+    for t in (dq, dk, dv):
+        args += list(_rows(t))
+    _check(_lib.attn_packed_backward_noalloc(_dtype_code(q), *args, cu_seqlens.data_ptr(),
+                                             cu_seqlens.numel() - 1, int(max_seqlen), n, n_heads,
+                                             head_dim, float(softmax_scale), int(bool(causal)),
+                                             _stream(stream)))
     return dq, dk, dv
 
 

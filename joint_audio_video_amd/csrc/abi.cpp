@@ -379,15 +379,16 @@ extern "C" size_t dit_attn_backward_workspace_bytes(int64_t n_tokens, int32_t n_
   return round256((size_t)n_tokens * (size_t)n_heads * 4);
 }
 
-extern "C" dit_status attn_packed_backward(
-    dit_dtype dt, const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
-    int64_t ld_v, const void* o, int64_t ld_o, const void* dout, int64_t ld_do, const float* lse,
-    void* dq, int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
+namespace {
+// The checks and the launch of attn_packed_backward, with delta (n_heads *
+// n_tokens floats) at `delta`, which holds `delta_bytes`.
+dit_status attn_backward_impl(
+    const char* who, dit_dtype dt, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+    const void* v, int64_t ld_v, const void* o, int64_t ld_o, const void* dout, int64_t ld_do,
+    const float* lse, void* dq, int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
     const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
-    int32_t n_heads, int32_t head_dim, float softmax_scale, int32_t causal, void* workspace,
-    size_t workspace_bytes, void* stream) {
-  clear_error();
-  const char* who = "attn_packed_backward";
+    int32_t n_heads, int32_t head_dim, float softmax_scale, int32_t causal, float* delta,
+    size_t delta_bytes, void* stream) {
   if (dit_status st = attn_check(dt, q, ld_q, k, ld_k, v, ld_v, const_cast<void*>(o), ld_o,
                                  cu_seqlens, n_seqs, max_seqlen, n_tokens, n_heads, head_dim,
                                  softmax_scale))
@@ -404,20 +405,91 @@ extern "C" dit_status attn_packed_backward(
       !ld_aligned(dt, ld_dv))
     return fail(DIT_EUNSUPPORTED, "%s: pointers/ld must be 16-byte aligned", who);
   const size_t need = dit_attn_backward_workspace_bytes(n_tokens, n_heads);
-  if (!workspace || workspace_bytes < need)
-    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
+  if (!delta || delta_bytes < need)
+    return fail(DIT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", who, delta_bytes, need);
   if (n_tokens == 0) return DIT_OK;
   if (validate_on()) {
-    if (dit_status st = validate_segments("attn_packed_backward", cu_seqlens, n_seqs, max_seqlen,
-                                          n_tokens, stream))
+    if (dit_status st = validate_segments(who, cu_seqlens, n_seqs, max_seqlen, n_tokens, stream))
       return st;
   }
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   hipError_t e = launch_attn_bwd(q, ld_q, k, ld_k, v, ld_v, o, ld_o, dout, ld_do, lse, dq, ld_dq,
                                  dk, ld_dk, dv, ld_dv, cu_seqlens, n_seqs, max_seqlen, n_tokens,
-                                 n_heads, scale, causal != 0, static_cast<float*>(workspace),
-                                 (hipStream_t)stream);
-  return e == hipSuccess ? DIT_OK : hip_fail(e, "attn_packed_backward launch");
+                                 n_heads, scale, causal != 0, delta, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : fail(DIT_EHIP, "%s launch: %s", who, hipGetErrorString(e));
+}
+}  // namespace
+
+extern "C" dit_status attn_packed_backward(
+    dit_dtype dt, const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
+    int64_t ld_v, const void* o, int64_t ld_o, const void* dout, int64_t ld_do, const float* lse,
+    void* dq, int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
+    const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
+    int32_t n_heads, int32_t head_dim, float softmax_scale, int32_t causal, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  clear_error();
+  return attn_backward_impl("attn_packed_backward", dt, q, ld_q, k, ld_k, v, ld_v, o, ld_o, dout,
+                            ld_do, lse, dq, ld_dq, dk, ld_dk, dv, ld_dv, cu_seqlens, n_seqs,
+                            max_seqlen, n_tokens, n_heads, head_dim, softmax_scale, causal,
+                            static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
+                            stream);
+}
+
+// attn_packed_backward without a workspace argument: delta lives in a fixed
+// file-scope device array (one copy per GPU, held until the process ends).
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress (on the first call with that device current) and only
+// that address is passed to the kernels.  Every call on a GPU shares that
+// GPU's array; calls that overlap on one GPU race.  Every delta value a call
+// reads it has first written, so nothing needs clearing between calls.
+constexpr size_t kNoAllocScratchFloats = (size_t)4 << 20;   // 16 MiB
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+dit_status scratch_address(const char* who, float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DIT_EHIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DIT_EUNSUPPORTED, "%s: device %d", who, dev);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DIT_EHIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return DIT_OK;
+}
+}  // namespace
+
+extern "C" size_t dit_attn_backward_noalloc_max_elements(void) { return kNoAllocScratchFloats; }
+
+extern "C" dit_status attn_packed_backward_noalloc(
+    dit_dtype dt, const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
+    int64_t ld_v, const void* o, int64_t ld_o, const void* dout, int64_t ld_do, const float* lse,
+    void* dq, int64_t ld_dq, void* dk, int64_t ld_dk, void* dv, int64_t ld_dv,
+    const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t n_tokens,
+    int32_t n_heads, int32_t head_dim, float softmax_scale, int32_t causal, void* stream) {
+  clear_error();
+  const char* who = "attn_packed_backward_noalloc";
+  if (n_tokens < 0 || n_heads < 1) return fail(DIT_EINVAL, "%s: n_tokens or n_heads", who);
+  if ((uint64_t)n_tokens * (uint64_t)n_heads > kNoAllocScratchFloats)
+    return fail(DIT_EWORKSPACE,
+                "%s: n_heads * n_tokens = %lld exceeds the fixed scratch of %zu values",
+                who, (long long)n_tokens * n_heads, kNoAllocScratchFloats);
+  float* delta = nullptr;
+  if (dit_status st = scratch_address(who, &delta)) return st;
+  return attn_backward_impl(who, dt, q, ld_q, k, ld_k, v, ld_v, o, ld_o, dout, ld_do, lse, dq,
+                            ld_dq, dk, ld_dk, dv, ld_dv, cu_seqlens, n_seqs, max_seqlen, n_tokens,
+                            n_heads, head_dim, softmax_scale, causal, delta,
+                            kNoAllocScratchFloats * sizeof(float), stream);
 }
 
 // ---------------------------------------------------------------------------
