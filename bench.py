@@ -87,19 +87,32 @@ def summarize_profile(kind: str, out_dir: str) -> int:
     Kernels are grouped by name and grid size, so launches of one kernel at
     different sizes (and the calibration copy) are reported apart."""
     if kind == "stats":
-        files = glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True)
-        if not files:
-            print(f"no kernel_trace.csv under {out_dir}", file=sys.stderr)
-            return 1
         per = {}
-        for r in csv.DictReader(open(files[0])):
-            name = r["Kernel_Name"]
-            if "dit::" not in name and "copyBuffer" not in name:
-                continue
-            key = (_short_kernel(name), int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
-                   * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1))
-            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
-            per.setdefault(key, []).append(dur)
+        files = glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True)
+        dbs = glob.glob(os.path.join(out_dir, "**", "*results.db"), recursive=True)
+        if files:
+            for r in csv.DictReader(open(files[0])):
+                name = r["Kernel_Name"]
+                if "dit::" not in name and "copyBuffer" not in name:
+                    continue
+                key = (_short_kernel(name), int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+                       * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1))
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+                per.setdefault(key, []).append(dur)
+        elif dbs:
+            # rocprofv3's default output: a rocpd SQLite database with a kernels view
+            import sqlite3
+            con = sqlite3.connect(dbs[0])
+            for name, gx, gy, gz, start, end in con.execute(
+                    "select name, grid_x, grid_y, grid_z, start, end from kernels"):
+                if "dit::" not in name and "copyBuffer" not in name:
+                    continue
+                key = (_short_kernel(name), int(gx) * int(gy) * int(gz))
+                per.setdefault(key, []).append((int(end) - int(start)) / 1e6)
+            con.close()
+        else:
+            print(f"no kernel_trace.csv or results.db under {out_dir}", file=sys.stderr)
+            return 1
         total = sum(sum(v) for v in per.values())
         print("| kernel | grid (work-items) | calls | avg ms | min ms | max ms | total % |")
         print("|---|---|---|---|---|---|---|")
@@ -922,12 +935,26 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         import oracle
+        # the whole block in the oracle on the two small workloads (no sample)
+        whole = {}
+        for label, name in (("tiny_f32", "tiny"), ("small", "small")):
+            wl_c = synth.WORKLOADS[name]
+            inp_c = synth.block_inputs(wl_c)
+            lay_c = oracle.pack_layout([r.grid for r in wl_c.requests])
+            t0 = time.perf_counter()
+            oracle.block_forward(inp_c.x, lay_c["modality"], lay_c["pos"], lay_c["cu_seqlens"],
+                                 inp_c.table, inp_c.w_qkv, inp_c.w_o, n_heads=wl_c.n_heads,
+                                 head_dim=wl_c.head_dim, sections=wl_c.sections,
+                                 theta=wl_c.theta, eps=wl_c.eps)
+            whole[label] = round((time.perf_counter() - t0) * 1e3, 1)
+        print(f"# oracle whole-block ms: {whole}", file=sys.stderr, flush=True)
         olay = oracle.pack_layout([r.grid for r in wl.requests])
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         cb = cpu_baseline(wl, inp, olay, args.cpu_rows, workers)
         cb.pop("seconds")
         cb["value"] = round(cb["value"], 6)
         cb["gpu_block_ms"] = rec["block_ms"]
+        cb["oracle_whole_block_ms"] = whole
         rec["cpu_baseline"] = cb
     print(json.dumps(rec), flush=True)
     return 0

@@ -579,8 +579,7 @@ typedef struct {
 
 /* Bytes of scratch dit_block_forward needs: five [N][D] planes y, q', k', v,
  * o (q', k', v are the fused projection's output split by column, q and k
- * rotated), each rounded up to 256 bytes, then a float [N][head_dim] table of
- * the rotation's (cos, sin) pairs.  0 for a bad descriptor. */
+ * rotated), each rounded up to 256 bytes.  0 for a bad descriptor. */
 size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
 
 /* x, out: [n_tokens][d_model] contiguous (out may equal x); modality, pos_thw,
@@ -589,8 +588,8 @@ size_t dit_block_workspace_bytes(const dit_block_desc* d, int64_t n_tokens);
  * dit_block_workspace_bytes() bytes, 256-byte aligned.  Enqueues the stages
  * of adaln_modulate -> qkv_project -> rope3d_apply -> attn_packed ->
  * out_proj_gated on stream; in bf16 the rotation of q and k is applied by the
- * QKV projection as it stores them (the same rotation, one bf16 rounding of
- * q' and k' instead of two).  On completion the workspace holds the block's
+ * QKV projection as it stores them (the same rotation with float32 angles
+ * and sines, one bf16 rounding of q' and k' instead of two).  On completion the workspace holds the block's
  * intermediates (dit_block_intermediates).  Errors: those of the stages, plus
  * DIT_EWORKSPACE. */
 dit_status dit_block_forward(const dit_block_desc* d, const void* x, void* out,

@@ -1051,23 +1051,20 @@ extern "C" dit_status dit_ffn_forward_fp8(const dit_ffn_desc* d, const void* x, 
 // ---------------------------------------------------------------------------
 
 // Block workspace: five [N][D] planes, y | q' | k' | v | o, each rounded up to
-// 256 bytes, then the rotation table [N][head_dim] float ((cos, sin) per
-// token and pair).  q, k and v are separate planes (not one [N][3D] array), so
-// the attention's K/V loads stream contiguous rows.  bf16: the QKV GEMM
-// rotates q and k in its epilogue (kind 3) with the table, built first by a
-// small kernel, and stores q', k', v straight into planes 1-3.  float32: the
-// GEMM stores q, k, v and RoPE then turns planes 1 and 2 in place.
+// 256 bytes.  q, k and v are separate planes (not one [N][3D] array), so the
+// attention's K/V loads stream contiguous rows.  bf16: the QKV GEMM rotates q
+// and k in its epilogue (kind 3, from the positions) and stores q', k', v
+// straight into planes 1-3.  float32: the GEMM stores q, k, v and RoPE then
+// turns planes 1 and 2 in place.
 namespace {
 struct BlockLayout {
-  size_t plane, table, total;
+  size_t plane, total;
 };
 BlockLayout block_layout(const dit_block_desc* d, int64_t n_tokens) {
   const size_t es = elt_size(d->dtype), n = (size_t)n_tokens, D = (size_t)d->d_model;
-  const size_t dh = d->head_dim > 0 ? (size_t)d->head_dim : 0;
   BlockLayout L;
   L.plane = round256(n * D * es);
-  L.table = 5 * L.plane;
-  L.total = L.table + round256(n * dh * 4);
+  L.total = 5 * L.plane;
   return L;
 }
 }  // namespace
@@ -1120,7 +1117,6 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   char* k = q + L.plane;
   char* v = k + L.plane;
   void* o = v + L.plane;
-  float* rope_tab = reinterpret_cast<float*>(ws + L.table);
 
   // Validate every stage before enqueuing any of them.
   if (dit_status st = adaln_check(dt, x, D, modality, ada_table, y, D, n_tokens, D, d->ln_eps))
@@ -1162,10 +1158,8 @@ extern "C" dit_status dit_block_forward(const dit_block_desc* d, const void* x, 
   // One GEMM over the fused W_qkv [3D][D], its output split into the q', k', v
   // planes; bf16 rotates q and k in the epilogue.
   if (dt == DIT_BF16) {
-    e = launch_rope_table(pos_thw, n_tokens, Dh, s_t, s_h, freq, rope_tab, s);
-    if (e != hipSuccess) return hip_fail(e, "dit_block_forward: rope table launch");
-    GemmEpilogue ep_qkv{3, b_qkv, nullptr, 0, nullptr, nullptr, D,
-                        (int64_t)(L.plane / es), rope_tab, Dh};
+    GemmEpilogue ep_qkv{3, b_qkv, nullptr, 0, nullptr, nullptr, D, (int64_t)(L.plane / es),
+                        pos_thw, freq, Dh, s_t / 2, (s_t + s_h) / 2};
     e = launch_gemm(1, y, D, w_qkv, q, D, n_tokens, 3 * D, D, ep_qkv, s);
     if (e != hipSuccess) return hip_fail(e, "dit_block_forward: qkv launch");
     mark(2);

@@ -109,11 +109,6 @@ hipError_t launch_adaln(int bf16, const void* x, int64_t ld_x, const uint8_t* mo
 // Rotates q into q_out and k into k_out (k, k_out null: q only); in place when
 // the outputs are the inputs; k_out may be q (each vector is loaded before the
 // same thread stores over it).
-// (cos, sin) of every (token, pair) of a head: tab[row][2p], tab[row][2p+1]
-// for pair p < head_dim / 2, float [n][head_dim], angles in double precision
-// exactly as launch_rope takes them (angle 0 gives exactly (1, 0)).
-hipError_t launch_rope_table(const int32_t* pos, int64_t n, int head_dim, int s_t, int s_h,
-                             const double* freq_d, float* tab, hipStream_t s);
 hipError_t launch_rope(int bf16, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
                        void* q_out, int64_t ld_qo, void* k_out, int64_t ld_ko,
                        const int32_t* pos, int64_t n, int n_heads, int head_dim,
@@ -171,9 +166,10 @@ hipError_t launch_attn_bwd(const void* q, int64_t ld_q, const void* k, int64_t l
 // j / plane_cols, column j % plane_cols, planes plane_stride elements apart
 // (row stride ldc inside a plane); plane_cols must be a multiple of 32.
 // Kind 3 (bf16 only) is kind 0 with the 3D rotary embedding applied to planes
-// 0 and 1 (q and k) before the store: rope is a float [M][rope_dh] table of
-// (cos, sin) pairs per token row (launch_rope_table), pair p of a head
-// turning columns 2p and 2p+1; plane_cols must be a multiple of rope_dh.
+// 0 and 1 (q and k) before the store: pos [M][3] (t, h, w) per row, rope_freq
+// the rope_dh / 2 pair frequencies (rope_freqs), pairs below rope_pair_h on
+// the t axis, below rope_pair_w on h, the rest on w; plane_cols and n must be
+// multiples of rope_dh (64 or 128).
 struct GemmEpilogue {
   int kind;                 // 0 plain, 1 gated residual, 2 GELU, 3 planes + RoPE
   const void* bias;         // [N] or null
@@ -183,8 +179,10 @@ struct GemmEpilogue {
   const float* gate;        // table + GATE row offset; row stride 3*N floats (kind 1)
   int plane_cols = 0;       // 0: one [M][ldc] output
   int64_t plane_stride = 0;
-  const float* rope = nullptr;   // kind 3
-  int rope_dh = 0;               // kind 3: head_dim, 64 or 128
+  const int32_t* pos = nullptr;       // kind 3
+  const double* rope_freq = nullptr;  // kind 3: [rope_dh / 2], host memory
+  int rope_dh = 0;                    // kind 3: head_dim, 64 or 128
+  int rope_pair_h = 0, rope_pair_w = 0;
 };
 hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c,
                        int64_t ldc, int64_t m, int n, int k, const GemmEpilogue& ep,

@@ -3,11 +3,16 @@
 //   gated residual: out = x + gate[m] * (o W_o^T + b)   (to_out.0, ff.net.2)
 //   GELU:           h = gelu_tanh(y W_1^T + b)   (ff.net.0.proj)
 //   planes + RoPE:  q', k', v = rotate(y W_qkv^T + b) into three planes, the
-//                   3D rotation applied to q and k from a per-token table of
-//                   (cos, sin) pairs before the single bf16 rounding
-//                   ([H3-NFT] section "MiniMax H3 and Why Joint Audio-Video
-//                   Generation Complicates RL Training": RoPE over time,
-//                   height and width)
+//                   3D rotation applied to q and k before the single bf16
+//                   rounding ([H3-NFT] section "MiniMax H3 and Why Joint
+//                   Audio-Video Generation Complicates RL Training": RoPE over
+//                   time, height and width).  Each lane holds 4 consecutive
+//                   columns of one row, i.e. 2 pairs of one head; the row's
+//                   (t, h, w) positions are loaded after the k loop, and a
+//                   pair's angle is pos * omega in turns, reduced to [-1/2, 1/2]
+//                   exactly, then sin and cos in float32 (the hardware's
+//                   turn-based sine and cosine).  A zero position leaves the
+//                   pair's bits as they are.
 // [VeRL-Omni] section 5.2 (Q, K, V packed into one matrix on the rollout
 // side); [H3-NFT] section "How VeRL-Omni's Adapter Architecture Keeps
 // H3-Specific Logic Contained" (projection names to_q, to_k, to_v, to_out.0,
@@ -33,17 +38,14 @@
 // step's closing barrier).
 // Tile order.  The hardware deals consecutive workgroups to the 8 XCDs (one
 // L2 each) round-robin, and an XCD runs about 32 of them at once (one per CU).
-//   bf16: workgroups in launch order walk groups of 4 M-tiles column by
-//   column, so each XCD sees one A panel of the group (kept in its L2) against
-//   every other B panel: 33 panel k-slices per k-step for 32 workgroups.
-//   FP8: workgroup pid = 8 j + x becomes the j-th tile of XCD x's contiguous
-//   share of a linear order in which 32 consecutive tiles form a block of
-//   4 M-tiles by 8 N-tiles, so the 32 workgroups an XCD runs together read 4 A
-//   and 8 B panels (12 slices); the last T mod 8 workgroups keep their index.
-// Measured on one box: the blocked order cuts the QKV product's L2 fills from
-// 40 to 16 GB and makes the FP8 QKV, out and up products 4-5% faster (the
-// down product 2% slower), but the bf16 products 0-2% slower, so each keeps
-// the order that is faster for it.
+// Workgroup pid = 8 j + x becomes the j-th tile of XCD x's contiguous share of
+// a linear order in which 32 consecutive tiles form a block of 4 M-tiles by 8
+// N-tiles, so the 32 workgroups an XCD runs together read 4 A and 8 B panels
+// (12 k-slices per k-step) instead of one A panel against 32 B panels (33);
+// the last T mod 8 workgroups keep their index.  Measured on one box: the
+// QKV product's L2 fills drop from 40 to 16 GB (FP8), and same-process A/B
+// times fall for bf16 QKV (7.73 -> 7.58 ms), to_out.0 (2.72 -> 2.63) and
+// ff.net.0.proj (10.52 -> 10.42) and for the FP8 products by 4-5%.
 //
 // float32 path: a plain LDS-tiled VALU kernel (the tiny float32 workload only
 // needs to be exact, not fast).
@@ -66,27 +68,21 @@ struct EpiArgs {
   int64_t gate_stride;      // floats between the gate rows of two modalities
   int plane_cols;           // kinds 0, 3: output split into planes of this many columns (0: none)
   int64_t plane_stride;     // elements between planes
-  const float* rope;        // kind 3: (cos, sin) per (row, pair), [M][rope_dh] floats
-  int rope_dh;              // kind 3: head_dim (a power of two dividing plane_cols)
+  // kinds 3 (head_dim 128) and 4 (head_dim 64): 3D RoPE on planes 0 and 1
+  const int32_t* pos;       // [M][3] (t, h, w) per row
+  int pair_h, pair_w;       // first pair of the h and of the w section
+  float rope_rev[64];       // per pair: omega / (2 pi), turns per unit of position
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// Tile of this workgroup: a bijection from workgroup ids onto the
-// tiles_m x tiles_n tiles (both orders checked exhaustively on the host for
-// the workloads' shapes and 3,000 random ones).
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int pid = blockIdx.x;
-  const int group_span = 4 * tiles_n;
-  const int group = pid / group_span;
-  const int first_m = group * 4;
-  const int gsize = min(tiles_m - first_m, 4);
-  const int in_group = pid - group * group_span;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
-}
-// The XCD-blocked order: linear index L in groups of 4 M-tiles, each walked in
-// chunks of 8 N-tiles, M fastest inside a chunk.
+// Tile of this workgroup (the XCD-blocked order above): linear index L in
+// groups of 4 M-tiles, each walked in chunks of 8 N-tiles, M fastest inside a
+// chunk.  A bijection from workgroup ids onto the tiles_m x tiles_n tiles for
+// any tile counts: pid -> L permutes the first 8 * per_xcd ids (x-major to
+// XCD-contiguous) and fixes the rest, and L -> (group, chunk, r) covers each
+// group's gsize x tiles_n tiles once, the last group and chunk partial (the
+// GPU tests' ragged shapes exercise both).
 __device__ __forceinline__ void tile_coords_xcd(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int pid = blockIdx.x;
   const int per_xcd = (tiles_m * tiles_n) / kXcds;
@@ -115,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -123,6 +119,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
+
+  constexpr bool kRope = KIND == 3 || KIND == 4;
 
   // Global -> LDS with buffer_load_dwordx4 ... lds: lane slot s = 256*i + tid
   // of a tile lands at LDS element 8*s, i.e. row s/8, physical chunk s%8.
@@ -223,6 +221,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     if (kt + 1 < nk) k_step(As0, Bs0, As1, Bs1, kt + 1, false);
   }
 
+  // RoPE (kinds 3, 4): the (t, h, w) positions of this lane's four rows, as
+  // floats (held across the k loop they would cost registers it needs).
+  float rpos[4][3];
+  // the half-wave bit again, from the lane id (kept from before the k loop it
+  // is one more register through the loop)
+  const int ge = kRope ? (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5)
+                       : 0;
+  if constexpr (kRope) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int row = min(m0 + wm * 128 + mb * 32 + l32, M - 1);
+#pragma unroll
+      for (int a = 0; a < 3; ++a) rpos[mb][a] = (float)ep.pos[3 * (int64_t)row + a];
+    }
+  }
+
   // Epilogue.  The MFMAs computed C^T: acc[mb][nb][i] is token row
   // m0 + wm*128 + mb*32 + l32 and feature column n0 + wn*128 + nb*32 +
   // (i/4)*8 + g*4 + i%4, so each lane holds runs of 4 consecutive features of
@@ -240,11 +254,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
       uint16_t* cbase = crow;
       int cshift = 0;
       bool rot = false;
-      if ((KIND == 0 || KIND == 3) && ep.plane_cols > 0) {
+      if ((KIND == 0 || kRope) && ep.plane_cols > 0) {
         const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
         cbase = crow + plane * ep.plane_stride;
         cshift = plane * ep.plane_cols;
-        rot = KIND == 3 && plane < 2;
+        rot = kRope && plane < 2;
       }
       // The block's accumulators move to VGPRs here, one 16-value block at a
       // time (left alone the compiler copies all 256 out of the AGPRs at once
@@ -274,21 +288,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
           v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
           v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
         }
-        if constexpr (KIND == 3) {
-          // the lane's 4 columns are pairs p, p+1 of one head (col - cshift
-          // and rope_dh are multiples of 4); a zero angle leaves a pair's bits
+        if constexpr (kRope) {
+          // The lane's 4 columns are pairs j0 and j0 + 1 of one head.  Plane
+          // bases and n0 are multiples of the head width, so the column in
+          // the head is (nb*32 + r*8) mod DH plus 4g: j0 is a constant plus 2g.
+          constexpr int DH = KIND == 3 ? 128 : 64;
           if (rot) {
-            const float4 cs = *reinterpret_cast<const float4*>(
-                ep.rope + (int64_t)row * ep.rope_dh + ((col - cshift) & (ep.rope_dh - 1)));
-            if (cs.y != 0.0f) {
-              const float u = v[0], w = v[1];
-              v[0] = fmaf(u, cs.x, -w * cs.y);
-              v[1] = fmaf(u, cs.y, w * cs.x);
-            }
-            if (cs.w != 0.0f) {
-              const float u = v[2], w = v[3];
-              v[2] = fmaf(u, cs.z, -w * cs.w);
-              v[3] = fmaf(u, cs.w, w * cs.z);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int ja = (((nb * 32 + r * 8) & (DH - 1)) >> 1) + t;   // g = 0
+              const int jb = ja + 2;                                       // g = 1
+              const int j = ge ? jb : ja;
+              const float turns_per_pos = ge ? ep.rope_rev[jb] : ep.rope_rev[ja];
+              const int axis = j < ep.pair_h ? 0 : (j < ep.pair_w ? 1 : 2);
+              const float p = axis == 0 ? rpos[mb][0] : (axis == 1 ? rpos[mb][1] : rpos[mb][2]);
+              if (p != 0.0f) {
+                float turns = p * turns_per_pos;
+                turns -= rintf(turns);                      // exact: |turns| < 2^23
+                const float sn = __builtin_amdgcn_sinf(turns);
+                const float cs = __builtin_amdgcn_cosf(turns);
+                const float u = v[2 * t], w = v[2 * t + 1];
+                v[2 * t] = fmaf(u, cs, -w * sn);
+                v[2 * t + 1] = fmaf(u, sn, w * cs);
+              }
             }
           }
         }
@@ -589,21 +611,31 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 hipError_t launch_gemm(int bf16, const void* a, int64_t lda, const void* b, void* c, int64_t ldc,
                        int64_t m, int n, int k, const GemmEpilogue& ep, hipStream_t s) {
   if (k % BK != 0 || m > INT32_MAX) return hipErrorInvalidValue;
+  const bool rope = ep.kind == 3;
   if (ep.plane_cols < 0 || ep.plane_cols % 32 != 0 ||
-      (ep.plane_cols > 0 && ep.kind != 0 && ep.kind != 3))
+      (ep.plane_cols > 0 && ep.kind != 0 && !rope))
     return hipErrorInvalidValue;
-  if (ep.kind == 3 && (!bf16 || !ep.rope || (ep.rope_dh != 64 && ep.rope_dh != 128) ||
-                       ep.plane_cols <= 0 || ep.plane_cols % ep.rope_dh != 0))
+  if (rope && (!bf16 || !ep.pos || !ep.rope_freq || (ep.rope_dh != 64 && ep.rope_dh != 128) ||
+               ep.plane_cols <= 0 || ep.plane_cols % ep.rope_dh != 0 || n % ep.rope_dh != 0))
     return hipErrorInvalidValue;
   // gate rows of the table are 3*N floats apart (table [3][3][N], N = d_model)
   const int64_t gate_stride = 3 * (int64_t)n;
   if (bf16) {
     const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
-              ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride, ep.rope,
-              ep.rope_dh};
-    if (ep.kind == 3)
+              ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride, ep.pos,
+              ep.rope_pair_h, ep.rope_pair_w, {}};
+    if (rope) {
+      constexpr double kTwoPi = 6.283185307179586476925;
+      for (int j = 0; j < 64; ++j)
+        e.rope_rev[j] = j < ep.rope_dh / 2 ? (float)(ep.rope_freq[j] / kTwoPi) : 0.0f;
+    }
+    if (rope && ep.rope_dh == 128)
       gemm_bf16_kernel<3><<<dim3(tiles), dim3(kThreads), 0, s>>>(
+          static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
+          static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
+    else if (rope)
+      gemm_bf16_kernel<4><<<dim3(tiles), dim3(kThreads), 0, s>>>(
           static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(b),
           static_cast<uint16_t*>(c), ldc, (int)m, n, k, e);
     else if (ep.kind == 1)
@@ -639,7 +671,8 @@ hipError_t launch_gemm_fp8(const uint8_t* a, int64_t lda, const float* sa, const
   const int64_t gate_stride = 3 * (int64_t)n;
   const int tiles = (int)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   EpiArgs e{ep.kind, static_cast<const uint16_t*>(ep.bias), static_cast<const uint16_t*>(ep.x),
-            ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride, nullptr, 0};
+            ep.ld_x, ep.mod, ep.gate, gate_stride, ep.plane_cols, ep.plane_stride, nullptr, 0, 0,
+            {}};
   EpiArgs8 e8{sa, sw};
   uint16_t* cp = static_cast<uint16_t*>(c);
   if (ep.kind == 1)

@@ -191,41 +191,7 @@ hipError_t dispatch(const RopeIO& io, const int32_t* pos, int64_t n, int n_heads
   return hipErrorInvalidValue;
 }
 
-// One thread per (token, pair): the angle and its cosine and sine in double
-// precision, rounded to float, exactly as rope_kernel computes them.
-__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ pos,
-                                                         int64_t n, int half_dh, int s_t, int s_h,
-                                                         Freqs fr, float2* __restrict__ tab) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n * half_dh) return;
-  const int64_t row = i / half_dh;
-  const int p = (int)(i - row * half_dh);
-  const int col = 2 * p;
-  const int axis = col < s_t ? 0 : (col < s_t + s_h ? 1 : 2);
-  const int32_t ps = pos[3 * row + axis];
-  float c = 1.0f, sn = 0.0f;
-  if (ps != 0) {
-    double sd, cd;
-    sincos((double)ps * fr.f[p], &sd, &cd);
-    sn = (float)sd;
-    c = (float)cd;
-  }
-  tab[i] = make_float2(c, sn);
-}
-
 }  // namespace
-
-hipError_t launch_rope_table(const int32_t* pos, int64_t n, int head_dim, int s_t, int s_h,
-                             const double* freq_d, float* tab, hipStream_t s) {
-  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
-  if (n == 0) return hipSuccess;
-  Freqs fr;
-  for (int p = 0; p < 64; ++p) fr.f[p] = p < head_dim / 2 ? freq_d[p] : 0.0;
-  const int64_t total = n * (head_dim / 2);
-  rope_table_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
-      pos, n, head_dim / 2, s_t, s_h, fr, reinterpret_cast<float2*>(tab));
-  return hipGetLastError();
-}
 
 hipError_t launch_rope(int bf16, const void* q, int64_t ld_q, const void* k, int64_t ld_k,
                        void* q_out, int64_t ld_qo, void* k_out, int64_t ld_ko,

@@ -132,8 +132,7 @@ def test_block_workspace_and_descriptor_checks():
     desc = jav.block_desc(jav.DIT_BF16, 5120, 40, 128, (32, 48, 48))
     n = 58758
     planes = 5 * (((n * 5120 * 2 + 255) // 256) * 256)    # y, q', k', v, o planes
-    table = ((n * 128 * 4 + 255) // 256) * 256             # (cos, sin) per token and pair
-    assert jav.block_workspace_bytes(desc, n) == planes + table
+    assert jav.block_workspace_bytes(desc, n) == planes
     fake = 1 << 20
     args = [fake, fake, fake, fake, fake, 1, 100, 100, fake, fake, None, fake, None]
     # workspace too small
