@@ -320,17 +320,23 @@ CONFIG_RUNS = (("tiny_f32", "tiny", False), ("small", "small", False), ("medium"
                ("varlen_bidirectional", "varlen", False), ("varlen_causal", "varlen", True))
 
 
-def _timed(torch, fn, reps, stream):
+def _timed(torch, fn, reps, stream, batches=3):
+    """ms per call: one untimed call, then the median over `batches` timed batches
+    of `reps` calls (a single batch also catches the clock's ramp after a change
+    of kernel)."""
     fn()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    per = []
+    for _ in range(batches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    return sorted(per)[len(per) // 2]
 
 
 def measure_workload(jav, torch, name, causal, stream, reps=10):
@@ -502,7 +508,8 @@ def main() -> int:
 
     # Each stage again on its own (fresh buffers, same inputs), so its rate can be
     # read apart from its neighbours in the block (the block's stage times include
-    # the event brackets and the power state the previous kernel left behind).
+    # the event brackets and the power state the previous kernel left behind):
+    # the median of three timed batches.
     print("# isolated stages ...", file=sys.stderr, flush=True)
     # q, k, v as three [N][D] planes, the layout dit_block_forward's workspace uses
     y = torch.empty_like(x)
@@ -529,16 +536,7 @@ def main() -> int:
     }
     iso_ms = {}
     for name, (reps, fn) in iso_ops.items():
-        fn()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        iso_ms[name] = e0.elapsed_time(e1) / reps
+        iso_ms[name] = _timed(torch, fn, reps, stream)
     del y, qkv, planes, spare, o, q_v, k_v, v_v
     print(f"# isolated: {iso_ms}", file=sys.stderr, flush=True)
 

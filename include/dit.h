@@ -54,7 +54,11 @@
  *   environment, the entry points that take cu_seqlens or modality ids
  *   (attention, AdaLN, the block and feed-forward halves, their FP8 and
  *   backward forms) first copy those arrays to the host on the call's stream,
- *   synchronously, and return DIT_EINVAL if they break the contract.
+ *   synchronously, and return DIT_EINVAL if they break the contract.  Without
+ *   it, the attention kernels (bf16, FP8, backward) still guard one breach
+ *   on the device: a segment longer than max_seqlen (which their grids and
+ *   32-bit buffer ranges are sized from) gets NaN in its output rows (and its
+ *   log-sum-exps) inside [0, n_tokens) instead of partly unwritten ones.
  */
 #ifndef DIT_H
 #define DIT_H

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
     const uint16_t* __restrict__ v, int64_t ld_v, uint16_t* __restrict__ o, int64_t ld_o,
     const int32_t* __restrict__ cu, float scale_log2, int causal, float* __restrict__ lse,
-    int64_t ld_lse) {
+    int64_t ld_lse, int max_seqlen, int64_t n_tokens) {
   // Two LDS buffers per tensor as distinct objects: with the key loop unrolled
   // by two, every access names its buffer at compile time, so the compiler can
   // tell the prefetch into one buffer from the reads of the other and does not
@@ -121,6 +121,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
+  if (seg1 - seg0 > max_seqlen) {
+    // cu_seqlens breaks its contract (a segment longer than max_seqlen): the
+    // grid does not cover the segment and its byte span may pass the buffer
+    // range's 4 GiB, so its rows of this head become NaN (and its lse).
+    poison_rows_bf16(o, ld_o, h * DH, DH, seg0, seg1, n_tokens, blockIdx.x, gridDim.x);
+    if (lse != nullptr)
+      for (int64_t r = (int64_t)seg0 + blockIdx.x * kAttnThreads + threadIdx.x;
+           r < seg1 && r < n_tokens; r += (int64_t)gridDim.x * kAttnThreads)
+        if (r >= 0) lse[(int64_t)h * ld_lse + r] = __builtin_nanf("");
+    return;
+  }
   const int nqt = (seg1 - seg0 + QBLK - 1) / QBLK;
   if ((int)blockIdx.x >= nqt) return;
   const int qt = causal ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;
@@ -439,7 +450,7 @@ hipError_t launch_attn(int bf16, const void* q, int64_t ld_q, const void* k, int
     attn_bf16_kernel<<<grid, dim3(kAttnThreads), 0, s>>>(
         static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
         static_cast<const uint16_t*>(v), ld_v, static_cast<uint16_t*>(o), ld_o, cu,
-        scale * 1.4426950408889634f, causal, lse, n_tokens);
+        scale * 1.4426950408889634f, causal, lse, n_tokens, max_seqlen, n_tokens);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)n_tokens, n_heads);

@@ -185,7 +185,8 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
     int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, int64_t ld_dk, uint16_t* __restrict__ dv, int64_t ld_dv,
-    const int32_t* __restrict__ cu, int64_t n, float scale, float scale_log2, int causal) {
+    const int32_t* __restrict__ cu, int64_t n, float scale, float scale_log2, int causal,
+    int max_seqlen) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs0[TB * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Qs1[TB * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Ds0[TB * DH];
@@ -195,6 +196,13 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
+  if (seg1 - seg0 > max_seqlen) {
+    // a segment longer than max_seqlen (cu_seqlens breaks its contract): the
+    // grid does not cover it; its dk and dv rows of this head become NaN
+    poison_rows_bf16(dk, ld_dk, h * DH, DH, seg0, seg1, n, blockIdx.x, gridDim.x);
+    poison_rows_bf16(dv, ld_dv, h * DH, DH, seg0, seg1, n, blockIdx.x, gridDim.x);
+    return;
+  }
   const int kb0 = seg0 + (int)blockIdx.x * BLKKV;
   if (kb0 >= seg1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ v, int64_t ld_v, const uint16_t* __restrict__ dout,
     int64_t ld_do, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int64_t ld_dq, const int32_t* __restrict__ cu, int64_t n,
-    float scale, float scale_log2, int causal) {
+    float scale, float scale_log2, int causal, int max_seqlen) {
   // Key and value tiles, three buffers each as distinct objects (the main loop
   // is unrolled by three, so every access names its buffer at compile time and
   // the compiler can tell a prefetch from the reads of another buffer).
@@ -346,6 +354,11 @@ __global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
+  if (seg1 - seg0 > max_seqlen) {
+    // as in the key kernel: the segment's dq rows of this head become NaN
+    poison_rows_bf16(dq, ld_dq, h * DH, DH, seg0, seg1, n, blockIdx.x, gridDim.x);
+    return;
+  }
   const int q0 = seg0 + (int)blockIdx.x * BLKQ;
   if (q0 >= seg1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -498,12 +511,12 @@ hipError_t launch_attn_bwd(const void* q, int64_t ld_q, const void* k, int64_t l
       static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
       static_cast<const uint16_t*>(v), ld_v, static_cast<const uint16_t*>(dout), ld_do, lse, delta,
       static_cast<uint16_t*>(dk), ld_dk, static_cast<uint16_t*>(dv), ld_dv, cu, n_tokens, scale,
-      sl2, causal);
+      sl2, causal, max_seqlen);
   const dim3 grid_q((max_seqlen + BLKQ - 1) / BLKQ, n_seqs, n_heads);
   attn_bwd_dq_kernel<<<grid_q, dim3(kThreadsQ), 0, s>>>(
       static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k), ld_k,
       static_cast<const uint16_t*>(v), ld_v, static_cast<const uint16_t*>(dout), ld_do, lse, delta,
-      static_cast<uint16_t*>(dq), ld_dq, cu, n_tokens, scale, sl2, causal);
+      static_cast<uint16_t*>(dq), ld_dq, cu, n_tokens, scale, sl2, causal, max_seqlen);
   return hipGetLastError();
 }
 

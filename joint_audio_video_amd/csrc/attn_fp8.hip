@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
     const uint8_t* __restrict__ k8, int64_t ld_k8, const float* __restrict__ sk,
     const uint8_t* __restrict__ vt, int64_t ld_vt, const float* __restrict__ sv,
     uint16_t* __restrict__ o, int64_t ld_o, const int32_t* __restrict__ cu, float scale_log2,
-    int causal) {
+    int causal, int max_seqlen, int64_t n_tokens) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks0[KB * DH];
   __shared__ __attribute__((aligned(16))) uint8_t Ks1[KB * DH];
   __shared__ __attribute__((aligned(16))) uint8_t Vs0[DH * KB];
@@ -218,6 +218,12 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
 
   const int h = blockIdx.z, seq = blockIdx.y;
   const int seg0 = cu[seq], seg1 = cu[seq + 1];
+  if (seg1 - seg0 > max_seqlen) {
+    // a segment longer than max_seqlen (cu_seqlens breaks its contract): the
+    // grid and the operand preparation do not cover it; its rows become NaN
+    poison_rows_bf16(o, ld_o, h * DH, DH, seg0, seg1, n_tokens, blockIdx.x, gridDim.x);
+    return;
+  }
   const int nqt = (seg1 - seg0 + QBLK - 1) / QBLK;
   if ((int)blockIdx.x >= nqt) return;
   const int qt = causal ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;
@@ -515,7 +521,7 @@ hipError_t launch_attn_fp8(const AttnFp8Ops& ops, uint16_t* o, int64_t ld_o, con
   const dim3 grid((max_seqlen + QBLK - 1) / QBLK, n_seqs, n_heads);
   attn_fp8_kernel<<<grid, dim3(kThreads), 0, s>>>(
       ops.q8, ops.ld8, ops.sq, n_tokens, ops.k8, ops.ld8, ops.sk, ops.vt, ops.ld_vt, ops.sv, o,
-      ld_o, cu, scale * 1.4426950408889634f, causal);
+      ld_o, cu, scale * 1.4426950408889634f, causal, max_seqlen, n_tokens);
   return hipGetLastError();
 }
 

@@ -96,6 +96,25 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float f0, float f1, float f2, flo
   return u;
 }
 
+// Rows [r0, r1) of a bf16 [n_rows][ld] array, columns [col0, col0 + ncols)
+// (ncols a multiple of 8, 16-byte aligned), set to NaN, clamped to
+// [0, n_rows): the workgroups part = 0 .. parts-1 of one launch share the rows.
+// The attention kernels' answer to a segment longer than the max_seqlen their
+// grid was sized for: its rows become NaN instead of being left unwritten.
+__device__ __forceinline__ void poison_rows_bf16(uint16_t* a, int64_t ld, int col0, int ncols,
+                                                 int64_t r0, int64_t r1, int64_t n_rows,
+                                                 int part, int parts) {
+  const int64_t lo = r0 < 0 ? 0 : r0, hi = r1 > n_rows ? n_rows : r1;
+  const int vpr = ncols / 8;
+  const uint4 nan4 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+  for (int64_t i = (int64_t)part * blockDim.x + threadIdx.x; lo + i / vpr < hi;
+       i += (int64_t)parts * blockDim.x) {
+    const int64_t row = lo + i / vpr;
+    const int c = (int)(i % vpr);
+    *reinterpret_cast<uint4*>(a + row * ld + col0 + 8 * c) = nan4;
+  }
+}
+
 }  // namespace dit
 
 // Launchers implemented in the .hip files; all return hipGetLastError() of the launch.

@@ -406,3 +406,20 @@ def test_backward_workspaces_poisoned_with_nan(jav):
     for key in ("dx", "dtable", "dw1", "dw2", "db1", "db2"):
         assert torch.isfinite(outs[1][1][key].float()).all(), key
         assert torch.equal(outs[0][1][key], outs[1][1][key]), key
+
+
+def test_backward_segment_longer_than_max_seqlen_becomes_nan(jav):
+    """cu_seqlens breaking its contract (a 400-row segment against max_seqlen 300,
+    inside the buffers): that segment's dq, dk and dv rows come out NaN, and the
+    other segment's gradients are bit-identical to a call with the right max_seqlen."""
+    import torch
+    n, H = 700, 2
+    q, k, v, do = (dev(a, "bf16") for a in _qkvo(n, H, 1400))
+    cu_d = dev_int(np.array([0, 300, 700], np.int32), torch.int32)
+    o, lse = jav.attn_packed_lse(q, k, v, cu_d, 400, H, 128)
+    good = jav.attn_packed_backward(q, k, v, o, do, lse, cu_d, 400, H, 128)
+    bad = jav.attn_packed_backward(q, k, v, o, do, lse, cu_d, 300, H, 128)
+    _sync()
+    for name, g, b in zip(("dq", "dk", "dv"), good, bad):
+        assert torch.equal(b[:300].view(torch.int16), g[:300].view(torch.int16)), name
+        assert torch.isnan(b[300:].float()).all(), name

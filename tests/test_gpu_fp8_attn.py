@@ -249,3 +249,22 @@ def test_fp8_attention_validate_env_rejects_broken_cu_seqlens(jav):
             os.environ.pop("DIT_VALIDATE", None)
         else:
             os.environ["DIT_VALIDATE"] = old
+
+
+def test_fp8_attention_segment_longer_than_max_seqlen_becomes_nan(jav):
+    """cu_seqlens breaking its contract (a 400-row segment against max_seqlen 300,
+    inside the buffers): the operand preparation and the attention do not cover that
+    segment, and its output rows come out NaN; the other segment is bit-identical to
+    a call with the right max_seqlen."""
+    import torch
+    n, H = 700, 2
+    q, k, v = (dev(synth.normal_array((n, H * 128), seed=270 + i, dtype="bf16"), "bf16")
+               for i in range(3))
+    cu_d = dev_int(np.array([0, 300, 700], np.int32), torch.int32)
+    ws = jav.attn_fp8_prepare(q, k, v, cu_d, 400, H)
+    good = jav.attn_packed_fp8(ws, cu_d, 400, n, H)
+    ws_bad = jav.attn_fp8_prepare(q, k, v, cu_d, 300, H)
+    bad = jav.attn_packed_fp8(ws_bad, cu_d, 300, n, H)
+    _sync()
+    assert torch.equal(bad[:300].view(torch.int16), good[:300].view(torch.int16))
+    assert torch.isnan(bad[300:].float()).all()

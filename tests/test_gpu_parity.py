@@ -604,3 +604,25 @@ def test_validate_env_rejects_broken_device_arrays(jav):
             os.environ.pop("DIT_VALIDATE", None)
         else:
             os.environ["DIT_VALIDATE"] = old
+
+
+def test_segment_longer_than_max_seqlen_becomes_nan(jav):
+    """cu_seqlens breaking its contract (the second segment, 400 rows, is longer than
+    the max_seqlen of 300 the grid is sized for; the rows lie inside the buffers, so
+    the call is memory-safe): that segment's output rows and log-sum-exps come out NaN
+    instead of partly unwritten, and the first segment is bit-identical to a call
+    with the right max_seqlen."""
+    import torch
+    n, H = 700, 2
+    cu = [0, 300, 700]
+    q, k, v = (dev(synth.normal_array((n, H * 128), seed=260 + i, dtype="bf16"), "bf16")
+               for i in range(3))
+    cu_d = dev_int(np.array(cu, np.int32), torch.int32)
+    good, lse_good = jav.attn_packed_lse(q, k, v, cu_d, 400, H, 128)
+    bad = torch.zeros_like(good)
+    bad, lse_bad = jav.attn_packed_lse(q, k, v, cu_d, 300, H, 128, out=bad)
+    _sync()
+    assert torch.equal(bad[:300].view(torch.int16), good[:300].view(torch.int16))
+    assert torch.isnan(bad[300:].float()).all()
+    assert torch.equal(lse_bad[:, :300], lse_good[:, :300])
+    assert torch.isnan(lse_bad[:, 300:]).all()
