@@ -421,8 +421,10 @@ dit_status linear_fp8(const uint8_t* a, int64_t ld_a, const float* a_scales, con
 /* The attention of attn_packed ([vLLM-Omni] section 3: softmax inside each
  * cu_seqlens segment, full or causal) with both products in FP8 (section 5:
  * the active layers in FP8; no recipe on the pages).  Here: q is quantized
- * per (token, head) row, k and v with one scale per head (amax / 448 over all
- * n_tokens rows of that head), codes and scales as quantize_rows_fp8.  Scores
+ * per (token, head) row, k and v with one scale per (segment, head) (amax /
+ * 448 over the segment's rows of that head, 1 for an empty segment: a
+ * request's codes do not depend on the other requests of its pack), codes and
+ * scales as quantize_rows_fp8.  Scores
  * and the softmax are float32; the probabilities enter the second product as
  * e4m3 codes of 2^8 times their value relative to the row's running maximum
  * (at most 2^8.75), o is float32 until its bf16 store.  Against attention of
@@ -434,8 +436,8 @@ dit_status linear_fp8(const uint8_t* a, int64_t ld_a, const float* a_scales, con
 /* Bytes of the operand workspace for n_tokens, n_seqs segments and n_heads:
  * q and k codes (n_tokens x n_heads x 128 bytes each), v codes transposed
  * (n_heads x 128 rows of ld_vt = roundup64(n_tokens) + 128 n_seqs bytes),
- * n_heads x n_tokens q scales, per-head k and v scales and 2 x n_heads words
- * of scratch, each part rounded up to 256.  0 for bad sizes or a head_dim
+ * n_heads x n_tokens q scales, n_seqs x n_heads k and v scales and 2 x n_seqs
+ * x n_heads words of scratch, each part rounded up to 256.  0 for bad sizes or a head_dim
  * other than 128. */
 size_t dit_attn_fp8_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads,
                                     int32_t head_dim);
@@ -445,7 +447,7 @@ size_t dit_attn_fp8_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_
  * vt e4m3 codes [n_heads * 128][ld_vt] (row h * 128 + d; segment s's key r at
  * column roundup64(cu_seqlens[s]) + 128 s + r, zero codes up to the segment's
  * next multiple of 64), sq float32 [n_heads][n_tokens], sk and sv float32
- * [n_heads].  Errors: DIT_EINVAL for a null out or bad sizes,
+ * [n_seqs][n_heads].  Errors: DIT_EINVAL for a null out or bad sizes,
  * DIT_EUNSUPPORTED for head_dim != 128. */
 dit_status dit_attn_fp8_layout(int64_t n_tokens, int32_t n_seqs, int32_t n_heads,
                                int32_t head_dim, int64_t* out);
@@ -456,7 +458,7 @@ dit_status dit_attn_fp8_layout(int64_t n_tokens, int32_t n_seqs, int32_t n_heads
  * cu_seqlens int32 [n_seqs + 1] (device), as attn_packed.  Errors: DIT_EINVAL
  * for a null pointer, n_seqs / n_heads < 1, an ld below n_heads * head_dim,
  * max_seqlen < 1 or above n_tokens; DIT_EUNSUPPORTED for head_dim != 128,
- * more than 65535 segments or heads, n_tokens * n_heads above 2^27, a
+ * more than 65535 segments or 32767 heads, n_tokens * n_heads above 2^27, a
  * segment's k codes spanning 2 GiB, or a pointer / ld off the 16-byte rule;
  * DIT_EWORKSPACE for a missing or short workspace; DIT_EHIP on a launch
  * failure. */

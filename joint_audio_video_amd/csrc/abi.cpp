@@ -509,9 +509,9 @@ Fp8AttnLayout fp8_attn_layout(int64_t n, int32_t n_seqs, int32_t h) {
   L.k8 = off;   off += round256((size_t)n * (size_t)L.ld8);
   L.vt = off;   off += round256((size_t)h * 128 * (size_t)L.ld_vt);
   L.sq = off;   off += round256((size_t)h * (size_t)n * 4);
-  L.sk = off;   off += round256((size_t)h * 4);
-  L.sv = off;   off += round256((size_t)h * 4);
-  L.amax = off; off += round256((size_t)h * 8);
+  L.sk = off;   off += round256((size_t)n_seqs * h * 4);     // [segment][head]
+  L.sv = off;   off += round256((size_t)n_seqs * h * 4);
+  L.amax = off; off += round256((size_t)n_seqs * h * 8);
   L.total = off;
   return L;
 }
@@ -563,8 +563,8 @@ static dit_status fp8_attn_check(const char* who, const int32_t* cu, int32_t n_s
   if (n_tokens > 0 && max_seqlen < 1) return fail(DIT_EINVAL, "%s: max_seqlen < 1", who);
   if (max_seqlen > n_tokens && n_tokens > 0)
     return fail(DIT_EINVAL, "%s: max_seqlen %d > n_tokens", who, max_seqlen);
-  if (n_seqs > 65535 || n_heads > 65535)
-    return fail(DIT_EUNSUPPORTED, "%s: more than 65535 segments or heads", who);
+  if (n_seqs > 65535 || n_heads > 32767)
+    return fail(DIT_EUNSUPPORTED, "%s: more than 65535 segments or 32767 heads", who);
   if ((double)n_tokens * (double)n_heads * 16.0 > 2147483647.0)
     return fail(DIT_EUNSUPPORTED, "%s: n_tokens * n_heads too large", who);
   if ((double)max_seqlen * (double)n_heads * 128.0 >= 2147483648.0)

@@ -3,20 +3,21 @@
 // [vLLM-Omni] section 5 ("Distributed Layerwise Offload") runs the active DiT
 // layers in FP8 and gives no scaling recipe; the attention of [vLLM-Omni]
 // section 3 (cu_seqlens segments, full or causal) is the operation.  Reading:
-// q carries one float32 scale per (token, head) row, k and v one per head
-// (amax / 448 over every packed token of the head), so every scale factors
-// out of its product: q's and k's out of s = q k^T, v's out of o = P v (a sum
-// over keys).  Scores, softmax and the output stay float32; the probabilities
+// q carries one float32 scale per (token, head) row, k and v one per
+// (segment, head) (amax / 448 over the segment's tokens of the head; the
+// requests of a pack are independent, so one request's codes do not depend on
+// the others'), so every scale factors out of its product: q's and k's out of
+// s = q k^T, v's out of o = P v (a sum over one segment's keys).  Scores, softmax and the output stay float32; the probabilities
 // enter the second product as e4m3 codes of 2^8 times their value relative to
 // the row's running maximum (at most 2^8.75 < 448, so no code saturates).
 //
 // Operand preparation (four small launches, all HBM-bound):
-//   * head_amax_kernel: amax |k| and |v| per head (a block max, then one
-//     vector atomic max per block on the float bits, which order like
-//     unsigned integers for non-negative values).
-//   * head_scale_kernel: the per-head scales amax / 448 (1 for zero).
-//   * quant_qk_kernel: q codes with per-row scales, k codes with the head
-//     scale; sixteen lanes per (token, head) row.
+//   * seg_amax_kernel: amax |k| and |v| per (segment, head) (a block max over
+//     256 of the segment's rows, then one vector atomic max per block on the
+//     float bits, which order like unsigned integers for non-negative values).
+//   * seg_scale_kernel: the scales amax / 448 (1 for zero).
+//   * quant_qk_kernel: q codes with per-row scales, k codes with the scale of
+//     the row's segment; sixteen lanes per (token, head) row.
 //   * quant_vt_kernel: v codes transposed to [head][d][key] through LDS, so
 //     that a V^T fragment is a plain row read.  Segment s occupies columns
 //     from vt_col0 = roundup64(cu[s]) + 128 s (aligned; the tile ends and the
@@ -77,22 +78,26 @@ __global__ void zero_u32_kernel(uint32_t* __restrict__ p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-// amax[z * n_heads + h] = max |x| over the head's columns of rows
-// [256 bx, 256 bx + 256), combined over blocks; z = 0: k, 1: v.
-__global__ __launch_bounds__(256) void head_amax_kernel(const uint16_t* __restrict__ k,
-                                                        int64_t ld_k,
-                                                        const uint16_t* __restrict__ v,
-                                                        int64_t ld_v, int64_t n, int n_heads,
-                                                        uint32_t* __restrict__ amax) {
-  const int h = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
+// amax[(z * n_seqs + s) * n_heads + h] = max |x| over the head's columns of
+// segment s's rows [seg0 + 256 bx, +256), combined over blocks; blockIdx.y = s,
+// blockIdx.z = 2 h + z with z = 0: k, 1: v.
+__global__ __launch_bounds__(256) void seg_amax_kernel(const uint16_t* __restrict__ k,
+                                                       int64_t ld_k,
+                                                       const uint16_t* __restrict__ v,
+                                                       int64_t ld_v, const int32_t* __restrict__ cu,
+                                                       int n_seqs, int n_heads,
+                                                       uint32_t* __restrict__ amax) {
+  const int s = blockIdx.y, h = blockIdx.z >> 1, z = blockIdx.z & 1, tid = threadIdx.x;
+  const int seg0 = cu[s], seg1 = cu[s + 1];
+  const int64_t r0 = (int64_t)seg0 + (int64_t)blockIdx.x * 256;
+  if (r0 >= seg1) return;
   const uint16_t* src = z ? v : k;
   const int64_t ld = z ? ld_v : ld_k;
-  const int64_t r0 = (int64_t)blockIdx.x * 256;
   float m = 0.0f;
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + 16 * i + (tid >> 4);
-    if (r < n) {
+    if (r < seg1) {
       const uint4 w = ld_stream(src + r * ld + h * DH + 8 * (tid & 15));
       m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16lo(w.x)), fabsf(bf16hi(w.x))),
                          fmaxf(fabsf(bf16lo(w.y)), fabsf(bf16hi(w.y)))));
@@ -106,26 +111,29 @@ __global__ __launch_bounds__(256) void head_amax_kernel(const uint16_t* __restri
   __syncthreads();
   if (tid == 0) {
     const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    atomicMax(amax + z * n_heads + h, __float_as_uint(a));
+    atomicMax(amax + ((int64_t)z * n_seqs + s) * n_heads + h, __float_as_uint(a));
   }
 }
 
-__global__ void head_scale_kernel(const uint32_t* __restrict__ amax, float* __restrict__ sk,
-                                  float* __restrict__ sv, int n_heads) {
+// sk[s * n_heads + h], sv[...] = amax / 448 (1 for zero) of k's and v's blocks.
+__global__ void seg_scale_kernel(const uint32_t* __restrict__ amax, float* __restrict__ sk,
+                                 float* __restrict__ sv, int count) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= 2 * n_heads) return;
+  if (i >= 2 * count) return;
   const float a = __uint_as_float(amax[i]);
   const float s = a > 0.0f ? a / 448.0f : 1.0f;
-  if (i < n_heads) sk[i] = s;
-  else sv[i - n_heads] = s;
+  if (i < count) sk[i] = s;
+  else sv[i - count] = s;
 }
 
 // Row (token, head) = 16 lanes x 8 values.  blockIdx.y = 0: q (own scale,
-// written to sq[h][token]), 1: k (the head's scale).
+// written to sq[h][token]), 1: k (the scale of the token's segment, the last
+// s with cu[s] <= token).
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
-    int n, int n_heads, const float* __restrict__ sk, uint8_t* __restrict__ q8,
-    uint8_t* __restrict__ k8, int64_t ld8, float* __restrict__ sq) {
+    int n, int n_heads, const int32_t* __restrict__ cu, int n_seqs,
+    const float* __restrict__ sk, uint8_t* __restrict__ q8, uint8_t* __restrict__ k8,
+    int64_t ld8, float* __restrict__ sq) {
   const int row = (int)(((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4);
   const int c = threadIdx.x & 15;
   const bool live = row < n * n_heads;      // the same for the 16 lanes of a row
@@ -152,7 +160,13 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
     inv = 1.0f / sc;
     if (live && c == 0) sq[(int64_t)h * n + tok] = sc;
   } else {
-    inv = 1.0f / sk[h];
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= tok) lo = mid;
+      else hi = mid - 1;
+    }
+    inv = 1.0f / sk[lo * n_heads + h];
   }
   if (live) {
     const uint2 w = make_uint2(e4m3_pack4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv),
@@ -162,8 +176,8 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
 }
 
 // One 64-key tile of segment blockIdx.y, head blockIdx.z: codes with the
-// head's scale, written transposed (d rows of 64 key bytes); keys past the
-// segment end are zero codes.
+// (segment, head) scale, written transposed (d rows of 64 key bytes); keys
+// past the segment end are zero codes.
 __global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restrict__ v,
                                                        int64_t ld_v,
                                                        const int32_t* __restrict__ cu,
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restric
   const int j = blockIdx.x, s = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
   const int seg0 = cu[s], seg1 = cu[s + 1];
   if (j * KB >= seg1 - seg0) return;
-  const float inv = 1.0f / sv[h];
+  const float inv = 1.0f / sv[s * gridDim.z + h];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int cidx = tid + 256 * i;         // key row cidx / 16, d chunk cidx % 16
@@ -250,8 +264,9 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
   }
   // S^T holds code products; times q's row scale, k's head scale and the
   // softmax scale (log2 units) it is the exponent.  One factor per lane.
-  const float cq = scale_log2 * (qlive ? sq[(int64_t)h * ld_sq + qrow] : 1.0f) * sk[h];
-  const float vscale = sv[h];
+  const int sh = seq * (int)gridDim.z + h;     // this (segment, head)'s k and v scales
+  const float cq = scale_log2 * (qlive ? sq[(int64_t)h * ld_sq + qrow] : 1.0f) * sk[sh];
+  const float vscale = sv[sh];
 
   const int kend = causal ? min(seg1, q0 + QBLK) : seg1;
   const int nkt = (kend - seg0 + KB - 1) / KB;
@@ -497,17 +512,18 @@ hipError_t launch_attn_fp8_prepare(const uint16_t* q, int64_t ld_q, const uint16
                                    int64_t n_tokens, int n_heads, const AttnFp8Ops& ops,
                                    hipStream_t s) {
   if (n_tokens <= 0) return hipSuccess;
-  if (n_tokens * n_heads > INT32_MAX / 16 || n_seqs > 65535 || n_heads > 65535)
+  if (n_tokens * n_heads > INT32_MAX / 16 || n_seqs > 65535 || n_heads > 32767 ||
+      (int64_t)n_seqs * n_heads > INT32_MAX / 2)
     return hipErrorInvalidValue;
   const int n = (int)n_tokens;
-  const int nh2 = 2 * n_heads;
-  zero_u32_kernel<<<(nh2 + 255) / 256, 256, 0, s>>>(ops.amax, nh2);
-  head_amax_kernel<<<dim3((unsigned)((n + 255) / 256), n_heads, 2), 256, 0, s>>>(
-      k, ld_k, v, ld_v, n_tokens, n_heads, ops.amax);
-  head_scale_kernel<<<(nh2 + 255) / 256, 256, 0, s>>>(ops.amax, ops.sk, ops.sv, n_heads);
+  const int count = n_seqs * n_heads;
+  zero_u32_kernel<<<(2 * count + 255) / 256, 256, 0, s>>>(ops.amax, 2 * count);
+  seg_amax_kernel<<<dim3((unsigned)((max_seqlen + 255) / 256), n_seqs, 2 * n_heads), 256, 0, s>>>(
+      k, ld_k, v, ld_v, cu, n_seqs, n_heads, ops.amax);
+  seg_scale_kernel<<<(2 * count + 255) / 256, 256, 0, s>>>(ops.amax, ops.sk, ops.sv, count);
   const int64_t rows = n_tokens * n_heads;
   quant_qk_kernel<<<dim3((unsigned)((rows + 15) / 16), 2), 256, 0, s>>>(
-      q, ld_q, k, ld_k, n, n_heads, ops.sk, ops.q8, ops.k8, ops.ld8, ops.sq);
+      q, ld_q, k, ld_k, n, n_heads, cu, n_seqs, ops.sk, ops.q8, ops.k8, ops.ld8, ops.sq);
   quant_vt_kernel<<<dim3((unsigned)((max_seqlen + KB - 1) / KB), n_seqs, n_heads), 256, 0, s>>>(
       v, ld_v, cu, ops.sv, ops.vt, ops.ld_vt);
   return hipGetLastError();

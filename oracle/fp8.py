@@ -26,9 +26,11 @@ layers in FP8; the pages give no scaling recipe.  Readings:
   row from its float32 value; rotary embedding, attention, the activation
   and the gated residual stay in the plain oracle's float64 arithmetic.
 * FP8 attention (the softmax products in FP8): q is quantized per (token,
-  head) row as above; k and v with one scale per head, amax / 448 over every
-  packed token of that head (one scale factors out of both products: out of
-  s = q k^T for k, out of o = P v for v, whose sum runs over keys).  The
+  head) row as above; k and v with one scale per (segment, head), amax / 448
+  over the segment's tokens of that head (one scale factors out of both
+  products: out of s = q k^T for k, out of o = P v for v, whose sum runs over
+  the keys of one segment; a request's operands do not depend on the other
+  requests of its pack).  The
   scores and o = softmax(s) v are then evaluated here in float64 from the
   dequantized operands with exact probabilities; the GPU also rounds the
   probabilities to e4m3 (2^8 times their value relative to a running row
@@ -214,33 +216,51 @@ def quantize_tensor(x):
     return codes.reshape(x32.shape), np.float32(s[0])
 
 
-def attention_fp8_operands(q, k, v, n_heads: int, head_dim: int) -> Dict[str, np.ndarray]:
+def attention_fp8_operands(q, k, v, n_heads: int, head_dim: int,
+                           cu_seqlens=None) -> Dict[str, np.ndarray]:
     """Codes and scales of the FP8 attention operands (q, k, v: [N][H*Dh]):
     q_codes [N][H*Dh] with q_scales [N][H] (one per token and head), k_codes /
-    v_codes [N][H*Dh] with k_scales / v_scales [H] (one per head)."""
+    v_codes [N][H*Dh] with k_scales / v_scales [S][H], one per (cu_seqlens
+    segment, head), the segment's rows of the head quantized as one tensor
+    (quantize_tensor; an empty segment keeps scale 1).  Reading: the requests
+    of a pack are independent ([vLLM-Omni] section 3: every sub-sequence
+    normalises over its own keys only), so a request's quantization depends on
+    its own values, not on what else was packed with it.  Without cu_seqlens
+    the rows form one segment.  The dict also carries the segments."""
     q = np.asarray(q, dtype=np.float32)
     n = q.shape[0]
+    cu = [0, n] if cu_seqlens is None else [int(c) for c in cu_seqlens]
     qc, qs = quantize_rows(q.reshape(n * n_heads, head_dim))
-    out = dict(q_codes=qc.reshape(n, n_heads * head_dim), q_scales=qs.reshape(n, n_heads))
+    out = dict(q_codes=qc.reshape(n, n_heads * head_dim), q_scales=qs.reshape(n, n_heads),
+               cu_seqlens=np.asarray(cu, dtype=np.int64))
     for name, t in (("k", k), ("v", v)):
         t = np.asarray(t, dtype=np.float32)
-        codes = np.empty(t.shape, dtype=np.uint8)
-        scales = np.empty(n_heads, dtype=np.float32)
-        for h in range(n_heads):
-            cols = slice(h * head_dim, (h + 1) * head_dim)
-            codes[:, cols], scales[h] = quantize_tensor(t[:, cols])
+        codes = np.zeros(t.shape, dtype=np.uint8)
+        scales = np.ones((len(cu) - 1, n_heads), dtype=np.float32)
+        for s, (a, b) in enumerate(zip(cu, cu[1:])):
+            if b <= a:
+                continue
+            for h in range(n_heads):
+                cols = slice(h * head_dim, (h + 1) * head_dim)
+                codes[a:b, cols], scales[s, h] = quantize_tensor(t[a:b, cols])
         out[name + "_codes"], out[name + "_scales"] = codes, scales
     return out
 
 
 def dequantize_attention_operands(ops: Dict[str, np.ndarray], n_heads: int, head_dim: int):
-    """float64 q, k, v [N][H*Dh] from attention_fp8_operands' codes and scales."""
+    """float64 q, k, v [N][H*Dh] from attention_fp8_operands' codes and scales
+    (k's and v's scale taken from each row's segment)."""
     tab = e4m3_table()
     qs = np.repeat(np.asarray(ops["q_scales"], np.float64), head_dim, axis=1)
     q = tab[ops["q_codes"]] * qs
-    k = tab[ops["k_codes"]] * np.repeat(np.asarray(ops["k_scales"], np.float64), head_dim)[None, :]
-    v = tab[ops["v_codes"]] * np.repeat(np.asarray(ops["v_scales"], np.float64), head_dim)[None, :]
-    return q, k, v
+    cu = [int(c) for c in ops["cu_seqlens"]]
+    n = q.shape[0]
+    seg = np.zeros(n, dtype=np.int64)
+    for s, (a, b) in enumerate(zip(cu, cu[1:])):
+        seg[a:b] = s
+    ks = np.repeat(np.asarray(ops["k_scales"], np.float64), head_dim, axis=1)[seg]
+    vs = np.repeat(np.asarray(ops["v_scales"], np.float64), head_dim, axis=1)[seg]
+    return q, tab[ops["k_codes"]] * ks, tab[ops["v_codes"]] * vs
 
 
 def attention_fp8(q, k, v, cu_seqlens, n_heads: int, head_dim: int, causal: bool = False,
@@ -249,7 +269,7 @@ def attention_fp8(q, k, v, cu_seqlens, n_heads: int, head_dim: int, causal: bool
     operands with exact probabilities.  Returns the operands' codes and
     scales, o (float64 [rows][H*Dh]) and o_abs, the same attention of |v|
     (sum_k P_k |v_k| / sum_k P_k, the weight of the probability-rounding bound)."""
-    ops = attention_fp8_operands(q, k, v, n_heads, head_dim)
+    ops = attention_fp8_operands(q, k, v, n_heads, head_dim, cu_seqlens)
     qd, kd, vd = dequantize_attention_operands(ops, n_heads, head_dim)
     o = attention(qd, kd, vd, cu_seqlens, n_heads, head_dim, causal, scale, rows)
     o_abs = attention(qd, kd, np.abs(vd), cu_seqlens, n_heads, head_dim, causal, scale, rows)

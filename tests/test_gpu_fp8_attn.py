@@ -59,8 +59,8 @@ def _views(jav, ws, n, n_seqs, H):
     k8 = ws[lay["k8"]:lay["k8"] + n * ld8].view(n, ld8)
     vt = ws[lay["vt"]:lay["vt"] + H * 128 * ld_vt].view(H * 128, ld_vt)
     sq = ws[lay["sq"]:lay["sq"] + 4 * H * n].view(torch.float32).view(H, n)
-    sk = ws[lay["sk"]:lay["sk"] + 4 * H].view(torch.float32)
-    sv = ws[lay["sv"]:lay["sv"] + 4 * H].view(torch.float32)
+    sk = ws[lay["sk"]:lay["sk"] + 4 * H * n_seqs].view(torch.float32).view(n_seqs, H)
+    sv = ws[lay["sv"]:lay["sv"] + 4 * H * n_seqs].view(torch.float32).view(n_seqs, H)
     return dict(q8=q8, k8=k8, vt=vt, sq=sq, sk=sk, sv=sv)
 
 
@@ -106,8 +106,8 @@ def _run(jav, q_h, k_h, v_h, cu, H, causal, rows=None, heads=None, label="", che
         np.testing.assert_array_equal(views["k8"][:, ct].cpu().numpy(), r["k_codes"])
         sq = views["sq"].cpu().numpy()[heads][:, qrows].T
         np.testing.assert_array_equal(sq, r["q_scales"][qrows])
-        np.testing.assert_array_equal(views["sk"].cpu().numpy()[heads], r["k_scales"])
-        np.testing.assert_array_equal(views["sv"].cpu().numpy()[heads], r["v_scales"])
+        np.testing.assert_array_equal(views["sk"].cpu().numpy()[:, heads], r["k_scales"])
+        np.testing.assert_array_equal(views["sv"].cpu().numpy()[:, heads], r["v_scales"])
         vt = views["vt"].cpu().numpy()
         for i, h in enumerate(heads):
             for s in range(n_seqs):
@@ -149,7 +149,7 @@ def test_fp8_attention_several_tiles_and_peaky_scores(jav):
 
 def test_fp8_attention_workspace_reuse_rescales(jav):
     """A second prepare into the same workspace with 1000x smaller k and v
-    recomputes the per-head scales from zero (no stale maximum)."""
+    recomputes the per-(segment, head) scales from zero (no stale maximum)."""
     import torch
     n, H = 200, 2
     cu = [0, 77, 200]
@@ -173,7 +173,7 @@ def test_fp8_attention_workspace_reuse_rescales(jav):
 def test_fp8_attention_full_shape(jav, variant):
     """58,758 tokens, 40 heads: the operands and o of heads 0, 17 and 39 on
     sampled rows (heads are independent: q's scales are per row and head, k's
-    and v's per head)."""
+    and v's per segment and head)."""
     wl = synth.WORKLOADS["varlen" if variant.startswith("varlen") else "full"]
     n, H = wl.n_tokens, wl.n_heads
     cu = list(wl.expected_cu_seqlens) if variant.startswith("varlen") else [0, n]

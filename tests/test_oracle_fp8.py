@@ -273,22 +273,29 @@ def test_quantize_tensor_scale_codes_and_zero():
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_attention_of_grid_operands_is_the_plain_attention(causal):
     """Operands on the e4m3 grid with q's power-of-two scale varying per
-    (token, head) row and k's, v's per head: quantization is lossless, so the
-    FP8 attention equals the plain one.  Quantizing q per head, or k or v per
-    row, would put non-power-of-two scales on these rows and fail."""
+    (token, head) row and k's, v's per (segment, head), each (segment, head)
+    block holding one +-448 * scale element: quantization is lossless, so the
+    FP8 attention equals the plain one.  The second segment's k and v scales
+    are 3/4 of the first's: a scale over the whole pack (one per head) would
+    put 0.75 m, off the e4m3 grid for most grid values m, on its codes and
+    fail, as would quantizing q per head or k, v per row."""
     rng = np.random.Generator(np.random.PCG64(11))
     n, hh, dh = 40, 2, 16
     cu = [0, 17, 40]
     q = _grid_rows(rng, n * hh, dh, rng.integers(-9, -4, n * hh)).reshape(n, hh * dh)
     k = np.empty((n, hh * dh))
     v = np.empty((n, hh * dh))
+    want = {"k": np.zeros((2, hh), np.float32), "v": np.zeros((2, hh), np.float32)}
     for h in range(hh):
         cols = slice(h * dh, (h + 1) * dh)
-        for t, e in ((k, -7 + h), (v, -6 - h)):
-            blk = _grid_rows(rng, n, dh, np.full(n, e))
-            blk[np.abs(blk) == 448.0 * 2.0 ** e] = 64.0 * 2.0 ** e   # one 448 per head only
-            blk[rng.integers(0, n), rng.integers(0, dh)] = -448.0 * 2.0 ** e
-            t[:, cols] = blk
+        for name, t, e in (("k", k, -7 + h), ("v", v, -6 - h)):
+            for s, (a, b) in enumerate(zip(cu, cu[1:])):
+                sc = 2.0 ** e * (1.0 if s == 0 else 0.75)
+                blk = _grid_rows(rng, b - a, dh, np.zeros(b - a))
+                blk[np.abs(blk) == 448.0] = 64.0                 # one 448 per block only
+                blk[rng.integers(0, b - a), rng.integers(0, dh)] = -448.0
+                t[a:b, cols] = blk * sc
+                want[name][s, h] = sc
     r = oracle.attention_fp8(q, k, v, cu, hh, dh, causal=causal)
     qd, kd, vd = oracle.dequantize_attention_operands(r, hh, dh)
     np.testing.assert_array_equal(qd, q)
@@ -296,8 +303,13 @@ def test_fp8_attention_of_grid_operands_is_the_plain_attention(causal):
     np.testing.assert_array_equal(vd, v)
     ref = oracle.attention(q, k, v, cu, hh, dh, causal=causal)
     np.testing.assert_allclose(r["o"], ref, rtol=1e-12, atol=1e-15)
-    assert np.array_equal(r["k_scales"], np.float32([2.0 ** -7, 2.0 ** -6]))
-    assert np.array_equal(r["v_scales"], np.float32([2.0 ** -6, 2.0 ** -7]))
+    assert np.array_equal(r["k_scales"], want["k"])
+    assert np.array_equal(r["v_scales"], want["v"])
+    # the same operands quantized with one scale per head over the whole pack
+    # are not lossless: the reading per segment is what the equality checks
+    whole = oracle.attention_fp8_operands(q, k, v, hh, dh)
+    _, kw, vw = oracle.dequantize_attention_operands(whole, hh, dh)
+    assert not (np.array_equal(kw, k) and np.array_equal(vw, v))
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -336,7 +348,7 @@ def test_fp8_attention_per_head_scaling():
     v2[:, dh:2 * dh] *= 8.0
     b = oracle.attention_fp8(q, k, v2, cu, hh, dh)
     np.testing.assert_array_equal(a["v_codes"], b["v_codes"])
-    assert b["v_scales"][1] == 8 * a["v_scales"][1]
+    assert np.array_equal(b["v_scales"][:, 1], 8 * a["v_scales"][:, 1])
     np.testing.assert_allclose(b["o"][:, dh:2 * dh], 8 * a["o"][:, dh:2 * dh], rtol=1e-12)
     np.testing.assert_array_equal(b["o"][:, :dh], a["o"][:, :dh])
     np.testing.assert_array_equal(b["o"][:, 2 * dh:], a["o"][:, 2 * dh:])
@@ -359,8 +371,8 @@ def test_fp8_block_with_fp8_attention_and_zero_queries_averages_v(causal):
     """With W_q = 0 (no bias) every key gets the same weight, so the FP8
     attention half's o is, per head, the mean of v's per-head dequantized codes
     over the query's keys (its segment, or the segment's prefix when causal):
-    checks that the half hands its own v, the segments and the per-head scale
-    (over all tokens) to the attention."""
+    checks that the half hands its own v, the segments and the per-(segment,
+    head) scale to the attention."""
     x, table, mod, pos, wq, wo, _, _ = _lossless_block(81, d=16, h=2, n=14, with_bias=False)
     codes, scales = wq
     codes = codes.copy()
@@ -372,10 +384,11 @@ def test_fp8_block_with_fp8_attention_and_zero_queries_averages_v(causal):
     assert not f8["q"].any()
     tab = oracle.e4m3_table()
     vd = np.empty_like(f8["v"])
-    for h in range(2):
-        cols = slice(8 * h, 8 * h + 8)
-        c, s = oracle.quantize_tensor(f8["v"][:, cols])
-        vd[:, cols] = tab[c] * np.float64(s)
+    for a, b in zip(cu, cu[1:]):
+        for h in range(2):
+            cols = slice(8 * h, 8 * h + 8)
+            c, s = oracle.quantize_tensor(f8["v"][a:b, cols])
+            vd[a:b, cols] = tab[c] * np.float64(s)
     for a, b in zip(cu, cu[1:]):
         for i in range(a, b):
             keys = slice(a, i + 1 if causal else b)
@@ -395,3 +408,26 @@ def test_fp8_block_with_fp8_attention_and_zero_values():
     assert not f8["v"].any() and not f8["o"].any()
     np.testing.assert_allclose(f8["out"], x + table[mod, 2, :] * b_o[None, :], rtol=1e-12,
                                atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_does_not_depend_on_what_else_is_packed(causal):
+    """Two requests packed together get exactly the FP8 attention each gets alone,
+    although the second one's keys and values are ten times larger (with one k or
+    v scale per head over the whole pack, the first request's codes would follow
+    the second's magnitude)."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    hh, dh = 2, 8
+    reqs = []
+    for n_r, mag in ((13, 1.0), (21, 10.0)):
+        q = rng.standard_normal((n_r, hh * dh))
+        reqs.append((q, rng.standard_normal((n_r, hh * dh)) * mag,
+                     rng.standard_normal((n_r, hh * dh)) * mag))
+    pack = [np.concatenate([r[i] for r in reqs]) for i in range(3)]
+    cu = [0, 13, 34]
+    both = oracle.attention_fp8(*pack, cu, hh, dh, causal=causal)
+    for (a, b), r in zip(zip(cu, cu[1:]), reqs):
+        alone = oracle.attention_fp8(*r, [0, b - a], hh, dh, causal=causal)
+        np.testing.assert_allclose(both["o"][a:b], alone["o"], rtol=1e-13, atol=1e-15)
+        np.testing.assert_array_equal(both["k_codes"][a:b], alone["k_codes"])
+        np.testing.assert_array_equal(both["v_codes"][a:b], alone["v_codes"])
