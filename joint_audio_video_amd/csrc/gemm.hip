@@ -23,8 +23,8 @@
 // Workgroup tile 256x256x64, four waves in a 2x2 arrangement, each owning a
 // 128x128 sub-tile as 4x4 MFMA blocks (256 accumulators per lane, held in the
 // AGPR half of the register file).  A and B tiles are staged through LDS
-// (double-buffered, 128 KB) by buffer loads that write straight into LDS,
-// with an XOR swizzle of the 16-byte chunk index so the rows an MFMA fragment
+// (double-buffered, 128 KB): global loads into registers a step ahead, then
+// LDS writes, with an XOR swizzle of the 16-byte chunk index so the rows an MFMA fragment
 // read touches spread over the banks.  The LDS has 64 four-byte banks, so a
 // 16-byte read is served 16 lanes at a time; a tile row is 128 bytes, so
 // those 16 rows must land on 16 distinct 16-byte slots of a 256-byte sweep,
@@ -33,9 +33,22 @@
 // ([rows][K]), so every fragment is one 16-byte LDS read.
 // With one wave per SIMD nothing else hides latency, so each k-step is laid
 // out by hand as 16 fenced groups of four independent MFMAs; the fragment
-// reads of the next sub-step and the next tile's global loads ride in the
-// groups' shadows (the loads in the first half, so they land before the
-// step's closing barrier).
+// reads of the next sub-step, one LDS write of the next tile and one global
+// load of the tile after it ride in each group's shadow.  Loading through
+// registers gives every global load a full step to land; loads that wrote
+// straight into LDS (buffer_load ... lds) had to wait for the barrier that
+// freed their stage and had half a step to a step.  Same-process A/B on the
+// block's shapes (58,758 tokens), four runs on different boxes: 0.5-3.8%
+// faster per product, about 2% on average (last run: QKV 7.46 -> 7.40 ms,
+// to_out.0 2.68 -> 2.65, ff.net.0.proj 10.23 -> 10.06, ff.net.2 9.83 ->
+// 9.77), bit-identical results.  Counters on the QKV product: the clock
+// under this load is about 1.72 GHz (0.72 of the 2.4 GHz peak rate is the
+// ceiling) and the MFMA pipe is busy 73% of cycles (70% before); the rest is
+// issue stalls behind memory instructions that one wave per SIMD cannot
+// cover.  Tried and slower: five 32-k LDS stages with direct-to-LDS loads
+// (two to three steps of cover, but 64-byte row segments cost more in the
+// load path than the cover gains), two staging register sets (two steps of
+// cover), and running the last sub-step after the barrier.
 // Tile order.  The hardware deals consecutive workgroups to the 8 XCDs (one
 // L2 each) round-robin, and an XCD runs about 32 of them at once (one per CU).
 // Workgroup pid = 8 j + x becomes the j-th tile of XCD x's contiguous share of
@@ -75,6 +88,7 @@ struct EpiArgs {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Tile of this workgroup (the XCD-blocked order above): linear index L in
 // groups of 4 M-tiles, each walked in chunks of 8 N-tiles, M fastest inside a
@@ -100,10 +114,7 @@ template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
     uint16_t* C, int64_t ldc, int M, int N, int K, EpiArgs ep) {
-  // Two LDS buffers per operand as distinct objects: with the k loop unrolled
-  // by two, every access names its buffer at compile time, so the compiler
-  // can tell the prefetch into one buffer from the fragment reads of the other
-  // and does not wait for the prefetch before reading.
+  // Two LDS stages per operand.
   __shared__ __attribute__((aligned(16))) uint16_t As0[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t As1[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * BK];
@@ -122,9 +133,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
   constexpr bool kRope = KIND == 3 || KIND == 4;
 
-  // Global -> LDS with buffer_load_dwordx4 ... lds: lane slot s = 256*i + tid
-  // of a tile lands at LDS element 8*s, i.e. row s/8, physical chunk s%8.
-  // The swizzle is applied on the global side: that slot holds logical chunk
+  // Global -> registers -> LDS: lane slot s = 256*i + tid of a tile is a
+  // 16-byte global load that is written to LDS element 8*s, i.e. row s/8,
+  // physical chunk s%8 (so each wave's LDS write is 1 KB contiguous).  The
+  // swizzle is applied on the global side: that slot holds logical chunk
   // (s%8) ^ ((row>>1) & 7).  For this thread the row is 32*i + tid/8 and the
   // logical chunk (tid&7) ^ ((tid>>4)&7) for every i.  Rows past M (N) are
   // clamped to the last valid row: their results are never stored.  Offsets
@@ -144,37 +156,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     aoff[i] = ((uint32_t)min(32 * i + lrow, rows_a - 1) * (uint32_t)lda + lchunk * 8) * 2u;
     boff[i] = ((uint32_t)min(32 * i + lrow, rows_b - 1) * (uint32_t)K + lchunk * 8) * 2u;
   }
-  // One 16-byte load of slot i (0..15: A rows 32i.., then B) into the stage buffers.
-  auto load1 = [&](uint16_t* adst, uint16_t* bdst, int k0, int i) {
-    if (i < 8)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, adst + (256 * i + 64 * wave) * 8, 16, aoff[i],
-                                               k0 * 2, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, bdst + (256 * (i - 8) + 64 * wave) * 8, 16,
-                                               boff[i - 8], k0 * 2, 0, 0);
+  // Slot i (0..15: A rows 32i.., then B): its global load, and its write
+  // into an LDS stage.
+  auto gload = [&](int k0, int i) -> uint4 {
+    const i32x4 v = i < 8 ? __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i], k0 * 2, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b128(rb, boff[i - 8], k0 * 2, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
   };
-  auto issue = [&](uint16_t* adst, uint16_t* bdst, int k0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) load1(adst, bdst, k0, i);
+  auto lput = [&](uint16_t* adst, uint16_t* bdst, int i, uint4 v) {
+    uint16_t* d = i < 8 ? adst + (256 * i + tid) * 8 : bdst + (256 * (i - 8) + tid) * 8;
+    *reinterpret_cast<uint4*>(d) = v;
+  };
+  // LDS barrier: orders this workgroup's LDS writes and reads (waits only for
+  // this wave's LDS operations, not for its global loads in flight).
+  auto lds_barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
   f32x16 acc[4][4];
   const f32x16 zero16 = {};
 
-  // One k-step of BK: multiply from (as, bs) while the next step's tile is
-  // loaded into (an, bn).  The step is written as 16 fenced groups of 4
-  // independent MFMAs; after each come 2 fragment reads for the next
-  // sub-step and, in the first 8 groups, 2 of the 16 global loads, so every
-  // read and load issues while an MFMA runs and the compiler cannot regroup
-  // them (left alone it sinks the reads next to their uses and bunches the
-  // loads, exposing both latencies).
+  // Pipeline.  Step t multiplies LDS stage t%2.  Tile t+1 waits in the
+  // staging registers st[] (loaded during step t-1); step t writes it into
+  // the idle stage (t+1)%2, slot by slot, and reloads each slot with tile t+2
+  // right after writing it, so every global load has one full step to land
+  // (loads that wrote straight into LDS could only be issued after the
+  // barrier freeing their stage and had half a step to a step).  The step is
+  // written as 16 fenced groups of four independent MFMAs; after each come
+  // the 2 fragment reads of the next sub-step and one slot's LDS write and
+  // reload, so reads, writes and loads issue in an MFMA's shadow and the
+  // compiler cannot regroup them.
   const int nk = K / BK;
   auto frag = [&](const uint16_t* base, int row, int ks) {
     return *reinterpret_cast<const bf16x8*>(&base[row * BK + swz(row, 2 * ks + g) * 8]);
   };
+  uint4 st[16];
   auto k_step = [&](const uint16_t* as, const uint16_t* bs, uint16_t* an, uint16_t* bn, int kt,
                     bool first) {
-    const int kload = min(kt + 1, nk - 1) * BK;   // last step: reload into the idle buffer
+    const int kload = min(kt + 2, nk - 1) * BK;   // past the end: reload the last tile
     bf16x8 af[4], bfr[4], an_[4], bn_[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) af[mb] = frag(as, wm * 128 + mb * 32 + l32, 0);
@@ -194,10 +215,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
           an_[mb] = frag(as, wm * 128 + mb * 32 + l32, ks + 1);
           bn_[mb] = frag(bs, wn * 128 + mb * 32 + l32, ks + 1);
         }
-        if (ks < 2) {                   // the 16 loads: two per group, first half
-          load1(an, bn, kload, 2 * (4 * ks + mb));
-          load1(an, bn, kload, 2 * (4 * ks + mb) + 1);
-        }
+        const int i = 4 * ks + mb;
+        lput(an, bn, i, st[i]);
+        st[i] = gload(kload, i);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ks + 1 < BK / 16) {
@@ -208,13 +228,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue(As0, Bs0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st[i] = gload(0, i);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lput(As0, Bs0, i, st[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st[i] = gload(min(1, nk - 1) * BK, i);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   k_step(As0, Bs0, As1, Bs1, 0, true);
   for (int kt = 1; kt < nk; kt += 2) {
     k_step(As1, Bs1, As0, Bs0, kt, false);
