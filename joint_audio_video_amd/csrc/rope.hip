@@ -16,6 +16,14 @@
 // read-modify-write of the same lines; an output may be the other input
 // (the rotated k may go to q's rows): every vector is loaded and stored by
 // the same thread, loads first.
+// Shape: one workgroup per token, thread t holding vector t of the token's q
+// and k rows, so the grid streams both arrays in address order with one
+// vector per thread and row.  On one MI355X, copies of a 601 MB array
+// sustain 81% of 8 TB/s with one 16-byte vector per thread against 71% with
+// eight (and 68-71% for rows of ten vectors per lane); at 58,758 tokens x 40
+// heads this form takes 396.5 us (75.9% of 8 TB/s) against 431.1 us (69.8%)
+// for two tokens per 128-thread workgroup with five vectors per thread and
+// row, bit-identical.  Rows wider than 1024 vectors keep that older form.
 #include "common.h"
 
 namespace dit {
@@ -46,9 +54,8 @@ __device__ __forceinline__ uint4 store_vec(const float* f, float) {
                     __float_as_uint(f[2]), __float_as_uint(f[3]));
 }
 
-// 128 threads (two tokens per workgroup at head_dim 128) and up to five
-// vectors per thread per row in one pass: measured best of 64-512 threads and
-// 3-10 vectors (70.1% of 8 TB/s against 67.8% for 256 threads).
+// Rows wider than 1024 vectors: 128 threads (two tokens per workgroup at
+// head_dim 128) and up to five vectors per thread per row in one pass.
 constexpr int kThreads = 128;
 
 // Workgroup = TOK tokens.  Thread tid handles vector tid + kThreads*j of each
@@ -147,6 +154,66 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const T* q, int64_t ld_q
   }
 }
 
+// Token-per-workgroup form (rows of at most 1024 vectors): thread t loads
+// vector t of the token's q row and of its k row, the first DH/2 threads
+// compute the token's angles into LDS, and thread t writes both rotated
+// vectors (loads before stores in one thread, so ko may be q).
+template <typename T, int DH>
+__global__ __launch_bounds__(1024) void rope_row_kernel(const T* q, int64_t ld_q, const T* k,
+                                                        int64_t ld_k, T* qo, int64_t ld_qo,
+                                                        T* ko, int64_t ld_ko,
+                                                        const int32_t* __restrict__ pos,
+                                                        int64_t n, int n_heads, int s_t, int s_h,
+                                                        Freqs fr) {
+  constexpr int P = DH / 2;
+  constexpr int E = VecE<T>::N;
+  __shared__ float2 cs[P];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nv = n_heads * DH / E;
+  const bool live = t < nv, has_k = k != nullptr;
+  const uint4 rq = live ? ld_stream(reinterpret_cast<const uint4*>(q + row * ld_q) + t)
+                        : make_uint4(0, 0, 0, 0);
+  const uint4 rk = live && has_k ? ld_stream(reinterpret_cast<const uint4*>(k + row * ld_k) + t)
+                                 : make_uint4(0, 0, 0, 0);
+  if (t < P) {
+    const int col = 2 * t;
+    const int axis = col < s_t ? 0 : (col < s_t + s_h ? 1 : 2);
+    const int32_t ps = pos[3 * row + axis];
+    float c = 1.0f, sn = 0.0f;
+    if (ps != 0) {
+      double sd, cd;
+      sincos((double)ps * fr.f[t], &sd, &cd);
+      sn = (float)sd;
+      c = (float)cd;
+    }
+    cs[t] = make_float2(c, sn);
+  }
+  __syncthreads();
+  if (!live) return;
+  const int p0 = ((t * E) % DH) / 2;
+  auto rotate = [&](const uint4& raw) {
+    float f[E];
+    load_vec(raw, f, T());
+#pragma unroll
+    for (int jj = 0; jj < E / 2; ++jj) {
+      const float2 r = cs[p0 + jj];
+      const float u = f[2 * jj], x = f[2 * jj + 1];
+      if (r.y != 0.0f) {
+        f[2 * jj] = fmaf(u, r.x, -x * r.y);
+        f[2 * jj + 1] = fmaf(u, r.y, x * r.x);
+      }
+    }
+    return store_vec(f, T());
+  };
+  const uint4 oq = rotate(rq);
+  if (has_k) {
+    const uint4 ok = rotate(rk);
+    st_stream(reinterpret_cast<uint4*>(ko + row * ld_ko) + t, ok);
+  }
+  st_stream(reinterpret_cast<uint4*>(qo + row * ld_qo) + t, oq);
+}
+
 struct RopeIO {
   const void* q;
   int64_t ld_q;
@@ -164,6 +231,14 @@ hipError_t launch_dh(const RopeIO& io, const int32_t* pos, int64_t n, int n_head
   constexpr int TOK = kThreads / (DH / 2);
   const int nv = n_heads * DH / VecE<T>::N;
   const int nj = (nv + kThreads - 1) / kThreads;     // vectors per thread per row
+  if (n == 0) return hipSuccess;
+  if (nv <= 1024) {
+    rope_row_kernel<T, DH><<<dim3((unsigned)n), dim3((unsigned)(64 * ((nv + 63) / 64))), 0, s>>>(
+        static_cast<const T*>(io.q), io.ld_q, static_cast<const T*>(io.k), io.ld_k,
+        static_cast<T*>(io.qo), io.ld_qo, static_cast<T*>(io.ko), io.ld_ko, pos, n, n_heads, s_t,
+        s_h, fr);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((n + TOK - 1) / TOK)), block(kThreads);
   const T* q = static_cast<const T*>(io.q);
   const T* k = static_cast<const T*>(io.k);
