@@ -19,10 +19,10 @@
 // ff.net.0.proj, ff.net.2); the feed-forward activation, tanh-form GELU, is a
 // reading (the pages name none).
 //
-// bf16 path: CDNA4 bf16 MFMA (v_mfma_f32_32x32x16_bf16), float32 accumulate.
+// bf16 path: CDNA4 bf16 MFMA (v_mfma_f32_16x16x32_bf16), float32 accumulate.
 // Workgroup tile 256x256x64, four waves in a 2x2 arrangement, each owning a
-// 128x128 sub-tile as 4x4 MFMA blocks (256 accumulators per lane, held in the
-// AGPR half of the register file).  A and B tiles are staged through LDS
+// 128x128 sub-tile as 8x8 MFMA blocks of 16x16 (256 accumulators per lane,
+// held in the AGPR half of the register file).  A and B tiles are staged through LDS
 // (double-buffered, 128 KB): global loads into registers a step ahead, then
 // LDS writes, with an XOR swizzle of the 16-byte chunk index so the rows an MFMA fragment
 // read touches spread over the banks.  The LDS has 64 four-byte banks, so a
@@ -32,9 +32,20 @@
 // differ by the 128-byte half).  Both operands are K-contiguous
 // ([rows][K]), so every fragment is one 16-byte LDS read.
 // With one wave per SIMD nothing else hides latency, so each k-step is laid
-// out by hand as 16 fenced groups of four independent MFMAs; the fragment
-// reads of the next sub-step, one LDS write of the next tile and one global
-// load of the tile after it ride in each group's shadow.  Loading through
+// out by hand as 32 fenced groups of four independent MFMAs; one fragment
+// read of the next sub-step rides in each group's shadow, and one LDS write
+// of the next tile and one global load of the tile after it in every second.
+// 16x16x32 rather than 32x32x16: the chip is power-limited under sustained
+// MFMA load, and the smaller instruction draws less power per FLOP.  A
+// register-only probe (independent MFMAs on every CU for tens of ms) keeps
+// the matrix pipe 93-95% busy with either, but at about 1.78 GHz with
+// 32x32x16 (69% of the 2.4 GHz peak rate) against 2.07 GHz with 16x16x32
+// (82%).  In this kernel the clock rises from 1.66 to 1.90 GHz while the
+// matrix pipe's busy share falls from 0.73 to 0.65 (memory latency is fixed
+// in time, so it costs more cycles, and a step issues twice the MFMAs).  Net,
+// in two same-process A/B runs on two boxes (rotated order, medians of six
+// rounds): QKV -1.2% / +1.4%, to_out.0 -1.6% / -1.5%, ff.net.0.proj -2.0% /
+// -0.2%, ff.net.2 -0.7% / -0.6% in time, bit-identical results.  Loading through
 // registers gives every global load a full step to land; loads that wrote
 // straight into LDS (buffer_load ... lds) had to wait for the barrier that
 // freed their stage and had half a step to a step.  Same-process A/B on the
@@ -129,7 +140,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, g = lane >> 5;
 
   constexpr bool kRope = KIND == 3 || KIND == 4;
 
@@ -175,54 +185,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  f32x16 acc[4][4];
-  const f32x16 zero16 = {};
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 acc[8][8];   // [token block][feature block], 16 x 16 each
+  const f32x4 zero4 = {};
+  const int l16 = lane & 15, q4 = lane >> 4;
 
   // Pipeline.  Step t multiplies LDS stage t%2.  Tile t+1 waits in the
   // staging registers st[] (loaded during step t-1); step t writes it into
   // the idle stage (t+1)%2, slot by slot, and reloads each slot with tile t+2
-  // right after writing it, so every global load has one full step to land
-  // (loads that wrote straight into LDS could only be issued after the
-  // barrier freeing their stage and had half a step to a step).  The step is
-  // written as 16 fenced groups of four independent MFMAs; after each come
-  // the 2 fragment reads of the next sub-step and one slot's LDS write and
-  // reload, so reads, writes and loads issue in an MFMA's shadow and the
-  // compiler cannot regroup them.
+  // right after writing it, so every global load has one full step to land.
+  // The products are v_mfma_f32_16x16x32_bf16 (two 32-deep sub-steps per
+  // step, 8 x 8 blocks per wave): under a sustained load on this chip they
+  // keep the matrix pipe at 81% of the peak rate against 69% for
+  // 32x32x16 (a register-only probe, one launch of each filling every CU for
+  // tens of milliseconds).  Each sub-step is 16 fenced groups of four
+  // independent MFMAs; after each come one fragment read of the next
+  // sub-step and, after every second group, one slot's LDS write and reload.
   const int nk = K / BK;
+  // 16 rows x 32 k: lane (row l16, k chunk 4 ks + q4) of sub-step ks.
   auto frag = [&](const uint16_t* base, int row, int ks) {
-    return *reinterpret_cast<const bf16x8*>(&base[row * BK + swz(row, 2 * ks + g) * 8]);
+    return *reinterpret_cast<const bf16x8*>(&base[row * BK + swz(row, 4 * ks + q4) * 8]);
   };
   uint4 st[16];
   auto k_step = [&](const uint16_t* as, const uint16_t* bs, uint16_t* an, uint16_t* bn, int kt,
                     bool first) {
     const int kload = min(kt + 2, nk - 1) * BK;   // past the end: reload the last tile
-    bf16x8 af[4], bfr[4], an_[4], bn_[4];
+    bf16x8 af[8], bfr[8], an_[8], bn_[8];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) af[mb] = frag(as, wm * 128 + mb * 32 + l32, 0);
+    for (int tb = 0; tb < 8; ++tb) af[tb] = frag(as, wm * 128 + tb * 16 + l16, 0);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(bs, wn * 128 + nb * 32 + l32, 0);
+    for (int fb = 0; fb < 8; ++fb) bfr[fb] = frag(bs, wn * 128 + fb * 16 + l16, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 32; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int gi = 0; gi < 16; ++gi) {
+        const int tb = gi >> 1, fb0 = (gi & 1) * 4;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              bfr[nb], af[mb], (first && ks == 0) ? zero16 : acc[mb][nb], 0, 0, 0);
-        if (ks + 1 < BK / 16) {
-          // reads for sub-step ks+1: A block mb and B block mb
-          an_[mb] = frag(as, wm * 128 + mb * 32 + l32, ks + 1);
-          bn_[mb] = frag(bs, wn * 128 + mb * 32 + l32, ks + 1);
+        for (int f = 0; f < 4; ++f)
+          acc[tb][fb0 + f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              bfr[fb0 + f], af[tb], (first && ks == 0) ? zero4 : acc[tb][fb0 + f], 0, 0, 0);
+        if (ks + 1 < BK / 32) {
+          if (gi < 8) an_[gi] = frag(as, wm * 128 + gi * 16 + l16, ks + 1);
+          else bn_[gi - 8] = frag(bs, wn * 128 + (gi - 8) * 16 + l16, ks + 1);
         }
-        const int i = 4 * ks + mb;
-        lput(an, bn, i, st[i]);
-        st[i] = gload(kload, i);
+        if (gi & 1) {
+          const int i = 8 * ks + (gi >> 1);
+          lput(an, bn, i, st[i]);
+          st[i] = gload(kload, i);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (ks + 1 < BK / 16) {
+      if (ks + 1 < BK / 32) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
           af[i] = an_[i];
           bfr[i] = bn_[i];
         }
@@ -246,102 +262,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     if (kt + 1 < nk) k_step(As0, Bs0, As1, Bs1, kt + 1, false);
   }
 
-  // RoPE (kinds 3, 4): the (t, h, w) positions of this lane's four rows, as
-  // floats (held across the k loop they would cost registers it needs).
-  float rpos[4][3];
-  // the half-wave bit again, from the lane id (kept from before the k loop it
-  // is one more register through the loop)
-  const int ge = kRope ? (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5)
+  // the lane's quarter again, from the lane id (kept from before the k loop
+  // it is one more register through the loop)
+  const int qe = kRope ? (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 4)
                        : 0;
-  if constexpr (kRope) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int row = min(m0 + wm * 128 + mb * 32 + l32, M - 1);
-#pragma unroll
-      for (int a = 0; a < 3; ++a) rpos[mb][a] = (float)ep.pos[3 * (int64_t)row + a];
-    }
-  }
 
-  // Epilogue.  The MFMAs computed C^T: acc[mb][nb][i] is token row
-  // m0 + wm*128 + mb*32 + l32 and feature column n0 + wn*128 + nb*32 +
-  // (i/4)*8 + g*4 + i%4, so each lane holds runs of 4 consecutive features of
-  // one token and stores them as 8 bytes.
+  // Epilogue.  The MFMAs computed C^T: acc[tb][fb][r] is token row
+  // m0 + wm*128 + tb*16 + l16 and feature column n0 + wn*128 + fb*16 +
+  // 4*q4 + r, so each lane holds 4 consecutive features of one token and
+  // stores them as 8 bytes.
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int row = m0 + wm * 128 + mb * 32 + l32;
+  for (int tb = 0; tb < 8; ++tb) {
+    const int row = m0 + wm * 128 + tb * 16 + l16;
     if (row >= M) continue;
     uint16_t* crow = C + (int64_t)row * ldc;
     const uint16_t* xrow = KIND == 1 ? ep.x + (int64_t)row * ep.ld_x : nullptr;
     const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
+    // RoPE (kinds 3, 4): this row's (t, h, w) positions as floats, loaded per
+    // token block after the k loop (held across it they would cost registers).
+    float rpos[3] = {0.0f, 0.0f, 0.0f};
+    if constexpr (kRope) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      // A 32-column block never straddles two planes (plane_cols is a multiple of 32).
+      for (int a = 0; a < 3; ++a) rpos[a] = (float)ep.pos[3 * (int64_t)row + a];
+    }
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb) {
+      // A 16-column block never straddles two planes (plane_cols is a multiple of 32).
       uint16_t* cbase = crow;
       int cshift = 0;
       bool rot = false;
       if ((KIND == 0 || kRope) && ep.plane_cols > 0) {
-        const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
+        const int plane = (n0 + wn * 128 + fb * 16) / ep.plane_cols;
         cbase = crow + plane * ep.plane_stride;
         cshift = plane * ep.plane_cols;
         rot = kRope && plane < 2;
       }
-      // The block's accumulators move to VGPRs here, one 16-value block at a
-      // time (left alone the compiler copies all 256 out of the AGPRs at once
-      // and spills).
-      f32x16 blk = acc[mb][nb];
+      const int col = n0 + wn * 128 + fb * 16 + 4 * q4;
+      if (col >= N) continue;
+      // The block's accumulators move to VGPRs here, one block at a time
+      // (left alone the compiler copies all 256 out of the AGPRs at once and
+      // spills).
+      f32x4 blk = acc[tb][fb];
       asm volatile("" : "+v"(blk));
+      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
-        if (col >= N) continue;
-        float v[4];
+      for (int e = 0; e < 4; ++e) v[e] = blk[e];
+      if (ep.bias) {
+        const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
+        v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
+      }
+      if constexpr (KIND == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = blk[4 * r + e];
-        if (ep.bias) {
-          const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
-          v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
-        }
-        if constexpr (KIND == 2) {
+        for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
+      }
+      if constexpr (KIND == 1) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
+        const float4 gt = *reinterpret_cast<const float4*>(grow + col);
+        v[0] = fmaf(gt.x, v[0], bf16lo(xv.x));
+        v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
+        v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
+        v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
+      }
+      if constexpr (kRope) {
+        // The lane's 4 columns are pairs j0 and j0 + 1 of one head.  Plane
+        // bases and n0 are multiples of the head width, so the column in the
+        // head is (fb*16) mod DH plus 4 qe: j0 is a constant plus 2 qe.
+        constexpr int DH = KIND == 3 ? 128 : 64;
+        if (rot) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
-        }
-        if constexpr (KIND == 1) {
-          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
-          const float4 gt = *reinterpret_cast<const float4*>(grow + col);
-          v[0] = fmaf(gt.x, v[0], bf16lo(xv.x));
-          v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
-          v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
-          v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
-        }
-        if constexpr (kRope) {
-          // The lane's 4 columns are pairs j0 and j0 + 1 of one head.  Plane
-          // bases and n0 are multiples of the head width, so the column in
-          // the head is (nb*32 + r*8) mod DH plus 4g: j0 is a constant plus 2g.
-          constexpr int DH = KIND == 3 ? 128 : 64;
-          if (rot) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int ja = (((nb * 32 + r * 8) & (DH - 1)) >> 1) + t;   // g = 0
-              const int jb = ja + 2;                                       // g = 1
-              const int j = ge ? jb : ja;
-              const float turns_per_pos = ge ? ep.rope_rev[jb] : ep.rope_rev[ja];
-              const int axis = j < ep.pair_h ? 0 : (j < ep.pair_w ? 1 : 2);
-              const float p = axis == 0 ? rpos[mb][0] : (axis == 1 ? rpos[mb][1] : rpos[mb][2]);
-              if (p != 0.0f) {
-                float turns = p * turns_per_pos;
-                turns -= rintf(turns);                      // exact: |turns| < 2^23
-                const float sn = __builtin_amdgcn_sinf(turns);
-                const float cs = __builtin_amdgcn_cosf(turns);
-                const float u = v[2 * t], w = v[2 * t + 1];
-                v[2 * t] = fmaf(u, cs, -w * sn);
-                v[2 * t + 1] = fmaf(u, sn, w * cs);
-              }
+          for (int t = 0; t < 2; ++t) {
+            const int j0 = (((fb * 16) & (DH - 1)) >> 1) + t;   // qe = 0
+            const int j = j0 + 2 * qe;
+            const float r0 = ep.rope_rev[j0], r1 = ep.rope_rev[j0 + 2];
+            const float r2 = ep.rope_rev[j0 + 4], r3 = ep.rope_rev[j0 + 6];
+            const float turns_per_pos = qe == 0 ? r0 : (qe == 1 ? r1 : (qe == 2 ? r2 : r3));
+            const int axis = j < ep.pair_h ? 0 : (j < ep.pair_w ? 1 : 2);
+            const float p = axis == 0 ? rpos[0] : (axis == 1 ? rpos[1] : rpos[2]);
+            if (p != 0.0f) {
+              float turns = p * turns_per_pos;
+              turns -= rintf(turns);                      // exact: |turns| < 2^23
+              const float sn = __builtin_amdgcn_sinf(turns);
+              const float cs = __builtin_amdgcn_cosf(turns);
+              const float u = v[2 * t], w = v[2 * t + 1];
+              v[2 * t] = fmaf(u, cs, -w * sn);
+              v[2 * t + 1] = fmaf(u, sn, w * cs);
             }
           }
         }
-        *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
+      *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
   }
 }
