@@ -9,14 +9,23 @@
 //
 // bf16 path (head_dim 128): flash-style forward on CDNA4 bf16 MFMA.
 //   * Workgroup = 8 waves = 256 queries of one (segment, head), two waves per
-//     SIMD; each wave owns 32 queries and walks the segment's keys in tiles
-//     of 64.
+//     SIMD; each wave owns 32 queries (two blocks of 16) and walks the
+//     segment's keys in tiles of 64.
 //   * The products are computed transposed, S^T = K Q^T and O^T = V^T P^T,
-//     with v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
-//     then holds one query column and 16 key (or head-dim) rows, so the
-//     softmax row max/sum is lane-local over 32 scores plus one exchange
-//     between lanes l and l^32 (v_permlane32_swap), and the online-softmax
-//     rescale of O is a per-lane scalar.
+//     with v_mfma_f32_16x16x32_bf16 (16 x 16 blocks, 32 deep).  Under a
+//     sustained MFMA load the chip is power-limited, and this instruction
+//     draws less power per FLOP than 32x32x16: the kernel runs at about
+//     2.09 GHz against 1.69 GHz, though its matrix pipe is busy a smaller
+//     share of the cycles (0.58 against 0.71), so it is 0-2% faster.  In the
+//     16x16 accumulator layout a lane holds, for each of its two queries, 4
+//     consecutive keys of every 16-key block; a query's 64 scores of a tile
+//     are spread over lanes l, l^16, l^32, l^48 (two lane exchanges give a
+//     row max; row sums stay per lane until the end), and the online-softmax
+//     rescale of O is a per-lane scalar per query.
+//   * P needs no lane exchange: the B operand of O^T += V^T P^T gives lane
+//     group g the key slots 8g .. 8g+7, mapped to keys 4g .. 4g+3 of one
+//     16-key block and of the next, which are the lane's own S^T values; the
+//     V^T fragment reads the same keys.
 //   * Q stays in registers for the whole key loop.  K tiles and V tiles (both
 //     [key][d], 256 B rows) are double-buffered in LDS (64 KB per workgroup)
 //     with XOR-swizzled 16-byte chunks, filled by buffer loads that write
@@ -99,11 +108,26 @@ constexpr int kTileLoads = KB * DH * 2 / 16 / kAttnThreads;   // 16-byte loads p
 // bank once and rows that a read serves together must sit in different chunks.
 // K: chunk ^ (row & 15): a 16-byte fragment read is served 16 lanes (16
 //    consecutive rows) at a time, which then touch 16 distinct chunks;
-// V: chunk ^ 4*(row & 3): a transposed 8-byte read is served 32 lanes at a time,
-//    four rows of 64 contiguous bytes each, which then touch four distinct
-//    64-byte quarters of the sweep.
+// V: chunk ^ 2*(row & 7): a transposed 8-byte read is served 32 lanes at a
+//    time, eight consecutive rows of 32 contiguous bytes each, which then
+//    touch eight distinct 32-byte slots of the sweep.
 __device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (4 * (row & 3)); }
+__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ (2 * (row & 7)); }
+
+constexpr int NKB2 = KB / 16;     // 16-key blocks per tile
+
+// Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one
+// query's scores), the same value in all four.
+__device__ __forceinline__ float quad_max(float v) {
+  v = half_swap_max(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v = half_swap_sum(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint16_t* __restrict__ k, int64_t ld_k,
@@ -139,19 +163,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
+  const int l16 = lane & 15, q4 = lane >> 4;
   const int qw0 = q0 + wave * 32;
-  const int qrow = qw0 + l32;
 
-  // Q^T fragments (B operand of S^T = K Q^T): lane (query l32, half g) holds
-  // d = 16*ks + 8*g .. +7.
-  bf16x8 qf[DH / 16];
-  {
-    const uint16_t* qp = q + (int64_t)qrow * ld_q + h * DH + g * 8;
+  // Q^T fragments (B operand of S^T = K Q^T, 16x16x32): lane (query l16 of
+  // query block qb, k group q4) holds d = 32*ds + 8*q4 .. +7.
+  bf16x8 qf[2][DH / 32];
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
-      uint4 r = qrow < seg1 ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, r);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw0 + qb * 16 + l16;
+    const uint16_t* qp = q + (int64_t)qrow * ld_q + h * DH + q4 * 8;
+#pragma unroll
+    for (int ds = 0; ds < DH / 32; ++ds) {
+      uint4 r = qrow < seg1 ? *reinterpret_cast<const uint4*>(qp + ds * 32) : make_uint4(0, 0, 0, 0);
+      qf[qb][ds] = __builtin_bit_cast(bf16x8, r);
     }
   }
 
@@ -190,35 +215,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
                                                voff[i], (int)(tile * v_tstep), 0, 0);
   };
 
-  // V^T fragment reads: 16-lane group t = lane/16 covers d = 32db + 16(t&1) + j
-  // and lane half g = t>>1; source lane i = 4k' + q points at key row
-  // base + k' (+8 for the second read), d column 32db + 16(t&1) + 4q, where
-  // base = 32b + 16u + 4g for PV step s = 2b + u.
-  const int tq = lane & 15, kk = tq >> 2, qq = tq & 3, t1 = (lane >> 4) & 1;
-  // The XOR swizzles distribute over these lane bits, so every fragment
-  // address is one of a few per-lane bases plus a compile-time offset.
-  // V: logical chunk 4db + x (x = 2t1 + q1) of row 4g + kk + ... lands at
-  // physical chunk 4(db ^ kk) + x.
-  int v_lane_off[DH / 32];
+  // K fragment (A operand, 16 keys x 32 d) of key block kb and d step ds:
+  // lane (key l16, k group q4) reads row 16 kb + l16, logical chunk 4 ds + q4,
+  // physical chunk (4 ds + q4) ^ l16.
+  int k_lane_off[DH / 32];
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
-    v_lane_off[db] = (4 * g + kk) * DH + 32 * (db ^ kk) + 16 * t1 + 4 * qq;
-  // K: chunk (2ks + g) ^ (l32 & 15) of row l32 = 2(ks ^ (w >> 1)) + (w & 1)
-  // with w = g ^ (l32 & 15).
-  int k_lane_off[DH / 16];
+  for (int ds = 0; ds < DH / 32; ++ds) k_lane_off[ds] = l16 * DH + ((4 * ds + q4) ^ l16) * 8;
+  // V^T fragment (A operand of O^T += V^T P^T, 16 d x 32 key slots) of d
+  // block db and key step ks: lane group q4 holds slots 8 q4 .. 8 q4 + 7 =
+  // keys 32 ks + 4 q4 + k, then 32 ks + 16 + 4 q4 + k (k < 4), the keys its
+  // own S^T accumulators hold, so P needs no lane exchange.  Two transposed
+  // reads; lane 4k' + qq of the group points at key row 4 q4 + k' (plus
+  // 32 ks, plus 16 for the second read), d = 16 db + 4 qq, whose physical
+  // chunk under c ^ 2 (row & 7) is 2 (db ^ rr) + (qq >> 1) with rr = row & 7.
+  int v_lane_off[DH / 16];
   {
-    const int w = g ^ (l32 & 15);
+    const int vrow = 4 * q4 + (l16 >> 2), rr = vrow & 7;
 #pragma unroll
-    for (int j = 0; j < DH / 16; ++j) k_lane_off[j] = l32 * DH + 16 * (j ^ (w >> 1)) + 8 * (w & 1);
+    for (int db = 0; db < DH / 16; ++db) v_lane_off[db] = vrow * DH + 16 * (db ^ rr) + 4 * (l16 & 3);
   }
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 oacc[DH / 32];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  f32x4 oacc[DH / 16][2];
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
+  for (int db = 0; db < DH / 16; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
-  const f32x16 zero16 = {};
+    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 zero4 = {};
 
   // Ping-pong: the two waves sharing a SIMD (w and w + kWaves/2) are half a
   // phase apart.  In phase t every wave runs PV of tile t-1 and S^T of tile t;
@@ -228,113 +251,134 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   // keeps the matrix pipe fed first).  Phase t reads K(t) and V(t-1) and
   // loads K(t+1) and V(t); the barrier ending it frees both buffers.
   const bool lagging = wave >= kWaves / 2;
-  f32x16 sacc[NKB];
-  bf16x8 pf[2 * NKB];
+  f32x4 sacc[NKB2][2];     // [key block of 16][query block of 16]
+  bf16x8 pf[KB / 32][2];   // [key step of 32][query block]
 
-  // S^T[key][query] of one tile: two 32-key blocks whose MFMA chains
-  // alternate.  Fragment (b, ks) sits at element k_lane_off[ks] + 4096*b.
+  // S^T[key][query] of one tile: 4 key blocks x 2 query blocks, 4 d steps.
   auto compute_s = [&](const uint16_t* ks_t) __attribute__((always_inline)) {
-    auto kfrag = [&](int b, int ks) {
-      return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ks] + 4096 * b);
+    auto kfrag = [&](int kb, int ds) {
+      return *reinterpret_cast<const bf16x8*>(ks_t + k_lane_off[ds] + 16 * DH * kb);
     };
-    bf16x8 kf[DH / 16][NKB];
+    bf16x8 kf[DH / 32][NKB2];
 #pragma unroll
-    for (int ks = 0; ks < kKAhead; ++ks)
+    for (int ds = 0; ds < kKAhead; ++ds)
 #pragma unroll
-      for (int b = 0; b < NKB; ++b) kf[ks][b] = kfrag(b, ks);
+      for (int kb = 0; kb < NKB2; ++kb) kf[ds][kb] = kfrag(kb, ds);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
+    for (int ds = 0; ds < DH / 32; ++ds) {
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][b], qf[ks], ks == 0 ? zero16 : sacc[b],
-                                                          0, 0, 0);
-      if (ks + kKAhead < DH / 16) {
+      for (int kb = 0; kb < NKB2; ++kb)
 #pragma unroll
-        for (int b = 0; b < NKB; ++b) kf[ks + kKAhead][b] = kfrag(b, ks + kKAhead);
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[ds][kb], qf[qb][ds], ds == 0 ? zero4 : sacc[kb][qb], 0, 0, 0);
+      if (ds + kKAhead < DH / 32) {
+#pragma unroll
+        for (int kb = 0; kb < NKB2; ++kb) kf[ds + kKAhead][kb] = kfrag(kb, ds + kKAhead);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Online softmax of tile j (scores in sacc) into the bf16 operand pf.
-  // Element e of block b is key kb + 32b + (e/4)*8 + 4g + e%4.
-  // The first key tile sets each row's reference max; later tiles exponentiate
-  // against it without taking their own max.  Only when a tile's probabilities
-  // could leave range (a lane's partial row sum above 2^kRefLog2, or not finite)
-  // does the rare path take that tile's max, move the reference and rescale
-  // O and l.  o = sum p v / sum p does not depend on the reference.
+  // Element r of sacc[kb][qb] is key kb0 + 16 kb + 4 q4 + r of query
+  // qw0 + 16 qb + l16; a query's 64 scores sit in lanes l16 + 16 q (q < 4),
+  // so a row max takes two lane exchanges and the row sums stay per lane
+  // until the end.  The first key tile sets each row's reference max; later
+  // tiles exponentiate against it without taking their own max.  Only when a
+  // tile's probabilities could leave range (a lane's partial row sum above
+  // 2^32, or not finite) does the rare path take that tile's max, move the
+  // reference and rescale O and l.  o = sum p v / sum p does not depend on the
+  // reference.
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int kb = seg0 + j * KB;
-    if ((kb + KB > seg1) || (causal && kb + KB - 1 > qw0)) {
+    const int kb0 = seg0 + j * KB;
+    if ((kb0 + KB > seg1) || (causal && kb0 + KB - 1 > qw0)) {
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
+      for (int kb = 0; kb < NKB2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
-          if (key >= seg1 || (causal && key > qrow)) sacc[b][e] = -INFINITY;
-        }
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb0 + 16 * kb + 4 * q4 + r;
+            const int qrow = qw0 + 16 * qb + l16;
+            if (key >= seg1 || (causal && key > qrow)) sacc[kb][qb][r] = -INFINITY;
+          }
     }
-    auto tile_max = [&]() __attribute__((always_inline)) {
-      float mx = sacc[0][0];
+    auto tile_max = [&](int qb) __attribute__((always_inline)) {
+      float mx = sacc[0][qb][0];
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
+      for (int kb = 0; kb < NKB2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[b][e]);
-      return half_swap_max(mx);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
+      return quad_max(mx);
     };
+    float rs[2];
     auto exps = [&]() __attribute__((always_inline)) {
-      const float nms = -(m_run == -INFINITY ? 0.0f : m_run) * scale_log2;
-      float rs = 0.0f;
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
+      for (int qb = 0; qb < 2; ++qb) {
+        const float nms = -(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]) * scale_log2;
+        float acc_rs = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, nms));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][e + 1], scale_log2, nms));
-          rs += p0 + p1;
-          pf[2 * b + (e >> 3)][e & 7] = (__bf16)p0;
-          pf[2 * b + (e >> 3)][(e & 7) + 1] = (__bf16)p1;
-        }
-      return rs;
+        for (int ks = 0; ks < KB / 32; ++ks)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], scale_log2, nms));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r + 1], scale_log2, nms));
+              acc_rs += p0 + p1;
+              pf[ks][qb][4 * hf + r] = (__bf16)p0;
+              pf[ks][qb][4 * hf + r + 1] = (__bf16)p1;
+            }
+        rs[qb] = acc_rs;
+      }
     };
-    if (j == 0) m_run = tile_max();
-    float rs = exps();
-    if (__builtin_amdgcn_ballot_w64(!(rs <= kRefBound)) != 0) {
-      const float m_new = fmaxf(m_run, tile_max());
-      const float alpha = m_run == -INFINITY ? 0.0f
-                                             : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      m_run = m_new;
-      rs = exps();
+    if (j == 0) {
+      m_run[0] = tile_max(0);
+      m_run[1] = tile_max(1);
     }
-    l_run += rs;
+    exps();
+    if (__builtin_amdgcn_ballot_w64(!(rs[0] <= kRefBound && rs[1] <= kRefBound)) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = fmaxf(m_run[qb], tile_max(qb));
+        const float alpha = m_run[qb] == -INFINITY ? 0.0f
+                                                   : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DH / 16; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[db][qb][e] *= alpha;
+        m_run[qb] = m_new;
+      }
+      exps();
+    }
+    l_run[0] += rs[0];
+    l_run[1] += rs[1];
   };
 
-  // O^T += V^T P^T.  MFMA i = 4s + db covers S^T block b = s/2, elements
-  // 8u..8u+7 (u = s%2): keys base..base+3 and base+8..base+11 with
-  // base = 32b + 16u + 4g, head-dim block db.
+  // O^T += V^T P^T: fragment i = 8 ks + db (key step ks, d block db) feeds
+  // the two query blocks' MFMAs.
   auto pv = [&](const uint16_t* vs_t) __attribute__((always_inline)) {
     auto vread = [&](int i) __attribute__((always_inline)) {
-      const int s = i >> 2, db = i & 3;
-      const int rows = 32 * (s >> 1) + 16 * (s & 1);
-      const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db] + rows * DH;
+      const int ks = i >> 3, db = i & 7;
+      const lds_u16* p = (const lds_u16*)vs_t + v_lane_off[db] + 32 * ks * DH;
       const v4i16 lo = lds_read_tr16(p);
-      const v4i16 hi = lds_read_tr16(p + 8 * DH);
+      const v4i16 hi = lds_read_tr16(p + 16 * DH);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    constexpr int kN = 2 * NKB * (DH / 32);
+    constexpr int kN = (KB / 32) * (DH / 16);
     bf16x8 vf[kN];
 #pragma unroll
     for (int i = 0; i < kVAhead; ++i) vf[i] = vread(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i >> 2], oacc[i & 3], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        oacc[i & 7][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], pf[i >> 3][qb],
+                                                                  oacc[i & 7][qb], 0, 0, 0);
       if (i + kVAhead < kN) vf[i + kVAhead] = vread(i + kVAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -362,22 +406,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     if (t + 1 <= nkt) phase(Ks1, Vs0, Ks0, Vs1, t + 1);
   }
 
-  const float l_tot = half_swap_sum(l_run);
-  const float inv = 1.0f / l_tot;
-  // log sum_j exp(s_j scale) = ln2 (m scale_log2 + log2 l), m the row's reference max
-  if (lse != nullptr && g == 0 && qrow < seg1)
-    lse[(int64_t)h * ld_lse + qrow] = (m_run * scale_log2 + log2f(l_tot)) * 0.69314718055994531f;
-  if (qrow < seg1) {
-    uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw0 + 16 * qb + l16;
+    const float l_tot = quad_sum(l_run[qb]);
+    const float inv = 1.0f / l_tot;
+    // log sum_j exp(s_j scale) = ln2 (m scale_log2 + log2 l), m the row's reference max
+    if (lse != nullptr && q4 == 0 && qrow < seg1)
+      lse[(int64_t)h * ld_lse + qrow] = (m_run[qb] * scale_log2 + log2f(l_tot)) * 0.69314718055994531f;
+    if (qrow < seg1) {
+      uint16_t* op = o + (int64_t)qrow * ld_o + h * DH;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d = 32 * db + qd * 8 + g * 4;
-        const uint2 w = make_uint2(pack_bf16x2(oacc[db][4 * qd + 0] * inv, oacc[db][4 * qd + 1] * inv),
-                                   pack_bf16x2(oacc[db][4 * qd + 2] * inv, oacc[db][4 * qd + 3] * inv));
+      for (int db = 0; db < DH / 16; ++db) {
+        const int d = 16 * db + 4 * q4;
+        const uint2 w = make_uint2(pack_bf16x2(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv),
+                                   pack_bf16x2(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv));
         *reinterpret_cast<uint2*>(op + d) = w;
       }
+    }
   }
 }
 
