@@ -262,24 +262,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     if (kt + 1 < nk) k_step(As0, Bs0, As1, Bs1, kt + 1, false);
   }
 
-  // the lane's quarter again, from the lane id (kept from before the k loop
-  // it is one more register through the loop)
-  const int qe = kRope ? (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 4)
-                       : 0;
+  // the lane's row and quarter again, from the lane id (kept from before the
+  // k loop they are registers held through it)
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int qe = lane_e >> 4, le16 = lane_e & 15;
 
   // Epilogue.  The MFMAs computed C^T: acc[tb][fb][r] is token row
   // m0 + wm*128 + tb*16 + l16 and feature column n0 + wn*128 + fb*16 +
   // 4*q4 + r, so each lane holds 4 consecutive features of one token and
-  // stores them as 8 bytes.
+  // stores them as 8 bytes.  What depends on the column only is set up once
+  // for the tile: each feature block's plane (a 16-column block never
+  // straddles two: plane_cols is a multiple of 32), whether RoPE rotates it,
+  // and the lane's RoPE pair frequencies and axes.  (The bias stays a load
+  // per block: held from here, the compiler issues those loads before the k
+  // loop and spills.)
+  const int ncol0 = n0 + wn * 128;   // wave-uniform
+  int64_t fb_off[8];                 // element offset of the block's plane: p (plane_stride - plane_cols)
+  bool fb_rot[8];
+#pragma unroll
+  for (int fb = 0; fb < 8; ++fb) {
+    fb_off[fb] = 0;
+    fb_rot[fb] = false;
+    if ((KIND == 0 || kRope) && ep.plane_cols > 0) {
+      const int plane = (ncol0 + fb * 16) / ep.plane_cols;
+      fb_off[fb] = (int64_t)plane * (ep.plane_stride - ep.plane_cols);
+      fb_rot[fb] = kRope && plane < 2;
+    }
+  }
+  const bool has_bias = ep.bias != nullptr;
+  // RoPE (kinds 3, 4): the lane's 4 columns of block fb are pairs j and j + 1
+  // of a head, j = 8 (fb mod DH/16) + 2 qe (plane bases and n0 are multiples
+  // of the head width); slot jj = 2 (fb mod DH/16) + t holds pair j + t.
+  constexpr int kRopeDH = KIND == 4 ? 64 : 128;
+  constexpr int kNJ = kRope ? kRopeDH / 8 : 1;
+  float rrev[kNJ];
+  int rax[kNJ];
+#pragma unroll
+  for (int jj = 0; jj < kNJ; ++jj) {
+    rrev[jj] = 0.0f;
+    rax[jj] = 0;
+    if constexpr (kRope) {
+      const int j0 = 8 * (jj >> 1) + (jj & 1);   // qe = 0
+      const float r0 = ep.rope_rev[j0], r1 = ep.rope_rev[j0 + 2];
+      const float r2 = ep.rope_rev[j0 + 4], r3 = ep.rope_rev[j0 + 6];
+      rrev[jj] = qe == 0 ? r0 : (qe == 1 ? r1 : (qe == 2 ? r2 : r3));
+      const int j = j0 + 2 * qe;
+      rax[jj] = j < ep.pair_h ? 0 : (j < ep.pair_w ? 1 : 2);
+    }
+  }
+
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb) {
-    const int row = m0 + wm * 128 + tb * 16 + l16;
+    const int row = m0 + wm * 128 + tb * 16 + le16;
     if (row >= M) continue;
     uint16_t* crow = C + (int64_t)row * ldc;
     const uint16_t* xrow = KIND == 1 ? ep.x + (int64_t)row * ep.ld_x : nullptr;
     const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
-    // RoPE (kinds 3, 4): this row's (t, h, w) positions as floats, loaded per
-    // token block after the k loop (held across it they would cost registers).
+    // RoPE: this row's (t, h, w) positions as floats, loaded per token block
+    // after the k loop (held across it they would cost registers).
     float rpos[3] = {0.0f, 0.0f, 0.0f};
     if constexpr (kRope) {
 #pragma unroll
@@ -287,17 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     }
 #pragma unroll
     for (int fb = 0; fb < 8; ++fb) {
-      // A 16-column block never straddles two planes (plane_cols is a multiple of 32).
-      uint16_t* cbase = crow;
-      int cshift = 0;
-      bool rot = false;
-      if ((KIND == 0 || kRope) && ep.plane_cols > 0) {
-        const int plane = (n0 + wn * 128 + fb * 16) / ep.plane_cols;
-        cbase = crow + plane * ep.plane_stride;
-        cshift = plane * ep.plane_cols;
-        rot = kRope && plane < 2;
-      }
-      const int col = n0 + wn * 128 + fb * 16 + 4 * q4;
+      const int col = ncol0 + fb * 16 + 4 * qe;
       if (col >= N) continue;
       // The block's accumulators move to VGPRs here, one block at a time
       // (left alone the compiler copies all 256 out of the AGPRs at once and
@@ -307,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = blk[e];
-      if (ep.bias) {
+      if (has_bias) {
         const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
         v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
       }
@@ -324,33 +354,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
       }
       if constexpr (kRope) {
-        // The lane's 4 columns are pairs j0 and j0 + 1 of one head.  Plane
-        // bases and n0 are multiples of the head width, so the column in the
-        // head is (fb*16) mod DH plus 4 qe: j0 is a constant plus 2 qe.
-        constexpr int DH = KIND == 3 ? 128 : 64;
-        if (rot) {
+        if (fb_rot[fb]) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int j0 = (((fb * 16) & (DH - 1)) >> 1) + t;   // qe = 0
-            const int j = j0 + 2 * qe;
-            const float r0 = ep.rope_rev[j0], r1 = ep.rope_rev[j0 + 2];
-            const float r2 = ep.rope_rev[j0 + 4], r3 = ep.rope_rev[j0 + 6];
-            const float turns_per_pos = qe == 0 ? r0 : (qe == 1 ? r1 : (qe == 2 ? r2 : r3));
-            const int axis = j < ep.pair_h ? 0 : (j < ep.pair_w ? 1 : 2);
-            const float p = axis == 0 ? rpos[0] : (axis == 1 ? rpos[1] : rpos[2]);
-            if (p != 0.0f) {
-              float turns = p * turns_per_pos;
-              turns -= rintf(turns);                      // exact: |turns| < 2^23
-              const float sn = __builtin_amdgcn_sinf(turns);
-              const float cs = __builtin_amdgcn_cosf(turns);
-              const float u = v[2 * t], w = v[2 * t + 1];
-              v[2 * t] = fmaf(u, cs, -w * sn);
-              v[2 * t + 1] = fmaf(u, sn, w * cs);
-            }
+            const int jj = 2 * (fb % (kRopeDH / 16)) + t;
+            const float p = rax[jj] == 0 ? rpos[0] : (rax[jj] == 1 ? rpos[1] : rpos[2]);
+            float turns = p * rrev[jj];
+            turns -= rintf(turns);                      // exact: |turns| < 2^23
+            const float sn = __builtin_amdgcn_sinf(turns);
+            const float cs = __builtin_amdgcn_cosf(turns);
+            const float u = v[2 * t], w = v[2 * t + 1];
+            // position 0 leaves the pair exactly as it is (a non-finite one too)
+            v[2 * t] = p != 0.0f ? fmaf(u, cs, -w * sn) : u;
+            v[2 * t + 1] = p != 0.0f ? fmaf(u, sn, w * cs) : w;
           }
         }
       }
-      *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
+      *reinterpret_cast<uint2*>(crow + fb_off[fb] + col) =
           make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
   }
@@ -486,7 +506,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
   }
 
   // Epilogue: acc^T as in the bf16 kernel, times the row scale of A and the
-  // column scales of W, then the bias and the epilogue kind.
+  // column scales of W, then the bias and the epilogue kind.  Each 32-column
+  // block's plane offset, p (plane_stride - plane_cols), is set up once.
+  int64_t nb_off[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    nb_off[nb] = 0;
+    if (KIND == 0 && ep.plane_cols > 0) {
+      const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
+      nb_off[nb] = (int64_t)plane * (ep.plane_stride - ep.plane_cols);
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int row = m0 + wm * 128 + mb * 32 + l32;
@@ -497,13 +527,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
     const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      uint16_t* cbase = crow;
-      int cshift = 0;
-      if (KIND == 0 && ep.plane_cols > 0) {
-        const int plane = (n0 + wn * 128 + nb * 32) / ep.plane_cols;
-        cbase = crow + plane * ep.plane_stride;
-        cshift = plane * ep.plane_cols;
-      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
@@ -527,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
           v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
           v[3] = fmaf(gt.w, v[3], bf16hi(xv.y));
         }
-        *reinterpret_cast<uint2*>(cbase + (col - cshift)) =
+        *reinterpret_cast<uint2*>(crow + nb_off[nb] + col) =
             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
