@@ -162,7 +162,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   const int q0 = seg0 + qt * QBLK;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wave-uniform in an SGPR: the lagging/leading branches are then scalar
+  // branches, with no exec-mask bookkeeping
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
   const int qw0 = q0 + wave * 32;
 
@@ -294,16 +297,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kb0 = seg0 + j * KB;
     if ((kb0 + KB > seg1) || (causal && kb0 + KB - 1 > qw0)) {
+      // Key kb0 + 16 kb + 4 q4 + r is visible to query row qrow when it lies
+      // below lim = min(seg1, qrow + 1 if causal): each element compares its
+      // constant part 16 kb + r with one per-lane value, lim - kb0 - 4 q4, and
+      // selects.  (Written as per-element conditions on the key, the compiler
+      // kept 64-bit compare masks for all 32 elements live, ran out of scalar
+      // registers and spilled them into vector lanes on every phase.)
 #pragma unroll
-      for (int kb = 0; kb < NKB2; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = qw0 + 16 * qb + l16;
+        const int lim = causal ? min(seg1, qrow + 1) : seg1;
+        const int rel = lim - kb0 - 4 * q4;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int kb = 0; kb < NKB2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kb0 + 16 * kb + 4 * q4 + r;
-            const int qrow = qw0 + 16 * qb + l16;
-            if (key >= seg1 || (causal && key > qrow)) sacc[kb][qb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r)
+            sacc[kb][qb][r] = 16 * kb + r < rel ? sacc[kb][qb][r] : -INFINITY;
+      }
     }
     auto tile_max = [&](int qb) __attribute__((always_inline)) {
       float mx = sacc[0][qb][0];

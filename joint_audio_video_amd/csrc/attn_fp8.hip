@@ -244,7 +244,8 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
   const int q0 = seg0 + qt * QBLK;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
@@ -387,13 +388,17 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void attn_fp8_kernel(
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kb = seg0 + j * KB;
     if ((kb + KB > seg1) || (causal && kb + KB - 1 > qw0)) {
+      // key kb + 32 b + 8 (e >> 2) + 4 g + (e & 3) is visible below lim =
+      // min(seg1, qrow + 1 if causal): compare the element's constant part
+      // with one per-lane value and select (per-element key conditions kept
+      // a 64-bit compare mask per element live in scalar registers)
+      const int lim = causal ? min(seg1, qrow + 1) : seg1;
+      const int rel = lim - kb - 4 * g;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb + 32 * b + (e >> 2) * 8 + g * 4 + (e & 3);
-          if (key >= seg1 || (causal && key > qrow)) sacc[b][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          sacc[b][e] = 32 * b + 8 * (e >> 2) + (e & 3) < rel ? sacc[b][e] : -INFINITY;
     }
     float mx = sacc[0][0];
 #pragma unroll
