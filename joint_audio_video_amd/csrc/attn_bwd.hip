@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
   }
   const int kb0 = seg0 + (int)blockIdx.x * BLKKV;
   if (kb0 >= seg1) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
   const int key = kb0 + 32 * wave + l32;
   RowFrag rf;
@@ -283,13 +284,17 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
                                                        rf.read(Vb, vrb, ks), pacc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool diag = causal && qbase + 32 * qb < key;   // some query of the block precedes this key
+      // some query of the block precedes some key of the wave (wave-uniform);
+      // then query qbase + 32 qb + 8 (e >> 2) + 4 g + (e & 3) of element e
+      // precedes this lane's key when its constant part is below rel
+      const bool diag = causal && qbase + 32 * qb < kb0 + 32 * wave + 31;
+      const int rel = key - qbase - 32 * qb - 4 * g;
       bf16x8 pf[2], sf[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 32 * qb + acc_row(e, g);
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -Ls[r]));
-        if (diag && qbase + r < key) p = 0.0f;
+        if (diag) p = 8 * (e >> 2) + (e & 3) < rel ? 0.0f : p;
         const float ds = p * (pacc[e] - Es[r]);
         pf[e >> 3][e & 7] = (__bf16)p;
         sf[e >> 3][e & 7] = (__bf16)ds;
@@ -361,7 +366,8 @@ __global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
   }
   const int q0 = seg0 + (int)blockIdx.x * BLKQ;
   if (q0 >= seg1) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
   const int qrow = q0 + 32 * wave + l32;
   const bool live = qrow < seg1;
@@ -425,13 +431,13 @@ __global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
     for (int b = 0; b < 2; ++b) {
       const int kb = kbase + 32 * b;
       const bool edge = kb + 32 > seg1 || (causal && kb + 31 > q0 + 32 * wave);
+      // key kb + 8 (e >> 2) + 4 g + (e & 3) of element e is visible below
+      // lim = min(seg1, qrow + 1 if causal): its constant part against rel
+      const int rel = (causal ? min(seg1, qrow + 1) : seg1) - kb - 4 * g;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], scale_log2, -lse2));
-        if (edge) {
-          const int kk = kb + acc_row(e, g);
-          if (kk >= seg1 || (causal && kk > qrow)) p = 0.0f;
-        }
+        if (edge) p = 8 * (e >> 2) + (e & 3) < rel ? p : 0.0f;
         sf[2 * b + (e >> 3)][e & 7] = (__bf16)(p * (pacc[b][e] - dlt));
       }
     }
