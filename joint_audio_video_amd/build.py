@@ -84,7 +84,7 @@ def resources() -> str:
     """Markdown table of the compiler's kernel-resource-usage remarks for every .hip source."""
     import re
     keys = ("VGPRs", "AGPRs", "ScratchSize [bytes/lane]", "Occupancy [waves/SIMD]",
-            "LDS Size [bytes/block]")
+            "LDS Size [bytes/block]", "SGPRs Spill")
     rows = []
     for src in SOURCES:
         if not src.endswith(".hip"):
@@ -103,11 +103,13 @@ def resources() -> str:
                 m = re.search(r"remark:\s+" + re.escape(k) + r": (\d+)", line)
                 if m and cur is not None:
                     cur[k] = m.group(1)
-    out = ["| source | kernel | VGPRs | AGPRs | scratch B/lane | LDS B/workgroup | waves/SIMD |",
-           "|---|---|---|---|---|---|---|"]
+    out = ["| source | kernel | VGPRs | AGPRs | scratch B/lane | SGPR spills | LDS B/workgroup | "
+           "waves/SIMD |",
+           "|---|---|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| {r['src']} | {r['name']} | {r.get('VGPRs', '')} | {r.get('AGPRs', '')} | "
-                   f"{r.get('ScratchSize [bytes/lane]', '')} | {r.get('LDS Size [bytes/block]', '')} | "
+                   f"{r.get('ScratchSize [bytes/lane]', '')} | {r.get('SGPRs Spill', '')} | "
+                   f"{r.get('LDS Size [bytes/block]', '')} | "
                    f"{r.get('Occupancy [waves/SIMD]', '')} |")
     return "\n".join(out)
 
