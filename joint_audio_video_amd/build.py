@@ -80,20 +80,25 @@ def _demangle(name: str) -> str:
     return out.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
-def resources() -> str:
-    """Markdown table of the compiler's kernel-resource-usage remarks for every .hip source."""
+def resource_rows(sources=None) -> list:
+    """The compiler's kernel-resource-usage remarks for the given .hip sources
+    (default: all), one dict per device kernel."""
     import re
     keys = ("VGPRs", "AGPRs", "ScratchSize [bytes/lane]", "Occupancy [waves/SIMD]",
             "LDS Size [bytes/block]", "SGPRs Spill")
-    rows = []
-    for src in SOURCES:
-        if not src.endswith(".hip"):
-            continue
+    srcs = [src for src in (SOURCES if sources is None else sources) if src.endswith(".hip")]
+
+    def remarks(src):
         cmd = [HIPCC, *COMMON_FLAGS, "-x", "hip", "--cuda-device-only", "-c",
                os.path.join(CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
-        r = subprocess.run(cmd, capture_output=True, text=True)
+        return subprocess.run(cmd, capture_output=True, text=True).stderr
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) or 1)) as ex:
+        outs = list(ex.map(remarks, srcs))
+    rows = []
+    for src, err in zip(srcs, outs):
         cur = None
-        for line in r.stderr.splitlines():
+        for line in err.splitlines():
             m = re.search(r"remark:\s+Function Name: (\S+)", line)
             if m:
                 cur = {"name": _demangle(m.group(1)), "src": src}
@@ -103,6 +108,12 @@ def resources() -> str:
                 m = re.search(r"remark:\s+" + re.escape(k) + r": (\d+)", line)
                 if m and cur is not None:
                     cur[k] = m.group(1)
+    return rows
+
+
+def resources() -> str:
+    """Markdown table of the compiler's kernel-resource-usage remarks for every .hip source."""
+    rows = resource_rows()
     out = ["| source | kernel | VGPRs | AGPRs | scratch B/lane | SGPR spills | LDS B/workgroup | "
            "waves/SIMD |",
            "|---|---|---|---|---|---|---|---|"]
