@@ -11,8 +11,8 @@
 // Three launches, no atomics, deterministic:
 //   * attn_delta_kernel: delta[h][row], sixteen lanes per (row, head).
 //   * attn_bwd_dkdv_kernel: a workgroup owns 256 keys of one (segment,
-//     head) (32 per wave, their K and V in registers; 8 waves, two per SIMD,
-//     share every streamed tile) and streams the
+//     head) (32 per wave, their K in registers, the block's V rows in LDS;
+//     8 waves, two per SIMD, share every streamed tile) and streams the
 //     segment's queries in tiles of 64 (q, do, lse, delta double-buffered in
 //     LDS).  Per tile a wave computes S = q k^T and dP = do v^T (rows =
 //     queries, so the 32x32 accumulator gives each lane one key column), P
@@ -25,8 +25,9 @@
 //     and streams the keys in tiles of 64 (triple-buffered):
 //     S^T = k q^T and dP^T = v do^T (rows = keys), dS^T, then
 //     dq^T += k^T dS^T, as the forward kernel computes O^T.
-// All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P
-// and dS are rounded to bf16 as MFMA operands.  Rows past a segment's end
+// All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation, their
+// LDS fragments read one or two products ahead; P and dS are rounded to bf16
+// as MFMA operands.  Rows past a segment's end
 // load as zeros (buffer range checks) and get P = 0.
 #include <cmath>
 
@@ -54,34 +55,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // LDS tiles are [row][d] with 256-byte rows; 16-byte chunk c of row r sits at
-// physical chunk c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1).  The tiles are
-// read both as rows (consecutive rows, one chunk each) and transposed (four
-// consecutive rows, two adjacent chunks each).  The LDS has 64 four-byte
-// banks and serves 16 lanes of a row read, 32 of a transposed read, per
-// cycle; f takes eight distinct values on any eight consecutive rows, so
-// each read is a 2-way conflict.  A conflict-free f (one-to-one on r & 15)
-// needs sixteen per-lane offsets instead of six, and the spills they cause
-// in these 256-register kernels cost more than the conflicts (measured: both
-// kernels 35-46% slower with conflicts at zero), so f stays.
-__device__ __forceinline__ int swz_f(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// physical chunk c ^ f(r), f(r) = (4 (r & 3) + ((r >> 1) & 3)) ^ 8 ((r >> 3) & 1).
+// The tiles are read both as rows (16 consecutive rows, one chunk each, per
+// cycle of a 16-byte read) and transposed (four consecutive rows, four
+// adjacent chunks, per cycle of an 8-byte transposing read).  The LDS has 64
+// four-byte banks, one sweep per 256-byte row, so a read is conflict-free
+// when its 16 chunks land on 16 distinct physical chunks: f is one-to-one on
+// r & 15 (row reads), and f >> 2 differs on every aligned four rows
+// (transposed reads).  f (r + 8) = f (r) ^ 8, so the second half of a
+// transposed fragment (rows + 8) is the first half's address with db ^ 2.
+__device__ __forceinline__ int swz_f(int row) {
+  return (4 * (row & 3) + ((row >> 1) & 3)) ^ (8 * ((row >> 3) & 1));
+}
 __device__ __forceinline__ int swz(int row, int c) { return c ^ swz_f(row); }
 
-// Fragment reads with per-lane bases and compile-time offsets (the swizzle
-// distributes over the lane bits, so every address is one of a few per-lane
-// bases plus a constant, which the LDS instructions take as an immediate).
+// Fragment reads.  Each lane keeps one byte offset per fragment kind; the
+// offset of a given k-slice or d block is that base with a few bits flipped
+// (the swizzle is an XOR on the chunk index, and row and tile bases have none
+// of those bits), computed next to its reads by one XOR in inline assembly.
+// Left to itself the compiler hoists every (offset, tile) combination out of
+// the tile loop into registers; at 256 registers that spilled, or left no
+// room to read fragments ahead of their products.  Tile bases and row blocks
+// go into the LDS instructions' immediate offset.
 //
-// Row fragment: lane (l32, g) reads tile row rb + l32 (rb a multiple of 8),
-// d = 16 ks + 8 g .. +7, i.e. logical chunk 2 ks + g; with ks = 4 a + j the
-// physical chunk is 8 a + ((2 j + g) ^ f(l32)).
+// Row fragment: lane (l32, g) reads tile row rb + l32 (rb a multiple of 16),
+// d = 16 ks + 8 g .. +7, i.e. logical chunk 2 ks + g, at physical chunk
+// (2 ks + g) ^ f(l32) = 2 ks ^ (g ^ f(l32)): byte offset base ^ 32 ks.
 struct RowFrag {
-  int off[4];
+  int base;   // bytes: row l32, chunk g ^ f(l32)
   __device__ void init(int lane) {
     const int l32 = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) off[j] = l32 * DH + 8 * ((2 * j + g) ^ swz_f(l32));
+    base = 2 * (l32 * DH + 8 * (g ^ swz_f(l32)));
   }
-  __device__ __forceinline__ bf16x8 read(const uint16_t* t, int rb, int ks) const {
-    return *reinterpret_cast<const bf16x8*>(t + off[ks & 3] + 64 * (ks >> 2) + rb * DH);
+  // byte offset of k-slice ks
+  __device__ __forceinline__ int at(int ks) const {
+    if (ks == 0) return base;
+    int r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(32 * ks), "v"(base));
+    return r;
+  }
+  __device__ __forceinline__ bf16x8 read_at(const uint16_t* t, int rb, int o) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(t) + o + rb * DH * 2);
   }
 };
 
@@ -90,22 +104,32 @@ struct RowFrag {
 // ds_read_b64_tr_b16.  In each 16-lane group (t = (lane >> 4) & 1) lane i
 // supplies row b0 + y, y = 4 g + (i >> 2), columns 32 db + 16 t + 4 (i & 3)
 // .. +3 and receives column 32 db + l32 of the four rows.  The column's
-// chunk 4 db + x (x = 2 t + ((i & 3) >> 1)) sits at 4 (db ^ (i >> 3)) +
-// (x ^ (f(y) & 3)) with f(y) = 2 (i >> 2) + g: 32 db + 32 (i >> 3) elements
-// (db even) or 32 db - 32 (i >> 3) (db odd), plus a lane part.
+// chunk 4 db + x (x = 2 t + ((i & 3) >> 1)) sits at physical chunk
+// 4 (db ^ (f(y) >> 2)) + (x ^ (f(y) & 3)): byte offset base ^ 64 db, and for
+// rows y + 8, where f flips bit 3, base ^ 64 (db ^ 2) one 8-row step on.
 struct TrFrag {
-  int off[2];
+  int base;   // bytes: the lane's half-chunk of row y for d block 0
   __device__ void init(int lane) {
     const int i = lane & 15, t = (lane >> 4) & 1, g = lane >> 5;
     const int y = 4 * g + (i >> 2), x = 2 * t + ((i & 3) >> 1);
-    const int base = y * DH + 8 * (x ^ (swz_f(y) & 3)) + 4 * (i & 1);
-    off[0] = base + 32 * (i >> 3);
-    off[1] = base - 32 * (i >> 3);
+    const int f = swz_f(y);
+    base = 2 * (y * DH + 8 * (x ^ (f & 3)) + 4 * (i & 1) + 32 * (f >> 2));
   }
-  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int b0, int db) const {
-    const lds_u16* p = (const lds_u16*)tile + off[db & 1] + 32 * db + b0 * DH;
+  __device__ __forceinline__ int xr(int c) const {
+    if (c == 0) return base;
+    int r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(c), "v"(base));
+    return r;
+  }
+  // byte offsets of d block db in the rows b0 + y and b0 + 8 + y
+  __device__ __forceinline__ int2 at(int db) const {
+    return make_int2(xr(64 * db), xr(64 * (db ^ 2)));
+  }
+  __device__ __forceinline__ bf16x8 read_at(const uint16_t* tile, int b0, int2 o) const {
+    const lds_u16* p = (const lds_u16*)((const char*)tile + o.x + b0 * DH * 2);
+    const lds_u16* p2 = (const lds_u16*)((const char*)tile + o.y + (b0 + 8) * DH * 2);
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * DH));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p2);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
@@ -187,10 +211,12 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
     uint16_t* __restrict__ dk, int64_t ld_dk, uint16_t* __restrict__ dv, int64_t ld_dv,
     const int32_t* __restrict__ cu, int64_t n, float scale, float scale_log2, int causal,
     int max_seqlen) {
-  __shared__ __attribute__((aligned(16))) uint16_t Qs0[TB * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs1[TB * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds0[TB * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds1[TB * DH];
+  // The streamed tiles are aligned so that they are laid out first, below
+  // 64 KB: their addresses then fit the LDS instructions' 16-bit offset.
+  __shared__ __attribute__((aligned(4096))) uint16_t Qs0[TB * DH];
+  __shared__ __attribute__((aligned(4096))) uint16_t Qs1[TB * DH];
+  __shared__ __attribute__((aligned(4096))) uint16_t Ds0[TB * DH];
+  __shared__ __attribute__((aligned(4096))) uint16_t Ds1[TB * DH];
   __shared__ float Ls0[TB], Ls1[TB], Es0[TB], Es1[TB];   // lse * log2(e), delta
   __shared__ __attribute__((aligned(16))) uint16_t Vb[BLKKV * DH];   // this block's V rows
 
@@ -276,13 +302,27 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 sacc = zero16, pacc = zero16;
+      // fragments of k-slice ks + 1 are read while the products of ks run
+      bf16x8 fq, fd, fv;
+      {
+        const int ro = rf.at(0);
+        fq = rf.read_at(Qs, 32 * qb, ro);
+        fd = rf.read_at(Ds, 32 * qb, ro);
+        fv = rf.read_at(Vb, vrb, ro);
+      }
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Qs, 32 * qb, ks), kf[ks], sacc, 0,
-                                                       0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Ds, 32 * qb, ks),
-                                                       rf.read(Vb, vrb, ks), pacc, 0, 0, 0);
+        bf16x8 nq = fq, nd = fd, nv = fv;
+        if (ks + 1 < DH / 16) {
+          const int ro = rf.at(ks + 1);
+          nq = rf.read_at(Qs, 32 * qb, ro);
+          nd = rf.read_at(Ds, 32 * qb, ro);
+          nv = rf.read_at(Vb, vrb, ro);
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, kf[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd, fv, pacc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        fq = nq; fd = nd; fv = nv;
       }
       // some query of the block precedes some key of the wave (wave-uniform);
       // then query qbase + 32 qb + 8 (e >> 2) + 4 g + (e & 3) of element e
@@ -300,17 +340,27 @@ __global__ __launch_bounds__(kThreadsKV, 1) void attn_bwd_dkdv_kernel(
         sf[e >> 3][e & 7] = (__bf16)ds;
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the next d block's transposed fragments are read during this one's products
+      bf16x8 td, tq;
+      {
+        const int2 to = tf.at(0);
+        td = tf.read_at(Ds, 32 * qb, to);
+        tq = tf.read_at(Qs, 32 * qb, to);
+      }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int b0 = 32 * qb + 16 * u;
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Ds, b0, db), pf[u], dva[db],
-                                                            0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Qs, b0, db), sf[u], dka[db],
-                                                            0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0; it < 2 * DH / 32; ++it) {
+        const int u = it >> 2, db = it & 3;
+        bf16x8 nd = td, nq = tq;
+        if (it + 1 < 2 * DH / 32) {
+          const int b1 = 32 * qb + 16 * ((it + 1) >> 2);
+          const int2 to = tf.at((it + 1) & 3);
+          nd = tf.read_at(Ds, b1, to);
+          nq = tf.read_at(Qs, b1, to);
         }
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(td, pf[u], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq, sf[u], dka[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        td = nd; tq = nq;
       }
     }
     if (t + 1 < nqt) put_ld(Ln, En, nxt);
@@ -415,12 +465,25 @@ __global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
     for (int b = 0; b < 2; ++b) {
       sacc[b] = zero16;
       pacc[b] = zero16;
+      // fragments of k-slice ks + 1 are read while the products of ks run
+      bf16x8 fk, fv;
+      {
+        const int ro = rf.at(0);
+        fk = rf.read_at(Ks, 32 * b, ro);
+        fv = rf.read_at(Vs, 32 * b, ro);
+      }
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Ks, 32 * b, ks), qf[ks],
-                                                          sacc[b], 0, 0, 0);
-        pacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.read(Vs, 32 * b, ks), df[ks],
-                                                          pacc[b], 0, 0, 0);
+        bf16x8 nk = fk, nv = fv;
+        if (ks + 1 < DH / 16) {
+          const int ro = rf.at(ks + 1);
+          nk = rf.read_at(Ks, 32 * b, ro);
+          nv = rf.read_at(Vs, 32 * b, ro);
+        }
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, qf[ks], sacc[b], 0, 0, 0);
+        pacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv, df[ks], pacc[b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fk = nk; fv = nv;
       }
     }
   };
@@ -444,12 +507,16 @@ __global__ __launch_bounds__(kThreadsQ, 1) void attn_bwd_dq_kernel(
   };
   // dq^T += K^T dS^T with tile t's K read transposed.
   auto accumulate = [&](const uint16_t* Ks) __attribute__((always_inline)) {
+    // K^T fragments are read two products ahead
+    bf16x8 t0 = tf.read_at(Ks, 0, tf.at(0)), t1 = tf.read_at(Ks, 0, tf.at(1));
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf.read(Ks, 16 * s, db), sf[s],
-                                                          dqa[db], 0, 0, 0);
+    for (int it = 0; it < 16; ++it) {
+      bf16x8 t2 = t1;
+      if (it + 2 < 16) t2 = tf.read_at(Ks, 16 * ((it + 2) >> 2), tf.at((it + 2) & 3));
+      dqa[it & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t0, sf[it >> 2], dqa[it & 3], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      t0 = t1; t1 = t2;
+    }
   };
 
   // Ping-pong between the two waves of a SIMD (w and w + 4), as in the

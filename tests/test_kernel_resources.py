@@ -27,8 +27,7 @@ HOT = [
     ("attn.hip", "dit::attn_bf16_kernel", 0),
     ("attn_fp8.hip", "dit::attn_fp8_kernel", 0),
     ("attn_bwd.hip", "dit::attn_bwd_dkdv_kernel", 0),
-    # one 8-byte value kept across the key loop (stored before it, reloaded after)
-    ("attn_bwd.hip", "dit::attn_bwd_dq_kernel", 12),
+    ("attn_bwd.hip", "dit::attn_bwd_dq_kernel", 0),
     ("gemm.hip", "dit::gemm_bf16_kernel<0>", 0),
     ("gemm.hip", "dit::gemm_bf16_kernel<1>", 0),
     ("gemm.hip", "dit::gemm_bf16_kernel<2>", 0),
