@@ -146,6 +146,45 @@ def test_attention_backward_full_shape(jav):
     assert r <= 1e-2
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_backward_varlen_pack(jav, causal):
+    """The 4-request pack (58,758 tokens in segments of 14,690 / 14,690 / 14,689 /
+    14,689, 40 heads): dq on rows at every segment's edges and spread through it against
+    the oracle; dk and dv through the softmax's invariants per segment and head (the
+    sum of dk over a segment's keys is 0, the sum of dv equals the sum of dout over its
+    queries); a second call gives the same bits."""
+    import torch
+    wl = synth.WORKLOADS["varlen"]
+    n, H = wl.n_tokens, wl.n_heads
+    cu = [int(c) for c in oracle.pack_layout([r.grid for r in wl.requests])["cu_seqlens"]]
+    ms = max(b - a for a, b in zip(cu, cu[1:]))
+    q, k, v, do = _qkvo(n, H, 1600 + int(causal))
+    cu_d = dev_int(np.asarray(cu), torch.int32)
+    print(f"attn backward varlen n={n} H={H} segs={len(cu) - 1} causal={causal}", flush=True)
+    qd, kd, vd, dod = (dev(a, "bf16") for a in (q, k, v, do))
+    o, lse = jav.attn_packed_lse(qd, kd, vd, cu_d, ms, H, 128, causal=causal)
+    dq, dk, dv = jav.attn_packed_backward(qd, kd, vd, o, dod, lse, cu_d, ms, H, 128,
+                                          causal=causal)
+    dq2, dk2, dv2 = jav.attn_packed_backward(qd, kd, vd, o, dod, lse, cu_d, ms, H, 128,
+                                             causal=causal)
+    _sync()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    edges = {r for a, b in zip(cu, cu[1:]) for r in (a, a + 1, b - 2, b - 1)}
+    rows = np.array(sorted(edges | set(range(0, n, 2999))), dtype=np.int64)
+    rq = oracle.attention_backward_rows(q, k, v, do, cu, H, 128, rows, causal=causal)
+    check_grad(host(dq[torch.from_numpy(rows).cuda()]), rq, f"varlen.c{int(causal)}.dq")
+    dk_h = dk.float().cpu().numpy().astype(np.float64)
+    dv_h = dv.float().cpu().numpy().astype(np.float64)
+    do_h = do.astype(np.float64)
+    for a, b in zip(cu, cu[1:]):
+        dk_sum, dk_abs = dk_h[a:b].sum(0), np.abs(dk_h[a:b]).sum(0)
+        assert np.all(np.abs(dk_sum) <= 1e-2 * dk_abs), (a, b)
+        r = rel_l2(dv_h[a:b].sum(0), do_h[a:b].sum(0))
+        print(f"  segment [{a}, {b}): max |sum dk| / sum |dk| "
+              f"{np.max(np.abs(dk_sum) / dk_abs):.2e}, sum dv vs sum dout rel_l2={r:.2e}", flush=True)
+        assert r <= 1e-2, (a, b, r)
+
+
 # ---------------------------------------------------------------------------
 # The attention half's backward
 # ---------------------------------------------------------------------------
