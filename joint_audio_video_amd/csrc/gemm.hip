@@ -273,9 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   // stores them as 8 bytes.  What depends on the column only is set up once
   // for the tile: each feature block's plane (a 16-column block never
   // straddles two: plane_cols is a multiple of 32), whether RoPE rotates it,
-  // and the lane's RoPE pair frequencies and axes.  (The bias stays a load
-  // per block: held from here, the compiler issues those loads before the k
-  // loop and spills.)
+  // and the lane's RoPE pair frequencies and axes.
   const int ncol0 = n0 + wn * 128;   // wave-uniform
   int64_t fb_off[8];                 // element offset of the block's plane: p (plane_stride - plane_cols)
   bool fb_rot[8];
@@ -311,20 +309,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     }
   }
 
+  // Every global input of the epilogue is loaded ahead of the stores that
+  // precede its use in program order (left in place, each load waits behind
+  // the previous block's stores, which may alias it, and its latency is
+  // paid once per 16x16 block): the bias of the lane's columns and the rows'
+  // modality once, the residual, gate and positions of token block tb + 1
+  // while block tb is computed.  A lane reads exactly the x elements it later
+  // writes, so an output written over x stays correct.
+  // (An opaque copy of the bias pointer keeps its loads after the k loop:
+  // issued before it, their registers are held through it and spill.)
+  const uint16_t* bias_p = ep.bias;
+  asm volatile("" : "+s"(bias_p));
+  // Loads past the last row or column read the last one instead (no
+  // branch around them; their values go unused).
+  uint2 bv[8];
+  if (has_bias) {
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb)
+      bv[fb] = *reinterpret_cast<const uint2*>(bias_p + min(ncol0 + fb * 16 + 4 * qe, N - 4));
+  }
+  int mrow[8];
+  if constexpr (KIND == 1) {
+#pragma unroll
+    for (int tb = 0; tb < 8; ++tb) mrow[tb] = ep.mod[min(m0 + wm * 128 + tb * 16 + le16, M - 1)];
+  }
+  constexpr int kNX = KIND == 1 ? 8 : 1;
+  uint2 xin[2][kNX];
+  float4 gin[2][kNX];
+  float rp[2][3];
+  auto load_tb = [&](int tb, int sl) __attribute__((always_inline)) {
+    const int row = min(m0 + wm * 128 + tb * 16 + le16, M - 1);
+    if constexpr (KIND == 1) {
+      const uint16_t* xrow = ep.x + (int64_t)row * ep.ld_x;
+      const float* grow = ep.gate + mrow[tb] * ep.gate_stride;
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) {
+        const int col = min(ncol0 + fb * 16 + 4 * qe, N - 4);
+        xin[sl][fb] = *reinterpret_cast<const uint2*>(xrow + col);
+        gin[sl][fb] = *reinterpret_cast<const float4*>(grow + col);
+      }
+    }
+    if constexpr (kRope) {
+#pragma unroll
+      for (int a = 0; a < 3; ++a) rp[sl][a] = (float)ep.pos[3 * (int64_t)row + a];
+    }
+  };
+  load_tb(0, 0);
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb) {
+    const int sl = tb & 1;
+    if (tb + 1 < 8) load_tb(tb + 1, sl ^ 1);
     const int row = m0 + wm * 128 + tb * 16 + le16;
     if (row >= M) continue;
     uint16_t* crow = C + (int64_t)row * ldc;
-    const uint16_t* xrow = KIND == 1 ? ep.x + (int64_t)row * ep.ld_x : nullptr;
-    const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
-    // RoPE: this row's (t, h, w) positions as floats, loaded per token block
-    // after the k loop (held across it they would cost registers).
-    float rpos[3] = {0.0f, 0.0f, 0.0f};
-    if constexpr (kRope) {
-#pragma unroll
-      for (int a = 0; a < 3; ++a) rpos[a] = (float)ep.pos[3 * (int64_t)row + a];
-    }
 #pragma unroll
     for (int fb = 0; fb < 8; ++fb) {
       const int col = ncol0 + fb * 16 + 4 * qe;
@@ -338,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = blk[e];
       if (has_bias) {
-        const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
+        const uint2 b = bv[fb];
         v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
       }
       if constexpr (KIND == 2) {
@@ -346,8 +383,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
       }
       if constexpr (KIND == 1) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
-        const float4 gt = *reinterpret_cast<const float4*>(grow + col);
+        const uint2 xv = xin[sl][fb];
+        const float4 gt = gin[sl][fb];
         v[0] = fmaf(gt.x, v[0], bf16lo(xv.x));
         v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
         v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
@@ -358,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int jj = 2 * (fb % (kRopeDH / 16)) + t;
-            const float p = rax[jj] == 0 ? rpos[0] : (rax[jj] == 1 ? rpos[1] : rpos[2]);
+            const float p = rax[jj] == 0 ? rp[sl][0] : (rax[jj] == 1 ? rp[sl][1] : rp[sl][2]);
             float turns = p * rrev[jj];
             turns -= rintf(turns);                      // exact: |turns| < 2^23
             const float sn = __builtin_amdgcn_sinf(turns);
