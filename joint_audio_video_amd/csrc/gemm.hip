@@ -554,25 +554,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
       nb_off[nb] = (int64_t)plane * (ep.plane_stride - ep.plane_cols);
     }
   }
+  // Global inputs are loaded ahead of the stores (as in the bf16 kernel):
+  // the column scales and bias of the lane's 16 column groups and every
+  // row's scale and modality once, then each row's residual and gate before
+  // any of that row's stores.  Past the last row or column the loads read
+  // the last one (their values go unused).
+  // (An opaque copy of the scale pointer keeps these loads after the k loop:
+  // issued before it, their registers are held through it and spill.)
+  const float* sw_p = sc.sw;
+  asm volatile("" : "+s"(sw_p));
+  float4 swv[4][4];
+  uint2 bv[4][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = min(n0 + wn * 128 + nb * 32 + r * 8 + g * 4, N - 4);
+      swv[nb][r] = *reinterpret_cast<const float4*>(sw_p + col);
+      if (ep.bias) bv[nb][r] = *reinterpret_cast<const uint2*>(ep.bias + col);
+    }
+  float sav[4];
+  int modv[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int rowc = min(m0 + wm * 128 + mb * 32 + l32, M - 1);
+    sav[mb] = sc.sa[rowc];
+    if constexpr (KIND == 1) modv[mb] = ep.mod[rowc];
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int row = m0 + wm * 128 + mb * 32 + l32;
-    if (row >= M) continue;
-    const float sa = sc.sa[row];
+    const float sa = sav[mb];
     uint16_t* crow = C + (int64_t)row * ldc;
-    const uint16_t* xrow = KIND == 1 ? ep.x + (int64_t)row * ep.ld_x : nullptr;
-    const float* grow = KIND == 1 ? ep.gate + ep.mod[row] * ep.gate_stride : nullptr;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
+      // the residual and gate of this 32-column group, before its stores
+      constexpr int kNX = KIND == 1 ? 4 : 1;
+      uint2 xin[kNX];
+      float4 gin[kNX];
+      if constexpr (KIND == 1) {
+        const uint16_t* xrow = ep.x + (int64_t)min(row, M - 1) * ep.ld_x;
+        const float* grow = ep.gate + modv[mb] * ep.gate_stride;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = min(n0 + wn * 128 + nb * 32 + r * 8 + g * 4, N - 4);
+          xin[r] = *reinterpret_cast<const uint2*>(xrow + col);
+          gin[r] = *reinterpret_cast<const float4*>(grow + col);
+        }
+      }
+      if (row >= M) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = n0 + wn * 128 + nb * 32 + r * 8 + g * 4;
         if (col >= N) continue;
-        const float4 sw = *reinterpret_cast<const float4*>(sc.sw + col);
+        const float4 sw = swv[nb][r];
         float v[4] = {acc[mb][nb][4 * r + 0] * sa * sw.x, acc[mb][nb][4 * r + 1] * sa * sw.y,
                       acc[mb][nb][4 * r + 2] * sa * sw.z, acc[mb][nb][4 * r + 3] * sa * sw.w};
         if (ep.bias) {
-          const uint2 b = *reinterpret_cast<const uint2*>(ep.bias + col);
+          const uint2 b = bv[nb][r];
           v[0] += bf16lo(b.x); v[1] += bf16hi(b.x); v[2] += bf16lo(b.y); v[3] += bf16hi(b.y);
         }
         if constexpr (KIND == 2) {
@@ -580,8 +619,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(
           for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
         }
         if constexpr (KIND == 1) {
-          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + col);
-          const float4 gt = *reinterpret_cast<const float4*>(grow + col);
+          const uint2 xv = xin[r];
+          const float4 gt = gin[r];
           v[0] = fmaf(gt.x, v[0], bf16lo(xv.x));
           v[1] = fmaf(gt.y, v[1], bf16hi(xv.x));
           v[2] = fmaf(gt.z, v[2], bf16lo(xv.y));
