@@ -299,13 +299,29 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_bwd_kernel(
   }
   const float m1 = wave_sum(a1) * inv_d, m2 = wave_sum(a2) * inv_d;
   if (lane == 0) stats[row] = make_float2(mean, rstd);
+  // Up to 10 vectors per lane (d_model 5,120) the row's dres vectors are all
+  // loaded before the first dx store: dx may be dres, so a load placed after
+  // a store waits for it and the row's latency is paid once per vector.
+  // (Past the row end the last vector is loaded instead; it is not stored.)
+  // Wider rows keep the loads in the loop: held, they would leave one wave
+  // per SIMD.
+  constexpr bool kAhead = NV <= 10;
+  uint4 rr[kAhead ? NV : 1];
+  if constexpr (kAhead) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      rr[i] = *(reinterpret_cast<const uint4*>(dres + row * ld_dres) + min(lane + 64 * i, nvec - 1));
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
     if (c >= nvec) continue;
     float xh[E], g[E], r[E];
     terms(i, xh, g);
-    unpack(*(reinterpret_cast<const uint4*>(dres + row * ld_dres) + c), r, uint16_t());
+    if constexpr (kAhead)
+      unpack(rr[i], r, uint16_t());
+    else
+      unpack(*(reinterpret_cast<const uint4*>(dres + row * ld_dres) + c), r, uint16_t());
 #pragma unroll
     for (int e = 0; e < E; ++e) r[e] += rstd * (g[e] - m1 - xh[e] * m2);
     *(reinterpret_cast<uint4*>(dx + row * ld_dx) + c) = pack(r, uint16_t());
