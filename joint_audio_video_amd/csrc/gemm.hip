@@ -314,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   // the previous block's stores, which may alias it, and its latency is
   // paid once per 16x16 block): the bias of the lane's columns and the rows'
   // modality once, the residual, gate and positions of token block tb + 1
-  // while block tb is computed.  A lane reads exactly the x elements it later
-  // writes, so an output written over x stays correct.
+  // while block tb is computed.  The x elements a lane uses are exactly the
+  // ones it later writes, so an output written over x stays correct.
   // (An opaque copy of the bias pointer keeps its loads after the k loop:
   // issued before it, their registers are held through it and spill.)
   const uint16_t* bias_p = ep.bias;
