@@ -31,6 +31,11 @@ HOT = [
     ("gemm.hip", "dit::gemm_bf16_kernel<0>", 0),
     ("gemm.hip", "dit::gemm_bf16_kernel<1>", 0),
     ("gemm.hip", "dit::gemm_bf16_kernel<2>", 0),
+    ("gemm.hip", "dit::gemm_bf16_kernel<3>", 0),
+    ("gemm.hip", "dit::gemm_fp8_kernel<0>", 0),
+    ("gemm.hip", "dit::gemm_fp8_kernel<1>", 0),
+    ("gemm.hip", "dit::gemm_fp8_kernel<2>", 0),
+    ("adaln.hip", "dit::adaln_bwd_kernel<10>", 0),
     ("adaln.hip", "dit::adaln_kernel<unsigned short, 10, 2, false>", 0),
     ("rope.hip", "dit::rope_row_kernel<unsigned short, 128>", 0),
 ]
